@@ -1,0 +1,225 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE layer library
+ * (libmoe.so).
+ *
+ * The layer: a sigmoid top-k router with a per-expert selection bias, per-
+ * expert token bucketing, a SwiGLU expert FFN over packed int4 / int8 / int2
+ * weights with fp32 per-row scales and int8 activations (exact int32 integer
+ * dot products, dequantisation on use), and a weighted combine with an
+ * always-on shared expert.
+ *
+ * Pages the operations come from:
+ *  [P-feat]  agentlenshq.com, "Colibri: running GLM-5.2 744B MoE on consumer
+ *            hardware", section "Key features": int8, packed int4 and packed
+ *            int2 kernels with per-row scales and dequantisation on use; int8
+ *            matmuls computed as integer dot products.
+ *  [P-mem]   same page, section "Memory split": shared experts stay resident;
+ *            a routed int4 expert is about 19 MB (three 6144 x 2048 matrices).
+ *  [P-load]  same page, section "Loading mechanism": a per-layer LRU keeps
+ *            experts resident; the next block is read while the current one
+ *            is computed.
+ *  [P-route] tech.takumi3488.com, "Trying colibri", self-test section: a
+ *            DeepSeek-V3-family router; section on the real 744B model:
+ *            hidden 6144, 256 experts per layer, top-8.
+ *  [P-moe]   remio.ai, "Colibri shows how to run GLM-5.2 on a low-spec PC",
+ *            section "How Colibri runs GLM-5.2": the router picks a few
+ *            feed-forward experts per token.
+ *  [P-dedup] same page, section "The RAM wall became a storage problem": an
+ *            expert requested by several batch positions is read once; an
+ *            expert's matrices are stored together and fetched in one go.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
+ *    unless the parameter name ends in _host. Arrays are row-major and
+ *    contiguous; device pointers must be 16-byte aligned.
+ *  - H (hidden) and I (expert intermediate) must be positive multiples of 64
+ *    and at most 8192. T (tokens) may be 0 (the call does nothing).
+ *  - Every call enqueues work on the context's stream and returns without
+ *    synchronising (unless stated); kernel faults surface at the caller's next
+ *    synchronisation. Invalid arguments are rejected before anything is
+ *    enqueued.
+ *  - Ownership: the caller owns every tensor it passes; the library never
+ *    frees caller memory. The library owns only the context's scratch memory
+ *    (grown on demand with hipMalloc, freed by moe_ctx_destroy) and pools.
+ *  - A context is bound to one device and one stream and is not thread-safe;
+ *    calls on one context must not overlap.
+ *  - Errors: every call returns a moe_status; on failure moe_last_error()
+ *    returns a thread-local description. No C++ exception crosses the ABI.
+ *
+ * Packed weight layout (bit-exact contract, [P-feat]): per-row symmetric
+ * absmax quantisation, qmax = 2^(bits-1)-1, scale s = max|w| / qmax (fp32),
+ * codes q = clamp(rint(w/s), -qmax, qmax) (round half to even); int8 codes
+ * are two's-complement bytes; int4 codes are nibbles q+8 with element 2i in
+ * the low nibble of byte i; int2 codes are 2-bit fields q+2 with element 4i+j
+ * in bits 2j..2j+1 of byte i. Rows are contiguous with no padding.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad argument (shape, pointer, alignment, value) */
+  MOE_ENOMEM = -2,       /* device or host allocation failed */
+  MOE_EHIP = -3,         /* a HIP runtime call failed (text in moe_last_error) */
+  MOE_EUNSUPPORTED = -4, /* valid but outside what the kernels handle */
+  MOE_EPOOL = -5,        /* expert pool cannot satisfy the request */
+  MOE_ETIMEOUT = -6      /* a bounded device-side wait gave up (see moe_ctx_check) */
+} moe_status;
+
+typedef struct moe_ctx moe_ctx;
+
+/* One expert's weights: device pointers, layout as above.
+ * gate, up: [I][H*bits/8]; down: [H][I*bits/8]; s_gate, s_up: [I]; s_down: [H]. */
+typedef struct {
+  const uint8_t *gate, *up, *down;
+  const float *s_gate, *s_up, *s_down;
+} moe_expert_w;
+
+/* Router configuration ([P-route], [P-moe]).
+ * n_experts: E routed experts (1..1024); top_k: k (1..min(E, 16));
+ * routed_scale: factor applied to the normalised weights (1.0 for plain
+ * normalisation); logits_in: 0 = the router computes logits from hidden
+ * states, 1 = the caller passes logits [T][E]. */
+typedef struct {
+  int n_experts;
+  int top_k;
+  float routed_scale;
+  int logits_in;
+} moe_router_cfg;
+
+/* ---------------------------------------------------------------------- */
+/* Context                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* Create a context on `device`. hip_stream: a hipStream_t to borrow (the
+ * caller keeps it alive), or NULL for the null stream. */
+moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out);
+/* Free the context's scratch memory. Waits for the stream first. */
+void moe_ctx_destroy(moe_ctx *ctx);
+/* Re-bind the context to another stream of the same device. */
+moe_status moe_ctx_set_stream(moe_ctx *ctx, void *hip_stream);
+/* Thread-local text of the last failure ("" if none). */
+const char *moe_last_error(void);
+int moe_abi_version(void);
+/* Synchronise the stream and report device-side errors recorded by earlier
+ * calls (a bounded wait that gave up -> MOE_ETIMEOUT). Clears the record. */
+moe_status moe_ctx_check(moe_ctx *ctx);
+
+/* One expert as a single contiguous block ([P-dedup]: an expert's matrices
+ * are stored together and fetched in one read): gate | up | down | s_gate |
+ * s_up | s_down, each part starting on a 256-byte boundary. Writes the six
+ * byte offsets to offsets_host[6] (nullable) and returns the block size in
+ * bytes, or 0 for invalid arguments (bits not in {8,4,2}, H or I not a
+ * positive multiple of 64). Host-only; enqueues nothing. At bits 4, H 6144,
+ * I 2048 the block is 18,915,328 bytes (the pages' "about 19 MB"). */
+size_t moe_expert_block_layout(int bits, int H, int I, size_t *offsets_host);
+
+/* ---------------------------------------------------------------------- */
+/* Quantisation ([P-feat])                                                */
+/* ---------------------------------------------------------------------- */
+
+/* Quantise and pack rows of w (fp32 [rows][cols]) at bits in {8,4,2}:
+ * packed uint8 [rows][cols*bits/8], scales fp32 [rows]. cols must be a
+ * positive multiple of 64. Bit-exact contract as in the header comment. */
+moe_status moe_quantize_rows(moe_ctx *ctx, int bits, const float *w, int64_t rows, int cols, uint8_t *packed,
+                             float *scales);
+
+/* Per-token int8 quantisation of hidden states: x fp32 [T][H] ->
+ * xq int8 [T][H], sx fp32 [T]; sx = max|x| / 127, xq = clamp(rint(x/sx)).
+ * A zero row gives sx = 0 and xq = 0. */
+moe_status moe_quantize_act_i8(moe_ctx *ctx, const float *x, int T, int H, int8_t *xq, float *sx);
+
+/* ---------------------------------------------------------------------- */
+/* Router ([P-route], [P-moe])                                            */
+/* ---------------------------------------------------------------------- */
+
+/* logits z = x w_router^T (x fp32 [T][H], w_router fp32 [E][H]; fp32
+ * arithmetic) or z = x when cfg->logits_in (x is fp32 [T][E], w_router
+ * ignored, H ignored). sig = 1/(1+exp(-z)); key = sig + bias[e] (bias fp32
+ * [E] or NULL); topk_idx int32 [T][k] = experts with the k largest keys in
+ * descending key order (equal keys: lower id first); topk_w fp32 [T][k] =
+ * routed_scale * sig / sum of the selected sig (the bias selects, it does not
+ * weight). */
+moe_status moe_router_topk(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x, const float *w_router,
+                           const float *bias, int T, int H, int32_t *topk_idx, float *topk_w);
+
+/* Per-expert bucketing ([P-dedup]): counts int32 [E]; offsets int32 [E+1]
+ * (exclusive prefix sums); perm int32 [T*k] = entries t*k+j grouped by
+ * expert, ascending (t, j) inside a group. Indices outside [0, E) are not
+ * counted and are reported by moe_ctx_check as MOE_EINVAL. */
+moe_status moe_bucket_tokens(moe_ctx *ctx, const int32_t *topk_idx, int T, int k, int E, int32_t *counts,
+                             int32_t *offsets, int32_t *perm);
+
+/* ---------------------------------------------------------------------- */
+/* Expert FFN ([P-feat], [P-mem], [P-dedup])                              */
+/* ---------------------------------------------------------------------- */
+
+/* For every token t and slot j < k: y_slots[t][j] = FFN_{e}(token t) with
+ * e = topk_idx[t][j]; if shared != NULL also y_slots[t][k] = FFN_shared(t).
+ * FFN(t): accg[i] = sum_h qg[i,h] xq[t,h] and accu likewise (exact int32);
+ * g = (float)accg * s_gate[i] * sx[t]; u likewise; a = silu(g) * u (fp32,
+ * silu(g) = g / (1 + exp(-g)) with exp by Cody-Waite reduction and a degree-7
+ * Taylor polynomial in fused multiply-adds); sa = max|a| / 127; aq =
+ * clamp(rint(a / sa)); accd[r] = sum_i qd[r,i] aq[i]; y[r] = (float)accd *
+ * s_down[r] * sa. Each expert's weights are streamed once per call for all
+ * the tokens routed to it.
+ *
+ * experts: DEVICE array [E] of moe_expert_w (the structs' members are device
+ * pointers). shared: HOST pointer to one moe_expert_w, or NULL.
+ * expert_bits: DEVICE uint8 [E] or NULL. When given, only experts whose
+ * entry equals this entry point's width are computed (slots of the others
+ * are left untouched), so a mixed-precision layer is one call per width.
+ * xq int8 [T][H], sx fp32 [T]: from moe_quantize_act_i8. topk_idx int32
+ * [T][k]. y_slots fp32 [T][k+1][H] (slot k is the shared expert's; it is
+ * written only when shared != NULL). */
+moe_status moe_expert_ffn_q4(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                             const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
+                             int T, int H, int I, int E, int k, float *y_slots);
+moe_status moe_expert_ffn_q8(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                             const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
+                             int T, int H, int I, int E, int k, float *y_slots);
+moe_status moe_expert_ffn_q2(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                             const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
+                             int T, int H, int I, int E, int k, float *y_slots);
+
+/* ---------------------------------------------------------------------- */
+/* Combine ([P-moe], [P-mem])                                             */
+/* ---------------------------------------------------------------------- */
+
+/* out fp32 [T][H] = (has_shared ? y_slots[t][k] : 0) + sum_{j<k}
+ * topk_w[t][j] * y_slots[t][j], accumulated in fp32 in that order.
+ * y_slots fp32 [T][k+1][H]. */
+moe_status moe_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, int T, int k, int H, int has_shared,
+                       float *out);
+
+/* ---------------------------------------------------------------------- */
+/* Test visibility                                                        */
+/* ---------------------------------------------------------------------- */
+
+/* Optional capture of the FFN's intermediates (all DEVICE pointers, each
+ * may be NULL). Pair index p = t*(k+1) + slot. accg, accu int32 [T*(k+1)][I];
+ * a fp32 [T*(k+1)][I]; aq int8 [T*(k+1)][I]; sa fp32 [T*(k+1)]; accd int32
+ * [T*(k+1)][H]. Passing NULL for dbg switches capture off. The pointers must
+ * stay valid until capture is switched off. */
+typedef struct {
+  int32_t *accg, *accu;
+  float *a;
+  int8_t *aq;
+  float *sa;
+  int32_t *accd;
+} moe_debug_bufs;
+moe_status moe_ctx_set_debug(moe_ctx *ctx, const moe_debug_bufs *dbg);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

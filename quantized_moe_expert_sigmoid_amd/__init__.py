@@ -1,0 +1,308 @@
+"""Python binding of libmoe.so, the MI355X (gfx950) routed-expert MoE layer.
+
+Argument marshalling only: every function here takes torch CUDA tensors,
+checks dtypes/shapes/devices, and calls the C entry point of the same name in
+``libmoe.so`` (declared in ``include/moe.h``). All arithmetic runs in the HIP
+kernels. If the library is missing or the device is not a gfx950 GPU the
+calls raise; there is no CPU fallback.
+
+PyTorch provides device memory and the stream: calls are enqueued on the
+torch current stream of the tensors' device at context creation (or on the
+stream passed to :class:`MoeCtx`).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+_lock = threading.Lock()
+_lib = None
+
+MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_EUNSUPPORTED, MOE_EPOOL, MOE_ETIMEOUT = 0, -1, -2, -3, -4, -5, -6
+_STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_EUNSUPPORTED",
+           -5: "MOE_EPOOL", -6: "MOE_ETIMEOUT"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class ExpertW(ctypes.Structure):
+    """moe_expert_w: six device pointers."""
+    _fields_ = [("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class RouterCfg(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int), ("top_k", ctypes.c_int), ("routed_scale", ctypes.c_float),
+                ("logits_in", ctypes.c_int)]
+
+
+class DebugBufs(ctypes.Structure):
+    _fields_ = [("accg", ctypes.c_void_p), ("accu", ctypes.c_void_p), ("a", ctypes.c_void_p),
+                ("aq", ctypes.c_void_p), ("sa", ctypes.c_void_p), ("accd", ctypes.c_void_p)]
+
+
+# name -> (restype, argtypes)
+_vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_SIGS = {
+    "moe_ctx_create": (_i32, [_i32, _vp, ctypes.POINTER(_vp)]),
+    "moe_ctx_destroy": (None, [_vp]),
+    "moe_ctx_set_stream": (_i32, [_vp, _vp]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_abi_version": (_i32, []),
+    "moe_ctx_check": (_i32, [_vp]),
+    "moe_expert_block_layout": (_sz, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "moe_quantize_rows": (_i32, [_vp, _i32, _vp, _i64, _i32, _vp, _vp]),
+    "moe_quantize_act_i8": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "moe_router_topk": (_i32, [_vp, ctypes.POINTER(RouterCfg), _vp, _vp, _vp, _i32, _i32, _vp, _vp]),
+    "moe_bucket_tokens": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "moe_expert_ffn_q4": (_i32, [_vp, _vp, ctypes.POINTER(ExpertW), _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                 _i32, _vp]),
+    "moe_expert_ffn_q8": (_i32, [_vp, _vp, ctypes.POINTER(ExpertW), _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                 _i32, _vp]),
+    "moe_expert_ffn_q2": (_i32, [_vp, _vp, ctypes.POINTER(ExpertW), _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                 _i32, _vp]),
+    "moe_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "moe_ctx_set_debug": (_i32, [_vp, ctypes.POINTER(DebugBufs)]),
+}
+
+
+def exported_names():
+    return list(_SIGS)
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -m quantized_moe_expert_sigmoid_amd.build` (no CPU fallback exists)")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+    return _lib
+
+
+def _ck(st: int):
+    if st != MOE_OK:
+        raise MoeError(st, lib().moe_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+    return t.data_ptr()
+
+
+class MoeCtx:
+    """moe_ctx bound to one device and one stream."""
+
+    def __init__(self, device: int = 0, stream: torch.cuda.Stream | None = None):
+        self.device = device
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+        self.stream = s
+        h = ctypes.c_void_p()
+        _ck(lib().moe_ctx_create(device, ctypes.c_void_p(s.cuda_stream), ctypes.byref(h)))
+        self.handle = h
+        self._dbg_keep = None
+
+    def close(self):
+        if self.handle:
+            lib().moe_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_stream(self, stream: torch.cuda.Stream):
+        _ck(lib().moe_ctx_set_stream(self.handle, ctypes.c_void_p(stream.cuda_stream)))
+        self.stream = stream
+
+    def check(self):
+        _ck(lib().moe_ctx_check(self.handle))
+
+    def set_debug(self, bufs: dict | None):
+        """bufs: dict with any of accg, accu, a, aq, sa, accd (device tensors) or None."""
+        if bufs is None:
+            _ck(lib().moe_ctx_set_debug(self.handle, None))
+            self._dbg_keep = None
+            return
+        d = DebugBufs(*[_ptr(bufs.get(n)) for n in ("accg", "accu", "a", "aq", "sa", "accd")])
+        self._dbg_keep = bufs
+        _ck(lib().moe_ctx_set_debug(self.handle, ctypes.byref(d)))
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def moe_expert_block_layout(bits: int, H: int, I: int):
+    offs = (ctypes.c_size_t * 6)()
+    n = lib().moe_expert_block_layout(bits, H, I, offs)
+    if n == 0:
+        raise MoeError(MOE_EINVAL, f"moe_expert_block_layout: bits {bits} H {H} I {I}")
+    return int(n), [int(o) for o in offs]
+
+
+def moe_quantize_rows(ctx: MoeCtx, bits: int, w: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor):
+    R, C = w.shape
+    _dev(w, torch.float32, "w")
+    _dev(packed, torch.uint8, "packed", (R, C * bits // 8))
+    _dev(scales, torch.float32, "scales", (R,))
+    _ck(lib().moe_quantize_rows(ctx.handle, bits, w.data_ptr(), R, C, packed.data_ptr(), scales.data_ptr()))
+    return packed, scales
+
+
+def moe_quantize_act_i8(ctx: MoeCtx, x: torch.Tensor, xq: torch.Tensor, sx: torch.Tensor):
+    T, H = x.shape
+    _dev(x, torch.float32, "x")
+    _dev(xq, torch.int8, "xq", (T, H))
+    _dev(sx, torch.float32, "sx", (T,))
+    _ck(lib().moe_quantize_act_i8(ctx.handle, x.data_ptr(), T, H, xq.data_ptr(), sx.data_ptr()))
+    return xq, sx
+
+
+def moe_router_topk(ctx: MoeCtx, x: torch.Tensor, w_router: torch.Tensor | None, bias: torch.Tensor | None, k: int,
+                    topk_idx: torch.Tensor, topk_w: torch.Tensor, routed_scale: float = 1.0,
+                    logits_in: bool = False, n_experts: int | None = None):
+    T = x.shape[0]
+    _dev(x, torch.float32, "x")
+    if logits_in:
+        E, H = x.shape[1], 0
+    else:
+        E, H = w_router.shape
+        _dev(w_router, torch.float32, "w_router", (E, x.shape[1]))
+    if n_experts is not None and n_experts != E:
+        raise ValueError("n_experts does not match the logits/router width")
+    if bias is not None:
+        _dev(bias, torch.float32, "bias", (E,))
+    _dev(topk_idx, torch.int32, "topk_idx", (T, k))
+    _dev(topk_w, torch.float32, "topk_w", (T, k))
+    cfg = RouterCfg(E, k, float(routed_scale), 1 if logits_in else 0)
+    _ck(lib().moe_router_topk(ctx.handle, ctypes.byref(cfg), x.data_ptr(),
+                              None if logits_in else w_router.data_ptr(), _ptr(bias), T, H,
+                              topk_idx.data_ptr(), topk_w.data_ptr()))
+    return topk_idx, topk_w
+
+
+def moe_bucket_tokens(ctx: MoeCtx, topk_idx: torch.Tensor, E: int, counts: torch.Tensor, offsets: torch.Tensor,
+                      perm: torch.Tensor):
+    T, k = topk_idx.shape
+    _dev(topk_idx, torch.int32, "topk_idx")
+    _dev(counts, torch.int32, "counts", (E,))
+    _dev(offsets, torch.int32, "offsets", (E + 1,))
+    _dev(perm, torch.int32, "perm", (T * k,))
+    _ck(lib().moe_bucket_tokens(ctx.handle, topk_idx.data_ptr(), T, k, E, counts.data_ptr(), offsets.data_ptr(),
+                                perm.data_ptr()))
+    return counts, offsets, perm
+
+
+def _ffn(name, ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E, y_slots):
+    T, k = topk_idx.shape
+    _dev(table, torch.int64, "experts table", (E, 6))
+    _dev(xq, torch.int8, "xq", (T, H))
+    _dev(sx, torch.float32, "sx", (T,))
+    _dev(topk_idx, torch.int32, "topk_idx")
+    _dev(y_slots, torch.float32, "y_slots", (T, k + 1, H))
+    if expert_bits is not None:
+        _dev(expert_bits, torch.uint8, "expert_bits", (E,))
+    sh = ctypes.byref(shared) if shared is not None else None
+    _ck(getattr(lib(), name)(ctx.handle, table.data_ptr(), sh, _ptr(expert_bits), xq.data_ptr(), sx.data_ptr(),
+                             topk_idx.data_ptr(), T, H, I, E, k, y_slots.data_ptr()))
+    return y_slots
+
+
+def moe_expert_ffn_q4(ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E, y_slots):
+    return _ffn("moe_expert_ffn_q4", ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E, y_slots)
+
+
+def moe_expert_ffn_q8(ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E, y_slots):
+    return _ffn("moe_expert_ffn_q8", ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E, y_slots)
+
+
+def moe_expert_ffn_q2(ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E, y_slots):
+    return _ffn("moe_expert_ffn_q2", ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E, y_slots)
+
+
+FFN_BY_BITS = {4: moe_expert_ffn_q4, 8: moe_expert_ffn_q8, 2: moe_expert_ffn_q2}
+
+
+def moe_combine(ctx: MoeCtx, y_slots: torch.Tensor, topk_w: torch.Tensor, has_shared: bool, out: torch.Tensor):
+    T, S, H = y_slots.shape
+    k = topk_w.shape[1]
+    if S != k + 1:
+        raise ValueError("y_slots must be [T][k+1][H]")
+    _dev(y_slots, torch.float32, "y_slots")
+    _dev(topk_w, torch.float32, "topk_w", (T, k))
+    _dev(out, torch.float32, "out", (T, H))
+    _ck(lib().moe_combine(ctx.handle, y_slots.data_ptr(), topk_w.data_ptr(), T, k, H, 1 if has_shared else 0,
+                          out.data_ptr()))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Expert storage helpers (device memory via torch, layout from the library)
+# ---------------------------------------------------------------------------
+
+class ExpertBlocks:
+    """n experts stored as contiguous blocks (moe_expert_block_layout) in one
+    device tensor, plus the device table of moe_expert_w pointers."""
+
+    def __init__(self, n: int, bits: int, H: int, I: int, device="cuda"):
+        self.n, self.bits, self.H, self.I = n, bits, H, I
+        self.block_bytes, self.offsets = moe_expert_block_layout(bits, H, I)
+        self.data = torch.empty((n, self.block_bytes), dtype=torch.uint8, device=device)
+        base = self.data.data_ptr()
+        rows = [[base + e * self.block_bytes + o for o in self.offsets] for e in range(n)]
+        self.table = torch.tensor(rows, dtype=torch.int64, device=device)
+
+    def views(self, e: int):
+        """(gate, up, down, s_gate, s_up, s_down) tensor views of expert e."""
+        H, I, b = self.H, self.I, self.bits
+        blk = self.data[e]
+        o = self.offsets
+        g = blk[o[0]:o[0] + I * H * b // 8].view(I, H * b // 8)
+        u = blk[o[1]:o[1] + I * H * b // 8].view(I, H * b // 8)
+        d = blk[o[2]:o[2] + H * I * b // 8].view(H, I * b // 8)
+        sg = blk[o[3]:o[3] + 4 * I].view(torch.float32)
+        su = blk[o[4]:o[4] + 4 * I].view(torch.float32)
+        sd = blk[o[5]:o[5] + 4 * H].view(torch.float32)
+        return g, u, d, sg, su, sd
+
+    def struct(self, e: int) -> ExpertW:
+        return ExpertW(*[self.data.data_ptr() + e * self.block_bytes + o for o in self.offsets])
+
+    def pack_from_fp32(self, ctx: MoeCtx, e: int, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor):
+        """Quantise fp32 gate/up/down on the GPU straight into expert e's block."""
+        g, u, d, sg, su, sd = self.views(e)
+        moe_quantize_rows(ctx, self.bits, wg, g, sg)
+        moe_quantize_rows(ctx, self.bits, wu, u, su)
+        moe_quantize_rows(ctx, self.bits, wd, d, sd)

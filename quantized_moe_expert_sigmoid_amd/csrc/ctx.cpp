@@ -1,0 +1,258 @@
+// Context, error reporting, argument validation and the exported C ABI.
+// Kernels live in the .hip files; every entry point here validates its
+// arguments completely before anything is enqueued.
+#include <new>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+static thread_local char g_err[512] = "";
+
+moe_status moe_fail(moe_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status moe_hip_fail(hipError_t e, const char *what) {
+  (void)hipGetLastError();  // clear the sticky launch error
+  return moe_fail(e == hipErrorOutOfMemory ? MOE_ENOMEM : MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+extern "C" const char *moe_last_error(void) { return g_err; }
+extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+moe_status moe_scratch(moe_ctx *ctx, size_t bytes, void **out) {
+  if (bytes > ctx->scratch_bytes) {
+    if (ctx->scratch) {
+      MOE_HIP(hipStreamSynchronize(ctx->stream));
+      MOE_HIP(hipFree(ctx->scratch));
+      ctx->scratch = nullptr;
+      ctx->scratch_bytes = 0;
+    }
+    size_t want = moe_round_up(bytes + bytes / 4, 1 << 20);
+    MOE_HIP(hipMalloc(&ctx->scratch, want));
+    ctx->scratch_bytes = want;
+  }
+  *out = ctx->scratch;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out) {
+  if (!out) return moe_fail(MOE_EINVAL, "moe_ctx_create: out is NULL");
+  *out = nullptr;
+  int n = 0;
+  MOE_HIP(hipGetDeviceCount(&n));
+  if (device < 0 || device >= n) return moe_fail(MOE_EINVAL, "moe_ctx_create: device %d of %d", device, n);
+  MOE_HIP(hipSetDevice(device));
+  hipDeviceProp_t prop;
+  MOE_HIP(hipGetDeviceProperties(&prop, device));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return moe_fail(MOE_EUNSUPPORTED, "moe_ctx_create: device %d is %s, this library is built for gfx950", device,
+                    prop.gcnArchName);
+  moe_ctx *c = new (std::nothrow) moe_ctx();
+  if (!c) return moe_fail(MOE_ENOMEM, "moe_ctx_create: host allocation");
+  c->device = device;
+  c->stream = (hipStream_t)hip_stream;
+  c->n_cu = prop.multiProcessorCount;
+  hipError_t e = hipMalloc(&c->dev_small, 4096);
+  if (e != hipSuccess) {
+    delete c;
+    return moe_hip_fail(e, "hipMalloc(ctx counters)");
+  }
+  e = hipMemset(c->dev_small, 0, 4096);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(c->dev_small);
+    delete c;
+    return moe_hip_fail(e, "hipMemset(ctx counters)");
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+extern "C" void moe_ctx_destroy(moe_ctx *ctx) {
+  if (!ctx) return;
+  (void)hipSetDevice(ctx->device);
+  (void)hipStreamSynchronize(ctx->stream);
+  if (ctx->scratch) (void)hipFree(ctx->scratch);
+  if (ctx->dev_small) (void)hipFree(ctx->dev_small);
+  delete ctx;
+}
+
+extern "C" moe_status moe_ctx_set_stream(moe_ctx *ctx, void *hip_stream) {
+  if (!ctx) return moe_fail(MOE_EINVAL, "moe_ctx_set_stream: ctx is NULL");
+  ctx->stream = (hipStream_t)hip_stream;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_ctx_check(moe_ctx *ctx) {
+  if (!ctx) return moe_fail(MOE_EINVAL, "moe_ctx_check: ctx is NULL");
+  MOE_HIP(hipSetDevice(ctx->device));
+  MOE_HIP(hipStreamSynchronize(ctx->stream));
+  uint32_t flags = 0;
+  MOE_HIP(hipMemcpy(&flags, ctx->dev_small, sizeof flags, hipMemcpyDeviceToHost));
+  if (flags) {
+    uint32_t zero = 0;
+    MOE_HIP(hipMemcpy(ctx->dev_small, &zero, sizeof zero, hipMemcpyHostToDevice));
+    if (flags & ERRF_TIMEOUT) return moe_fail(MOE_ETIMEOUT, "device: a bounded wait gave up (flags 0x%x)", flags);
+    if (flags & ERRF_BAD_INDEX) return moe_fail(MOE_EINVAL, "device: expert index out of range (flags 0x%x)", flags);
+    return moe_fail(MOE_EINVAL, "device: error flags 0x%x", flags);
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_ctx_set_debug(moe_ctx *ctx, const moe_debug_bufs *dbg) {
+  if (!ctx) return moe_fail(MOE_EINVAL, "moe_ctx_set_debug: ctx is NULL");
+  if (dbg) {
+    ctx->dbg = *dbg;
+    ctx->dbg_on = true;
+  } else {
+    ctx->dbg = moe_debug_bufs{};
+    ctx->dbg_on = false;
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Validation helpers
+// ---------------------------------------------------------------------------
+
+static bool dim_ok(int v) { return v > 0 && v % 64 == 0 && v <= 8192; }
+
+#define REQUIRE(cond, ...)                                 \
+  do {                                                     \
+    if (!(cond)) return moe_fail(MOE_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+static moe_status bind(moe_ctx *ctx, const char *fn) {
+  if (!ctx) return moe_fail(MOE_EINVAL, "%s: ctx is NULL", fn);
+  MOE_HIP(hipSetDevice(ctx->device));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Exported entry points
+// ---------------------------------------------------------------------------
+
+extern "C" moe_status moe_quantize_rows(moe_ctx *ctx, int bits, const float *w, int64_t rows, int cols,
+                                        uint8_t *packed, float *scales) {
+  moe_status st = bind(ctx, "moe_quantize_rows");
+  if (st) return st;
+  REQUIRE(bits == 8 || bits == 4 || bits == 2, "moe_quantize_rows: bits %d not in {8,4,2}", bits);
+  REQUIRE(cols > 0 && cols % 64 == 0 && cols <= (1 << 20), "moe_quantize_rows: cols %d", cols);
+  REQUIRE(rows >= 0 && rows <= (int64_t)1 << 31, "moe_quantize_rows: rows %lld", (long long)rows);
+  if (rows == 0) return MOE_OK;
+  REQUIRE(w && packed && scales, "moe_quantize_rows: NULL pointer");
+  REQUIRE(moe_aligned16(w) && moe_aligned16(packed), "moe_quantize_rows: pointers must be 16-byte aligned");
+  return launch_quantize_rows(ctx, bits, w, rows, cols, packed, scales);
+}
+
+extern "C" moe_status moe_quantize_act_i8(moe_ctx *ctx, const float *x, int T, int H, int8_t *xq, float *sx) {
+  moe_status st = bind(ctx, "moe_quantize_act_i8");
+  if (st) return st;
+  REQUIRE(T >= 0, "moe_quantize_act_i8: T %d", T);
+  REQUIRE(dim_ok(H), "moe_quantize_act_i8: H %d must be a positive multiple of 64, <= 8192", H);
+  if (T == 0) return MOE_OK;
+  REQUIRE(x && xq && sx, "moe_quantize_act_i8: NULL pointer");
+  REQUIRE(moe_aligned16(x) && moe_aligned16(xq), "moe_quantize_act_i8: pointers must be 16-byte aligned");
+  return launch_quantize_act(ctx, x, T, H, xq, sx);
+}
+
+extern "C" moe_status moe_router_topk(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x, const float *w_router,
+                                      const float *bias, int T, int H, int32_t *topk_idx, float *topk_w) {
+  moe_status st = bind(ctx, "moe_router_topk");
+  if (st) return st;
+  REQUIRE(cfg, "moe_router_topk: cfg is NULL");
+  REQUIRE(cfg->n_experts >= 1 && cfg->n_experts <= 1024, "moe_router_topk: n_experts %d", cfg->n_experts);
+  REQUIRE(cfg->top_k >= 1 && cfg->top_k <= 16 && cfg->top_k <= cfg->n_experts, "moe_router_topk: top_k %d",
+          cfg->top_k);
+  REQUIRE(T >= 0, "moe_router_topk: T %d", T);
+  if (!cfg->logits_in) {
+    REQUIRE(dim_ok(H), "moe_router_topk: H %d must be a positive multiple of 64, <= 8192", H);
+    REQUIRE(w_router, "moe_router_topk: w_router is NULL");
+    REQUIRE(moe_aligned16(w_router), "moe_router_topk: w_router must be 16-byte aligned");
+  }
+  if (T == 0) return MOE_OK;
+  REQUIRE(x && topk_idx && topk_w, "moe_router_topk: NULL pointer");
+  REQUIRE(moe_aligned16(x), "moe_router_topk: x must be 16-byte aligned");
+  return launch_router(ctx, cfg, x, w_router, bias, T, H, topk_idx, topk_w);
+}
+
+extern "C" moe_status moe_bucket_tokens(moe_ctx *ctx, const int32_t *topk_idx, int T, int k, int E, int32_t *counts,
+                                        int32_t *offsets, int32_t *perm) {
+  moe_status st = bind(ctx, "moe_bucket_tokens");
+  if (st) return st;
+  REQUIRE(T >= 0 && k >= 1 && k <= 16 && E >= 1 && E <= 1024, "moe_bucket_tokens: T %d k %d E %d", T, k, E);
+  REQUIRE((int64_t)T * k <= (1 << 24), "moe_bucket_tokens: T*k too large");
+  REQUIRE(counts && offsets && (T == 0 || (topk_idx && perm)), "moe_bucket_tokens: NULL pointer");
+  return launch_bucket_public(ctx, topk_idx, T, k, E, counts, offsets, perm);
+}
+
+static moe_status ffn_entry(const char *fn, int bits, moe_ctx *ctx, const moe_expert_w *experts,
+                            const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                            const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots) {
+  moe_status st = bind(ctx, fn);
+  if (st) return st;
+  REQUIRE(T >= 0, "%s: T %d", fn, T);
+  REQUIRE(dim_ok(H) && dim_ok(I), "%s: H %d and I %d must be positive multiples of 64, <= 8192", fn, H, I);
+  REQUIRE(E >= 1 && E <= 1024 && k >= 1 && k <= 16 && k <= E, "%s: E %d k %d", fn, E, k);
+  REQUIRE((int64_t)T * (k + 1) <= (1 << 22), "%s: T*(k+1) too large", fn);
+  if (T == 0) return MOE_OK;
+  REQUIRE(experts && xq && sx && topk_idx && y_slots, "%s: NULL pointer", fn);
+  REQUIRE(moe_aligned16(xq) && moe_aligned16(y_slots), "%s: xq and y_slots must be 16-byte aligned", fn);
+  if (shared) {
+    REQUIRE(shared->gate && shared->up && shared->down && shared->s_gate && shared->s_up && shared->s_down,
+            "%s: shared expert has a NULL member", fn);
+    REQUIRE(moe_aligned16(shared->gate) && moe_aligned16(shared->up) && moe_aligned16(shared->down),
+            "%s: shared expert weights must be 16-byte aligned", fn);
+  }
+  return launch_expert_ffn(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots);
+}
+
+extern "C" moe_status moe_expert_ffn_q4(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                                        const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                                        const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots) {
+  return ffn_entry("moe_expert_ffn_q4", 4, ctx, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k,
+                   y_slots);
+}
+extern "C" moe_status moe_expert_ffn_q8(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                                        const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                                        const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots) {
+  return ffn_entry("moe_expert_ffn_q8", 8, ctx, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k,
+                   y_slots);
+}
+extern "C" moe_status moe_expert_ffn_q2(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                                        const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                                        const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots) {
+  return ffn_entry("moe_expert_ffn_q2", 2, ctx, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k,
+                   y_slots);
+}
+
+extern "C" moe_status moe_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, int T, int k, int H,
+                                  int has_shared, float *out) {
+  moe_status st = bind(ctx, "moe_combine");
+  if (st) return st;
+  REQUIRE(T >= 0 && k >= 1 && k <= 16, "moe_combine: T %d k %d", T, k);
+  REQUIRE(dim_ok(H), "moe_combine: H %d must be a positive multiple of 64, <= 8192", H);
+  if (T == 0) return MOE_OK;
+  REQUIRE(y_slots && topk_w && out, "moe_combine: NULL pointer");
+  REQUIRE(moe_aligned16(y_slots) && moe_aligned16(out), "moe_combine: pointers must be 16-byte aligned");
+  return launch_combine(ctx, y_slots, topk_w, T, k, H, has_shared, out);
+}
+
+extern "C" size_t moe_expert_block_layout(int bits, int H, int I, size_t *offsets_host) {
+  if (!(bits == 8 || bits == 4 || bits == 2) || H <= 0 || I <= 0 || H % 64 || I % 64) return 0;
+  const size_t part[6] = {(size_t)I * H * bits / 8, (size_t)I * H * bits / 8, (size_t)H * I * bits / 8,
+                          4 * (size_t)I, 4 * (size_t)I, 4 * (size_t)H};
+  size_t off = 0;
+  for (int i = 0; i < 6; ++i) {
+    if (offsets_host) offsets_host[i] = off;
+    off = moe_round_up(off + part[i], 256);
+  }
+  return off;
+}

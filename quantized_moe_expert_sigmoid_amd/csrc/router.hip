@@ -1,0 +1,367 @@
+// Sigmoid top-k router with a selection bias, and per-expert bucketing.
+//
+// tech.takumi3488.com, "Trying colibri": a DeepSeek-V3-family router
+// (self-test section); 256 experts per layer, top-8 (section on the real
+// 744B model). remio.ai, "How Colibri runs GLM-5.2": the router picks a few
+// experts per token; "The RAM wall became a storage problem": requests for
+// one expert from several batch positions are served by one read, which is
+// what the per-expert buckets give the FFN.
+//
+// Logits are fp32 dot products, split over K into fixed slices whose partial
+// sums are added in slice order (deterministic). Top-k runs one wave per
+// token: sigmoid via the library's fp32 exp, key = sigmoid + bias, k rounds
+// of a wave-wide (key desc, id asc) arg-max, weights = sigmoid / sum.
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kSmallT = 8;      // GEMV path up to this many tokens
+constexpr int kTile = 64;       // GEMM tile (tokens x experts)
+constexpr int kTileK = 16;      // GEMM K step through LDS
+
+// --- logits, T <= kSmallT: one wave per (expert, K slice), all tokens -------
+__global__ __launch_bounds__(256) void router_gemv_kernel(const float *__restrict__ x, const float *__restrict__ wr,
+                                                          int T, int H, int E, int kl,
+                                                          float *__restrict__ partial) {
+  const int lane = threadIdx.x & (MOE_WAVE - 1);
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int ks = blockIdx.y;
+  if (e >= E) return;
+  const int k0 = ks * kl;
+  const float *wrow = wr + (int64_t)e * H + k0;
+  float acc[kSmallT];
+#pragma unroll
+  for (int t = 0; t < kSmallT; ++t) acc[t] = 0.0f;
+  for (int c = lane * 4; c < kl; c += MOE_WAVE * 4) {
+    const float4 wv = *reinterpret_cast<const float4 *>(wrow + c);
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) {
+      if (t < T) {
+        const float4 xv = *reinterpret_cast<const float4 *>(x + (int64_t)t * H + k0 + c);
+        acc[t] = __builtin_fmaf(wv.x, xv.x, acc[t]);
+        acc[t] = __builtin_fmaf(wv.y, xv.y, acc[t]);
+        acc[t] = __builtin_fmaf(wv.z, xv.z, acc[t]);
+        acc[t] = __builtin_fmaf(wv.w, xv.w, acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kSmallT; ++t) {
+    if (t < T) {
+      const float s = wave_sum_f32(acc[t]);
+      if (lane == 0) partial[((int64_t)ks * T + t) * E + e] = s;
+    }
+  }
+}
+
+// --- logits, general T: 64x64 register-tiled GEMM over one K slice ----------
+__global__ __launch_bounds__(256) void router_gemm_kernel(const float *__restrict__ x, const float *__restrict__ wr,
+                                                          int T, int H, int E, int kl,
+                                                          float *__restrict__ partial) {
+  __shared__ float xs[kTileK][kTile + 4];
+  __shared__ float ws[kTileK][kTile + 4];
+  const int t0 = blockIdx.x * kTile;
+  const int e0 = blockIdx.y * kTile;
+  const int ks = blockIdx.z;
+  const int k0 = ks * kl;
+  const int tx = threadIdx.x & 15;  // expert sub-tile
+  const int ty = threadIdx.x >> 4;  // token sub-tile
+  float acc[4][4] = {};
+  for (int kk = 0; kk < kl; kk += kTileK) {
+    // each thread loads 4 floats of x and 4 of w: 64 rows x 16 k each
+    const int r = threadIdx.x >> 2, c4 = (threadIdx.x & 3) * 4;
+    {
+      const int t = t0 + r;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < T) v = *reinterpret_cast<const float4 *>(x + (int64_t)t * H + k0 + kk + c4);
+      xs[c4 + 0][r] = v.x; xs[c4 + 1][r] = v.y; xs[c4 + 2][r] = v.z; xs[c4 + 3][r] = v.w;
+      const int e = e0 + r;
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < E) u = *reinterpret_cast<const float4 *>(wr + (int64_t)e * H + k0 + kk + c4);
+      ws[c4 + 0][r] = u.x; ws[c4 + 1][r] = u.y; ws[c4 + 2][r] = u.z; ws[c4 + 3][r] = u.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kTileK; ++q) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[q][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ws[q][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) partial[((int64_t)ks * T + t) * E + e] = acc[i][j];
+    }
+  }
+}
+
+// (key, id) order: a before b iff key_a > key_b, or equal keys and id_a < id_b.
+// NaN keys never win against a number.
+__device__ __forceinline__ bool key_before(float ka, int ia, float kb, int ib) {
+  if (ia < 0) return false;
+  if (ib < 0) return true;
+  if (ka > kb) return true;
+  if (ka == kb) return ia < ib;
+  return (kb != kb) && (ka == ka);
+}
+
+// --- top-k: one wave per token ---------------------------------------------
+constexpr int kMaxPerLane = 1024 / MOE_WAVE;  // E <= 1024
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ partial, int nslices, int T,
+                                                          int E, int k, const float *__restrict__ bias,
+                                                          float routed_scale, int32_t *__restrict__ topk_idx,
+                                                          float *__restrict__ topk_w) {
+  const int lane = threadIdx.x & (MOE_WAVE - 1);
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
+  float sig[kMaxPerLane], key[kMaxPerLane];
+#pragma unroll
+  for (int m = 0; m < kMaxPerLane; ++m) {
+    sig[m] = 0.0f;
+    key[m] = 0.0f;
+    const int e = lane + m * MOE_WAVE;
+    if (m < per && e < E) {
+      float z = 0.0f;
+      for (int s = 0; s < nslices; ++s) z += partial[((int64_t)s * T + t) * E + e];
+      sig[m] = 1.0f / (1.0f + moe_exp_f32(-z));
+      key[m] = sig[m] + (bias ? bias[e] : 0.0f);
+    }
+  }
+  unsigned taken = 0;  // bit m: element m of this lane already selected
+  float my_sig = 0.0f;
+  int my_id = -1;
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bk = 0.0f;
+    int bi = -1;
+#pragma unroll
+    for (int m = 0; m < kMaxPerLane; ++m) {
+      const int e = lane + m * MOE_WAVE;
+      if (m < per && e < E && !(taken & (1u << m)) && key_before(key[m], e, bk, bi)) {
+        bk = key[m];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ok = __shfl_xor(bk, o, MOE_WAVE);
+      const int oi = __shfl_xor(bi, o, MOE_WAVE);
+      if (key_before(ok, oi, bk, bi)) {
+        bk = ok;
+        bi = oi;
+      }
+    }
+    // bi is now the same on every lane; its owner marks it and shares sigmoid
+    float s = 0.0f;
+    if ((bi & (MOE_WAVE - 1)) == lane) {
+      const int m = bi / MOE_WAVE;
+      taken |= 1u << m;
+#pragma unroll
+      for (int mm = 0; mm < kMaxPerLane; ++mm)
+        if (mm == m) s = sig[mm];
+    }
+    s = __shfl(s, bi & (MOE_WAVE - 1), MOE_WAVE);
+    sum += s;
+    if (lane == j) {
+      my_sig = s;
+      my_id = bi;
+    }
+  }
+  if (lane < k) {
+    topk_idx[(int64_t)t * k + lane] = my_id;
+    topk_w[(int64_t)t * k + lane] = routed_scale * (my_sig / sum);
+  }
+}
+
+// --- bucketing: one workgroup, stable per-expert lists ----------------------
+constexpr int kBThreads = 1024;
+constexpr int kBitmapWords = 8192;
+
+struct BucketArgs {
+  const int32_t *idx;
+  int T, k, E;
+  int32_t *counts, *offsets, *perm;
+  const uint8_t *expert_bits;  // nullable filter for the active list
+  int want_bits;
+  int32_t *active;    // nullable: experts with count > 0 passing the filter
+  int32_t *n_active;  // nullable
+  uint32_t *err;
+};
+
+__device__ int block_exclusive_scan(int v, int *tmp) {
+  // Hillis-Steele over kBThreads entries in LDS
+  const int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < kBThreads; o <<= 1) {
+    const int add = tid >= o ? tmp[tid - o] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  const int incl = tmp[tid];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
+  __shared__ int cnt[1024];
+  __shared__ int off[1025];
+  __shared__ int cursor[1024];
+  __shared__ int tmp[kBThreads];
+  __shared__ uint32_t bitmap[kBitmapWords];
+  const int tid = threadIdx.x;
+  const int lane = tid & (MOE_WAVE - 1);
+  const int wave = tid >> 6;
+  const int E = a.E, k = a.k, T = a.T;
+  const int64_t n = (int64_t)T * k;
+
+  for (int e = tid; e < 1024; e += kBThreads) {
+    cnt[e] = 0;
+    cursor[e] = 0;
+  }
+  __syncthreads();
+  bool bad = false;
+  for (int64_t i = tid; i < n; i += kBThreads) {
+    const int e = a.idx[i];
+    bool dup = false;  // an expert repeated inside one token counts once (first slot)
+    for (int64_t j = i - i % k; j < i; ++j) dup |= (a.idx[j] == e);
+    if (e < 0 || e >= E || dup)
+      bad = true;
+    else
+      atomicAdd(&cnt[e], 1);
+  }
+  if (bad) atomicOr(a.err, (uint32_t)ERRF_BAD_INDEX);
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  const int ex = block_exclusive_scan(c, tmp);
+  if (tid < E) {
+    off[tid] = ex;
+    a.counts[tid] = c;
+    a.offsets[tid] = ex;
+  }
+  if (tid == E - 1) {
+    off[E] = ex + c;
+    a.offsets[E] = ex + c;
+  }
+  const int act = (tid < E && c > 0 && (!a.expert_bits || a.expert_bits[tid] == a.want_bits)) ? 1 : 0;
+  const int apos = block_exclusive_scan(act, tmp);
+  if (a.active && act) a.active[apos] = tid;
+  if (a.n_active && tid == E - 1) *a.n_active = apos + act;
+  __syncthreads();
+  if (T == 0) return;
+
+  // stable placement, tokens in chunks that fit the LDS bitmap
+  int W = kBitmapWords / E;  // words per expert
+  if (W > 64) W = 64;
+  const int TC = 32 * W;
+  for (int c0 = 0; c0 < T; c0 += TC) {
+    const int nt = min(TC, T - c0);
+    for (int i = tid; i < E * W; i += kBThreads) bitmap[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < nt * k; i += kBThreads) {
+      const int tl = i / k;
+      const int e = a.idx[(int64_t)(c0 + tl) * k + (i % k)];
+      if (e >= 0 && e < E) atomicOr(&bitmap[e * W + (tl >> 5)], 1u << (tl & 31));
+    }
+    __syncthreads();
+    for (int e = wave; e < E; e += kBThreads / MOE_WAVE) {
+      if (cnt[e] == 0) continue;
+      int base = cursor[e];
+      for (int w0 = 0; w0 < W; w0 += MOE_WAVE) {
+        uint32_t word = (w0 + lane < W) ? bitmap[e * W + w0 + lane] : 0u;
+        const int pc = __popc(word);
+        int incl = pc;
+#pragma unroll
+        for (int o = 1; o < MOE_WAVE; o <<= 1) {
+          const int v = __shfl_up(incl, o, MOE_WAVE);
+          if (lane >= o) incl += v;
+        }
+        const int total = __shfl(incl, MOE_WAVE - 1, MOE_WAVE);
+        int r = base + incl - pc;
+        while (word) {
+          const int b = __ffs(word) - 1;
+          word &= word - 1;
+          const int t = c0 + 32 * (w0 + lane) + b;
+          int jj = k - 1;
+          for (int j = k - 1; j >= 0; --j)
+            if (a.idx[(int64_t)t * k + j] == e) jj = j;
+          a.perm[off[e] + r] = t * k + jj;
+          ++r;
+        }
+        base += total;
+      }
+      if (lane == 0) cursor[e] = base;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
+                         int32_t *perm, const uint8_t *expert_bits, int want_bits, int32_t *active,
+                         int32_t *n_active) {
+  BucketArgs a{idx, T, k, E, counts, offsets, perm, expert_bits, want_bits, active, n_active, ctx->dev_small};
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBThreads), 0, ctx->stream, a);
+  MOE_CHECK_LAUNCH("bucket_kernel");
+  return MOE_OK;
+}
+
+moe_status launch_bucket_public(moe_ctx *ctx, const int32_t *topk_idx, int T, int k, int E, int32_t *counts,
+                                int32_t *offsets, int32_t *perm) {
+  return launch_bucket(ctx, topk_idx, T, k, E, counts, offsets, perm, nullptr, 0, nullptr, nullptr);
+}
+
+moe_status launch_router(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x, const float *w_router,
+                         const float *bias, int T, int H, int32_t *topk_idx, float *topk_w) {
+  const int E = cfg->n_experts, k = cfg->top_k;
+  const float *partial = x;
+  int nslices = 1;
+  if (!cfg->logits_in) {
+    int ks;
+    if (T <= kSmallT) {
+      // enough waves to stream w_router with the whole chip: ~4 waves per CU
+      const int groups = (E + 3) / 4;
+      ks = 1;
+      while (groups * ks < 2 * ctx->n_cu && H % (ks * 2 * 256) == 0) ks *= 2;
+    } else {
+      const int tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
+      ks = 1;
+      while (tiles * ks < 2 * ctx->n_cu && H % (ks * 2 * kTileK) == 0 && H / (ks * 2) >= 256) ks *= 2;
+    }
+    const int kl = H / ks;
+    void *scr = nullptr;
+    moe_status st = moe_scratch(ctx, sizeof(float) * (size_t)ks * T * E, &scr);
+    if (st) return st;
+    float *part = static_cast<float *>(scr);
+    if (T <= kSmallT) {
+      hipLaunchKernelGGL(router_gemv_kernel, dim3((E + 3) / 4, ks), dim3(256), 0, ctx->stream, x, w_router, T, H, E,
+                         kl, part);
+    } else {
+      hipLaunchKernelGGL(router_gemm_kernel, dim3((T + kTile - 1) / kTile, (E + kTile - 1) / kTile, ks), dim3(256),
+                         0, ctx->stream, x, w_router, T, H, E, kl, part);
+    }
+    MOE_CHECK_LAUNCH("router logits kernel");
+    partial = part;
+    nslices = ks;
+  }
+  hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, ctx->stream, partial, nslices, T, E, k,
+                     bias, cfg->routed_scale, topk_idx, topk_w);
+  MOE_CHECK_LAUNCH("router_topk_kernel");
+  return MOE_OK;
+}

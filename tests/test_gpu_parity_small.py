@@ -1,0 +1,309 @@
+"""GPU parity at sizes the oracle finishes in seconds (several tiles, ragged
+tails), through the C ABI. Bar: bit-exact for packed weights, activation
+codes and scales, integer accumulators, requantised intermediates and expert
+outputs; router indices exact away from near-ties; combined outputs within
+1e-3 of the per-row max (fp32 accumulation vs the oracle's fp64).
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import compare_router, log, rel_row_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import quantized_moe_expert_sigmoid_amd as m
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def ctx(moe):
+    c = moe.MoeCtx(0)
+    yield c
+    c.close()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# --------------------------------------------------------------------------
+# quantisation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("R,C", [(37, 320), (5, 64), (300, 6144)])
+def test_quantize_rows_bitexact(moe, ctx, orc, syn, bits, R, C):
+    log(f"quantize_rows bits={bits} R={R} C={C}")
+    w = syn.normal(11, syn.stream_id(syn.K_MISC, R, C), (R, C), 0.02)
+    w[R // 2] = 0.0
+    ref_p, ref_s = orc.quantize_rows(bits, w)
+    p = torch.empty((R, C * bits // 8), dtype=torch.uint8, device="cuda")
+    s = torch.empty((R,), dtype=torch.float32, device="cuda")
+    moe.moe_quantize_rows(ctx, bits, dev(w), p, s)
+    assert np.array_equal(host(p), ref_p)
+    assert np.array_equal(host(s).view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_quantize_rows_half_ties(moe, ctx, orc):
+    # values exactly halfway between codes: round half to even on both sides
+    w = np.tile(np.array([3.5, -1.75, 0.25, 0, 0.75, -3.5, 1.25, 0.5], np.float32), (4, 8))
+    for bits in (8, 4, 2):
+        ref_p, ref_s = orc.quantize_rows(bits, w)
+        p = torch.empty((4, 64 * bits // 8), dtype=torch.uint8, device="cuda")
+        s = torch.empty((4,), dtype=torch.float32, device="cuda")
+        moe.moe_quantize_rows(ctx, bits, dev(w), p, s)
+        assert np.array_equal(host(p), ref_p) and np.array_equal(host(s), ref_s)
+
+
+@pytest.mark.parametrize("T,H", [(1, 6144), (33, 128), (64, 6144)])
+def test_quantize_act_bitexact(moe, ctx, orc, syn, T, H):
+    log(f"quantize_act T={T} H={H}")
+    x = syn.hidden(21, T, H)
+    if T > 2:
+        x[1] = 0.0
+    ref_q, ref_s = orc.quantize_act(x)
+    q = torch.empty((T, H), dtype=torch.int8, device="cuda")
+    s = torch.empty((T,), dtype=torch.float32, device="cuda")
+    moe.moe_quantize_act_i8(ctx, dev(x), q, s)
+    assert np.array_equal(host(q), ref_q)
+    assert np.array_equal(host(s), ref_s)
+
+
+# --------------------------------------------------------------------------
+# router and bucketing
+# --------------------------------------------------------------------------
+
+def run_router(moe, ctx, x, wr, bias, k, logits_in=False, scale=1.0):
+    T = x.shape[0]
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(ctx, dev(x), None if wr is None else dev(wr), None if bias is None else dev(bias), k, idx, w,
+                        scale, logits_in=logits_in)
+    return host(idx), host(w)
+
+
+@pytest.mark.parametrize("T,H,E,k", [(32, 128, 8, 2), (1, 6144, 256, 8), (7, 6144, 256, 8), (64, 6144, 256, 8),
+                                     (130, 384, 64, 6), (5, 128, 8, 8)])
+def test_router_hidden(moe, ctx, orc, syn, T, H, E, k):
+    log(f"router T={T} H={H} E={E} k={k}")
+    x = syn.hidden(31, T, H)
+    wr = syn.router_weights(31, 0, E, H)
+    bias = syn.router_bias(31, 0, E)
+    idx_o, w_o, keys, sig = orc.router(x, wr, bias, k, want_keys=True)
+    idx_g, w_g = run_router(moe, ctx, x, wr, bias, k)
+    near = compare_router(idx_g, w_g, idx_o, keys, sig)
+    assert near <= max(1, T // 50)
+
+
+def test_router_logits_zipf_and_ties(moe, ctx, orc, syn):
+    z = syn.zipf_logits(2, 0, 64, 256, 1.1)
+    idx_o, w_o, keys, sig = orc.router(z, None, None, 8, logits_in=True, want_keys=True)
+    idx_g, w_g = run_router(moe, ctx, z, None, None, 8, logits_in=True)
+    compare_router(idx_g, w_g, idx_o, keys, sig)
+    # exact ties: equal keys go to the lower expert id
+    zt = np.array([[0.5, 1.0, 1.0, -2.0, 1.0, 0.5, 0.0, 0.0]], np.float32)
+    idx_g, w_g = run_router(moe, ctx, zt, None, None, 4, logits_in=True)
+    assert idx_g[0].tolist() == [1, 2, 4, 0]
+    # routed scale multiplies the normalised weights
+    idx_g, w_g = run_router(moe, ctx, zt, None, None, 2, logits_in=True, scale=2.5)
+    assert abs(w_g[0].sum() - 2.5) < 1e-5
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (64, 256, 8), (2048, 256, 8), (37, 8, 2), (1500, 1024, 16)])
+def test_bucket_exact(moe, ctx, orc, syn, T, E, k):
+    log(f"bucket T={T} E={E} k={k}")
+    z = syn.normal(5, syn.stream_id(syn.K_MISC, T, E), (T, E))
+    idx, _ = orc.router(z, None, None, k, logits_in=True)
+    c_o, o_o, p_o = orc.bucket(idx, E)
+    c = torch.empty((E,), dtype=torch.int32, device="cuda")
+    o = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
+    p = torch.empty((T * k,), dtype=torch.int32, device="cuda")
+    moe.moe_bucket_tokens(ctx, dev(idx), E, c, o, p)
+    assert np.array_equal(host(c), c_o) and np.array_equal(host(o), o_o) and np.array_equal(host(p), p_o)
+
+
+def test_bucket_bad_index_reported(moe, ctx):
+    idx = torch.tensor([[0, 9], [1, 2]], dtype=torch.int32, device="cuda")
+    c = torch.empty((8,), dtype=torch.int32, device="cuda")
+    o = torch.empty((9,), dtype=torch.int32, device="cuda")
+    p = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    moe.moe_bucket_tokens(ctx, idx, 8, c, o, p)
+    with pytest.raises(moe.MoeError):
+        ctx.check()
+    assert host(c).sum() == 3
+    ctx.check()  # cleared
+
+
+def test_invalid_arguments_rejected(moe, ctx):
+    x = torch.zeros((2, 100), dtype=torch.float32, device="cuda")  # H not a multiple of 64
+    with pytest.raises(moe.MoeError):
+        moe.moe_quantize_act_i8(ctx, x, torch.empty((2, 100), dtype=torch.int8, device="cuda"),
+                                torch.empty((2,), dtype=torch.float32, device="cuda"))
+    # T = 0 is a no-op
+    moe.moe_quantize_act_i8(ctx, torch.zeros((0, 64), device="cuda"), torch.empty((0, 64), dtype=torch.int8,
+                            device="cuda"), torch.empty((0,), device="cuda"))
+
+
+# --------------------------------------------------------------------------
+# expert FFN stage with captured intermediates
+# --------------------------------------------------------------------------
+
+def make_experts(moe, orc, syn, bits, H, I, E, seed):
+    """GPU expert blocks packed on the GPU and the oracle's own packing of the
+    same fp32 weights (never the GPU's bytes)."""
+    blocks = moe.ExpertBlocks(E, bits, H, I)
+    shared = moe.ExpertBlocks(1, bits, H, I)
+    ctx = moe.MoeCtx(0)
+    oexp = []
+    for e in range(E):
+        wg, wu, wd = syn.expert_weights(seed, 0, e, H, I)
+        blocks.pack_from_fp32(ctx, e, dev(wg), dev(wu), dev(wd))
+        oexp.append(orc.pack_expert(bits, wg, wu, wd))
+    wg, wu, wd = syn.expert_weights(seed, 0, 0, H, I, shared=True)
+    shared.pack_from_fp32(ctx, 0, dev(wg), dev(wu), dev(wd))
+    osh = orc.pack_expert(bits, wg, wu, wd)
+    torch.cuda.synchronize()
+    ctx.close()
+    return blocks, shared, oexp, osh
+
+
+def random_routing(syn, T, E, k, seed):
+    z = syn.normal(seed, syn.stream_id(syn.K_MISC, 77, T), (T, E))
+    return np.argsort(-z, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("T,H,I,E,k", [(32, 128, 64, 8, 2), (37, 256, 192, 8, 2), (3, 512, 128, 16, 4)])
+def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, bits, T, H, I, E, k):
+    log(f"ffn bits={bits} T={T} H={H} I={I} E={E} k={k}")
+    blocks, shared, oexp, osh = make_experts(moe, orc, syn, bits, H, I, E, seed=40 + bits)
+    x = syn.hidden(41, T, H)
+    xq_o, sx_o = orc.quantize_act(x)
+    idx = random_routing(syn, T, E, k, 42)
+    P = T * (k + 1)
+    dbg = dict(accg=torch.zeros((P, I), dtype=torch.int32, device="cuda"),
+               accu=torch.zeros((P, I), dtype=torch.int32, device="cuda"),
+               a=torch.zeros((P, I), dtype=torch.float32, device="cuda"),
+               aq=torch.zeros((P, I), dtype=torch.int8, device="cuda"),
+               sa=torch.zeros((P,), dtype=torch.float32, device="cuda"),
+               accd=torch.zeros((P, H), dtype=torch.int32, device="cuda"))
+    y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
+    ctx.set_debug(dbg)
+    try:
+        moe.FFN_BY_BITS[bits](ctx, blocks.table, shared.struct(0), None, dev(xq_o), dev(sx_o), dev(idx), H, I, E, y)
+        ctx.check()
+    finally:
+        ctx.set_debug(None)
+    got = {n: host(t) for n, t in dbg.items()}
+    yg = host(y)
+    for t in range(T):
+        for j in range(k + 1):
+            ex = osh if j == k else oexp[idx[t, j]]
+            r = orc.expert_token(ex, xq_o[t], float(sx_o[t]))
+            p = t * (k + 1) + j
+            assert np.array_equal(got["accg"][p], r["accg"]), (t, j)
+            assert np.array_equal(got["accu"][p], r["accu"]), (t, j)
+            assert np.array_equal(got["a"][p].view(np.uint32), r["a"].view(np.uint32)), (t, j)
+            assert np.array_equal(got["aq"][p], r["aq"]), (t, j)
+            assert got["sa"][p] == np.float32(r["sa"]), (t, j)
+            assert np.array_equal(got["accd"][p], r["accd"]), (t, j)
+            assert np.array_equal(yg[t, j].view(np.uint32), r["y"].view(np.uint32)), (t, j)
+
+
+def test_ffn_without_shared_leaves_slot(moe, ctx, orc, syn):
+    H, I, E, k, T = 128, 64, 8, 2, 5
+    blocks, shared, oexp, osh = make_experts(moe, orc, syn, 4, H, I, E, seed=50)
+    x = syn.hidden(51, T, H)
+    xq_o, sx_o = orc.quantize_act(x)
+    idx = random_routing(syn, T, E, k, 52)
+    y = torch.full((T, k + 1, H), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn_q4(ctx, blocks.table, None, None, dev(xq_o), dev(sx_o), dev(idx), H, I, E, y)
+    yg = host(y)
+    assert np.all(yg[:, k] == 7.0)
+    for t in range(T):
+        r = orc.expert_token(oexp[idx[t, 0]], xq_o[t], float(sx_o[t]))
+        assert np.array_equal(yg[t, 0], r["y"])
+
+
+def test_ffn_mixed_precision_filter(moe, ctx, orc, syn):
+    """expert_bits selects which experts a width's entry point computes: a
+    mixed int4/int2 layer is two calls writing disjoint slots."""
+    H, I, E, k, T = 256, 128, 8, 3, 9
+    b4, sh4, o4, osh4 = make_experts(moe, orc, syn, 4, H, I, E, seed=60)
+    b2, _, o2, _ = make_experts(moe, orc, syn, 2, H, I, E, seed=60)
+    bits = np.array([4, 2, 4, 2, 2, 4, 4, 2], np.uint8)
+    # one table: int4 blocks for 4-bit experts, int2 blocks for the others
+    table = torch.where(torch.from_numpy(bits == 4).cuda()[:, None], b4.table, b2.table).contiguous()
+    x = syn.hidden(61, T, H)
+    xq_o, sx_o = orc.quantize_act(x)
+    idx = random_routing(syn, T, E, k, 62)
+    y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
+    eb = dev(bits)
+    moe.moe_expert_ffn_q4(ctx, table, sh4.struct(0), eb, dev(xq_o), dev(sx_o), dev(idx), H, I, E, y)
+    moe.moe_expert_ffn_q2(ctx, table, None, eb, dev(xq_o), dev(sx_o), dev(idx), H, I, E, y)
+    yg = host(y)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            ex = o4[e] if bits[e] == 4 else o2[e]
+            assert np.array_equal(yg[t, j], orc.expert_token(ex, xq_o[t], float(sx_o[t]))["y"]), (t, j)
+        assert np.array_equal(yg[t, k], orc.expert_token(osh4, xq_o[t], float(sx_o[t]))["y"])
+
+
+# --------------------------------------------------------------------------
+# combine and the whole layer
+# --------------------------------------------------------------------------
+
+def test_combine(moe, ctx, orc, syn):
+    T, k, H = 9, 8, 6144
+    y = syn.normal(70, syn.stream_id(syn.K_MISC, 70), (T, k + 1, H))
+    w = np.abs(syn.normal(70, syn.stream_id(syn.K_MISC, 71), (T, k)))
+    for has_shared in (True, False):
+        out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        moe.moe_combine(ctx, dev(y), dev(w), has_shared, out)
+        ys = y if has_shared else np.ascontiguousarray(y[:, :k])
+        ref = orc.combine(ys, w, has_shared)
+        assert rel_row_err(host(out), ref).max() < 1e-5
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+def test_layer_tiny_end_to_end(moe, ctx, orc, syn, bits):
+    """Tiny layer: hidden 128, 8 routed experts + 1 shared, top-2, intermediate
+    64, 32 tokens, seed 0, through quantize_act -> router -> ffn -> combine."""
+    from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
+    from synth import workloads as wl
+    w = wl.TINY
+    L = MoeLayer(ctx, w.H, w.I, w.E, w.k, bits=bits)
+    oexp = []
+    for e in range(w.E):
+        g, u, d = wl.expert_fp32(w, e)
+        L.set_expert_fp32(e, g, u, d)
+        oexp.append(orc.pack_expert(bits, g, u, d))
+    g, u, d = wl.shared_fp32(w)
+    L.set_shared_fp32(g, u, d)
+    osh = orc.pack_expert(bits, g, u, d)
+    wr, bias = wl.router_fp32(w)
+    L.set_router(wr, bias)
+    x = wl.hidden_fp32(w)
+    res = L.forward(dev(x))
+    ctx.check()
+    ref = orc.layer(x, orc.ExpertTable(oexp), osh, w.k, wr=wr, bias=bias)
+    _, _, keys, sig = orc.router(x, wr, bias, w.k, want_keys=True)
+    assert np.array_equal(host(res["xq"]), ref["xq"])
+    near = compare_router(host(res["idx"]), host(res["w"]), ref["idx"], keys, sig)
+    assert near == 0
+    assert np.array_equal(host(res["y"]), ref["y_slots"])
+    err = rel_row_err(host(res["out"]), ref["out"])
+    assert err.max() < 1e-3, err.max()
