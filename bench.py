@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one full pass of the layer's hot path over one batch of synthetic
+input: int8 activation quantisation, sigmoid top-k routing, per-expert
+bucketing, the SwiGLU expert FFN over packed int4 weights (routed experts +
+shared expert), and the weighted combine. Default workload: a GLM-5.2-shaped
+layer (hidden 6144, 256 routed experts + 1 shared, top-8, intermediate 2048,
+int4 weights with fp32 row scales) decoding one token per step; the tokens
+rotate through a pool of distinct hidden states already in HBM, so successive
+steps route to different experts.
+
+Prints one JSON line (rank 0): value = tokens/s; effective expert-weight GB/s
+and the roofline of the expert FFN (events around its launches on the
+context's stream) ride along; cpu_baseline = the scalar CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + effective expert-weight HBM GB/s (int4 decode, 1 GPU)"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_gpu_layer(ctx, w, bits):
+    import torch
+    from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
+    from synth import workloads as wl
+    L = MoeLayer(ctx, w.H, w.I, w.E, w.k, bits=bits, has_shared=w.has_shared)
+    t0 = time.time()
+    for e, g, u, d in wl.iter_experts(w, range(w.E)):
+        L.set_expert_fp32(e, g, u, d)
+        if e % 64 == 63:
+            log(f"[bench] packed {e + 1}/{w.E} experts ({time.time() - t0:.1f}s)")
+    if w.has_shared:
+        L.set_shared_fp32(*wl.shared_fp32(w))
+    wr, b = wl.router_fp32(w)
+    L.set_router(wr, b)
+    torch.cuda.synchronize()
+    return L
+
+
+def cpu_baseline(w, bits, n_tokens, repeats):
+    """Time the oracle's full layer on n_tokens distinct tokens x repeats."""
+    import oracle as orc
+    from synth import workloads as wl
+    orc.build()
+    T = n_tokens
+    x = wl.hidden_fp32(w, T, batch=0)
+    logits = wl.logits_fp32(w, T) if w.routing == "zipf" else None
+    wr, b = wl.router_fp32(w)
+    idx, _ = (orc.router(logits, None, b, w.k, logits_in=True) if logits is not None
+              else orc.router(x, wr, b, w.k))
+    need = sorted({int(e) for e in idx.ravel()})
+    exps = [None] * w.E
+    for e, g, u, d in wl.iter_experts(w, need):
+        exps[e] = orc.pack_expert(bits, g, u, d)
+    sh = orc.pack_expert(bits, *wl.shared_fp32(w)) if w.has_shared else None
+    table = orc.ExpertTable(exps)
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        orc.layer(x, table, sh, w.k, wr=wr, bias=b, logits=logits)
+    dt = time.perf_counter() - t0
+    return {"value": round(T * repeats / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{T} distinct tokens x {repeats} repeats of the full layer ({len(need)} routed experts "
+                      f"packed beforehand, untimed); {dt:.1f} s single-threaded scalar C"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="glm_decode_t1")
+    ap.add_argument("--bits", type=int, default=4)
+    ap.add_argument("--pool", type=int, default=64, help="distinct input batches rotated through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--cpu-repeats", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_moe_expert_sigmoid_amd as moe
+    from synth import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.lib()
+    w = wl.ALL[args.workload]
+    bits = args.bits
+    ctx = moe.MoeCtx(0)
+    L = build_gpu_layer(ctx, w, bits)
+
+    # input pool in HBM
+    T = w.T
+    npool = max(1, min(args.pool, 4096 // max(1, T)))
+    xs = [torch.from_numpy(wl.hidden_fp32(w, T, batch=i)).cuda() for i in range(npool)]
+    zs = [torch.from_numpy(wl.logits_fp32(w, T, batch=i)).cuda() for i in range(npool)] if w.routing == "zipf" \
+        else [None] * npool
+    torch.cuda.synchronize()
+
+    def step(i):
+        L.forward(xs[i % npool], zs[i % npool])
+
+    # eager warm-up (sizes the context scratch) and the distinct experts each
+    # pool entry streams
+    for i in range(2 * npool):
+        step(i)
+    torch.cuda.synchronize()
+    ctx.check()
+    distinct = []
+    b = L.buffers(T)
+    for i in range(npool):
+        step(i)
+        torch.cuda.synchronize()
+        distinct.append(len(np.unique(b["idx"].cpu().numpy())) + (1 if w.has_shared else 0))
+    H, I = w.H, w.I
+    o = L.experts.offsets
+    gu_bytes = 2 * (o[1] - o[0]) + 8 * I          # packed gate + up rows and their fp32 scales
+    dn_bytes = (o[3] - o[2]) + 4 * H              # packed down rows and fp32 scales
+    n_avg = float(np.mean(distinct))
+    avg_bytes = n_avg * (gu_bytes + dn_bytes)
+    router_bytes = 4 * w.E * H + 4 * w.E if w.routing != "zipf" else 4 * T * w.E
+
+    # tokens/s: one HIP graph holds npool consecutive layer calls (one per pool
+    # entry); the timed region replays it back to back.
+    cap = torch.cuda.Stream()
+    ctx.set_stream(cap)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(npool):
+            step(i)
+    ctx.set_stream(torch.cuda.current_stream())
+    reps = max(1, args.steps // npool)
+    warm_reps = max(1, args.warmup // npool)
+    steps = reps * npool
+    for _ in range(warm_reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ctx.check()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ctx.check()
+    gpu_ms = t0.elapsed_time(t1)
+    ms_per_step = gpu_ms / steps
+
+    # per-kernel durations: hipEvents the library records around each of its
+    # kernels on the context stream (eager calls over the same pool)
+    ctx.enable_timing(True)
+    n_timed = max(npool, min(steps, 4 * npool))
+    for i in range(n_timed):
+        step(i)
+    tm = ctx.read_timing()
+    ctx.enable_timing(False)
+    ctx.check()
+    per_call = {k_: (v[0] / max(1, n_timed), v[1] / n_timed) for k_, v in tm.items() if v[1] > 0}
+    gu_ms = per_call["gateup"][0]
+    dn_ms = per_call["down"][0]
+    tokens_per_s = T * steps / (gpu_ms / 1e3)
+    eff_gbps = avg_bytes / (ms_per_step / 1e3) / 1e9
+    gu_gbps = n_avg * gu_bytes / (gu_ms / 1e3) / 1e9
+    ffn_ms = sum(per_call[s_][0] for s_ in ("bucket", "gateup", "requant", "down") if s_ in per_call)
+    ffn_gbps = avg_bytes / (ffn_ms / 1e3) / 1e9
+    log(f"[bench] {steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / steps * 1e6:.1f} us), "
+        f"{avg_bytes / 1e6:.1f} MB/step, layer {eff_gbps:.0f} GB/s; kernels per call: " +
+        ", ".join(f"{k_} {v[0] * 1e3:.1f} us" for k_, v in per_call.items()) +
+        f"; gate/up {gu_gbps:.0f} GB/s, FFN {ffn_gbps:.0f} GB/s")
+    args.steps, args.warmup = steps, warm_reps * npool
+    kernel_names = {"router": "router_t1_kernel" if T == 1 else "router kernels",
+                    "gateup": "gateup_t1_kernel" if T == 1 else "ffn_gateup_kernel",
+                    "down": "down_combine_t1_kernel" if T == 1 else "ffn_down_kernel"}
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"w{bits}a8_i32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "hidden": w.H, "intermediate": w.I, "routed_experts": w.E, "top_k": w.k,
+                   "shared_experts": 1 if w.has_shared else 0, "tokens_per_step": T, "weight_bits": bits,
+                   "routing": w.routing, "input_pool": npool},
+        "effective_weight_GBps": round(eff_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": kernel_names["gateup"], "achieved": round(gu_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": round(n_avg * gu_bytes),
+                     "avg_launch_us": round(gu_ms * 1e3, 2)},
+        "kernels": {k_: {"avg_us": round(v[0] * 1e3, 2), "launches_per_call": v[1]} for k_, v in per_call.items()},
+        "expert_ffn": {"kernels": kernel_names["gateup"] + " + " + kernel_names["down"],
+                       "algorithmic_bytes": round(avg_bytes), "avg_us": round(ffn_ms * 1e3, 2),
+                       "achieved_GBps": round(ffn_gbps, 1), "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4)},
+        "router_bytes": router_bytes,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        result["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_tokens, args.cpu_repeats)
+        log(f"[bench] cpu baseline done in {time.time() - t0:.1f}s")
+    print(json.dumps(result), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -202,6 +202,56 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, 
                        float *out);
 
 /* ---------------------------------------------------------------------- */
+/* Whole layer in one call                                                */
+/* ---------------------------------------------------------------------- */
+
+/* The layer's hot path for T tokens in one call, all steps on the context
+ * stream: activation quantisation, router (on x with w_router, or on the
+ * given logits when cfg->logits_in), expert FFN of every routed expert and of
+ * the shared expert at `bits` (8, 4 or 2; every expert at that width), and
+ * the combine. Results equal moe_quantize_act_i8 -> moe_router_topk ->
+ * moe_expert_ffn_q* -> moe_combine on the same inputs (the same arithmetic
+ * in the same order; a single token runs three fused kernels: router with
+ * top-k and activation quantisation, gate/up with requantisation, and down
+ * fused with the combine).
+ *
+ * x fp32 [T][H] hidden states; logits fp32 [T][E] (only with
+ * cfg->logits_in, else NULL); w_router fp32 [E][H] (ignored with logits);
+ * bias fp32 [E] or NULL; experts DEVICE array [E]; shared HOST pointer or
+ * NULL. out fp32 [T][H] (required). Optional outputs (NULL = not returned):
+ * topk_idx int32 [T][k], topk_w fp32 [T][k], xq int8 [T][H], sx fp32 [T],
+ * y_slots fp32 [T][k+1][H]. */
+moe_status moe_layer_forward(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x, const float *logits,
+                             const float *w_router, const float *bias, const moe_expert_w *experts,
+                             const moe_expert_w *shared, int T, int H, int I, float *out, int32_t *topk_idx,
+                             float *topk_w, int8_t *xq, float *sx, float *y_slots);
+
+/* ---------------------------------------------------------------------- */
+/* Measurement                                                            */
+/* ---------------------------------------------------------------------- */
+
+/* Kernel stages the library times when timing is on. */
+enum {
+  MOE_STAGE_ROUTER = 0,   /* activation quantisation + router (+ top-k) */
+  MOE_STAGE_BUCKET = 1,   /* per-expert bucketing */
+  MOE_STAGE_GATEUP = 2,   /* gate/up GEMV with the SwiGLU epilogue */
+  MOE_STAGE_REQUANT = 3,  /* int8 requantisation of the intermediate */
+  MOE_STAGE_DOWN = 4,     /* down GEMV (fused with the combine for one token) */
+  MOE_STAGE_COMBINE = 5,  /* weighted combine */
+  MOE_N_STAGES = 6
+};
+
+/* Switch per-kernel timing on or off. When on, every kernel launched by
+ * moe_layer_forward and moe_expert_ffn_* is bracketed by two hipEvents
+ * recorded on the context stream (must not be on during graph capture).
+ * Switching changes nothing else. */
+moe_status moe_ctx_enable_timing(moe_ctx *ctx, int enable);
+/* Wait for the recorded events and return, per stage, the summed kernel
+ * time in milliseconds (ms_host[MOE_N_STAGES]) and the number of launches
+ * (n_host[MOE_N_STAGES]); then forget the records. Either pointer may be NULL. */
+moe_status moe_ctx_read_timing(moe_ctx *ctx, double *ms_host, int *n_host);
+
+/* ---------------------------------------------------------------------- */
 /* Test visibility                                                        */
 /* ---------------------------------------------------------------------- */
 

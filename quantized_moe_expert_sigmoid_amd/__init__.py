@@ -72,6 +72,10 @@ _SIGS = {
                                  _i32, _vp]),
     "moe_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "moe_ctx_set_debug": (_i32, [_vp, ctypes.POINTER(DebugBufs)]),
+    "moe_ctx_enable_timing": (_i32, [_vp, _i32]),
+    "moe_ctx_read_timing": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
+    "moe_layer_forward": (_i32, [_vp, _i32, ctypes.POINTER(RouterCfg), _vp, _vp, _vp, _vp, _vp,
+                                 ctypes.POINTER(ExpertW), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -148,6 +152,18 @@ class MoeCtx:
 
     def check(self):
         _ck(lib().moe_ctx_check(self.handle))
+
+    STAGES = ("router", "bucket", "gateup", "requant", "down", "combine")
+
+    def enable_timing(self, on: bool = True):
+        _ck(lib().moe_ctx_enable_timing(self.handle, 1 if on else 0))
+
+    def read_timing(self) -> dict:
+        """{stage: (total_ms, launches)} since the last read (waits for the events)."""
+        ms = (ctypes.c_double * len(self.STAGES))()
+        n = (ctypes.c_int * len(self.STAGES))()
+        _ck(lib().moe_ctx_read_timing(self.handle, ms, n))
+        return {name: (ms[i], n[i]) for i, name in enumerate(self.STAGES)}
 
     def set_debug(self, bufs: dict | None):
         """bufs: dict with any of accg, accu, a, aq, sa, accd (device tensors) or None."""
@@ -265,6 +281,36 @@ def moe_combine(ctx: MoeCtx, y_slots: torch.Tensor, topk_w: torch.Tensor, has_sh
     _dev(out, torch.float32, "out", (T, H))
     _ck(lib().moe_combine(ctx.handle, y_slots.data_ptr(), topk_w.data_ptr(), T, k, H, 1 if has_shared else 0,
                           out.data_ptr()))
+    return out
+
+
+def moe_layer_forward(ctx: MoeCtx, bits: int, x: torch.Tensor, table: torch.Tensor, shared: ExpertW | None,
+                      k: int, I: int, out: torch.Tensor, w_router: torch.Tensor | None = None,
+                      bias: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                      routed_scale: float = 1.0, topk_idx=None, topk_w=None, xq=None, sx=None, y_slots=None):
+    """Whole layer in one call (see include/moe.h). Optional outputs may be None."""
+    T, H = x.shape
+    E = table.shape[0]
+    _dev(x, torch.float32, "x")
+    _dev(table, torch.int64, "experts table", (E, 6))
+    _dev(out, torch.float32, "out", (T, H))
+    if logits is not None:
+        _dev(logits, torch.float32, "logits", (T, E))
+    else:
+        _dev(w_router, torch.float32, "w_router", (E, H))
+    if bias is not None:
+        _dev(bias, torch.float32, "bias", (E,))
+    for t, dt, shp, nm in ((topk_idx, torch.int32, (T, k), "topk_idx"), (topk_w, torch.float32, (T, k), "topk_w"),
+                           (xq, torch.int8, (T, H), "xq"), (sx, torch.float32, (T,), "sx"),
+                           (y_slots, torch.float32, (T, k + 1, H), "y_slots")):
+        if t is not None:
+            _dev(t, dt, nm, shp)
+    cfg = RouterCfg(E, k, float(routed_scale), 1 if logits is not None else 0)
+    sh = ctypes.byref(shared) if shared is not None else None
+    _ck(lib().moe_layer_forward(ctx.handle, bits, ctypes.byref(cfg), x.data_ptr(), _ptr(logits),
+                                None if logits is not None else w_router.data_ptr(), _ptr(bias), table.data_ptr(), sh,
+                                T, H, I, out.data_ptr(), _ptr(topk_idx), _ptr(topk_w), _ptr(xq), _ptr(sx),
+                                _ptr(y_slots)))
     return out
 
 

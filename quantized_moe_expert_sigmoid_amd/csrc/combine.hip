@@ -35,8 +35,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 moe_status launch_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, int T, int k, int H,
                           int has_shared, float *out) {
   const int64_t n4 = (int64_t)T * (H / 4);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, ctx->stream, y_slots, topk_w,
-                     T, k, H, has_shared, out);
+  {
+    MoeTimer tm_(ctx, MOE_STAGE_COMBINE);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, ctx->stream, y_slots, topk_w,
+                       T, k, H, has_shared, out);
+  }
   MOE_CHECK_LAUNCH("combine_kernel");
   return MOE_OK;
 }

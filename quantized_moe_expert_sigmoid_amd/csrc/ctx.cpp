@@ -26,20 +26,28 @@ moe_status moe_hip_fail(hipError_t e, const char *what) {
 extern "C" const char *moe_last_error(void) { return g_err; }
 extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-moe_status moe_scratch(moe_ctx *ctx, size_t bytes, void **out) {
-  if (bytes > ctx->scratch_bytes) {
-    if (ctx->scratch) {
+static moe_status grow(moe_ctx *ctx, void **buf, size_t *have, size_t bytes, void **out) {
+  if (bytes > *have) {
+    if (*buf) {
       MOE_HIP(hipStreamSynchronize(ctx->stream));
-      MOE_HIP(hipFree(ctx->scratch));
-      ctx->scratch = nullptr;
-      ctx->scratch_bytes = 0;
+      MOE_HIP(hipFree(*buf));
+      *buf = nullptr;
+      *have = 0;
     }
     size_t want = moe_round_up(bytes + bytes / 4, 1 << 20);
-    MOE_HIP(hipMalloc(&ctx->scratch, want));
-    ctx->scratch_bytes = want;
+    MOE_HIP(hipMalloc(buf, want));
+    *have = want;
   }
-  *out = ctx->scratch;
+  *out = *buf;
   return MOE_OK;
+}
+
+moe_status moe_scratch(moe_ctx *ctx, size_t bytes, void **out) {
+  return grow(ctx, &ctx->scratch, &ctx->scratch_bytes, bytes, out);
+}
+
+moe_status moe_io_scratch(moe_ctx *ctx, size_t bytes, void **out) {
+  return grow(ctx, &ctx->io, &ctx->io_bytes, bytes, out);
 }
 
 extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out) {
@@ -75,11 +83,80 @@ extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out
   return MOE_OK;
 }
 
+static hipEvent_t pool_event(moe_ctx *ctx) {
+  if (!ctx->event_pool.empty()) {
+    hipEvent_t e = ctx->event_pool.back();
+    ctx->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+MoeTimer::MoeTimer(moe_ctx *c, int s) : ctx(c), stage(s) {
+  if (!ctx->timing) return;
+  start = pool_event(ctx);
+  if (start && hipEventRecord(start, ctx->stream) != hipSuccess) {
+    ctx->event_pool.push_back(start);
+    start = nullptr;
+  }
+}
+
+MoeTimer::~MoeTimer() {
+  if (!start) return;
+  hipEvent_t stop = pool_event(ctx);
+  if (stop && hipEventRecord(stop, ctx->stream) == hipSuccess) {
+    ctx->timed.push_back({start, stop, stage});
+  } else {
+    ctx->event_pool.push_back(start);
+    if (stop) ctx->event_pool.push_back(stop);
+  }
+}
+
+extern "C" moe_status moe_ctx_enable_timing(moe_ctx *ctx, int enable) {
+  if (!ctx) return moe_fail(MOE_EINVAL, "moe_ctx_enable_timing: ctx is NULL");
+  ctx->timing = enable != 0;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_ctx_read_timing(moe_ctx *ctx, double *ms_host, int *n_host) {
+  if (!ctx) return moe_fail(MOE_EINVAL, "moe_ctx_read_timing: ctx is NULL");
+  MOE_HIP(hipSetDevice(ctx->device));
+  double ms[MOE_N_STAGES] = {};
+  int n[MOE_N_STAGES] = {};
+  moe_status st = MOE_OK;
+  for (auto &t : ctx->timed) {
+    float v = 0.0f;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&v, t.start, t.stop);
+    if (e != hipSuccess && st == MOE_OK) st = moe_hip_fail(e, "hipEventElapsedTime");
+    if (t.stage >= 0 && t.stage < MOE_N_STAGES) {
+      ms[t.stage] += v;
+      n[t.stage] += 1;
+    }
+    ctx->event_pool.push_back(t.start);
+    ctx->event_pool.push_back(t.stop);
+  }
+  ctx->timed.clear();
+  for (int i = 0; i < MOE_N_STAGES; ++i) {
+    if (ms_host) ms_host[i] = ms[i];
+    if (n_host) n_host[i] = n[i];
+  }
+  return st;
+}
+
 extern "C" void moe_ctx_destroy(moe_ctx *ctx) {
   if (!ctx) return;
   (void)hipSetDevice(ctx->device);
   (void)hipStreamSynchronize(ctx->stream);
+  for (auto &t : ctx->timed) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  for (auto e : ctx->event_pool) (void)hipEventDestroy(e);
   if (ctx->scratch) (void)hipFree(ctx->scratch);
+  if (ctx->io) (void)hipFree(ctx->io);
   if (ctx->dev_small) (void)hipFree(ctx->dev_small);
   delete ctx;
 }
@@ -255,4 +332,56 @@ extern "C" size_t moe_expert_block_layout(int bits, int H, int I, size_t *offset
     off = moe_round_up(off + part[i], 256);
   }
   return off;
+}
+
+extern "C" moe_status moe_layer_forward(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x,
+                                        const float *logits, const float *w_router, const float *bias,
+                                        const moe_expert_w *experts, const moe_expert_w *shared, int T, int H, int I,
+                                        float *out, int32_t *topk_idx, float *topk_w, int8_t *xq, float *sx,
+                                        float *y_slots) {
+  moe_status st = bind(ctx, "moe_layer_forward");
+  if (st) return st;
+  REQUIRE(bits == 8 || bits == 4 || bits == 2, "moe_layer_forward: bits %d not in {8,4,2}", bits);
+  REQUIRE(cfg, "moe_layer_forward: cfg is NULL");
+  const int E = cfg->n_experts, k = cfg->top_k;
+  REQUIRE(E >= 1 && E <= 1024 && k >= 1 && k <= 16 && k <= E, "moe_layer_forward: E %d k %d", E, k);
+  REQUIRE(T >= 0 && (int64_t)T * (k + 1) <= (1 << 22), "moe_layer_forward: T %d", T);
+  REQUIRE(dim_ok(H) && dim_ok(I), "moe_layer_forward: H %d and I %d must be positive multiples of 64, <= 8192", H, I);
+  if (T == 0) return MOE_OK;
+  REQUIRE(x && experts && out, "moe_layer_forward: NULL pointer");
+  REQUIRE(cfg->logits_in ? (logits != nullptr) : (w_router != nullptr),
+          "moe_layer_forward: logits_in needs logits, otherwise w_router is required");
+  REQUIRE(moe_aligned16(x) && moe_aligned16(out) && (!xq || moe_aligned16(xq)) && (!y_slots || moe_aligned16(y_slots)),
+          "moe_layer_forward: pointers must be 16-byte aligned");
+  REQUIRE(cfg->logits_in || moe_aligned16(w_router), "moe_layer_forward: w_router must be 16-byte aligned");
+  if (shared)
+    REQUIRE(shared->gate && shared->up && shared->down && shared->s_gate && shared->s_up && shared->s_down,
+            "moe_layer_forward: shared expert has a NULL member");
+  const float *lg = cfg->logits_in ? logits : nullptr;
+  if (T == 1 && decode_t1_supported(bits, H, I, k, shared ? 1 : 0, ctx->n_cu))
+    return launch_layer_t1(ctx, bits, cfg, x, lg, w_router, bias, experts, shared, H, I, out, topk_idx, topk_w, xq, sx,
+                           y_slots);
+  // composed path: intermediates the caller did not ask for live in io scratch
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = moe_round_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_idx = take(4 * (size_t)T * k), o_w = take(4 * (size_t)T * k), o_xq = take((size_t)T * H),
+               o_sx = take(4 * (size_t)T), o_y = take(4 * (size_t)T * (k + 1) * H);
+  void *io = nullptr;
+  st = moe_io_scratch(ctx, off, &io);
+  if (st) return st;
+  char *b = static_cast<char *>(io);
+  if (!topk_idx) topk_idx = reinterpret_cast<int32_t *>(b + o_idx);
+  if (!topk_w) topk_w = reinterpret_cast<float *>(b + o_w);
+  if (!xq) xq = reinterpret_cast<int8_t *>(b + o_xq);
+  if (!sx) sx = reinterpret_cast<float *>(b + o_sx);
+  if (!y_slots) y_slots = reinterpret_cast<float *>(b + o_y);
+  if ((st = launch_quantize_act(ctx, x, T, H, xq, sx))) return st;
+  if ((st = launch_router(ctx, cfg, lg ? lg : x, w_router, bias, T, H, topk_idx, topk_w))) return st;
+  if ((st = launch_expert_ffn(ctx, bits, experts, shared, nullptr, xq, sx, topk_idx, T, H, I, E, k, y_slots)))
+    return st;
+  return launch_combine(ctx, y_slots, topk_w, T, k, H, shared ? 1 : 0, out);
 }

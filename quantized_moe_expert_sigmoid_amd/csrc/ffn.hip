@@ -429,11 +429,20 @@ __global__ __launch_bounds__(kThreads) void ffn_down_kernel(FfnArgs a) {
 
 template <int BITS>
 moe_status launch_ffn_bits(moe_ctx *ctx, FfnArgs &a, int dmax) {
-  hipLaunchKernelGGL(ffn_gateup_kernel<BITS>, dim3(dmax * a.tiles1), dim3(kThreads), 0, ctx->stream, a);
+  {
+    MoeTimer tm_(ctx, MOE_STAGE_GATEUP);
+    hipLaunchKernelGGL(ffn_gateup_kernel<BITS>, dim3(dmax * a.tiles1), dim3(kThreads), 0, ctx->stream, a);
+  }
   MOE_CHECK_LAUNCH("ffn_gateup_kernel");
-  hipLaunchKernelGGL(ffn_requant_kernel, dim3(a.T * (a.k + 1)), dim3(kThreads), 0, ctx->stream, a);
+  {
+    MoeTimer tm_(ctx, MOE_STAGE_REQUANT);
+    hipLaunchKernelGGL(ffn_requant_kernel, dim3(a.T * (a.k + 1)), dim3(kThreads), 0, ctx->stream, a);
+  }
   MOE_CHECK_LAUNCH("ffn_requant_kernel");
-  hipLaunchKernelGGL(ffn_down_kernel<BITS>, dim3(dmax * a.tiles2), dim3(kThreads), 0, ctx->stream, a);
+  {
+    MoeTimer tm_(ctx, MOE_STAGE_DOWN);
+    hipLaunchKernelGGL(ffn_down_kernel<BITS>, dim3(dmax * a.tiles2), dim3(kThreads), 0, ctx->stream, a);
+  }
   MOE_CHECK_LAUNCH("ffn_down_kernel");
   return MOE_OK;
 }

@@ -1,0 +1,166 @@
+// Device helpers shared by the streaming GEMV kernels: DPP wave reductions,
+// activation chunks held in registers in the packed weights' field order,
+// and the integer dot product of one 16-byte weight chunk.
+#pragma once
+
+#include "moe_internal.h"
+
+// Pointers read from memory are generic (flat) to the compiler; flat loads
+// also count against the scalar-load counter, so a wait for a scalar load
+// would stall on them. Weight and activation reads go through this cast to
+// the global address space instead.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T *gptr(const T *p) {
+  return (const __attribute__((address_space(1))) T *)p;
+}
+typedef unsigned int moe_u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte global load of p[idx]
+__device__ __forceinline__ uint4 ldg16(const void *p, int idx) {
+  const moe_u32x4 v = gptr(reinterpret_cast<const moe_u32x4 *>(p))[idx];
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
+// wave reductions with DPP (sum lands in lane 63)
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ int wave_sum_to63(int v) {
+  v += dpp_i<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_i<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_i<0x141>(v);       // row_half_mirror
+  v += dpp_i<0x140>(v);       // row_mirror
+  v += dpp_i<0x142, 0xa>(v);  // row_bcast:15 -> rows 1, 3
+  v += dpp_i<0x143, 0xc>(v);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+// wave-uniform total
+__device__ __forceinline__ int wave_sum_all(int v) { return __builtin_amdgcn_readlane(wave_sum_to63(v), 63); }
+
+// max / min reductions: lanes of masked rows keep their own value
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_keep(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ float fmax_dpp_step(float v, int d) { return fmaxf(v, __int_as_float(d)); }
+// wave-uniform maximum (no NaN inputs)
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmax_dpp_step(v, dpp_keep<0xB1>(__float_as_int(v)));
+  v = fmax_dpp_step(v, dpp_keep<0x4E>(__float_as_int(v)));
+  v = fmax_dpp_step(v, dpp_keep<0x141>(__float_as_int(v)));
+  v = fmax_dpp_step(v, dpp_keep<0x140>(__float_as_int(v)));
+  v = fmax_dpp_step(v, dpp_keep<0x142, 0xa>(__float_as_int(v)));
+  v = fmax_dpp_step(v, dpp_keep<0x143, 0xc>(__float_as_int(v)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// wave-uniform minimum
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  v = min(v, dpp_keep<0xB1>(v));
+  v = min(v, dpp_keep<0x4E>(v));
+  v = min(v, dpp_keep<0x141>(v));
+  v = min(v, dpp_keep<0x140>(v));
+  v = min(v, dpp_keep<0x142, 0xa>(v));
+  v = min(v, dpp_keep<0x143, 0xc>(v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ float wave_max_all(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// activation bytes met by one 16-byte chunk of a packed row, in field order
+// (8-bit weights: 16 bytes, 4-bit: 32, 2-bit: 64)
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct ActChunk {
+  static constexpr int kDw = QFmt<BITS>::kEpc / 4;
+  uint32_t d[kDw];
+};
+
+template <int BITS>
+__device__ __forceinline__ void act_chunk_from(const uint4 *v, ActChunk<BITS> &o, int &bytesum) {
+  constexpr int EPC = QFmt<BITS>::kEpc;
+  bytesum = 0;
+#pragma unroll
+  for (int u = 0; u < EPC / 16; ++u) {
+    const uint4 x = v[u];
+    const int ones = 0x01010101;
+    bytesum = sdot4((int)x.x, ones, bytesum);
+    bytesum = sdot4((int)x.y, ones, bytesum);
+    bytesum = sdot4((int)x.z, ones, bytesum);
+    bytesum = sdot4((int)x.w, ones, bytesum);
+    if constexpr (BITS == 4) {
+      act_order_q4(x.x, x.y, o.d[4 * u + 0], o.d[4 * u + 1]);
+      act_order_q4(x.z, x.w, o.d[4 * u + 2], o.d[4 * u + 3]);
+    } else if constexpr (BITS == 2) {
+      const uint32_t in[4] = {x.x, x.y, x.z, x.w};
+      uint32_t out[4];
+      act_order_q2(in, out);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o.d[4 * u + j] = out[j];
+    } else {
+      o.d[0] = x.x;
+      o.d[1] = x.y;
+      o.d[2] = x.z;
+      o.d[3] = x.w;
+    }
+  }
+}
+
+// Load the chunk's activation bytes (row of int8, chunk index c) and order them.
+template <int BITS>
+__device__ __forceinline__ void load_act_chunk(const int8_t *row, int c, ActChunk<BITS> &o, int &bytesum) {
+  constexpr int EPC = QFmt<BITS>::kEpc;
+  uint4 v[EPC / 16];
+  const int8_t *p = row + (int64_t)c * EPC;
+#pragma unroll
+  for (int u = 0; u < EPC / 16; ++u) v[u] = ldg16(p, u);
+  act_chunk_from<BITS>(v, o, bytesum);
+}
+
+template <int BITS>
+__device__ __forceinline__ void zero_chunk(ActChunk<BITS> &o) {
+#pragma unroll
+  for (int q = 0; q < ActChunk<BITS>::kDw; ++q) o.d[q] = 0;
+}
+
+// sum over the chunk of code(w) * x, codes still offset (q + kOff)
+template <int BITS>
+__device__ __forceinline__ int dot_regs(uint4 w, const ActChunk<BITS> &x, int acc) {
+  if constexpr (BITS == 8) {
+    acc = sdot4((int)w.x, (int)x.d[0], acc);
+    acc = sdot4((int)w.y, (int)x.d[1], acc);
+    acc = sdot4((int)w.z, (int)x.d[2], acc);
+    return sdot4((int)w.w, (int)x.d[3], acc);
+  } else if constexpr (BITS == 4) {
+    constexpr uint32_t M = 0x0f0f0f0fu;
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc = sdot4((int)(wd[m] & M), (int)x.d[2 * m], acc);
+      acc = sdot4((int)((wd[m] >> 4) & M), (int)x.d[2 * m + 1], acc);
+    }
+    return acc;
+  } else {
+    constexpr uint32_t M = 0x03030303u;
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc = sdot4((int)(wd[m] & M), (int)x.d[4 * m + 0], acc);
+      acc = sdot4((int)((wd[m] >> 2) & M), (int)x.d[4 * m + 1], acc);
+      acc = sdot4((int)((wd[m] >> 4) & M), (int)x.d[4 * m + 2], acc);
+      acc = sdot4((int)((wd[m] >> 6) & M), (int)x.d[4 * m + 3], acc);
+    }
+    return acc;
+  }
+}
+
+// chunks per lane (ceil) of a packed row of n elements
+__host__ __device__ constexpr int moe_chunks_per_lane(int n, int bits) {
+  return (n * bits / 8 / 16 + MOE_WAVE - 1) / MOE_WAVE;
+}

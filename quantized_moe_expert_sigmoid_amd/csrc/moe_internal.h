@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "moe.h"
 
 // ---------------------------------------------------------------------------
@@ -24,16 +26,38 @@ struct moe_ctx {
   // growable scratch (device)
   void *scratch = nullptr;
   size_t scratch_bytes = 0;
+  // intermediates of the composed whole-layer path (kept apart from scratch,
+  // which the per-step entry points reuse)
+  void *io = nullptr;
+  size_t io_bytes = 0;
   // small persistent device block: error flags and counters
   uint32_t *dev_small = nullptr;  // [0] error flags, [1..] counters
   bool dbg_on = false;
   moe_debug_bufs dbg{};
+  // per-kernel timing (measurement only)
+  bool timing = false;
+  struct TimedLaunch {
+    hipEvent_t start, stop;
+    int stage;
+  };
+  std::vector<TimedLaunch> timed;      // recorded, not yet read
+  std::vector<hipEvent_t> event_pool;  // reusable events
+};
+
+// Bracket one kernel launch with timing events when ctx->timing is on.
+struct MoeTimer {
+  moe_ctx *ctx;
+  int stage;
+  hipEvent_t start = nullptr;
+  MoeTimer(moe_ctx *c, int s);
+  ~MoeTimer();
 };
 
 moe_status moe_fail(moe_status st, const char *fmt, ...);
 moe_status moe_hip_fail(hipError_t e, const char *what);
 // Make the scratch at least `bytes` large; returns its pointer or nullptr.
 moe_status moe_scratch(moe_ctx *ctx, size_t bytes, void **out);
+moe_status moe_io_scratch(moe_ctx *ctx, size_t bytes, void **out);
 
 #define MOE_HIP(expr)                                   \
   do {                                                  \
@@ -63,6 +87,11 @@ moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts
                              int T, int H, int I, int E, int k, float *y_slots);
 moe_status launch_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, int T, int k, int H,
                           int has_shared, float *out);
+bool decode_t1_supported(int bits, int H, int I, int k, int has_shared, int n_cu);
+moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x, const float *logits,
+                           const float *w_router, const float *bias, const moe_expert_w *experts,
+                           const moe_expert_w *shared, int H, int I, float *out, int32_t *topk_idx, float *topk_w,
+                           int8_t *xq, float *sx, float *y_slots);
 
 // ---------------------------------------------------------------------------
 // Device side

@@ -85,5 +85,6 @@ moe_status launch_quantize_rows(moe_ctx *ctx, int bits, const float *w, int64_t 
 
 // The activation rule is the 8-bit row rule applied per token.
 moe_status launch_quantize_act(moe_ctx *ctx, const float *x, int T, int H, int8_t *xq, float *sx) {
+  MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
   return launch_q<8>(ctx, x, T, H, reinterpret_cast<uint8_t *>(xq), sx);
 }

@@ -135,10 +135,18 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
     key[m] = 0.0f;
     const int e = lane + m * MOE_WAVE;
     if (m < per && e < E) {
+      // all slice loads issued together, then added in slice order
+      constexpr int kMaxSlices = 16;
+      float zs[kMaxSlices];
+#pragma unroll
+      for (int s = 0; s < kMaxSlices; ++s) zs[s] = (s < nslices) ? partial[((int64_t)s * T + t) * E + e] : 0.0f;
       float z = 0.0f;
-      for (int s = 0; s < nslices; ++s) z += partial[((int64_t)s * T + t) * E + e];
+#pragma unroll
+      for (int s = 0; s < kMaxSlices; ++s)
+        if (s < nslices) z += zs[s];
       sig[m] = 1.0f / (1.0f + moe_exp_f32(-z));
       key[m] = sig[m] + (bias ? bias[e] : 0.0f);
+      if (key[m] != key[m]) key[m] = -__builtin_inff();  // a NaN key ranks last
     }
   }
   unsigned taken = 0;  // bit m: element m of this lane already selected
@@ -317,7 +325,10 @@ moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, 
                          int32_t *perm, const uint8_t *expert_bits, int want_bits, int32_t *active,
                          int32_t *n_active) {
   BucketArgs a{idx, T, k, E, counts, offsets, perm, expert_bits, want_bits, active, n_active, ctx->dev_small};
-  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBThreads), 0, ctx->stream, a);
+  {
+    MoeTimer tm_(ctx, MOE_STAGE_BUCKET);
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBThreads), 0, ctx->stream, a);
+  }
   MOE_CHECK_LAUNCH("bucket_kernel");
   return MOE_OK;
 }
@@ -338,11 +349,11 @@ moe_status launch_router(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x
       // enough waves to stream w_router with the whole chip: ~4 waves per CU
       const int groups = (E + 3) / 4;
       ks = 1;
-      while (groups * ks < 2 * ctx->n_cu && H % (ks * 2 * 256) == 0) ks *= 2;
+      while (groups * ks < 2 * ctx->n_cu && H % (ks * 2 * 256) == 0 && ks < 16) ks *= 2;
     } else {
       const int tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
       ks = 1;
-      while (tiles * ks < 2 * ctx->n_cu && H % (ks * 2 * kTileK) == 0 && H / (ks * 2) >= 256) ks *= 2;
+      while (tiles * ks < 2 * ctx->n_cu && H % (ks * 2 * kTileK) == 0 && H / (ks * 2) >= 256 && ks < 16) ks *= 2;
     }
     const int kl = H / ks;
     void *scr = nullptr;
@@ -350,18 +361,27 @@ moe_status launch_router(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x
     if (st) return st;
     float *part = static_cast<float *>(scr);
     if (T <= kSmallT) {
-      hipLaunchKernelGGL(router_gemv_kernel, dim3((E + 3) / 4, ks), dim3(256), 0, ctx->stream, x, w_router, T, H, E,
-                         kl, part);
+      {
+        MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
+        hipLaunchKernelGGL(router_gemv_kernel, dim3((E + 3) / 4, ks), dim3(256), 0, ctx->stream, x, w_router, T, H, E,
+                           kl, part);
+      }
     } else {
-      hipLaunchKernelGGL(router_gemm_kernel, dim3((T + kTile - 1) / kTile, (E + kTile - 1) / kTile, ks), dim3(256),
-                         0, ctx->stream, x, w_router, T, H, E, kl, part);
+      {
+        MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
+        hipLaunchKernelGGL(router_gemm_kernel, dim3((T + kTile - 1) / kTile, (E + kTile - 1) / kTile, ks), dim3(256),
+                           0, ctx->stream, x, w_router, T, H, E, kl, part);
+      }
     }
     MOE_CHECK_LAUNCH("router logits kernel");
     partial = part;
     nslices = ks;
   }
-  hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, ctx->stream, partial, nslices, T, E, k,
-                     bias, cfg->routed_scale, topk_idx, topk_w);
+  {
+    MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
+    hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, ctx->stream, partial, nslices, T, E, k,
+                       bias, cfg->routed_scale, topk_idx, topk_w);
+  }
   MOE_CHECK_LAUNCH("router_topk_kernel");
   return MOE_OK;
 }

@@ -11,7 +11,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (FFN_BY_BITS, ExpertBlocks, MoeCtx, moe_combine, moe_quantize_act_i8, moe_router_topk)
+from . import (FFN_BY_BITS, ExpertBlocks, MoeCtx, moe_combine, moe_layer_forward, moe_quantize_act_i8,
+               moe_router_topk)
 
 
 def _to_dev(a, device):
@@ -61,8 +62,22 @@ class MoeLayer:
 
     # -- forward -----------------------------------------------------------
     def forward(self, x: torch.Tensor, logits: torch.Tensor | None = None) -> dict:
-        """x: fp32 [T][H] device tensor; logits (optional) fp32 [T][E] to route
-        on given logits instead of the router weights. Returns the buffers."""
+        """The whole layer in one library call (moe_layer_forward). x: fp32
+        [T][H] device tensor; logits (optional) fp32 [T][E] to route on given
+        logits instead of the router weights. Returns the buffers (out, idx,
+        w, xq, sx, y)."""
+        T = x.shape[0]
+        b = self.buffers(T)
+        sh = self.shared.struct(0) if self.shared is not None else None
+        moe_layer_forward(self.ctx, self.bits, x, self.experts.table, sh, self.k, self.I, b["out"],
+                          w_router=None if logits is not None else self.w_router, bias=self.bias, logits=logits,
+                          routed_scale=self.routed_scale, topk_idx=b["idx"], topk_w=b["w"], xq=b["xq"], sx=b["sx"],
+                          y_slots=b["y"])
+        return b
+
+    def forward_steps(self, x: torch.Tensor, logits: torch.Tensor | None = None) -> dict:
+        """The same layer through the per-step entry points: moe_quantize_act_i8
+        -> moe_router_topk -> moe_expert_ffn_q* -> moe_combine."""
         T = x.shape[0]
         b = self.buffers(T)
         ctx = self.ctx

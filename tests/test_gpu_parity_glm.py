@@ -1,0 +1,180 @@
+"""GPU parity at the full GLM-5.2 layer shape (hidden 6144, 256 routed experts
++ 1 shared, top-8, intermediate 2048, int4), in the launch configuration the
+benchmark times, on sampled tokens the oracle computes one by one.
+
+Shape source: tech.takumi3488.com "Trying colibri", section on the real 744B
+model (hidden 6144, 256 experts/layer, top-8); agentlenshq.com "Colibri ...",
+section "Memory split" (about 19 MB per int4 expert -> intermediate 2048).
+
+One layer's weights (seed 1) serve every batch size below; the batches differ
+in their hidden states and, for the Zipf cases, in the given router logits.
+Checked per sampled token: packed bytes of every routed expert and of the
+shared expert (bit-exact against the oracle's own packing of the same fp32
+weights), activation codes, router indices (exact away from near-ties) and
+weights, every expert output slot (bit-exact), the combined output (1e-3 of
+the row max). Over all tokens: routing validity.
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import compare_router, log, rel_row_err
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def glm():
+    assert torch.cuda.is_available()
+    import bench
+    import quantized_moe_expert_sigmoid_amd as moe
+    from synth import workloads as wl
+    moe.lib()
+    ctx = moe.MoeCtx(0)
+    log("building GLM layer (257 experts)")
+    L = bench.build_gpu_layer(ctx, wl.DECODE1, 4)
+    log("built")
+    yield moe, ctx, L
+    ctx.close()
+
+
+class OracleExperts:
+    """Oracle-side packing of the same fp32 weights, built lazily per expert."""
+
+    def __init__(self, orc, w):
+        self.orc, self.w, self.cache = orc, w, {}
+        from synth import workloads as wl
+        self.wl = wl
+        self.shared = orc.pack_expert(4, *wl.shared_fp32(w))
+
+    def get(self, e):
+        if e not in self.cache:
+            self.cache[e] = self.orc.pack_expert(4, *self.wl.expert_fp32(self.w, e))
+        return self.cache[e]
+
+
+@pytest.fixture(scope="module")
+def oexp(orc):
+    from synth import workloads as wl
+    return OracleExperts(orc, wl.DECODE1)
+
+
+def check_packed(L, e, ex):
+    g, u, d, sg, su, sd = L.experts.views(e) if e >= 0 else L.shared.views(0)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), ex.gate) and np.array_equal(u.cpu().numpy(), ex.up)
+    assert np.array_equal(d.cpu().numpy(), ex.down)
+    assert np.array_equal(sg.cpu().numpy(), ex.s_gate) and np.array_equal(su.cpu().numpy(), ex.s_up)
+    assert np.array_equal(sd.cpu().numpy(), ex.s_down)
+
+
+def run_and_check(glm, orc, oexp, x, logits, sample, checked_packed):
+    moe, ctx, L = glm
+    wl = oexp.wl
+    w = oexp.w
+    T = x.shape[0]
+    res = L.forward(torch.from_numpy(x).cuda(), None if logits is None else torch.from_numpy(logits).cuda())
+    ctx.check()
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in res.items()}
+    wr, bias = wl.router_fp32(w)
+    if logits is None:
+        idx_o, w_o, keys, sig = orc.router(x, wr, bias, w.k, want_keys=True)
+    else:
+        idx_o, w_o, keys, sig = orc.router(logits, None, None, w.k, logits_in=True, want_keys=True)
+    near = compare_router(got["idx"], got["w"], idx_o, keys, sig)
+    assert near <= max(1, T // 100), near
+    xq_o, sx_o = orc.quantize_act(x)
+    assert np.array_equal(got["xq"], xq_o) and np.array_equal(got["sx"], sx_o)
+    if -1 not in checked_packed:
+        check_packed(L, -1, oexp.shared)
+        checked_packed.add(-1)
+    for t in sample:
+        ys = []
+        for j in range(w.k):
+            e = int(got["idx"][t, j])
+            ex = oexp.get(e)
+            if e not in checked_packed:
+                check_packed(L, e, ex)
+                checked_packed.add(e)
+            y = orc.expert_token(ex, xq_o[t], float(sx_o[t]))["y"]
+            assert np.array_equal(got["y"][t, j].view(np.uint32), y.view(np.uint32)), (t, j, e)
+            ys.append(y)
+        ysh = orc.expert_token(oexp.shared, xq_o[t], float(sx_o[t]))["y"]
+        assert np.array_equal(got["y"][t, w.k], ysh)
+        ref = orc.combine(np.stack(ys + [ysh])[None], got["w"][t:t + 1], True)
+        err = rel_row_err(got["out"][t:t + 1], ref)
+        assert err.max() < 1e-3, err
+    return got
+
+
+@pytest.fixture(scope="module")
+def packed_seen():
+    return set()
+
+
+def test_glm_decode_t1(glm, orc, oexp, packed_seen):
+    from synth import workloads as wl
+    for batch in range(3):
+        log(f"decode T=1 batch {batch}")
+        x = wl.hidden_fp32(wl.DECODE1, 1, batch=batch)
+        run_and_check(glm, orc, oexp, x, None, [0], packed_seen)
+
+
+def test_glm_decode_t64_zipf(glm, orc, oexp, packed_seen):
+    from synth import workloads as wl
+    log("decode T=64 zipf")
+    x = wl.hidden_fp32(wl.DECODE64, 64)
+    z = wl.logits_fp32(wl.DECODE64, 64)
+    L = glm[2]
+    keep, L.bias = L.bias, None  # Zipf logits route without a selection bias
+    try:
+        got = run_and_check(glm, orc, oexp, x, z, [0, 37, 63], packed_seen)
+    finally:
+        L.bias = keep
+    assert len(np.unique(got["idx"])) < 200  # Zipf concentrates the routing
+
+
+def test_glm_mtp_verify_t96(glm, orc, oexp, packed_seen):
+    from synth import workloads as wl
+    log("mtp verify T=96")
+    x = wl.hidden_fp32(wl.MTP96, 96)
+    run_and_check(glm, orc, oexp, x, None, [5, 95], packed_seen)
+
+
+def test_glm_prefill_t2048(glm, orc, oexp, packed_seen):
+    from synth import workloads as wl
+    log("prefill T=2048")
+    x = wl.hidden_fp32(wl.PREFILL2048, 2048)
+    run_and_check(glm, orc, oexp, x, None, [0, 2047], packed_seen)
+
+
+def test_glm_graph_replay_matches_eager(glm):
+    """The benchmark replays the hot path as a HIP graph: every replay, with
+    eager work and synchronisations in between, equals the eager result."""
+    from synth import workloads as wl
+    moe, ctx, L = glm
+    xs = [torch.from_numpy(wl.hidden_fp32(wl.DECODE1, 1, batch=b)).cuda() for b in range(4)]
+    eager = []
+    for x in xs:
+        r = L.forward(x)
+        torch.cuda.synchronize()
+        eager.append((r["idx"].clone(), r["y"].clone(), r["out"].clone()))
+    cap = torch.cuda.Stream()
+    old = ctx.stream
+    ctx.set_stream(cap)
+    g = torch.cuda.CUDAGraph()
+    outs = []
+    with torch.cuda.graph(g, stream=cap):
+        for x in xs:
+            r = L.forward(x)
+            outs.append(r["out"].clone())
+    ctx.set_stream(old)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(4):
+            assert torch.equal(outs[i], eager[i][2]), (rep, i)
+        L.forward(xs[rep])  # eager work between replays
+        torch.cuda.synchronize()
+    ctx.check()

@@ -307,3 +307,65 @@ def test_layer_tiny_end_to_end(moe, ctx, orc, syn, bits):
     assert np.array_equal(host(res["y"]), ref["y_slots"])
     err = rel_row_err(host(res["out"]), ref["out"])
     assert err.max() < 1e-3, err.max()
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("H,I,E,k,shared", [(128, 64, 8, 2, True), (512, 192, 16, 8, True), (256, 128, 8, 3, False)])
+def test_layer_t1_fused_intermediates(moe, ctx, orc, syn, bits, H, I, E, k, shared):
+    """One token through moe_layer_forward (router+top-k+quant, gate/up with
+    last-wave requantisation, down fused with the combine): every captured
+    intermediate bit-exact against the oracle, and the output bit-identical to
+    the per-step entry points."""
+    from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
+    log(f"fused t1 bits={bits} H={H} I={I} E={E} k={k} shared={shared}")
+    seed = 80 + bits
+    L = MoeLayer(ctx, H, I, E, k, bits=bits, has_shared=shared)
+    oexp = []
+    for e in range(E):
+        g, u, d = syn.expert_weights(seed, 0, e, H, I)
+        L.set_expert_fp32(e, g, u, d)
+        oexp.append(orc.pack_expert(bits, g, u, d))
+    osh = None
+    if shared:
+        g, u, d = syn.expert_weights(seed, 0, 0, H, I, shared=True)
+        L.set_shared_fp32(g, u, d)
+        osh = orc.pack_expert(bits, g, u, d)
+    wr = syn.router_weights(seed, 0, E, H)
+    bias = syn.router_bias(seed, 0, E)
+    L.set_router(wr, bias)
+    S = k + 1
+    for tok in range(3):
+        x = syn.hidden(seed, 1, H, batch=tok)
+        dbg = dict(accg=torch.zeros((S, I), dtype=torch.int32, device="cuda"),
+                   accu=torch.zeros((S, I), dtype=torch.int32, device="cuda"),
+                   a=torch.zeros((S, I), dtype=torch.float32, device="cuda"),
+                   aq=torch.zeros((S, I), dtype=torch.int8, device="cuda"),
+                   sa=torch.zeros((S,), dtype=torch.float32, device="cuda"),
+                   accd=torch.zeros((S, H), dtype=torch.int32, device="cuda"))
+        ctx.set_debug(dbg)
+        try:
+            res = L.forward(dev(x))
+            ctx.check()
+        finally:
+            ctx.set_debug(None)
+        got = {n: host(t) for n, t in dbg.items()}
+        fused = {n: host(t).copy() for n, t in res.items()}
+        ref = orc.layer(x, orc.ExpertTable(oexp), osh, k, wr=wr, bias=bias)
+        _, _, keys, sig = orc.router(x, wr, bias, k, want_keys=True)
+        assert compare_router(fused["idx"], fused["w"], ref["idx"], keys, sig) == 0
+        assert np.array_equal(fused["xq"], ref["xq"]) and np.array_equal(fused["sx"], ref["sx"])
+        for j in range(k + (1 if shared else 0)):
+            ex = osh if j == k else oexp[fused["idx"][0, j]]
+            r = orc.expert_token(ex, ref["xq"][0], float(ref["sx"][0]))
+            assert np.array_equal(got["accg"][j], r["accg"]), j
+            assert np.array_equal(got["accu"][j], r["accu"]), j
+            assert np.array_equal(got["a"][j].view(np.uint32), r["a"].view(np.uint32)), j
+            assert np.array_equal(got["aq"][j], r["aq"]), j
+            assert got["sa"][j] == np.float32(r["sa"]), j
+            assert np.array_equal(got["accd"][j], r["accd"]), j
+            assert np.array_equal(fused["y"][0, j], r["y"]), j
+        assert rel_row_err(fused["out"], ref["out"]).max() < 1e-3
+        steps = L.forward_steps(dev(x))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(steps["out"]), fused["out"])
+        assert np.array_equal(host(steps["idx"]), fused["idx"])
