@@ -1,4 +1,4 @@
-// Single-token (decode) layer path in three kernels: router logits with the
+// Single-token (decode) layer path in three kernels: router logits and the
 // activation quantisation; top-k fused with a streaming gate/up GEMV; and the
 // int8 requantisation fused with the down GEMV and the combine.
 //
@@ -14,27 +14,31 @@
 // kernels work on "slots": slot j < k is the j-th ranked expert, slot k the
 // shared expert.
 //  K1 router_gemv_t1_kernel: E/4 x KS workgroups compute K-slices of the
-//     logits (one wave per expert and slice); the workgroups of column 0 also
-//     find max|x| over the token and quantise their slice of x to int8.
-//  K2 gateup_t1_kernel (one 512-thread workgroup per CU): every workgroup
-//     sums the logit slices in fixed order, applies the sigmoid and the bias,
-//     selects the top-k in one wave (k rounds of a DPP wave max; equal keys go
-//     to the lower id) and builds the slot table in LDS; workgroup 0 also
-//     publishes ids, weights and the slot table. Then the S*I (gate row, up
-//     row) pairs, split into equal contiguous ranges over all waves, stream
-//     through 16-byte loads two batches deep against the token's int8
-//     activations held in registers (field order); DPP reductions; one store
-//     of a = silu(g)*u per row pair.
-//  K3 down_combine_t1_kernel (one 512-thread workgroup per CU): each wave
-//     issues its first down-row loads, then the workgroup loads every slot's
-//     a (an L2 hit), finds max|a| per slot and writes the int8 codes to LDS
-//     while the weights are in flight; each wave then multiplies its H rows
-//     of every slot's down matrix, writes y per slot and the combined output
+//     logits (one wave per expert and slice); KS more workgroups (the last
+//     column) find max|x| over the token and quantise one slice of x each.
+//  K2 gateup_t1_kernel (one 512-thread workgroup per CU): every wave first
+//     issues the loads of its share of the shared expert's gate/up rows (known
+//     before routing); meanwhile every workgroup sums the logit slices in fixed
+//     order, applies the sigmoid and the bias, and one wave selects the top-k
+//     (k rounds of a DPP wave max over order-preserving integer keys; equal
+//     keys go to the lower id) and builds the slot table in LDS; workgroup 0
+//     also publishes ids, weights and the slot table. Then the k*I routed
+//     (gate row, up row) pairs, split into equal contiguous ranges over all
+//     waves, stream through 16-byte loads two batches deep against the token's
+//     int8 activations held in registers (field order); DPP reductions; one
+//     store of a = silu(g)*u per row pair.
+//  K3 down_combine_t1_kernel (one 512-thread workgroup per CU): the workgroup
+//     loads every slot's a, then each wave issues its first down-row loads;
+//     while they are in flight the workgroup finds max|a| per slot and writes
+//     the int8 codes to LDS, already in the weights' field order, with their
+//     per-slot sums; each wave then multiplies its H rows of every slot's down
+//     matrix, writes y per slot and the combined output
 //     out[r] = y_shared + sum_j w_j y_j (the same fma order as moe_combine).
-// Kernel boundaries order the three steps: no atomics, no cross-workgroup
-// waits (contended device-scope atomics serialise at the memory side).
-// Streaming loads are branch-free: a lane whose chunk index passes the row
-// end reads a clamped in-bounds address and meets zero activation bytes.
+// Kernel boundaries order the three steps: no atomics across workgroups, no
+// cross-workgroup waits (contended device-scope atomics serialise at the
+// memory side). Streaming loads are branch-free: a lane whose chunk index
+// passes the row end reads a clamped in-bounds address and meets zero
+// activation bytes.
 #include "gemv_common.h"
 
 namespace {
@@ -45,7 +49,7 @@ constexpr int kFfnWaves = kFfnThreads / MOE_WAVE;  // 8 waves: one workgroup per
 constexpr int kMaxSlots = 9;                       // top-k <= 8 plus the shared expert
 constexpr int kMaxSlices = 16;                     // K slices of the router logits
 constexpr int kMaxE = 1024;
-constexpr int kMaxX4 = 8;       // float4 of x per thread in the max pass: H <= 8192
+constexpr int kMaxX4 = 8;        // float4 of x per thread in the max pass: H <= 8192
 constexpr int kMaxIDown = 4096;  // intermediate held in LDS by the down kernel
 
 // One slot of the token: the expert's weights and its routing weight.
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void router_gemv_t1_kernel(RouterT1Args a
   const int wave = threadIdx.x >> 6;
   const int ks = blockIdx.y;
   const int k0 = ks * a.kl;
-  if (!a.logits) {
+  if (blockIdx.x + 1 < gridDim.x) {  // a logits workgroup
     const int e = blockIdx.x * (kThreads / MOE_WAVE) + wave;
     if (e < a.E) {
       const float *wrow = a.wr + (int64_t)e * a.H + k0;
@@ -122,9 +126,9 @@ __global__ __launch_bounds__(kThreads) void router_gemv_t1_kernel(RouterT1Args a
       const float s = wave_sum_f32(acc);
       if (lane == 0) a.partial[(int64_t)ks * a.E + e] = s;
     }
+    return;
   }
-  if (blockIdx.x != 0) return;
-  // column 0: max|x| over the whole token, then quantise this slice of x
+  // the last column: max|x| over the whole token, then quantise this slice
   __shared__ float red[kThreads / MOE_WAVE];
   float4 xv[kMaxX4];
 #pragma unroll
@@ -186,31 +190,95 @@ struct GateUpT1Args {
   int dbg_on;
 };
 
-// k rounds of (lane-local best, wave max of the keys, lowest id among the
-// maxima) over keys in LDS: descending key, then ascending id.
-__device__ __forceinline__ void wave_topk(const float *key_s, const float *sig_s, int E, int k, int lane,
-                                          int *sel_id, float *sel_sig) {
-  const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
-  unsigned taken = 0;
+// Order-preserving integer image of a float: a > b as floats (no NaN, no -0)
+// if and only if key_bits(a) > key_bits(b) as signed integers.
+__device__ __forceinline__ int key_bits(float f) {
+  const int i = __float_as_int(f);
+  return i ^ ((i >> 31) & 0x7fffffff);
+}
+// wave-uniform maximum of an int (DPP; lanes of masked rows keep their value)
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, dpp_keep<0xB1>(v));
+  v = max(v, dpp_keep<0x4E>(v));
+  v = max(v, dpp_keep<0x141>(v));
+  v = max(v, dpp_keep<0x140>(v));
+  v = max(v, dpp_keep<0x142, 0xa>(v));
+  v = max(v, dpp_keep<0x143, 0xc>(v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int64_t cat_key(int kb, int id) {
+  return (int64_t)(((uint64_t)(uint32_t)kb << 32) | (uint32_t)~id);
+}
+__device__ __forceinline__ void cex(int64_t &a, int64_t &b) {  // (a, b) <- (max, min)
+  const bool sw = b > a;
+  const int64_t t = a;
+  a = sw ? b : a;
+  b = sw ? t : b;
+}
+
+// Top-k over the keys in LDS (descending key, then ascending id), run by one
+// wave; lane r < k returns the id of rank r. Lane l holds keys l*4 .. l*4+3
+// (E <= 256) as 64-bit (key, ~id) entries sorted in descending order, so
+// every lane's head is its best and, since lanes hold ascending id ranges,
+// the lowest lane whose head equals the wave maximum holds the lowest id among
+// equal keys. Each round takes that head and shifts the winner's list.
+__device__ __forceinline__ int wave_topk4(const float *key_s, int E, int k, int lane) {
+  constexpr int64_t kNone = INT64_MIN;
+  int64_t h[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane * 4 + m;
+    h[m] = e < E ? cat_key(key_bits(key_s[e]), e) : kNone;
+  }
+  cex(h[0], h[1]);
+  cex(h[2], h[3]);
+  cex(h[0], h[2]);
+  cex(h[1], h[3]);
+  cex(h[1], h[2]);
+  int my_id = 0;
   for (int r = 0; r < k; ++r) {
-    float lb = -__builtin_inff();
-    int li = 0x7fffffff;
-    for (int m = 0; m < per; ++m) {
-      const int e = lane + m * MOE_WAVE;
-      const bool ok = (e < E) & !((taken >> m) & 1u);
-      const float kk = key_s[e < E ? e : E - 1];
-      const bool better = ok & ((li == 0x7fffffff) | (kk > lb));
-      lb = better ? kk : lb;
-      li = better ? e : li;
-    }
-    const float wm = wave_max_dpp(lb);
-    const int wid = wave_min_dpp((lb == wm) ? li : 0x7fffffff);
-    if ((wid & (MOE_WAVE - 1)) == lane) taken |= 1u << (wid / MOE_WAVE);
-    if (lane == 0) {
-      sel_id[r] = wid;
-      sel_sig[r] = sig_s[wid];
+    const int hk = (int)(h[0] >> 32);
+    const int wm = wave_max_i32(hk);
+    const uint64_t mask = __ballot(hk == wm);
+    const int wl = (int)__builtin_ctzll(mask);
+    const int id = ~__builtin_amdgcn_readlane((int)(uint32_t)h[0], wl);
+    if (lane == r) my_id = id;
+    if (lane == wl) {
+      h[0] = h[1];
+      h[1] = h[2];
+      h[2] = h[3];
+      h[3] = kNone;
     }
   }
+  return my_id;
+}
+// The same for E <= 1024: 16 keys per lane, each round recomputes the lane's
+// best among the keys not yet taken.
+__device__ __forceinline__ int wave_topk16(const float *key_s, int E, int k, int lane) {
+  constexpr int64_t kNone = INT64_MIN;
+  int64_t h[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int e = lane * 16 + m;
+    h[m] = e < E ? cat_key(key_bits(key_s[e]), e) : kNone;
+  }
+  int my_id = 0;
+  for (int r = 0; r < k; ++r) {
+    int64_t best = h[0];
+#pragma unroll
+    for (int m = 1; m < 16; ++m) best = h[m] > best ? h[m] : best;
+    const int hk = (int)(best >> 32);
+    const int wm = wave_max_i32(hk);
+    const uint64_t mask = __ballot(hk == wm);
+    const int wl = (int)__builtin_ctzll(mask);
+    const int id = ~__builtin_amdgcn_readlane((int)(uint32_t)best, wl);
+    if (lane == r) my_id = id;
+    if (lane == wl) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) h[m] = h[m] == best ? kNone : h[m];
+    }
+  }
+  return my_id;
 }
 
 template <int BITS, int JG, int NB>
@@ -218,20 +286,22 @@ struct GuBatch {
   uint4 g[NB][JG], u[NB][JG];
 };
 
-// Row pointers of a wave's (at most two) slots.
+// Row pointers of a wave's (at most two) routed slots.
 struct WaveSlots {
   int s_first, I;
   const uint8_t *gate0, *up0, *gate1, *up1;
 };
 
-// Load NB row pairs starting at row pair qb; rows past the wave's range
-// re-read its last row (their results are dropped).
+// Load NB routed row pairs starting at routed pair qb; pairs past qlast (the
+// wave's last pair, or pair 0 for a wave without routed pairs) re-read it
+// (their results are dropped). The loads are unconditional, so the compiler
+// can count them when it waits for older loads.
 template <int BITS, int JG, int NB>
-__device__ __forceinline__ void gu_load(const WaveSlots &ws, int qb, int q1, int lane, int rowbytes, int cpr,
+__device__ __forceinline__ void gu_load(const WaveSlots &ws, int qb, int qlast, int lane, int rowbytes, int cpr,
                                         GuBatch<BITS, JG, NB> &bt) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int q = (qb + b < q1) ? qb + b : q1 - 1;
+    const int q = (qb + b < qlast) ? qb + b : qlast;
     const int slot = uniform(q / ws.I);
     const int i = q - slot * ws.I;
     const bool first = slot == ws.s_first;
@@ -247,13 +317,34 @@ __device__ __forceinline__ void gu_load(const WaveSlots &ws, int qb, int q1, int
   }
 }
 
-// Dot products of one batch; lane (row pair - q0) keeps that pair's sums.
+// Load the wave's ns <= NB shared row pairs starting at row i0. Pair 0 is
+// always loaded (a wave without shared pairs reads an in-bounds dummy row).
 template <int BITS, int JG, int NB>
-__device__ __forceinline__ void gu_compute(int qb, int q0, int q1, int lane, const GuBatch<BITS, JG, NB> &bt,
+__device__ __forceinline__ void gu_load_shared(const uint8_t *gate, const uint8_t *up, int i0, int ns, int lane,
+                                               int rowbytes, int cpr, GuBatch<BITS, JG, NB> &bt) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b == 0 || b < ns) {
+      const int64_t o = (int64_t)(i0 + b) * rowbytes;
+#pragma unroll
+      for (int j = 0; j < JG; ++j) {
+        int c = lane + j * MOE_WAVE;
+        c = c < cpr ? c : cpr - 1;
+        bt.g[b][j] = ldg16(gate + o, c);
+        bt.u[b][j] = ldg16(up + o, c);
+      }
+    }
+  }
+}
+
+// Dot products of the first n pairs of a batch; lane (lane0 + b) keeps pair
+// b's sums.
+template <int BITS, int JG, int NB>
+__device__ __forceinline__ void gu_compute(int n, int lane0, int lane, const GuBatch<BITS, JG, NB> &bt,
                                            const ActChunk<BITS> (&xr)[JG], int &res_g, int &res_u) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    if (qb + b < q1) {
+    if (b < n) {
       int ag = 0, au = 0;
 #pragma unroll
       for (int j = 0; j < JG; ++j) {
@@ -262,7 +353,7 @@ __device__ __forceinline__ void gu_compute(int qb, int q0, int q1, int lane, con
       }
       ag = wave_sum_all(ag);
       au = wave_sum_all(au);
-      if (lane == qb + b - q0) {
+      if (lane == lane0 + b) {
         res_g = ag;
         res_u = au;
       }
@@ -275,63 +366,112 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   constexpr int OFF = QFmt<BITS>::kOff;
   __shared__ float key_s[kMaxE], sig_s[kMaxE];
   __shared__ __align__(16) moe_expert_w exp_s[kMaxE];
-  __shared__ int sel_id[16];
-  __shared__ float sel_sig[16];
   __shared__ SlotEntry slot_s[kMaxSlots];
   const int tid = threadIdx.x;
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
   const int nw = gridDim.x * kFfnWaves;
   const int gw = blockIdx.x * kFfnWaves + wave;
-  const int Q = a.S * a.I;
-  const int q0 = uniform((int)((int64_t)gw * Q / nw)), q1 = uniform((int)((int64_t)(gw + 1) * Q / nw));
   const int rowbytes = a.H * BITS / 8;
   const int cpr = rowbytes / 16;
+  // this wave's shared pairs [sh0, sh0 + ns) and routed pairs [q0, q1); lanes
+  // [0, ns) keep the shared results, lanes [ns, ns + q1 - q0) the routed ones
+  const int sh0 = a.has_shared ? uniform((int)((int64_t)gw * a.I / nw)) : 0;
+  const int ns = a.has_shared ? uniform((int)((int64_t)(gw + 1) * a.I / nw)) - sh0 : 0;
+  const int R = a.k * a.I;
+  const int q0 = uniform((int)((int64_t)gw * R / nw)), q1 = uniform((int)((int64_t)(gw + 1) * R / nw));
 
-  // ---- routing keys (every thread, loads first) ----
+  // ---- loads first: the routing inputs, the expert table, the token's int8
+  // activations, all consumed only after the shared rows below are issued.
+  // The loads are unconditional with clamped indices (slices past ks re-read
+  // slice ks-1, experts past E re-read expert E-1): a load under a branch
+  // makes the compiler wait for every older load at the branch's join. ----
   constexpr int kPer = kMaxE / kFfnThreads;
+  const float *zsrc = a.logits ? a.logits : a.partial;
+  const int nsum = a.logits ? 1 : a.ks;
+  const float *bsrc = a.bias ? a.bias : zsrc;
+  // (uniform branches cover the parts only large E or many slices need; at
+  // most 63 loads can be outstanding, so the common case stays well below)
   float zs[kPer][kMaxSlices], bs[kPer];
 #pragma unroll
   for (int m = 0; m < kPer; ++m) {
-    const int e = tid + m * kFfnThreads;
-    const bool ok = e < a.E;
+    if (m == 0 || a.E > m * kFfnThreads) {
+      const int e = min(tid + m * kFfnThreads, a.E - 1);
 #pragma unroll
-    for (int s = 0; s < kMaxSlices; ++s) {
-      zs[m][s] = 0.0f;
-      if (ok && (a.logits ? s == 0 : s < a.ks))
-        zs[m][s] = a.logits ? a.logits[e] : a.partial[(int64_t)s * a.E + e];
+      for (int s = 0; s < kMaxSlices / 2; ++s) zs[m][s] = gptr(zsrc)[(int64_t)min(s, nsum - 1) * a.E + e];
+      if (nsum > kMaxSlices / 2) {
+#pragma unroll
+        for (int s = kMaxSlices / 2; s < kMaxSlices; ++s) zs[m][s] = gptr(zsrc)[(int64_t)min(s, nsum - 1) * a.E + e];
+      }
+      bs[m] = gptr(bsrc)[e];
     }
-    bs[m] = (ok && a.bias) ? a.bias[e] : 0.0f;
   }
-  // the expert pointer table into LDS (48 bytes per expert, 16-byte pieces)
+  constexpr int kExpPer = (3 * kMaxE + kFfnThreads - 1) / kFfnThreads;  // 16-byte pieces per thread
+  uint4 exr[kExpPer];
+#pragma unroll
+  for (int i = 0; i < kExpPer; ++i)
+    if (i < 2 || 3 * a.E > i * kFfnThreads) exr[i] = ldg16(a.experts, min(tid + i * kFfnThreads, 3 * a.E - 1));
+  constexpr int EPC = QFmt<BITS>::kEpc;
+  uint4 xraw[JG][EPC / 16];
+#pragma unroll
+  for (int j = 0; j < JG; ++j) {
+    const int c = min(lane + j * MOE_WAVE, cpr - 1);
+#pragma unroll
+    for (int u = 0; u < EPC / 16; ++u) xraw[j][u] = ldg16(a.xq + (int64_t)c * EPC, u);
+  }
+  const float sxv = a.sx[0];
+  asm volatile("" ::: "memory");
+
+  // ---- the shared expert's rows: known before routing, so they stream while
+  // the keys are formed and ranked (unconditional loads; without a shared
+  // expert a dummy in-bounds row of xq is read and dropped) ----
+  GuBatch<BITS, JG, NB> b0, b1;
   {
-    const uint4 *src = reinterpret_cast<const uint4 *>(a.experts);
-    uint4 *dst = reinterpret_cast<uint4 *>(exp_s);
-    for (int i = tid; i < 3 * a.E; i += kFfnThreads) dst[i] = ldg16(src, i);
+    const uint8_t *sg_p = a.has_shared ? a.shared.gate : reinterpret_cast<const uint8_t *>(a.xq);
+    const uint8_t *su_p = a.has_shared ? a.shared.up : reinterpret_cast<const uint8_t *>(a.xq);
+    gu_load_shared<BITS, JG, NB>(sg_p, su_p, a.has_shared ? sh0 : 0, ns, lane, rowbytes, cpr, b0);
   }
-  // the token's activations in registers (the same for every slot)
+  float sg_sh, su_sh;
+  {
+    const bool use = a.has_shared != 0;
+    const int li = use ? sh0 + min(lane, max(ns - 1, 0)) : 0;
+    sg_sh = gptr(use ? a.shared.s_gate : a.sx)[li];
+    su_sh = gptr(use ? a.shared.s_up : a.sx)[li];
+  }
+  asm volatile("" ::: "memory");
+
+  // ---- now consume: the expert table to LDS, the activations in field
+  // order, the routing keys ----
+#pragma unroll
+  for (int i = 0; i < kExpPer; ++i) {
+    const int idx = tid + i * kFfnThreads;
+    if (idx < 3 * a.E) reinterpret_cast<uint4 *>(exp_s)[idx] = exr[i];
+  }
   ActChunk<BITS> xr[JG];
   int xs_lane = 0;
 #pragma unroll
   for (int j = 0; j < JG; ++j) {
     int bs1 = 0;
-    act_chunk_clamped<BITS>(a.xq, lane + j * MOE_WAVE, cpr, xr[j], bs1);
+    act_chunk_from<BITS>(xraw[j], xr[j], bs1);
+    if (lane + j * MOE_WAVE >= cpr) {
+      zero_chunk<BITS>(xr[j]);
+      bs1 = 0;
+    }
     xs_lane += bs1;
   }
-  const float sxv = a.sx[0];
-  const int nsum = a.logits ? 1 : a.ks;
 #pragma unroll
   for (int m = 0; m < kPer; ++m) {
     const int e = tid + m * kFfnThreads;
-    float z = 0.0f;
+    if (m > 0 && a.E <= m * kFfnThreads) break;
+    float z = zs[m][0];  // slices in order
 #pragma unroll
-    for (int s = 0; s < kMaxSlices; ++s)
+    for (int s = 1; s < kMaxSlices; ++s)
       if (s < nsum) z += zs[m][s];
     const float sg = 1.0f / (1.0f + moe_exp_f32(-z));
-    float key = sg + bs[m];
+    float key = sg + (a.bias ? bs[m] : 0.0f);
     if (key != key) key = -__builtin_inff();  // a NaN key ranks last
     if (e < a.E) {
-      key_s[e] = key;
+      key_s[e] = key + 0.0f;  // no -0 keys
       sig_s[e] = sg;
     }
   }
@@ -339,22 +479,22 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
 
   // ---- top-k and the slot table (wave 0) ----
   if (wave == 0) {
-    wave_topk(key_s, sig_s, a.E, a.k, lane, sel_id, sel_sig);
-    float sum = 0.0f;
-    for (int j = 0; j < a.k; ++j) sum += sel_sig[j];
+    const int my_id = (a.E <= 4 * MOE_WAVE) ? wave_topk4(key_s, a.E, a.k, lane) : wave_topk16(key_s, a.E, a.k, lane);
+    const float my_sig = lane < a.k ? sig_s[my_id] : 0.0f;
+    float sum = 0.0f;  // in rank order
+    for (int j = 0; j < a.k; ++j) sum += readlane_f(my_sig, j);
     uint4 row[4];
     bool have = false;
     if (lane < a.k) {
-      const int e = sel_id[lane];
-      const float wgt = a.routed_scale * (sel_sig[lane] / sum);
-      const uint4 *src = reinterpret_cast<const uint4 *>(exp_s + e);
+      const float wgt = a.routed_scale * (my_sig / sum);
+      const uint4 *src = reinterpret_cast<const uint4 *>(exp_s + my_id);
       row[0] = src[0];
       row[1] = src[1];
       row[2] = src[2];
-      row[3] = make_uint4(__float_as_uint(wgt), (uint32_t)e, 0u, 0u);
+      row[3] = make_uint4(__float_as_uint(wgt), (uint32_t)my_id, 0u, 0u);
       have = true;
       if (blockIdx.x == 0) {
-        a.topk_idx[lane] = e;
+        a.topk_idx[lane] = my_id;
         a.topk_w[lane] = wgt;
       }
     } else if (lane == a.k && a.has_shared) {
@@ -379,36 +519,50 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
     }
   }
   __syncthreads();
-  if (q0 >= q1) return;
+  if (ns == 0 && q0 >= q1) return;
 
-  // ---- this wave's slots and row pairs ----
+  // ---- this wave's routed slots; the first routed batch goes out ----
   WaveSlots ws;
   ws.I = a.I;
-  ws.s_first = uniform(q0 / a.I);
-  const int s_last = uniform((q1 - 1) / a.I);
+  const int qlast = q0 < q1 ? q1 - 1 : 0;
+  ws.s_first = uniform((q0 < q1 ? q0 : 0) / a.I);
+  const int s_last = uniform(qlast / a.I);
   ws.gate0 = uniform_p(slot_s[ws.s_first].w.gate);
   ws.up0 = uniform_p(slot_s[ws.s_first].w.up);
   ws.gate1 = uniform_p(slot_s[s_last].w.gate);
   ws.up1 = uniform_p(slot_s[s_last].w.up);
+  gu_load<BITS, JG, NB>(ws, q0, qlast, lane, rowbytes, cpr, b1);
 
-  GuBatch<BITS, JG, NB> b0, b1;
-  gu_load<BITS, JG, NB>(ws, q0, q1, lane, rowbytes, cpr, b0);
-
-  const int my_q = q0 + lane;
-  const bool mine = my_q < q1;
-  const int my_slot = (mine ? my_q : q0) / a.I;
-  const int my_i = (mine ? my_q : q0) - my_slot * a.I;
-  const float sg = gptr(slot_s[my_slot].w.s_gate)[my_i];
-  const float su = gptr(slot_s[my_slot].w.s_up)[my_i];
+  // lane -> (slot, row) of the pair it keeps, and that pair's scales
+  const int nr = q1 - q0;
+  const bool mine = lane < ns + nr;
+  const bool is_sh = lane < ns;
+  int my_slot = a.k, my_i = sh0 + lane;
+  float sg = sg_sh, su = su_sh;
+  {
+    const int q = min(q0 + max(lane - ns, 0), qlast);
+    const int rs = q / a.I;
+    const int ri = q - rs * a.I;
+    const float g2 = gptr(slot_s[rs].w.s_gate)[ri];
+    const float u2 = gptr(slot_s[rs].w.s_up)[ri];
+    if (!is_sh) {
+      my_slot = rs;
+      my_i = ri;
+      sg = g2;
+      su = u2;
+    }
+  }
   const int xsum = wave_sum_all(xs_lane);
 
   int res_g = 0, res_u = 0;
+  if (ns > 0) gu_compute<BITS, JG, NB>(ns, 0, lane, b0, xr, res_g, res_u);
+  // routed batches alternate b1, b0, b1, ...
   for (int qb = q0; qb < q1; qb += 2 * NB) {
-    if (qb + NB < q1) gu_load<BITS, JG, NB>(ws, qb + NB, q1, lane, rowbytes, cpr, b1);
-    gu_compute<BITS, JG, NB>(qb, q0, q1, lane, b0, xr, res_g, res_u);
+    if (qb + NB < q1) gu_load<BITS, JG, NB>(ws, qb + NB, qlast, lane, rowbytes, cpr, b0);
+    gu_compute<BITS, JG, NB>(min(NB, q1 - qb), ns + qb - q0, lane, b1, xr, res_g, res_u);
     if (qb + NB >= q1) break;
-    if (qb + 2 * NB < q1) gu_load<BITS, JG, NB>(ws, qb + 2 * NB, q1, lane, rowbytes, cpr, b0);
-    gu_compute<BITS, JG, NB>(qb + NB, q0, q1, lane, b1, xr, res_g, res_u);
+    if (qb + 2 * NB < q1) gu_load<BITS, JG, NB>(ws, qb + 2 * NB, qlast, lane, rowbytes, cpr, b1);
+    gu_compute<BITS, JG, NB>(min(NB, q1 - qb - NB), ns + qb + NB - q0, lane, b0, xr, res_g, res_u);
   }
 
   if (mine) {
@@ -442,11 +596,59 @@ struct DownT1Args {
 
 constexpr int kRqF4 = kMaxIDown / 4 / kFfnThreads;  // float4 of one slot's a per thread (2)
 
+// int8 code of v under the scale sc = m/127 with inv = 1/sc (both correctly
+// rounded): rint(v * inv) equals rint(v / sc) (the fp32 quotient) unless
+// v * inv lies within 2^-15 of a half-integer. With |v| <= m the quotient is
+// at most 127 in magnitude, where v * inv differs from the exact ratio by less
+// than 2^-16 and the rounded quotient by less than 2^-15 (one rounding of 1/sc
+// and one of the product, 2^-24 relative each), so outside that band both
+// round to the same integer. `near` is raised for a value in the band; the
+// caller then recomputes the code with the division.
+__device__ __forceinline__ float code_fast(float v, float inv, bool &near) {
+  const float t = v * inv;
+  const float n = __builtin_rintf(t);
+  near |= fabsf(t - n) > (0.5f - 0x1p-15f);  // t - n is exact (Sterbenz)
+  return n;
+}
+__device__ __forceinline__ float code_exact(float v, float sc) {
+  float r = __builtin_rintf(v / sc);
+  return fminf(fmaxf(r, -127.0f), 127.0f);
+}
+// four codes (as floats in [-127, 127]) -> one dword of int8 codes
+__device__ __forceinline__ uint32_t pack_codes(float c0, float c1, float c2, float c3) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(c0 + 128.0f, 0, 0u);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(c1 + 128.0f, 1, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(c2 + 128.0f, 2, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(c3 + 128.0f, 3, w);
+  return w ^ 0x80808080u;
+}
+// A lane's natural-order code dword -> the dword at the same position in the
+// weights' field order (int4: pairs of lanes hold the 8 elements of a group;
+// int2: quads of lanes hold the 16 elements of a group).
+template <int BITS>
+__device__ __forceinline__ uint32_t field_order(uint32_t w, int lane) {
+  if constexpr (BITS == 4) {
+    const uint32_t o = (uint32_t)dpp_i<0xB1>((int)w);  // the neighbour's dword
+    return (lane & 1) ? perm_b32(w, o, 0x07050301u) : perm_b32(o, w, 0x06040200u);
+  } else if constexpr (BITS == 2) {
+    const uint32_t d0 = (uint32_t)dpp_i<0x00>((int)w), d1 = (uint32_t)dpp_i<0x55>((int)w);
+    const uint32_t d2 = (uint32_t)dpp_i<0xAA>((int)w), d3 = (uint32_t)dpp_i<0xFF>((int)w);
+    const uint32_t j = (uint32_t)(lane & 3);
+    const uint32_t sel = j | ((4u + j) << 8) | 0x0c0c0000u;
+    const uint32_t lo = perm_b32(d1, d0, sel), hi = perm_b32(d3, d2, sel);
+    return perm_b32(hi, lo, 0x05040100u);
+  } else {
+    return w;
+  }
+}
+
 template <int BITS, int JD, int RB>
 __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args a) {
   constexpr int OFF = QFmt<BITS>::kOff;
+  constexpr int EPC = QFmt<BITS>::kEpc;
   __shared__ __align__(16) int8_t aq_s[kMaxSlots * kMaxIDown];
-  __shared__ float red_s[kFfnWaves][kMaxSlots];
+  __shared__ float red_s[kMaxSlots][kFfnWaves];
+  __shared__ int sum_s[kMaxSlots];
   const int tid = threadIdx.x;
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
@@ -457,53 +659,56 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   const int cpr = rowbytes / 16;
   const int S = a.S;
 
-  // lane s < S holds slot s's fields; the down pointers become uniform
+  // ---- slot fields (lane s < S holds slot s's) and every slot's a ----
   const int ls = lane < S ? lane : S - 1;
   const uint8_t *down_l = a.slots[ls].w.down;
   const float *sdown_l = a.slots[ls].w.s_down;
   const float w_l = a.slots[ls].weight;
-  const uint8_t *dp[kMaxSlots];
-#pragma unroll
-  for (int s = 0; s < kMaxSlots; ++s) dp[s] = readlane_p(down_l, s < S ? s : S - 1);
-
-  // ---- every slot's a first (an L2 hit), then the first down rows ----
   const int n4 = a.I / 4;  // float4 per slot
+  // unconditional loads (the compiler can then count them): slots past S
+  // re-read slot S-1 and elements past I re-read element I-4..I-1, which
+  // leaves the per-slot maxima unchanged
   float4 av[kMaxSlots][kRqF4];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
 #pragma unroll
     for (int c = 0; c < kRqF4; ++c) {
-      const int f = tid + c * kFfnThreads;
-      av[s][c] = (s < S && f < n4) ? reinterpret_cast<const float4 *>(a.A + (int64_t)s * a.I)[f]
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int f = min(tid + c * kFfnThreads, n4 - 1);
+      av[s][c] = reinterpret_cast<const float4 *>(a.A + (int64_t)min(s, S - 1) * a.I)[f];
     }
+  const uint8_t *dp[kMaxSlots];
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s) dp[s] = readlane_p(down_l, s < S ? s : S - 1);
+
+  // ---- the first down rows go out ----
   struct RowBatch {
     uint4 w[RB][kMaxSlots][JD];
     float sd[RB];
   };
+  // rows past the wave's range re-read an in-bounds row, slots past S re-read
+  // slot S-1 (unconditional loads; those results are dropped)
   auto load_rows = [&](int rb, RowBatch &bt) {
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      const int r = (rb + b < r1) ? rb + b : r1 - 1;
+      const int r = max((rb + b < r1) ? rb + b : r1 - 1, 0);
 #pragma unroll
       for (int s = 0; s < kMaxSlots; ++s) {
-        if (s < S) {
 #pragma unroll
-          for (int j = 0; j < JD; ++j) {
-            int c = lane + j * MOE_WAVE;
-            c = c < cpr ? c : cpr - 1;
-            bt.w[b][s][j] = ldg16(dp[s] + (int64_t)r * rowbytes, c);
-          }
+        for (int j = 0; j < JD; ++j) {
+          int c = lane + j * MOE_WAVE;
+          c = c < cpr ? c : cpr - 1;
+          bt.w[b][s][j] = ldg16(dp[s] + (int64_t)r * rowbytes, c);
         }
       }
       bt.sd[b] = gptr(sdown_l)[r];
     }
   };
   RowBatch b0, b1;
-  if (r0 < r1) load_rows(r0, b0);
-  if (r0 + RB < r1) load_rows(r0 + RB, b1);
+  load_rows(r0, b0);
+  load_rows(r0 + RB, b1);
 
-  // ---- requantise every slot's a into LDS (the workgroup together) ----
+  // ---- max|a| per slot ----
+  if (tid < kMaxSlots) sum_s[tid] = 0;
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s) {
     float m = 0.0f;
@@ -511,45 +716,61 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
     for (int c = 0; c < kRqF4; ++c)
       m = fmaxf(m, fmaxf(fmaxf(fabsf(av[s][c].x), fabsf(av[s][c].y)), fmaxf(fabsf(av[s][c].z), fabsf(av[s][c].w))));
     m = wave_max_dpp(m);
-    if (lane == 0) red_s[wave][s] = m;
+    if (lane == 0) red_s[s][wave] = m;
   }
   __syncthreads();
-#pragma unroll
-  for (int s = 0; s < kMaxSlots; ++s) {
-    if (s < S) {
-      float m = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kFfnWaves; ++w) m = fmaxf(m, red_s[w][s]);
-      const float sc = (m == 0.0f) ? 0.0f : m / 127.0f;
-#pragma unroll
-      for (int c = 0; c < kRqF4; ++c) {
-        const int f = tid + c * kFfnThreads;
-        if (f < n4) {
-          const float vv[4] = {av[s][c].x, av[s][c].y, av[s][c].z, av[s][c].w};
-          uint32_t word = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            int q = 0;
-            if (m != 0.0f) {
-              float r = __builtin_rintf(vv[j] / sc);
-              r = fminf(fmaxf(r, -127.0f), 127.0f);
-              q = (int)r;
-            }
-            word |= (uint32_t)(uint8_t)(int8_t)q << (8 * j);
-          }
-          reinterpret_cast<uint32_t *>(aq_s + s * a.I)[f] = word;
-          if (blockIdx.x == 0 && a.dbg_on && a.dbg.aq) reinterpret_cast<uint32_t *>(a.dbg.aq + (int64_t)s * a.I)[f] = word;
-        }
-      }
-      if (blockIdx.x == 0 && tid == 0 && a.dbg_on && a.dbg.sa) a.dbg.sa[s] = sc;
-    }
-  }
-  float sa_l = 0.0f;  // lane s < S: slot s's scale
+  // lane s < S: slot s's scale and its reciprocal
+  float sa_l, inv_l;
+  bool zero_l, fast_l;
   {
     float m = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kFfnWaves; ++w) m = fmaxf(m, red_s[w][ls]);
-    sa_l = (m == 0.0f) ? 0.0f : m / 127.0f;
+    for (int w = 0; w < kFfnWaves; ++w) m = fmaxf(m, red_s[ls][w]);
+    zero_l = m == 0.0f;
+    sa_l = zero_l ? 0.0f : m / 127.0f;
+    inv_l = zero_l ? 0.0f : 1.0f / sa_l;
+    fast_l = sa_l >= 0x1p-126f && sa_l <= 0x1.fffffep127f;
+  }
+
+  // ---- int8 codes into LDS in field order, and their per-slot sums ----
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s) {
+    if (s < S) {
+      const float sc = readlane_f(sa_l, s), inv = readlane_f(inv_l, s);
+      const bool zero = __builtin_amdgcn_readlane((int)zero_l, s) != 0;
+      const bool fast = __builtin_amdgcn_readlane((int)fast_l, s) != 0;
+      int csum = 0;
+#pragma unroll
+      for (int c = 0; c < kRqF4; ++c) {
+        const int f = tid + c * kFfnThreads;
+        if (c * kFfnThreads < n4) {  // uniform: this pass holds data
+          const float4 v = av[s][c];
+          uint32_t word = 0;
+          if (!zero) {
+            bool near = !fast;
+            float q0 = code_fast(v.x, inv, near), q1 = code_fast(v.y, inv, near);
+            float q2 = code_fast(v.z, inv, near), q3 = code_fast(v.w, inv, near);
+            if (near) {
+              q0 = code_exact(v.x, sc);
+              q1 = code_exact(v.y, sc);
+              q2 = code_exact(v.z, sc);
+              q3 = code_exact(v.w, sc);
+            }
+            word = pack_codes(q0, q1, q2, q3);
+          }
+          if (f >= n4) word = 0;
+          csum = sdot4((int)word, 0x01010101, csum);
+          const uint32_t fw = field_order<BITS>(word, lane);
+          if (f < n4) {
+            reinterpret_cast<uint32_t *>(aq_s + s * a.I)[f] = fw;
+            if (blockIdx.x == 0 && a.dbg_on && a.dbg.aq) reinterpret_cast<uint32_t *>(a.dbg.aq + (int64_t)s * a.I)[f] = word;
+          }
+        }
+      }
+      csum = wave_sum_to63(csum);
+      if (lane == 63) atomicAdd(&sum_s[s], csum);
+      if (blockIdx.x == 0 && tid == 0 && a.dbg_on && a.dbg.sa) a.dbg.sa[s] = sc;
+    }
   }
   __syncthreads();
   if (r0 >= r1) return;
@@ -559,23 +780,23 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   int aqsum[kMaxSlots];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s) {
-    int bs_lane = 0;
+    aqsum[s] = s < S ? sum_s[s] : 0;
 #pragma unroll
     for (int j = 0; j < JD; ++j) {
       const int c = lane + j * MOE_WAVE;
       if (s < S && c < cpr) {
-        constexpr int EPC = QFmt<BITS>::kEpc;
-        uint4 v[EPC / 16];
 #pragma unroll
-        for (int u = 0; u < EPC / 16; ++u) v[u] = reinterpret_cast<const uint4 *>(aq_s + s * a.I + c * EPC)[u];
-        int bs = 0;
-        act_chunk_from<BITS>(v, aqr[s][j], bs);
-        bs_lane += bs;
+        for (int u = 0; u < EPC / 16; ++u) {
+          const uint4 v = reinterpret_cast<const uint4 *>(aq_s + s * a.I + c * EPC)[u];
+          aqr[s][j].d[4 * u + 0] = v.x;
+          aqr[s][j].d[4 * u + 1] = v.y;
+          aqr[s][j].d[4 * u + 2] = v.z;
+          aqr[s][j].d[4 * u + 3] = v.w;
+        }
       } else {
         zero_chunk<BITS>(aqr[s][j]);
       }
     }
-    aqsum[s] = wave_sum_all(bs_lane);
   }
 
   auto compute_rows = [&](int rb, const RowBatch &bt) {
@@ -661,14 +882,17 @@ struct T1Shape<2> {
 // Whether the single-token kernels handle this shape.
 bool decode_t1_supported(int bits, int H, int I, int k, int has_shared, int n_cu) {
   if (k + has_shared > kMaxSlots || H / 4 > kMaxX4 * kThreads || I > kMaxIDown) return false;
-  // each gate/up wave owns at most 64 row pairs (one per lane)
+  // a gate/up wave keeps its shared and routed row pairs one per lane, and
+  // loads its shared pairs in one batch
   const int64_t waves = (int64_t)n_cu * kFfnWaves;
-  if ((int64_t)(k + has_shared) * I > 64 * waves) return false;
+  const int64_t ns = has_shared ? (I + waves - 1) / waves : 0;
+  const int64_t nr = ((int64_t)k * I + waves - 1) / waves;
+  if (ns + nr > MOE_WAVE) return false;
   const int jg = moe_chunks_per_lane(H, bits), jd = moe_chunks_per_lane(I, bits);
   switch (bits) {
-    case 4: return jg <= T1Shape<4>::JG && jd <= T1Shape<4>::JD;
-    case 8: return jg <= T1Shape<8>::JG && jd <= T1Shape<8>::JD;
-    default: return jg <= T1Shape<2>::JG && jd <= T1Shape<2>::JD;
+    case 4: return jg <= T1Shape<4>::JG && jd <= T1Shape<4>::JD && ns <= T1Shape<4>::NB;
+    case 8: return jg <= T1Shape<8>::JG && jd <= T1Shape<8>::JD && ns <= T1Shape<8>::NB;
+    default: return jg <= T1Shape<2>::JG && jd <= T1Shape<2>::JD && ns <= T1Shape<2>::NB;
   }
 }
 
@@ -719,7 +943,9 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
   r.sx = sx;
   {
     MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
-    hipLaunchKernelGGL(router_gemv_t1_kernel, dim3(logits ? 1 : (E + 3) / 4, ks), dim3(kThreads), 0, ctx->stream, r);
+    // (E+3)/4 logits workgroups per slice plus one that quantises the slice
+    hipLaunchKernelGGL(router_gemv_t1_kernel, dim3(logits ? 1 : (E + 3) / 4 + 1, ks), dim3(kThreads), 0, ctx->stream,
+                       r);
   }
   MOE_CHECK_LAUNCH("router_gemv_t1_kernel");
 
