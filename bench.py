@@ -2,6 +2,8 @@
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-probe MB        # only a device copy of MB megabytes (counter calibration)
+    python bench.py --pmc-summary BENCH_FETCH BENCH_WRITE COPY_FETCH COPY_WRITE OUT.md
 
 A step is one full pass of the layer's hot path over one batch of synthetic
 input: int8 activation quantisation, sigmoid top-k routing, per-expert
@@ -20,6 +22,9 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +38,103 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s + effective expert-weight HBM GB/s (int4 decode, 1 GPU)"
 HBM_PEAK_GBPS = 8000.0
+COPY_PROBE_MB = 512  # larger than the 256 MB last-level cache: the copy streams HBM
+# sources of the single-token kernels: a traffic figure measured on other
+# sources is stale and is not reported
+KERNEL_SOURCES = ["quantized_moe_expert_sigmoid_amd/csrc/decode.hip", "quantized_moe_expert_sigmoid_amd/csrc/gemv_common.h",
+                  "quantized_moe_expert_sigmoid_amd/csrc/moe_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_glm_decode_t1_int4.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe(mb: float) -> None:
+    """A plain device-to-device copy of a known size, repeated: the counter
+    runs scale FETCH_SIZE / WRITE_SIZE by what they read for it."""
+    import torch
+    n = int(mb * 1e6) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": 4 * n, "copies": 8}), flush=True)
+
+
+def _pmc_means(d: str, counter: str) -> dict:
+    """Mean counter value per kernel name over the dispatches of a rocprofv3
+    --pmc run (counter_collection CSV under directory d)."""
+    acc = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                s, n = acc.get(name, (0.0, 0))
+                acc[name] = (s + float(row["Counter_Value"]), n + 1)
+    return {k: (s / n, n) for k, (s, n) in acc.items()}
+
+
+def pmc_summary(bench_fetch, bench_write, copy_fetch, copy_write, out_md) -> None:
+    """Turn four counter runs into HBM bytes per launch of the single-token
+    kernels, each counter scaled by its reading on the copy probe."""
+    def pick(m, key):
+        ks = [k for k in m if key in k]
+        if not ks:
+            raise SystemExit(f"no kernel matching {key}")
+        return max(ks, key=lambda k: m[k][1])
+    cf, cw = _pmc_means(copy_fetch, "FETCH_SIZE"), _pmc_means(copy_write, "WRITE_SIZE")
+    ck_f, ck_w = max(cf, key=lambda k: cf[k][0]), max(cw, key=lambda k: cw[k][0])
+    copy_bytes = (COPY_PROBE_MB * 1e6) // 4 * 4
+    f_scale = copy_bytes / (cf[ck_f][0] * 1024.0)   # FETCH_SIZE is in KiB
+    w_scale = copy_bytes / (cw[ck_w][0] * 1024.0)
+    bf, bw = _pmc_means(bench_fetch, "FETCH_SIZE"), _pmc_means(bench_write, "WRITE_SIZE")
+    rows, traffic = [], {}
+    for short, key in (("router", "router_gemv_t1_kernel"), ("gateup", "gateup_t1_kernel"),
+                       ("down", "down_combine_t1_kernel")):
+        kf, kw = pick(bf, key), pick(bw, key)
+        fb = bf[kf][0] * 1024.0 * f_scale
+        wb = bw[kw][0] * 1024.0 * w_scale
+        traffic[short] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": bf[kf][1]}
+        rows.append(f"| {key} | {bf[kf][1]} | {bf[kf][0]:.0f} | {bw[kw][0]:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.3f} |")
+    info = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale, "kernels": traffic}
+    with open(out_md, "w") as fh:
+        fh.write("# HBM traffic per launch: single-token kernels, GLM decode (T=1, int4)\n\n")
+        fh.write("Commands (from the repository root, each counter in a run of its own):\n\n")
+        fh.write("    rocprofv3 --pmc FETCH_SIZE -d <dir> --output-format csv -- python3 bench.py --steps 64 --warmup 64 --no-cpu-baseline\n")
+        fh.write("    rocprofv3 --pmc WRITE_SIZE -d <dir> --output-format csv -- python3 bench.py --steps 64 --warmup 64 --no-cpu-baseline\n")
+        fh.write(f"    rocprofv3 --pmc FETCH_SIZE -d <dir> --output-format csv -- python3 bench.py --copy-probe {COPY_PROBE_MB}\n")
+        fh.write(f"    rocprofv3 --pmc WRITE_SIZE -d <dir> --output-format csv -- python3 bench.py --copy-probe {COPY_PROBE_MB}\n")
+        fh.write("    python3 bench.py --pmc-summary <4 dirs> profiles/traffic_glm_decode_t1_int4.md\n\n")
+        fh.write(f"Copy probe ({copy_bytes / 1e6:.0f} MB read and written by `{ck_f[:60]}`): FETCH_SIZE "
+                 f"{cf[ck_f][0]:.0f} KiB, WRITE_SIZE {cw[ck_w][0]:.0f} KiB per dispatch; scale factors "
+                 f"{f_scale:.4f} (fetch), {w_scale:.4f} (write).\n\n")
+        fh.write("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB (scaled) | HBM write MB (scaled) |\n")
+        fh.write("|---|---|---|---|---|---|\n")
+        fh.write("\n".join(rows) + "\n\n")
+        fh.write("traffic_json: " + json.dumps(info) + "\n")
+    print(open(out_md).read())
+
+
+def load_traffic():
+    """Scaled HBM bytes per launch from the committed counter summary, or None
+    when it is missing or was measured on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic_json: "):
+                    info = json.loads(line[len("traffic_json: "):])
+                    return info if info.get("source_hash") == kernel_source_hash() else None
+    except OSError:
+        pass
+    return None
 
 
 def log(*a):
@@ -94,7 +196,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--cpu-repeats", type=int, default=8)
+    ap.add_argument("--copy-probe", type=float, default=0.0, help="only run a device copy of this many MB")
+    ap.add_argument("--pmc-summary", nargs=5, default=None,
+                    metavar=("BENCH_FETCH", "BENCH_WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"))
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -108,6 +216,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a HIP GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe)
+        return
     moe.lib()
     w = wl.ALL[args.workload]
     bits = args.bits
@@ -196,7 +307,12 @@ def main():
         ", ".join(f"{k_} {v[0] * 1e3:.1f} us" for k_, v in per_call.items()) +
         f"; gate/up {gu_gbps:.0f} GB/s, FFN {ffn_gbps:.0f} GB/s")
     args.steps, args.warmup = steps, warm_reps * npool
-    kernel_names = {"router": "router_t1_kernel" if T == 1 else "router kernels",
+    traffic_gu = None
+    tr = load_traffic() if (T == 1 and bits == 4 and w.name == "glm_decode_t1") else None
+    if tr:
+        k_ = tr["kernels"]["gateup"]
+        traffic_gu = k_["fetch_bytes"] + k_["write_bytes"]
+    kernel_names = {"router": "router_gemv_t1_kernel" if T == 1 else "router kernels",
                     "gateup": "gateup_t1_kernel" if T == 1 else "ffn_gateup_kernel",
                     "down": "down_combine_t1_kernel" if T == 1 else "ffn_down_kernel"}
 
@@ -219,7 +335,7 @@ def main():
         "effective_weight_GBps": round(eff_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": kernel_names["gateup"], "achieved": round(gu_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": round(n_avg * gu_bytes),
+                     "traffic": traffic_gu, "algorithmic_bytes_per_launch": round(n_avg * gu_bytes),
                      "avg_launch_us": round(gu_ms * 1e3, 2)},
         "kernels": {k_: {"avg_us": round(v[0] * 1e3, 2), "launches_per_call": v[1]} for k_, v in per_call.items()},
         "expert_ffn": {"kernels": kernel_names["gateup"] + " + " + kernel_names["down"],

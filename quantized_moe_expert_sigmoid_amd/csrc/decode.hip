@@ -842,19 +842,13 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
 // ---------------------------------------------------------------------------
 template <int BITS, int JG, int NB>
 moe_status launch_gu(moe_ctx *ctx, const GateUpT1Args &g, int nwg) {
-  {
-    MoeTimer tm_(ctx, MOE_STAGE_GATEUP);
-    hipLaunchKernelGGL((gateup_t1_kernel<BITS, JG, NB>), dim3(nwg), dim3(kFfnThreads), 0, ctx->stream, g);
-  }
+  moe_launch(ctx, MOE_STAGE_GATEUP, gateup_t1_kernel<BITS, JG, NB>, dim3(nwg), dim3(kFfnThreads), g);
   MOE_CHECK_LAUNCH("gateup_t1_kernel");
   return MOE_OK;
 }
 template <int BITS, int JD, int RB>
 moe_status launch_dn(moe_ctx *ctx, const DownT1Args &d, int nwg) {
-  {
-    MoeTimer tm_(ctx, MOE_STAGE_DOWN);
-    hipLaunchKernelGGL((down_combine_t1_kernel<BITS, JD, RB>), dim3(nwg), dim3(kFfnThreads), 0, ctx->stream, d);
-  }
+  moe_launch(ctx, MOE_STAGE_DOWN, down_combine_t1_kernel<BITS, JD, RB>, dim3(nwg), dim3(kFfnThreads), d);
   MOE_CHECK_LAUNCH("down_combine_t1_kernel");
   return MOE_OK;
 }
@@ -941,12 +935,8 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
   r.partial = partial;
   r.xq = xq;
   r.sx = sx;
-  {
-    MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
-    // (E+3)/4 logits workgroups per slice plus one that quantises the slice
-    hipLaunchKernelGGL(router_gemv_t1_kernel, dim3(logits ? 1 : (E + 3) / 4 + 1, ks), dim3(kThreads), 0, ctx->stream,
-                       r);
-  }
+  // (E+3)/4 logits workgroups per slice plus one that quantises the slice
+  moe_launch(ctx, MOE_STAGE_ROUTER, router_gemv_t1_kernel, dim3(logits ? 1 : (E + 3) / 4 + 1, ks), dim3(kThreads), r);
   MOE_CHECK_LAUNCH("router_gemv_t1_kernel");
 
   GateUpT1Args g{};

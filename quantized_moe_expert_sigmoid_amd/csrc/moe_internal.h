@@ -1,6 +1,7 @@
 // Internal declarations of libmoe (gfx950). Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,6 +53,24 @@ struct MoeTimer {
   MoeTimer(moe_ctx *c, int s);
   ~MoeTimer();
 };
+
+hipEvent_t moe_pool_event(moe_ctx *ctx);
+
+// Launch a kernel on the context stream. With timing on, the dispatch itself
+// carries the start/stop events (hipExtLaunchKernelGGL), so the recorded time
+// is the kernel's own execution, not that of extra event packets around it.
+template <typename K, typename... Args>
+void moe_launch(moe_ctx *ctx, int stage, K kernel, dim3 grid, dim3 block, Args... args) {
+  hipEvent_t s = ctx->timing ? moe_pool_event(ctx) : nullptr;
+  hipEvent_t e = s ? moe_pool_event(ctx) : nullptr;
+  if (s && e) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, ctx->stream, s, e, 0, args...);
+    ctx->timed.push_back({s, e, stage});
+    return;
+  }
+  if (s) ctx->event_pool.push_back(s);
+  hipLaunchKernelGGL(kernel, grid, block, 0, ctx->stream, args...);
+}
 
 moe_status moe_fail(moe_status st, const char *fmt, ...);
 moe_status moe_hip_fail(hipError_t e, const char *what);
