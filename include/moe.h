@@ -227,6 +227,60 @@ moe_status moe_layer_forward(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, 
                              float *topk_w, int8_t *xq, float *sx, float *y_slots);
 
 /* ---------------------------------------------------------------------- */
+/* Expert pool ([P-load], [P-mem], [P-dedup])                             */
+/* ---------------------------------------------------------------------- */
+
+/* An HBM cache of expert blocks (the moe_expert_block_layout layout) for a
+ * stack of layers, refilled from caller-owned host memory: [P-load] keeps
+ * experts resident under an LRU and reads the next block while the current
+ * one computes; [P-dedup] reads an expert needed by several tokens once.
+ * Blocks of different widths share one slab (first fit with coalescing). One
+ * least-recently-used order spans every layer's resident experts; a pinned
+ * expert, once resident, is never evicted. Refills run on the pool's own copy
+ * stream; the context stream waits for them. Not thread-safe; destroy a pool
+ * before its context. */
+typedef struct moe_pool moe_pool;
+
+/* Create a pool of capacity_bytes of HBM (allocated now on ctx's device) for
+ * n_layers x n_experts experts of hidden H and intermediate I (multiples of
+ * 64). ctx == NULL creates a bookkeeping-only pool: no memory and no copies,
+ * the same residency decisions and statistics (capacity planning, tests on a
+ * host without a GPU). MOE_ENOMEM if the slab cannot be allocated. */
+moe_status moe_pool_create(moe_ctx *ctx, size_t capacity_bytes, int n_layers, int n_experts, int H, int I,
+                           moe_pool **out);
+/* Wait for the pool's copies and for the context stream (whose kernels may
+ * read the slab), then free everything the pool owns. */
+void moe_pool_destroy(moe_pool *pool);
+/* Register expert (layer, expert) at `bits` in {8,4,2}: block_host holds its
+ * block (bytes must equal moe_expert_block_layout(bits, H, I)); the caller
+ * owns it and keeps it alive and unchanged until moe_pool_destroy. It should
+ * be pinned memory (hipHostMalloc, torch pin_memory) for the refill to be an
+ * asynchronous DMA. block_host may be NULL for a bookkeeping-only pool.
+ * pin != 0: never evicted once resident. Registering twice is MOE_EINVAL. */
+moe_status moe_pool_register(moe_pool *pool, int layer, int expert, int bits, const void *block_host,
+                             size_t bytes, int pin);
+/* Make the distinct experts of topk_idx_host (HOST int32 [T][k]) of `layer`
+ * resident. Hits move to the most-recently-used end; each miss takes slab
+ * space, evicting from the least-recently-used end experts this call does
+ * not need, and is copied from its host block on the copy stream, after the
+ * context stream has passed every earlier call that could read the evicted
+ * bytes. The context stream then waits for this call's copies and receives,
+ * in order, the layer's table: table_dev DEVICE moe_expert_w [E] (resident
+ * experts point into the slab, the others are zero) and bits_dev DEVICE
+ * uint8 [E] (the experts' widths, 0 when absent; nullable) -- ready for
+ * moe_expert_ffn_q* with expert_bits = bits_dev. n_miss_host (nullable): this
+ * call's misses. MOE_EINVAL for an id outside [0, E) or an unregistered
+ * expert; MOE_EPOOL when the slab cannot hold this call's experts beside the
+ * pinned ones (the pool stays consistent). A bookkeeping-only pool takes
+ * table_dev = bits_dev = NULL. */
+moe_status moe_pool_prepare(moe_pool *pool, int layer, const int32_t *topk_idx_host, int T, int k,
+                            moe_expert_w *table_dev, uint8_t *bits_dev, int *n_miss_host);
+/* Cumulative expert hits, misses and bytes copied host-to-device. */
+moe_status moe_pool_stats(const moe_pool *pool, uint64_t *hits, uint64_t *misses, uint64_t *bytes_h2d);
+/* 1 if (layer, expert) is resident, 0 if not, -1 for invalid arguments. */
+int moe_pool_resident(const moe_pool *pool, int layer, int expert);
+
+/* ---------------------------------------------------------------------- */
 /* Measurement                                                            */
 /* ---------------------------------------------------------------------- */
 

@@ -76,6 +76,13 @@ _SIGS = {
     "moe_ctx_read_timing": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
     "moe_layer_forward": (_i32, [_vp, _i32, ctypes.POINTER(RouterCfg), _vp, _vp, _vp, _vp, _vp,
                                  ctypes.POINTER(ExpertW), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_pool_create": (_i32, [_vp, _sz, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp)]),
+    "moe_pool_destroy": (None, [_vp]),
+    "moe_pool_register": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz, _i32]),
+    "moe_pool_prepare": (_i32, [_vp, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(ctypes.c_int)]),
+    "moe_pool_stats": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64),
+                              ctypes.POINTER(ctypes.c_uint64)]),
+    "moe_pool_resident": (_i32, [_vp, _i32, _i32]),
 }
 
 
@@ -352,3 +359,79 @@ class ExpertBlocks:
         moe_quantize_rows(ctx, self.bits, wg, g, sg)
         moe_quantize_rows(ctx, self.bits, wu, u, su)
         moe_quantize_rows(ctx, self.bits, wd, d, sd)
+
+
+# ---------------------------------------------------------------------------
+# Expert pool
+# ---------------------------------------------------------------------------
+
+class MoePool:
+    """moe_pool: HBM cache of expert blocks refilled from pinned host memory.
+    ctx=None gives a bookkeeping-only pool (no device memory, no copies)."""
+
+    def __init__(self, ctx: MoeCtx | None, capacity_bytes: int, n_layers: int, n_experts: int, H: int, I: int):
+        self.ctx, self.n_layers, self.n_experts, self.H, self.I = ctx, n_layers, n_experts, H, I
+        h = ctypes.c_void_p()
+        _ck(lib().moe_pool_create(ctx.handle if ctx is not None else None, capacity_bytes, n_layers, n_experts,
+                                  H, I, ctypes.byref(h)))
+        self.handle = h.value
+        self._blocks = {}  # keeps the registered host blocks alive
+
+    def close(self):
+        if self.handle:
+            lib().moe_pool_destroy(self.handle)
+            self.handle = None
+            self._blocks.clear()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def register(self, layer: int, expert: int, bits: int, block_host: torch.Tensor | None, pin: bool = False,
+                 nbytes: int | None = None):
+        """block_host: CPU uint8 tensor holding the block (pinned for an
+        asynchronous refill); None only for a bookkeeping-only pool."""
+        if block_host is not None:
+            if block_host.is_cuda or block_host.dtype != torch.uint8 or not block_host.is_contiguous():
+                raise TypeError("block_host must be a contiguous CPU uint8 tensor")
+            nbytes = block_host.numel()
+            ptr = block_host.data_ptr()
+        else:
+            nbytes = moe_expert_block_layout(bits, self.H, self.I)[0] if nbytes is None else nbytes
+            ptr = None
+        _ck(lib().moe_pool_register(self.handle, layer, expert, bits, ptr, nbytes, 1 if pin else 0))
+        if block_host is not None:
+            self._blocks[(layer, expert)] = block_host
+
+    def prepare(self, layer: int, topk_idx_host, table: torch.Tensor | None = None,
+                bits: torch.Tensor | None = None) -> int:
+        """topk_idx_host: int32 [T][k] on the host (numpy array or CPU tensor).
+        table: device int64 [E][6] (moe_expert_w rows), bits: device uint8 [E].
+        Returns the number of misses."""
+        import numpy as np
+        idx = np.ascontiguousarray(topk_idx_host if not isinstance(topk_idx_host, torch.Tensor)
+                                   else topk_idx_host.cpu().numpy(), dtype=np.int32)
+        if idx.ndim != 2:
+            raise ValueError("topk_idx_host must be [T][k]")
+        T, k = idx.shape
+        if table is not None:
+            _dev(table, torch.int64, "table", (self.n_experts, 6))
+        if bits is not None:
+            _dev(bits, torch.uint8, "bits", (self.n_experts,))
+        n = ctypes.c_int(0)
+        _ck(lib().moe_pool_prepare(self.handle, layer, idx.ctypes.data if idx.size else None, T, k,
+                                   _ptr(table), _ptr(bits), ctypes.byref(n)))
+        return n.value
+
+    def stats(self):
+        h, m, b = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+        _ck(lib().moe_pool_stats(self.handle, ctypes.byref(h), ctypes.byref(m), ctypes.byref(b)))
+        return {"hits": h.value, "misses": m.value, "bytes_h2d": b.value}
+
+    def resident(self, layer: int, expert: int) -> bool:
+        r = lib().moe_pool_resident(self.handle, layer, expert)
+        if r < 0:
+            raise MoeError(MOE_EINVAL, "moe_pool_resident: invalid arguments")
+        return bool(r)

@@ -83,7 +83,7 @@ extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out
   return MOE_OK;
 }
 
-hipEvent_t moe_pool_event(moe_ctx *ctx) {
+hipEvent_t moe_timing_event(moe_ctx *ctx) {
   if (!ctx->event_pool.empty()) {
     hipEvent_t e = ctx->event_pool.back();
     ctx->event_pool.pop_back();
@@ -96,7 +96,7 @@ hipEvent_t moe_pool_event(moe_ctx *ctx) {
 
 MoeTimer::MoeTimer(moe_ctx *c, int s) : ctx(c), stage(s) {
   if (!ctx->timing) return;
-  start = moe_pool_event(ctx);
+  start = moe_timing_event(ctx);
   if (start && hipEventRecord(start, ctx->stream) != hipSuccess) {
     ctx->event_pool.push_back(start);
     start = nullptr;
@@ -105,7 +105,7 @@ MoeTimer::MoeTimer(moe_ctx *c, int s) : ctx(c), stage(s) {
 
 MoeTimer::~MoeTimer() {
   if (!start) return;
-  hipEvent_t stop = moe_pool_event(ctx);
+  hipEvent_t stop = moe_timing_event(ctx);
   if (stop && hipEventRecord(stop, ctx->stream) == hipSuccess) {
     ctx->timed.push_back({start, stop, stage});
   } else {

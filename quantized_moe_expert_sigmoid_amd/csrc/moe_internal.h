@@ -54,15 +54,15 @@ struct MoeTimer {
   ~MoeTimer();
 };
 
-hipEvent_t moe_pool_event(moe_ctx *ctx);
+hipEvent_t moe_timing_event(moe_ctx *ctx);
 
 // Launch a kernel on the context stream. With timing on, the dispatch itself
 // carries the start/stop events (hipExtLaunchKernelGGL), so the recorded time
 // is the kernel's own execution, not that of extra event packets around it.
 template <typename K, typename... Args>
 void moe_launch(moe_ctx *ctx, int stage, K kernel, dim3 grid, dim3 block, Args... args) {
-  hipEvent_t s = ctx->timing ? moe_pool_event(ctx) : nullptr;
-  hipEvent_t e = s ? moe_pool_event(ctx) : nullptr;
+  hipEvent_t s = ctx->timing ? moe_timing_event(ctx) : nullptr;
+  hipEvent_t e = s ? moe_timing_event(ctx) : nullptr;
   if (s && e) {
     hipExtLaunchKernelGGL(kernel, grid, block, 0, ctx->stream, s, e, 0, args...);
     ctx->timed.push_back({s, e, stage});

@@ -1,0 +1,322 @@
+// HBM expert pool: a slab of device memory that caches expert blocks for a
+// stack of layers, refilled from caller-owned pinned host memory on a copy
+// stream.
+//
+// Pages: agentlenshq.com, "Colibri: running GLM-5.2 744B MoE on consumer
+// hardware", section "Loading mechanism" (experts stay resident under an LRU;
+// the next block is read while the current one is computed) and section
+// "Memory split" (the dense part and shared experts stay resident, the routed
+// experts are streamed); remio.ai, "Colibri shows how to run GLM-5.2 on a
+// low-spec PC", section "The RAM wall became a storage problem" (an expert
+// needed by several batch positions is read once; an expert's matrices are
+// stored together and fetched in one read).
+//
+// Host-side design:
+//  - The slab is carved first-fit from a free list (offset -> length) with
+//    coalescing; blocks of different widths (int8 / int4 / int2) share it.
+//  - One least-recently-used list over every resident unpinned expert of
+//    every layer. A miss evicts from its cold end until the block fits,
+//    never an expert the same call needs. Pinned experts, once resident,
+//    are never evicted.
+//  - Each prepare call is an epoch. At its start an event is recorded on the
+//    context stream: it completes once every kernel enqueued before the call
+//    (the readers of the experts earlier calls made resident) has finished.
+//    A refill into memory freed by evicting an expert last used in epoch n
+//    makes the copy stream wait for the event of epoch n+1 first.
+//  - The context stream waits for this call's refills, then receives the
+//    layer's expert table (and widths) from a pinned staging buffer.
+//  - Without a context the pool only keeps the books (no memory, no copies):
+//    hit rates of a capacity can be planned, and the policy tested, on a
+//    host without a GPU.
+#include <list>
+#include <map>
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kEpochEvents = 64;  // ring of per-call events on the context stream
+constexpr int kStaging = 8;       // ring of pinned table staging buffers
+
+struct Entry {
+  bool registered = false;
+  int bits = 0;
+  const void *host = nullptr;
+  size_t bytes = 0;
+  bool pin = false;
+  bool resident = false;
+  size_t off = 0;
+  uint64_t last_use = 0;           // epoch of the last call that needed it
+  std::list<int>::iterator lru;    // valid while resident and unpinned
+  hipEvent_t ready = nullptr;      // refill completion (copy stream)
+};
+
+}  // namespace
+
+struct moe_pool {
+  moe_ctx *ctx = nullptr;  // null: bookkeeping only
+  size_t capacity = 0;
+  int n_layers = 0, n_experts = 0, H = 0, I = 0;
+  char *slab = nullptr;
+  hipStream_t copy_stream = nullptr;
+  std::vector<Entry> entries;          // [n_layers * n_experts]
+  std::list<int> lru;                  // front = least recently used
+  std::map<size_t, size_t> free_list;  // offset -> length
+  uint64_t epoch = 0;
+  hipEvent_t epoch_ev[kEpochEvents] = {};
+  uint8_t *staging[kStaging] = {};
+  hipEvent_t staging_ev[kStaging] = {};
+  bool staging_used[kStaging] = {};
+  int staging_next = 0;
+  uint64_t hits = 0, misses = 0, bytes_h2d = 0;
+};
+
+namespace {
+
+bool slab_alloc(moe_pool *p, size_t len, size_t *off) {
+  for (auto it = p->free_list.begin(); it != p->free_list.end(); ++it) {
+    if (it->second >= len) {
+      *off = it->first;
+      const size_t rest = it->second - len, roff = it->first + len;
+      p->free_list.erase(it);
+      if (rest) p->free_list[roff] = rest;
+      return true;
+    }
+  }
+  return false;
+}
+
+void slab_free(moe_pool *p, size_t off, size_t len) {
+  auto it = p->free_list.emplace(off, len).first;
+  auto nx = std::next(it);
+  if (nx != p->free_list.end() && it->first + it->second == nx->first) {
+    it->second += nx->second;
+    p->free_list.erase(nx);
+  }
+  if (it != p->free_list.begin()) {
+    auto pv = std::prev(it);
+    if (pv->first + pv->second == it->first) {
+      pv->second += it->second;
+      p->free_list.erase(it);
+    }
+  }
+}
+
+size_t block_bytes(const moe_pool *p, int bits) { return moe_expert_block_layout(bits, p->H, p->I, nullptr); }
+
+}  // namespace
+
+extern "C" moe_status moe_pool_create(moe_ctx *ctx, size_t capacity_bytes, int n_layers, int n_experts, int H, int I,
+                                      moe_pool **out) {
+  if (!out) return moe_fail(MOE_EINVAL, "moe_pool_create: out is NULL");
+  *out = nullptr;
+  if (n_layers < 1 || n_experts < 1 || n_experts > 1024 || (int64_t)n_layers * n_experts > (1 << 24))
+    return moe_fail(MOE_EINVAL, "moe_pool_create: n_layers %d n_experts %d", n_layers, n_experts);
+  if (moe_expert_block_layout(4, H, I, nullptr) == 0)
+    return moe_fail(MOE_EINVAL, "moe_pool_create: H %d and I %d must be positive multiples of 64", H, I);
+  if (capacity_bytes < 256) return moe_fail(MOE_EINVAL, "moe_pool_create: capacity %zu bytes", capacity_bytes);
+  moe_pool *p = new (std::nothrow) moe_pool();
+  if (!p) return moe_fail(MOE_ENOMEM, "moe_pool_create: host allocation");
+  p->ctx = ctx;
+  p->capacity = capacity_bytes / 256 * 256;
+  p->n_layers = n_layers;
+  p->n_experts = n_experts;
+  p->H = H;
+  p->I = I;
+  p->entries.resize((size_t)n_layers * n_experts);
+  p->free_list[0] = p->capacity;
+  if (ctx) {
+    auto fail = [&](hipError_t e, const char *what) {
+      moe_pool_destroy(p);
+      return moe_hip_fail(e, what);
+    };
+    hipError_t e = hipSetDevice(ctx->device);
+    if (e != hipSuccess) return fail(e, "hipSetDevice");
+    e = hipMalloc((void **)&p->slab, p->capacity);
+    if (e != hipSuccess) {
+      moe_pool_destroy(p);
+      (void)hipGetLastError();
+      return moe_fail(MOE_ENOMEM, "moe_pool_create: hipMalloc of %zu bytes failed", p->capacity);
+    }
+    e = hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking);
+    if (e != hipSuccess) return fail(e, "hipStreamCreateWithFlags");
+    for (int i = 0; i < kEpochEvents; ++i) {
+      e = hipEventCreateWithFlags(&p->epoch_ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) return fail(e, "hipEventCreateWithFlags");
+    }
+    const size_t sbytes = (size_t)n_experts * (sizeof(moe_expert_w) + 1);
+    for (int i = 0; i < kStaging; ++i) {
+      e = hipHostMalloc((void **)&p->staging[i], sbytes, hipHostMallocDefault);
+      if (e != hipSuccess) return fail(e, "hipHostMalloc");
+      e = hipEventCreateWithFlags(&p->staging_ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) return fail(e, "hipEventCreateWithFlags");
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+extern "C" void moe_pool_destroy(moe_pool *p) {
+  if (!p) return;
+  if (p->ctx) {
+    (void)hipSetDevice(p->ctx->device);
+    if (p->copy_stream) (void)hipStreamSynchronize(p->copy_stream);
+    (void)hipStreamSynchronize(p->ctx->stream);  // kernels may still read the slab
+    for (auto &en : p->entries)
+      if (en.ready) (void)hipEventDestroy(en.ready);
+    for (int i = 0; i < kEpochEvents; ++i)
+      if (p->epoch_ev[i]) (void)hipEventDestroy(p->epoch_ev[i]);
+    for (int i = 0; i < kStaging; ++i) {
+      if (p->staging_ev[i]) (void)hipEventDestroy(p->staging_ev[i]);
+      if (p->staging[i]) (void)hipHostFree(p->staging[i]);
+    }
+    if (p->copy_stream) (void)hipStreamDestroy(p->copy_stream);
+    if (p->slab) (void)hipFree(p->slab);
+  }
+  delete p;
+}
+
+extern "C" moe_status moe_pool_register(moe_pool *p, int layer, int expert, int bits, const void *block_host,
+                                        size_t bytes, int pin) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_register: pool is NULL");
+  if (layer < 0 || layer >= p->n_layers || expert < 0 || expert >= p->n_experts)
+    return moe_fail(MOE_EINVAL, "moe_pool_register: (layer %d, expert %d) out of range", layer, expert);
+  if (!(bits == 8 || bits == 4 || bits == 2)) return moe_fail(MOE_EINVAL, "moe_pool_register: bits %d", bits);
+  const size_t need = block_bytes(p, bits);
+  if (bytes != need)
+    return moe_fail(MOE_EINVAL, "moe_pool_register: block of %zu bytes, the int%d layout needs %zu", bytes, bits, need);
+  if (p->ctx && !block_host) return moe_fail(MOE_EINVAL, "moe_pool_register: block_host is NULL");
+  if (need > p->capacity)
+    return moe_fail(MOE_EPOOL, "moe_pool_register: a %zu-byte block exceeds the %zu-byte pool", need, p->capacity);
+  Entry &en = p->entries[(size_t)layer * p->n_experts + expert];
+  if (en.registered) return moe_fail(MOE_EINVAL, "moe_pool_register: (layer %d, expert %d) already registered", layer, expert);
+  en.registered = true;
+  en.bits = bits;
+  en.host = block_host;
+  en.bytes = bytes;
+  en.pin = pin != 0;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *topk_idx_host, int T, int k,
+                                       moe_expert_w *table_dev, uint8_t *bits_dev, int *n_miss_host) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_prepare: pool is NULL");
+  if (layer < 0 || layer >= p->n_layers) return moe_fail(MOE_EINVAL, "moe_pool_prepare: layer %d", layer);
+  if (T < 0 || k < 1 || k > 16 || (T > 0 && !topk_idx_host))
+    return moe_fail(MOE_EINVAL, "moe_pool_prepare: T %d k %d idx %p", T, k, (const void *)topk_idx_host);
+  if (!p->ctx && (table_dev || bits_dev))
+    return moe_fail(MOE_EINVAL, "moe_pool_prepare: a pool without a context writes no device table");
+  if (p->ctx && !table_dev) return moe_fail(MOE_EINVAL, "moe_pool_prepare: table_dev is NULL");
+  const int E = p->n_experts;
+  Entry *row = &p->entries[(size_t)layer * E];
+  // the call's distinct experts, ascending (each expert is read once)
+  std::vector<uint8_t> want(E, 0);
+  for (int64_t i = 0; i < (int64_t)T * k; ++i) {
+    const int e = topk_idx_host[i];
+    if (e < 0 || e >= E) return moe_fail(MOE_EINVAL, "moe_pool_prepare: expert id %d at %lld", e, (long long)i);
+    if (!row[e].registered)
+      return moe_fail(MOE_EINVAL, "moe_pool_prepare: (layer %d, expert %d) is not registered", layer, e);
+    want[e] = 1;
+  }
+  if (p->ctx) {
+    MOE_HIP(hipSetDevice(p->ctx->device));
+  }
+  const uint64_t ep = ++p->epoch;
+  if (p->ctx) MOE_HIP(hipEventRecord(p->epoch_ev[ep % kEpochEvents], p->ctx->stream));
+  // hits first: they move to the hot end and cannot be evicted below
+  for (int e = 0; e < E; ++e) {
+    if (!want[e] || !row[e].resident) continue;
+    Entry &en = row[e];
+    en.last_use = ep;
+    if (!en.pin) p->lru.splice(p->lru.end(), p->lru, en.lru);
+    ++p->hits;
+  }
+  int n_miss = 0;
+  for (int e = 0; e < E; ++e) {
+    if (!want[e] || row[e].resident) continue;
+    Entry &en = row[e];
+    size_t off = 0;
+    uint64_t wait_ep = 0;  // the epoch whose start event the refill waits for
+    while (!slab_alloc(p, en.bytes, &off)) {
+      if (p->lru.empty() || p->entries[p->lru.front()].last_use == ep) {
+        // the books stay consistent: refills already issued stay resident
+        return moe_fail(MOE_EPOOL,
+                        "moe_pool_prepare: layer %d: the pool (%zu bytes) cannot hold this call's experts "
+                        "beside its pinned and in-use blocks",
+                        layer, p->capacity);
+      }
+      const int vi = p->lru.front();
+      Entry &v = p->entries[vi];
+      p->lru.pop_front();
+      v.resident = false;
+      slab_free(p, v.off, v.bytes);
+      if (v.last_use + 1 > wait_ep) wait_ep = v.last_use + 1;
+    }
+    en.off = off;
+    en.resident = true;
+    en.last_use = ep;
+    if (!en.pin) en.lru = p->lru.insert(p->lru.end(), (int)(&en - p->entries.data()));
+    ++p->misses;
+    p->bytes_h2d += en.bytes;
+    ++n_miss;
+    if (p->ctx) {
+      if (wait_ep) {
+        // events before the ring's oldest are gone; a later one is a safe wait
+        const uint64_t w = wait_ep + kEpochEvents <= ep ? ep - kEpochEvents + 1 : wait_ep;
+        MOE_HIP(hipStreamWaitEvent(p->copy_stream, p->epoch_ev[w % kEpochEvents], 0));
+      }
+      MOE_HIP(hipMemcpyAsync(p->slab + off, en.host, en.bytes, hipMemcpyHostToDevice, p->copy_stream));
+      if (!en.ready) MOE_HIP(hipEventCreateWithFlags(&en.ready, hipEventDisableTiming));
+      MOE_HIP(hipEventRecord(en.ready, p->copy_stream));
+    }
+  }
+  if (n_miss_host) *n_miss_host = n_miss;
+  if (!p->ctx) return MOE_OK;
+
+  // the context stream waits for every refill this call's experts depend on
+  for (int e = 0; e < E; ++e)
+    if (want[e] && row[e].ready) MOE_HIP(hipStreamWaitEvent(p->ctx->stream, row[e].ready, 0));
+  // the layer's table from a pinned staging buffer
+  const int si = p->staging_next;
+  p->staging_next = (si + 1) % kStaging;
+  if (p->staging_used[si]) MOE_HIP(hipEventSynchronize(p->staging_ev[si]));
+  moe_expert_w *tab = reinterpret_cast<moe_expert_w *>(p->staging[si]);
+  uint8_t *bits = p->staging[si] + (size_t)E * sizeof(moe_expert_w);
+  for (int e = 0; e < E; ++e) {
+    const Entry &en = row[e];
+    if (en.resident) {
+      size_t o[6];
+      moe_expert_block_layout(en.bits, p->H, p->I, o);
+      const char *b = p->slab + en.off;
+      tab[e].gate = reinterpret_cast<const uint8_t *>(b + o[0]);
+      tab[e].up = reinterpret_cast<const uint8_t *>(b + o[1]);
+      tab[e].down = reinterpret_cast<const uint8_t *>(b + o[2]);
+      tab[e].s_gate = reinterpret_cast<const float *>(b + o[3]);
+      tab[e].s_up = reinterpret_cast<const float *>(b + o[4]);
+      tab[e].s_down = reinterpret_cast<const float *>(b + o[5]);
+      bits[e] = (uint8_t)en.bits;
+    } else {
+      tab[e] = moe_expert_w{};
+      bits[e] = 0;
+    }
+  }
+  MOE_HIP(hipMemcpyAsync(table_dev, tab, (size_t)E * sizeof(moe_expert_w), hipMemcpyHostToDevice, p->ctx->stream));
+  if (bits_dev) MOE_HIP(hipMemcpyAsync(bits_dev, bits, (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
+  MOE_HIP(hipEventRecord(p->staging_ev[si], p->ctx->stream));
+  p->staging_used[si] = true;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_stats(const moe_pool *p, uint64_t *hits, uint64_t *misses, uint64_t *bytes_h2d) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_stats: pool is NULL");
+  if (hits) *hits = p->hits;
+  if (misses) *misses = p->misses;
+  if (bytes_h2d) *bytes_h2d = p->bytes_h2d;
+  return MOE_OK;
+}
+
+extern "C" int moe_pool_resident(const moe_pool *p, int layer, int expert) {
+  if (!p || layer < 0 || layer >= p->n_layers || expert < 0 || expert >= p->n_experts) return -1;
+  return p->entries[(size_t)layer * p->n_experts + expert].resident ? 1 : 0;
+}

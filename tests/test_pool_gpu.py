@@ -1,0 +1,203 @@
+"""Expert pool on the GPU, through the C ABI: refilled slots hold exactly the
+host blocks, and expert FFN outputs computed from pool tables are bit-equal
+to those from an all-resident table, over many calls enqueued without
+synchronisation while the pool keeps evicting (so every refill into memory
+an earlier call still reads must wait for it), for one width and for a
+mixed int4/int2 layer.
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+H, I = 256, 128
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import quantized_moe_expert_sigmoid_amd as m
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def ctx(moe):
+    c = moe.MoeCtx(0)
+    yield c
+    c.close()
+
+
+_hip = None
+
+
+def dev_bytes(ptr, n):
+    """Copy n bytes at a raw device address to a host uint8 tensor (hipMemcpy)."""
+    import ctypes
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip.hipMemcpy.restype = ctypes.c_int
+    out = torch.empty(n, dtype=torch.uint8)
+    assert _hip.hipMemcpy(out.data_ptr(), ptr, n, 2) == 0  # hipMemcpyDeviceToHost
+    return out
+
+
+def make_blocks(moe, ctx, syn, bits, E, seed):
+    blocks = moe.ExpertBlocks(E, bits, H, I)
+    for e in range(E):
+        g, u, d = syn.expert_weights(seed, 0, e, H, I)
+        blocks.pack_from_fp32(ctx, e, *(torch.from_numpy(a).cuda() for a in (g, u, d)))
+    torch.cuda.synchronize()
+    host = []
+    for e in range(E):
+        h = torch.empty(blocks.block_bytes, dtype=torch.uint8, pin_memory=True)
+        h.copy_(blocks.data[e])
+        host.append(h)
+    return blocks, host
+
+
+def token_inputs(moe, ctx, syn, T, seed):
+    x = torch.from_numpy(syn.hidden(seed, T, H)).cuda()
+    xq = torch.empty((T, H), dtype=torch.int8, device="cuda")
+    sx = torch.empty((T,), dtype=torch.float32, device="cuda")
+    moe.moe_quantize_act_i8(ctx, x, xq, sx)
+    return xq, sx
+
+
+def test_refilled_slots_equal_host_blocks(moe, ctx, syn):
+    E = 6
+    blocks, host = make_blocks(moe, ctx, syn, 4, E, seed=31)
+    pool = moe.MoePool(ctx, 3 * blocks.block_bytes, 1, E, H, I)
+    for e in range(E):
+        pool.register(0, e, 4, host[e])
+    table = torch.zeros((E, 6), dtype=torch.int64, device="cuda")
+    bits = torch.zeros((E,), dtype=torch.uint8, device="cuda")
+    for ids in ([[0, 1]], [[2, 3]], [[1, 4]], [[5, 0]]):
+        pool.prepare(0, np.array(ids, np.int32), table, bits)
+        torch.cuda.synchronize()
+        tab = table.cpu().numpy()
+        bb = bits.cpu().numpy()
+        for e in range(E):
+            if pool.resident(0, e):
+                assert bb[e] == 4
+                got = dev_bytes(int(tab[e, 0]), blocks.block_bytes)
+                assert torch.equal(got, host[e]), e
+                # the table's six pointers follow the block layout
+                assert [int(tab[e, j]) - int(tab[e, 0]) for j in range(6)] == blocks.offsets
+            else:
+                assert bb[e] == 0 and not tab[e].any()
+    st = pool.stats()
+    assert st["misses"] == 7 and st["hits"] == 1 and st["bytes_h2d"] == 7 * blocks.block_bytes
+    pool.close()
+
+
+@pytest.mark.parametrize("slots", [4, 8])
+def test_pool_ffn_bit_equal_under_eviction(moe, ctx, syn, slots):
+    """40 calls, two tokens of top-2 each, enqueued back to back; the pool
+    holds `slots` blocks (4 = one call's worst case, so calls keep evicting
+    what the previous call read)."""
+    E, T, k = 10, 2, 2
+    blocks, host = make_blocks(moe, ctx, syn, 4, E, seed=32)
+    shared_blocks, _ = make_blocks(moe, ctx, syn, 4, 1, seed=33)
+    shared = shared_blocks.struct(0)
+    pool = moe.MoePool(ctx, slots * blocks.block_bytes, 1, E, H, I)
+    for e in range(E):
+        pool.register(0, e, 4, host[e])
+    table = torch.zeros((E, 6), dtype=torch.int64, device="cuda")
+    bits = torch.zeros((E,), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(slots)
+    calls = []
+    for c in range(40):
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        xq, sx = token_inputs(moe, ctx, syn, T, seed=100 + c)
+        idx = torch.from_numpy(ids).cuda()
+        y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
+        pool.prepare(0, ids, table, bits)
+        moe.moe_expert_ffn_q4(ctx, table, shared, bits, xq, sx, idx, H, I, E, y)
+        calls.append((xq, sx, idx, y))
+    torch.cuda.synchronize()
+    ctx.check()
+    for c, (xq, sx, idx, y) in enumerate(calls):
+        ref = torch.zeros_like(y)
+        moe.moe_expert_ffn_q4(ctx, blocks.table, shared, None, xq, sx, idx, H, I, E, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), c
+    st = pool.stats()
+    log(f"pool slots={slots}: {st}")
+    assert st["hits"] + st["misses"] == sum(len(set(i.cpu().numpy().ravel())) for _, _, i, _ in calls)
+    if slots == 4:
+        assert st["misses"] > 60
+    pool.close()
+
+
+def test_pool_mixed_widths(moe, ctx, syn):
+    """Even experts int4, odd experts int2, two layers sharing one slab; one
+    FFN call per width with the pool's width table."""
+    E, T, k, L = 8, 3, 2, 2
+    b4, h4 = make_blocks(moe, ctx, syn, 4, E, seed=34)
+    b2, h2 = make_blocks(moe, ctx, syn, 2, E, seed=35)
+    cap = 3 * b4.block_bytes + 3 * b2.block_bytes
+    pool = moe.MoePool(ctx, cap, L, E, H, I)
+    for layer in range(L):
+        for e in range(E):
+            if e % 2 == 0:
+                pool.register(layer, e, 4, h4[e])
+            else:
+                pool.register(layer, e, 2, h2[e])
+    ref_table = torch.stack([b4.table[e] if e % 2 == 0 else b2.table[e] for e in range(E)]).contiguous()
+    ref_bits = torch.tensor([4 if e % 2 == 0 else 2 for e in range(E)], dtype=torch.uint8, device="cuda")
+    table = torch.zeros((E, 6), dtype=torch.int64, device="cuda")
+    bits = torch.zeros((E,), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(9)
+    outs = []
+    for c in range(24):
+        layer = c % L
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        if len(set(ids.ravel()) & set(range(0, E, 2))) > 3 or len(set(ids.ravel()) & set(range(1, E, 2))) > 3:
+            continue  # more of one width than the slab holds beside the other
+        xq, sx = token_inputs(moe, ctx, syn, T, seed=200 + c)
+        idx = torch.from_numpy(ids).cuda()
+        y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
+        try:
+            pool.prepare(layer, ids, table, bits)
+        except moe.MoeError as ex:  # first-fit fragmentation can refuse a mixed call
+            assert ex.status == moe.MOE_EPOOL
+            continue
+        moe.moe_expert_ffn_q4(ctx, table, None, bits, xq, sx, idx, H, I, E, y)
+        moe.moe_expert_ffn_q2(ctx, table, None, bits, xq, sx, idx, H, I, E, y)
+        outs.append((xq, sx, idx, y))
+    torch.cuda.synchronize()
+    ctx.check()
+    assert len(outs) >= 8
+    for xq, sx, idx, y in outs:
+        ref = torch.zeros_like(y)
+        moe.moe_expert_ffn_q4(ctx, ref_table, None, ref_bits, xq, sx, idx, H, I, E, ref)
+        moe.moe_expert_ffn_q2(ctx, ref_table, None, ref_bits, xq, sx, idx, H, I, E, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+    pool.close()
+
+
+def test_pool_capacity_refusal_and_reuse(moe, ctx, syn):
+    E = 4
+    blocks, host = make_blocks(moe, ctx, syn, 4, E, seed=36)
+    pool = moe.MoePool(ctx, 2 * blocks.block_bytes, 1, E, H, I)
+    for e in range(E):
+        pool.register(0, e, 4, host[e], pin=(e == 0))
+    table = torch.zeros((E, 6), dtype=torch.int64, device="cuda")
+    pool.prepare(0, np.array([[0, 1]], np.int32), table)
+    with pytest.raises(moe.MoeError) as ex:
+        pool.prepare(0, np.array([[2, 3]], np.int32), table)  # expert 0 is pinned: one free block only
+    assert ex.value.status == moe.MOE_EPOOL
+    pool.prepare(0, np.array([[2]], np.int32), table)
+    torch.cuda.synchronize()
+    assert pool.resident(0, 0) and pool.resident(0, 2)
+    tab = table.cpu().numpy()
+    assert torch.equal(dev_bytes(int(tab[2, 0]), blocks.block_bytes), host[2])
+    pool.close()
