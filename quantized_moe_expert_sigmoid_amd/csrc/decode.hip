@@ -28,12 +28,16 @@
 //     int8 activations held in registers (field order); DPP reductions; one
 //     store of a = silu(g)*u per row pair.
 //  K3 down_combine_t1_kernel (one 512-thread workgroup per CU): the workgroup
-//     loads every slot's a, then each wave issues its first down-row loads;
-//     while they are in flight the workgroup finds max|a| per slot and writes
-//     the int8 codes to LDS, already in the weights' field order, with their
-//     per-slot sums; each wave then multiplies its H rows of every slot's down
-//     matrix, writes y per slot and the combined output
-//     out[r] = y_shared + sum_j w_j y_j (the same fma order as moe_combine).
+//     loads every slot's a and finds max|a| per slot before any weight load
+//     is queued behind it (a wave's loads complete in order); then each wave
+//     issues one down row of every slot and, while it is in flight, the
+//     workgroup writes the int8 codes to LDS, already in the weights' field
+//     order, with their per-slot sums; each wave then multiplies its rows of
+//     every slot's down matrix (one row in flight ahead), writes y per slot
+//     and the combined output out[r] = y_shared + sum_j w_j y_j (the same fma
+//     order as moe_combine). A CU keeps only some tens of KB of loads in
+//     flight; a wave that queues more stalls at issue, so the kernels queue
+//     about that much at a time.
 // Kernel boundaries order the three steps: no atomics across workgroups, no
 // cross-workgroup waits (contended device-scope atomics serialise at the
 // memory side). Streaming loads are branch-free: a lane whose chunk index
@@ -704,10 +708,8 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
     }
   };
   RowBatch b0, b1;
-  load_rows(r0, b0);
-  load_rows(r0 + RB, b1);
 
-  // ---- max|a| per slot ----
+  // ---- max|a| per slot (a arrives first: no weight load is queued before it) ----
   if (tid < kMaxSlots) sum_s[tid] = 0;
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s) {
@@ -731,6 +733,10 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
     inv_l = zero_l ? 0.0f : 1.0f / sa_l;
     fast_l = sa_l >= 0x1p-126f && sa_l <= 0x1.fffffep127f;
   }
+  // the first down rows go out now: one row of every slot per wave, about
+  // what a CU keeps in flight, so the requantisation below does not stall
+  // behind its own loads
+  load_rows(r0, b0);
 
   // ---- int8 codes into LDS in field order, and their per-slot sums ----
 #pragma unroll
@@ -774,6 +780,7 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   }
   __syncthreads();
   if (r0 >= r1) return;
+  load_rows(r0 + RB, b1);
 
   // every slot's codes, in registers in field order
   ActChunk<BITS> aqr[kMaxSlots][JD];
@@ -858,9 +865,12 @@ moe_status launch_dn(moe_ctx *ctx, const DownT1Args &d, int nwg) {
 // batch (NB), down rows per batch (RB).
 template <int BITS>
 struct T1Shape;
+#ifndef MOE_T1_NB4
+#define MOE_T1_NB4 1
+#endif
 template <>
 struct T1Shape<4> {
-  static constexpr int JG = 3, JD = 1, NB = 3, RB = 1;
+  static constexpr int JG = 3, JD = 1, NB = MOE_T1_NB4, RB = 1;
 };
 template <>
 struct T1Shape<8> {
