@@ -1,6 +1,7 @@
-// Single-token (decode) layer path in three kernels: router logits and the
-// activation quantisation; top-k fused with a streaming gate/up GEMV; and the
-// int8 requantisation fused with the down GEMV and the combine.
+// Single-token (decode) layer path in four kernels: router logits and the
+// activation quantisation; top-k fused with a streaming gate/up GEMV; the int8
+// requantisation of the SwiGLU intermediate; the down GEMV fused with the
+// combine.
 //
 // Pages: agentlenshq.com, "Colibri: running GLM-5.2 744B MoE on consumer
 // hardware", section "Key features" (packed int4/int8/int2 with per-row
@@ -27,18 +28,19 @@
 //     waves, stream through 16-byte loads two batches deep against the token's
 //     int8 activations held in registers (field order); DPP reductions; one
 //     store of a = silu(g)*u per row pair.
-//  K3 down_combine_t1_kernel (one 512-thread workgroup per CU): the workgroup
-//     loads every slot's a and finds max|a| per slot before any weight load
-//     is queued behind it (a wave's loads complete in order); then each wave
-//     issues one down row of every slot and, while it is in flight, the
-//     workgroup writes the int8 codes to LDS, already in the weights' field
-//     order, with their per-slot sums; each wave then multiplies its rows of
+//  K3 requant_t1_kernel (one workgroup per slot): max|a| of the slot, the
+//     scale, the int8 codes (written already in the packed weights' field
+//     order) and their sum. Done once per slot rather than by every
+//     workgroup of the down kernel, at full occupancy.
+//  K4 down_combine_t1_kernel (one 512-thread workgroup per CU): the
+//     workgroup loads every slot's codes into LDS (the first down rows of
+//     every slot go out right behind them); each wave multiplies its rows of
 //     every slot's down matrix (one row in flight ahead), writes y per slot
 //     and the combined output out[r] = y_shared + sum_j w_j y_j (the same fma
 //     order as moe_combine). A CU keeps only some tens of KB of loads in
-//     flight; a wave that queues more stalls at issue, so the kernels queue
-//     about that much at a time.
-// Kernel boundaries order the three steps: no atomics across workgroups, no
+//     flight and a wave that queues more stalls at issue, so the kernels
+//     queue about that much at a time.
+// Kernel boundaries order the four steps: no atomics across workgroups, no
 // cross-workgroup waits (contended device-scope atomics serialise at the
 // memory side). Streaming loads are branch-free: a lane whose chunk index
 // passes the row end reads a clamped in-bounds address and meets zero
@@ -586,20 +588,8 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
 }
 
 // ---------------------------------------------------------------------------
-// K3: requantisation + down projection of every slot + combine
+// K3: requantisation of every slot's a (one workgroup per slot)
 // ---------------------------------------------------------------------------
-struct DownT1Args {
-  const SlotEntry *slots;
-  const float *A;  // [S][I]
-  int H, I, S, k, has_shared;
-  float *y;    // [S][H] (the token's y_slots; slot stride H)
-  float *out;  // [H]
-  moe_debug_bufs dbg;
-  int dbg_on;
-};
-
-constexpr int kRqF4 = kMaxIDown / 4 / kFfnThreads;  // float4 of one slot's a per thread (2)
-
 // int8 code of v under the scale sc = m/127 with inv = 1/sc (both correctly
 // rounded): rint(v * inv) equals rint(v / sc) (the fp32 quotient) unless
 // v * inv lies within 2^-15 of a half-integer. With |v| <= m the quotient is
@@ -646,13 +636,129 @@ __device__ __forceinline__ uint32_t field_order(uint32_t w, int lane) {
   }
 }
 
+constexpr int kRqThreads = 256;
+
+struct RequantT1Args {
+  const float *A;  // [S][I]
+  int I, S;
+  uint32_t *aqf;   // [S][I/4] int8 codes, in the packed weights' field order
+  int *sums;       // [S] sum of the codes per slot
+  float *sa;       // [S] per-slot scale
+  moe_debug_bufs dbg;
+  int dbg_on;
+};
+
+// Slot blockIdx.x: sa = max|a|/127 and aq = rint(a/sa) (the activation rule),
+// written as int8 codes in the field order of BITS-bit weights: each thread
+// holds whole field groups (int8: 4 elements, int4: 8, int2: 16), so the
+// reordering stays in registers.
+template <int BITS>
+__global__ __launch_bounds__(kRqThreads) void requant_t1_kernel(RequantT1Args a) {
+  constexpr int G = (BITS == 8) ? 4 : (BITS == 4 ? 8 : 16);
+  constexpr int GD = G / 4;  // dwords (float4 of a) per group
+  __shared__ float red_m[kRqThreads / MOE_WAVE];
+  __shared__ int red_c[kRqThreads / MOE_WAVE];
+  const int tid = threadIdx.x;
+  const int lane = tid & (MOE_WAVE - 1);
+  const int wave = tid >> 6;
+  const int s = blockIdx.x;
+  const float4 *As = reinterpret_cast<const float4 *>(a.A + (int64_t)s * a.I);
+  const int ng = a.I / G;
+  // the thread's groups stay in registers between the two passes
+  constexpr int kIt = (kMaxIDown / G + kRqThreads - 1) / kRqThreads;
+  float4 v4[kIt][GD];
+  float m = 0.0f;
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int g = min(tid + it * kRqThreads, ng - 1);  // past the end: a re-read group, same maximum
+#pragma unroll
+    for (int d = 0; d < GD; ++d) v4[it][d] = As[g * GD + d];
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it)
+#pragma unroll
+    for (int d = 0; d < GD; ++d) {
+      const float4 v = v4[it][d];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+  m = wave_max_dpp(m);
+  if (lane == 0) red_m[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  const bool zero = m == 0.0f;
+  const float sc = zero ? 0.0f : m / 127.0f;
+  const float inv = zero ? 0.0f : 1.0f / sc;
+  const bool fast = sc >= 0x1p-126f && sc <= 0x1.fffffep127f;
+  int csum = 0;
+  uint32_t *dst = a.aqf + (int64_t)s * (a.I / 4);
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int g = tid + it * kRqThreads;
+    if (g >= ng) break;
+    uint32_t nat[GD];
+#pragma unroll
+    for (int d = 0; d < GD; ++d) {
+      const float4 v = v4[it][d];
+      uint32_t word = 0;
+      if (!zero) {
+        bool near = !fast;
+        float q0 = code_fast(v.x, inv, near), q1 = code_fast(v.y, inv, near);
+        float q2 = code_fast(v.z, inv, near), q3 = code_fast(v.w, inv, near);
+        if (near) {
+          q0 = code_exact(v.x, sc);
+          q1 = code_exact(v.y, sc);
+          q2 = code_exact(v.z, sc);
+          q3 = code_exact(v.w, sc);
+        }
+        word = pack_codes(q0, q1, q2, q3);
+      }
+      nat[d] = word;
+      csum = sdot4((int)word, 0x01010101, csum);
+      if (a.dbg_on && a.dbg.aq) reinterpret_cast<uint32_t *>(a.dbg.aq + (int64_t)s * a.I)[g * GD + d] = word;
+    }
+    uint32_t fo[GD];
+    if constexpr (BITS == 4) {
+      act_order_q4(nat[0], nat[1], fo[0], fo[1]);
+    } else if constexpr (BITS == 2) {
+      act_order_q2(nat, fo);
+    } else {
+      fo[0] = nat[0];
+    }
+#pragma unroll
+    for (int d = 0; d < GD; ++d) dst[g * GD + d] = fo[d];
+  }
+  csum = wave_sum_all(csum);
+  if (lane == 0) red_c[wave] = csum;
+  __syncthreads();
+  if (tid == 0) {
+    a.sums[s] = red_c[0] + red_c[1] + red_c[2] + red_c[3];
+    a.sa[s] = sc;
+    if (a.dbg_on && a.dbg.sa) a.dbg.sa[s] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K4: down projection of every slot + combine
+// ---------------------------------------------------------------------------
+struct DownT1Args {
+  const SlotEntry *slots;
+  const uint32_t *aqf;  // [S][I/4] codes in field order
+  const int *sums;      // [S]
+  const float *sa;      // [S]
+  int H, I, S, k, has_shared;
+  float *y;    // [S][H] (the token's y_slots; slot stride H)
+  float *out;  // [H]
+  moe_debug_bufs dbg;
+  int dbg_on;
+};
+
+constexpr int kAq16 = (kMaxSlots * kMaxIDown / 16 + kFfnThreads - 1) / kFfnThreads;  // 16-byte code pieces per thread
+
 template <int BITS, int JD, int RB>
 __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args a) {
   constexpr int OFF = QFmt<BITS>::kOff;
   constexpr int EPC = QFmt<BITS>::kEpc;
   __shared__ __align__(16) int8_t aq_s[kMaxSlots * kMaxIDown];
-  __shared__ float red_s[kMaxSlots][kFfnWaves];
-  __shared__ int sum_s[kMaxSlots];
   const int tid = threadIdx.x;
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
@@ -663,28 +769,23 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   const int cpr = rowbytes / 16;
   const int S = a.S;
 
-  // ---- slot fields (lane s < S holds slot s's) and every slot's a ----
+  // ---- slot fields (lane s < S holds slot s's), then the codes ----
   const int ls = lane < S ? lane : S - 1;
   const uint8_t *down_l = a.slots[ls].w.down;
   const float *sdown_l = a.slots[ls].w.s_down;
   const float w_l = a.slots[ls].weight;
-  const int n4 = a.I / 4;  // float4 per slot
-  // unconditional loads (the compiler can then count them): slots past S
-  // re-read slot S-1 and elements past I re-read element I-4..I-1, which
-  // leaves the per-slot maxima unchanged
-  float4 av[kMaxSlots][kRqF4];
+  const int aqsum_l = a.sums[ls];
+  const float sa_l = a.sa[ls];
+  // every slot's codes (S*I bytes), unconditional loads: pieces past the end
+  // re-read the last one
+  const int n16 = S * a.I / 16;
+  uint4 aqv[kAq16];
 #pragma unroll
-  for (int s = 0; s < kMaxSlots; ++s)
-#pragma unroll
-    for (int c = 0; c < kRqF4; ++c) {
-      const int f = min(tid + c * kFfnThreads, n4 - 1);
-      av[s][c] = reinterpret_cast<const float4 *>(a.A + (int64_t)min(s, S - 1) * a.I)[f];
-    }
+  for (int j = 0; j < kAq16; ++j) aqv[j] = ldg16(a.aqf, min(tid + j * kFfnThreads, n16 - 1));
   const uint8_t *dp[kMaxSlots];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s) dp[s] = readlane_p(down_l, s < S ? s : S - 1);
 
-  // ---- the first down rows go out ----
   struct RowBatch {
     uint4 w[RB][kMaxSlots][JD];
     float sd[RB];
@@ -708,75 +809,13 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
     }
   };
   RowBatch b0, b1;
+  load_rows(r0, b0);  // the first down rows of every slot go out right behind the codes
 
-  // ---- max|a| per slot (a arrives first: no weight load is queued before it) ----
-  if (tid < kMaxSlots) sum_s[tid] = 0;
+  // ---- the codes into LDS ----
 #pragma unroll
-  for (int s = 0; s < kMaxSlots; ++s) {
-    float m = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kRqF4; ++c)
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(av[s][c].x), fabsf(av[s][c].y)), fmaxf(fabsf(av[s][c].z), fabsf(av[s][c].w))));
-    m = wave_max_dpp(m);
-    if (lane == 0) red_s[s][wave] = m;
-  }
-  __syncthreads();
-  // lane s < S: slot s's scale and its reciprocal
-  float sa_l, inv_l;
-  bool zero_l, fast_l;
-  {
-    float m = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kFfnWaves; ++w) m = fmaxf(m, red_s[ls][w]);
-    zero_l = m == 0.0f;
-    sa_l = zero_l ? 0.0f : m / 127.0f;
-    inv_l = zero_l ? 0.0f : 1.0f / sa_l;
-    fast_l = sa_l >= 0x1p-126f && sa_l <= 0x1.fffffep127f;
-  }
-  // the first down rows go out now: one row of every slot per wave, about
-  // what a CU keeps in flight, so the requantisation below does not stall
-  // behind its own loads
-  load_rows(r0, b0);
-
-  // ---- int8 codes into LDS in field order, and their per-slot sums ----
-#pragma unroll
-  for (int s = 0; s < kMaxSlots; ++s) {
-    if (s < S) {
-      const float sc = readlane_f(sa_l, s), inv = readlane_f(inv_l, s);
-      const bool zero = __builtin_amdgcn_readlane((int)zero_l, s) != 0;
-      const bool fast = __builtin_amdgcn_readlane((int)fast_l, s) != 0;
-      int csum = 0;
-#pragma unroll
-      for (int c = 0; c < kRqF4; ++c) {
-        const int f = tid + c * kFfnThreads;
-        if (c * kFfnThreads < n4) {  // uniform: this pass holds data
-          const float4 v = av[s][c];
-          uint32_t word = 0;
-          if (!zero) {
-            bool near = !fast;
-            float q0 = code_fast(v.x, inv, near), q1 = code_fast(v.y, inv, near);
-            float q2 = code_fast(v.z, inv, near), q3 = code_fast(v.w, inv, near);
-            if (near) {
-              q0 = code_exact(v.x, sc);
-              q1 = code_exact(v.y, sc);
-              q2 = code_exact(v.z, sc);
-              q3 = code_exact(v.w, sc);
-            }
-            word = pack_codes(q0, q1, q2, q3);
-          }
-          if (f >= n4) word = 0;
-          csum = sdot4((int)word, 0x01010101, csum);
-          const uint32_t fw = field_order<BITS>(word, lane);
-          if (f < n4) {
-            reinterpret_cast<uint32_t *>(aq_s + s * a.I)[f] = fw;
-            if (blockIdx.x == 0 && a.dbg_on && a.dbg.aq) reinterpret_cast<uint32_t *>(a.dbg.aq + (int64_t)s * a.I)[f] = word;
-          }
-        }
-      }
-      csum = wave_sum_to63(csum);
-      if (lane == 63) atomicAdd(&sum_s[s], csum);
-      if (blockIdx.x == 0 && tid == 0 && a.dbg_on && a.dbg.sa) a.dbg.sa[s] = sc;
-    }
+  for (int j = 0; j < kAq16; ++j) {
+    const int i = tid + j * kFfnThreads;
+    if (i < n16) reinterpret_cast<uint4 *>(aq_s)[i] = aqv[j];
   }
   __syncthreads();
   if (r0 >= r1) return;
@@ -787,7 +826,7 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   int aqsum[kMaxSlots];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s) {
-    aqsum[s] = s < S ? sum_s[s] : 0;
+    aqsum[s] = __builtin_amdgcn_readlane(aqsum_l, s < S ? s : S - 1);
 #pragma unroll
     for (int j = 0; j < JD; ++j) {
       const int c = lane + j * MOE_WAVE;
@@ -805,7 +844,6 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
       }
     }
   }
-
   auto compute_rows = [&](int rb, const RowBatch &bt) {
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
@@ -862,15 +900,13 @@ moe_status launch_dn(moe_ctx *ctx, const DownT1Args &d, int nwg) {
 
 // Per-width kernel shapes: 16-byte chunks per lane of a gate/up row (JG) and
 // of a down row (JD) the kernels are compiled for, row pairs per gate/up
-// batch (NB), down rows per batch (RB).
+// batch (NB) and down rows per batch (RB), two batches in flight each. A CU
+// keeps some tens of KB of loads in flight; deeper queues only stall issue.
 template <int BITS>
 struct T1Shape;
-#ifndef MOE_T1_NB4
-#define MOE_T1_NB4 1
-#endif
 template <>
 struct T1Shape<4> {
-  static constexpr int JG = 3, JD = 1, NB = MOE_T1_NB4, RB = 1;
+  static constexpr int JG = 3, JD = 1, NB = 1, RB = 1;
 };
 template <>
 struct T1Shape<8> {
@@ -923,8 +959,9 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
     return o;
   };
   const size_t o_part = take(sizeof(float) * ks * E), o_slots = take(sizeof(SlotEntry) * kMaxSlots),
-               o_A = take(sizeof(float) * S * I), o_idx = take(4 * k), o_w = take(4 * k), o_xq = take(H),
-               o_sx = take(4), o_y = take(sizeof(float) * (k + 1) * H);
+               o_A = take(sizeof(float) * S * I), o_aq = take((size_t)S * I), o_sum = take(4 * S),
+               o_sa = take(4 * S), o_idx = take(4 * k), o_w = take(4 * k), o_xq = take(H), o_sx = take(4),
+               o_y = take(sizeof(float) * (k + 1) * H);
   void *scr = nullptr;
   moe_status st = moe_scratch(ctx, off, &scr);
   if (st) return st;
@@ -975,9 +1012,27 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
   }
   if (st) return st;
 
+  RequantT1Args q{};
+  q.A = g.A;
+  q.I = I;
+  q.S = S;
+  q.aqf = reinterpret_cast<uint32_t *>(base + o_aq);
+  q.sums = reinterpret_cast<int *>(base + o_sum);
+  q.sa = reinterpret_cast<float *>(base + o_sa);
+  q.dbg = ctx->dbg;
+  q.dbg_on = ctx->dbg_on ? 1 : 0;
+  switch (bits) {
+    case 4: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<4>, dim3(S), dim3(kRqThreads), q); break;
+    case 8: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<8>, dim3(S), dim3(kRqThreads), q); break;
+    default: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<2>, dim3(S), dim3(kRqThreads), q); break;
+  }
+  MOE_CHECK_LAUNCH("requant_t1_kernel");
+
   DownT1Args d{};
   d.slots = slots;
-  d.A = g.A;
+  d.aqf = q.aqf;
+  d.sums = q.sums;
+  d.sa = q.sa;
   d.H = H; d.I = I; d.S = S; d.k = k;
   d.has_shared = shared ? 1 : 0;
   d.y = y_slots;
