@@ -56,7 +56,8 @@ constexpr int kMaxSlots = 9;                       // top-k <= 8 plus the shared
 constexpr int kMaxSlices = 16;                     // K slices of the router logits
 constexpr int kMaxE = 1024;
 constexpr int kMaxX4 = 8;        // float4 of x per thread in the max pass: H <= 8192
-constexpr int kMaxIDown = 4096;  // intermediate held in LDS by the down kernel
+constexpr int kMaxIDown = 4096;
+constexpr int kMaxPairsWg = kFfnThreads;  // routed row pairs per gate/up workgroup (one per thread)  // intermediate held in LDS by the down kernel
 
 // One slot of the token: the expert's weights and its routing weight.
 struct SlotEntry {
@@ -369,10 +370,13 @@ __device__ __forceinline__ void gu_compute(int n, int lane0, int lane, const GuB
 
 template <int BITS, int JG, int NB>
 __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) {
+  static_assert(NB == 1, "routed pairs are taken one at a time");
   constexpr int OFF = QFmt<BITS>::kOff;
   __shared__ float key_s[kMaxE], sig_s[kMaxE];
   __shared__ __align__(16) moe_expert_w exp_s[kMaxE];
   __shared__ SlotEntry slot_s[kMaxSlots];
+  __shared__ int next_s;                   // the workgroup's routed-pair counter
+  __shared__ int2 res_s[kMaxPairsWg];      // (gate, up) sums of the workgroup's routed pairs
   const int tid = threadIdx.x;
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
@@ -380,12 +384,15 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   const int gw = blockIdx.x * kFfnWaves + wave;
   const int rowbytes = a.H * BITS / 8;
   const int cpr = rowbytes / 16;
-  // this wave's shared pairs [sh0, sh0 + ns) and routed pairs [q0, q1); lanes
-  // [0, ns) keep the shared results, lanes [ns, ns + q1 - q0) the routed ones
+  // this wave's shared pairs [sh0, sh0 + ns); lanes [0, ns) keep their sums
   const int sh0 = a.has_shared ? uniform((int)((int64_t)gw * a.I / nw)) : 0;
   const int ns = a.has_shared ? uniform((int)((int64_t)(gw + 1) * a.I / nw)) - sh0 : 0;
   const int R = a.k * a.I;
-  const int q0 = uniform((int)((int64_t)gw * R / nw)), q1 = uniform((int)((int64_t)(gw + 1) * R / nw));
+  // the workgroup's routed pairs [Q0, Q0 + np), taken one at a time by its
+  // waves from an LDS counter: a wave whose loads are served late takes fewer
+  const int Q0 = uniform((int)((int64_t)blockIdx.x * R / gridDim.x));
+  const int np = uniform((int)((int64_t)(blockIdx.x + 1) * R / gridDim.x)) - Q0;
+  if (tid == 0) next_s = 0;
 
   // ---- loads first: the routing inputs, the expert table, the token's int8
   // activations, all consumed only after the shared rows below are issued.
@@ -525,65 +532,88 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
     }
   }
   __syncthreads();
-  if (ns == 0 && q0 >= q1) return;
 
-  // ---- this wave's routed slots; the first routed batch goes out ----
+  // ---- the workgroup's routed slots (a contiguous range spans at most two) ----
   WaveSlots ws;
   ws.I = a.I;
-  const int qlast = q0 < q1 ? q1 - 1 : 0;
-  ws.s_first = uniform((q0 < q1 ? q0 : 0) / a.I);
+  const int qlast = np > 0 ? Q0 + np - 1 : 0;
+  ws.s_first = uniform((np > 0 ? Q0 : 0) / a.I);
   const int s_last = uniform(qlast / a.I);
   ws.gate0 = uniform_p(slot_s[ws.s_first].w.gate);
   ws.up0 = uniform_p(slot_s[ws.s_first].w.up);
   ws.gate1 = uniform_p(slot_s[s_last].w.gate);
   ws.up1 = uniform_p(slot_s[s_last].w.up);
-  gu_load<BITS, JG, NB>(ws, q0, qlast, lane, rowbytes, cpr, b1);
+  // the global routed pair loaded for workgroup-local pair p: pairs past the
+  // range re-read its last pair, and a workgroup without routed pairs reads
+  // pair 0 (always valid; its results are never used)
+  auto pair_at = [&](int p) { return np > 0 ? Q0 + min(p, np - 1) : 0; };
+  // take the next routed pair (workgroup-local index; >= np when none is left)
+  auto grab = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_s, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int pa = grab();
+  gu_load<BITS, JG, NB>(ws, pair_at(pa), qlast, lane, rowbytes, cpr, b1);
 
-  // lane -> (slot, row) of the pair it keeps, and that pair's scales
-  const int nr = q1 - q0;
-  const bool mine = lane < ns + nr;
-  const bool is_sh = lane < ns;
-  int my_slot = a.k, my_i = sh0 + lane;
-  float sg = sg_sh, su = su_sh;
+  // thread t < np: routed pair t's slot, row and scales (used after the loop)
+  const bool rt_mine = tid < np;
+  int rt_slot = 0, rt_i = 0;
+  float rt_sg = 0.0f, rt_su = 0.0f;
   {
-    const int q = min(q0 + max(lane - ns, 0), qlast);
-    const int rs = q / a.I;
-    const int ri = q - rs * a.I;
-    const float g2 = gptr(slot_s[rs].w.s_gate)[ri];
-    const float u2 = gptr(slot_s[rs].w.s_up)[ri];
-    if (!is_sh) {
-      my_slot = rs;
-      my_i = ri;
-      sg = g2;
-      su = u2;
-    }
+    const int q = Q0 + min(tid, max(np - 1, 0));
+    rt_slot = q / a.I;
+    rt_i = q - rt_slot * a.I;
+    rt_sg = gptr(slot_s[rt_slot].w.s_gate)[rt_i];
+    rt_su = gptr(slot_s[rt_slot].w.s_up)[rt_i];
   }
   const int xsum = wave_sum_all(xs_lane);
 
+  // the wave's shared pairs (lanes [0, ns) keep their sums)
   int res_g = 0, res_u = 0;
   if (ns > 0) gu_compute<BITS, JG, NB>(ns, 0, lane, b0, xr, res_g, res_u);
-  // routed batches alternate b1, b0, b1, ...
-  for (int qb = q0; qb < q1; qb += 2 * NB) {
-    if (qb + NB < q1) gu_load<BITS, JG, NB>(ws, qb + NB, qlast, lane, rowbytes, cpr, b0);
-    gu_compute<BITS, JG, NB>(min(NB, q1 - qb), ns + qb - q0, lane, b1, xr, res_g, res_u);
-    if (qb + NB >= q1) break;
-    if (qb + 2 * NB < q1) gu_load<BITS, JG, NB>(ws, qb + 2 * NB, qlast, lane, rowbytes, cpr, b1);
-    gu_compute<BITS, JG, NB>(min(NB, q1 - qb - NB), ns + qb + NB - q0, lane, b0, xr, res_g, res_u);
+  int pb = grab();
+  gu_load<BITS, JG, NB>(ws, pair_at(pb), qlast, lane, rowbytes, cpr, b0);
+  // routed pairs, two in flight (pairs past np re-read the last one; pa < pb)
+  for (;;) {
+    if (pa >= np) break;
+    {
+      int g0 = 0, u0 = 0;
+      gu_compute<BITS, JG, NB>(1, 0, lane, b1, xr, g0, u0);
+      if (lane == 0) res_s[pa] = make_int2(__builtin_amdgcn_readfirstlane(g0), __builtin_amdgcn_readfirstlane(u0));
+    }
+    pa = grab();
+    gu_load<BITS, JG, NB>(ws, pair_at(pa), qlast, lane, rowbytes, cpr, b1);
+    if (pb >= np) break;
+    {
+      int g0 = 0, u0 = 0;
+      gu_compute<BITS, JG, NB>(1, 0, lane, b0, xr, g0, u0);
+      if (lane == 0) res_s[pb] = make_int2(__builtin_amdgcn_readfirstlane(g0), __builtin_amdgcn_readfirstlane(u0));
+    }
+    pb = grab();
+    gu_load<BITS, JG, NB>(ws, pair_at(pb), qlast, lane, rowbytes, cpr, b0);
   }
 
-  if (mine) {
-    const int gi = res_g - OFF * xsum;
-    const int ui = res_u - OFF * xsum;
+  // a = silu(g) * u: the wave's shared pairs, then the workgroup's routed pairs
+  auto epilogue = [&](int gsum, int usum, float sg, float su, int slot, int i) {
+    const int gi = gsum - OFF * xsum;
+    const int ui = usum - OFF * xsum;
     const float g = (float)gi * sg * sxv;
     const float u = (float)ui * su * sxv;
     const float av = moe_silu_f32(g) * u;
-    const int64_t o = (int64_t)my_slot * a.I + my_i;
+    const int64_t o = (int64_t)slot * a.I + i;
     a.A[o] = av;
     if (a.dbg_on) {
       if (a.dbg.accg) a.dbg.accg[o] = gi;
       if (a.dbg.accu) a.dbg.accu[o] = ui;
       if (a.dbg.a) a.dbg.a[o] = av;
     }
+  };
+  if (lane < ns) epilogue(res_g, res_u, sg_sh, su_sh, a.k, sh0 + lane);
+  __syncthreads();
+  if (rt_mine) {
+    const int2 r = res_s[tid];
+    epilogue(r.x, r.y, rt_sg, rt_su, rt_slot, rt_i);
   }
 }
 
@@ -910,11 +940,11 @@ struct T1Shape<4> {
 };
 template <>
 struct T1Shape<8> {
-  static constexpr int JG = 6, JD = 2, NB = 2, RB = 1;
+  static constexpr int JG = 6, JD = 2, NB = 1, RB = 1;
 };
 template <>
 struct T1Shape<2> {
-  static constexpr int JG = 2, JD = 1, NB = 4, RB = 1;
+  static constexpr int JG = 2, JD = 1, NB = 1, RB = 1;
 };
 
 }  // namespace
@@ -926,8 +956,9 @@ bool decode_t1_supported(int bits, int H, int I, int k, int has_shared, int n_cu
   // loads its shared pairs in one batch
   const int64_t waves = (int64_t)n_cu * kFfnWaves;
   const int64_t ns = has_shared ? (I + waves - 1) / waves : 0;
-  const int64_t nr = ((int64_t)k * I + waves - 1) / waves;
-  if (ns + nr > MOE_WAVE) return false;
+  if (ns > MOE_WAVE) return false;
+  // a gate/up workgroup's routed pairs: one per thread in its epilogue
+  if (((int64_t)k * I + n_cu - 1) / n_cu > kMaxPairsWg) return false;
   const int jg = moe_chunks_per_lane(H, bits), jd = moe_chunks_per_lane(I, bits);
   switch (bits) {
     case 4: return jg <= T1Shape<4>::JG && jd <= T1Shape<4>::JD && ns <= T1Shape<4>::NB;
