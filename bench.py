@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --copy-probe MB        # only a device copy of MB megabytes (counter calibration)
     python bench.py --pmc-summary BENCH_FETCH BENCH_WRITE COPY_FETCH COPY_WRITE OUT.md
+    python bench.py --workload glm_stack_pool [--stack-layers L] [--stack-pool-gb G]   # decode through the expert pool
 
 A step is one full pass of the layer's hot path over one batch of synthetic
 input: int8 activation quantisation, sigmoid top-k routing, per-expert
@@ -123,6 +124,131 @@ def pmc_summary(bench_fetch, bench_write, copy_fetch, copy_write, out_md) -> Non
     print(open(out_md).read())
 
 
+def stack_pool_bench(args) -> None:
+    """Decode through the HBM expert pool: a stack of GLM-shaped MoE layers
+    whose routed experts live in pinned host memory (hot experts, the layer's
+    top Zipf ranks, at int4; the rest at int2), with a slab smaller than their
+    total, refilled over PCIe on misses. One token per step; each layer's
+    routing comes from a correlated Zipf trace (a slot keeps the previous
+    token's expert with probability 0.6). Per layer: quantise the token,
+    prepare the pool (misses refill on the copy stream), the int4 and int2
+    FFN calls, the combine. Prints one JSON line."""
+    import torch
+    import quantized_moe_expert_sigmoid_amd as moe
+    from synth import workloads as wl
+
+    Lr, E, k, H, I = args.stack_layers, 256, 8, 6144, 2048
+    w = wl.Workload("glm_stack_pool", H=H, I=I, E=E, k=k, T=1, seed=6)
+    ctx = moe.MoeCtx(0)
+    b4, _ = moe.moe_expert_block_layout(4, H, I)
+    b2, _ = moe.moe_expert_block_layout(2, H, I)
+    hot = args.stack_hot
+    # a few distinct packed blocks per width, packed on the GPU from seeded
+    # fp32 weights, tiled over the stack's host memory (pinned)
+    nsrc = 4
+    src = {}
+    for bits in (4, 2):
+        blk = moe.ExpertBlocks(nsrc, bits, H, I)
+        for e in range(nsrc):
+            g, u, d = wl.expert_fp32(w, e)
+            blk.pack_from_fp32(ctx, e, *(torch.from_numpy(a).cuda() for a in (g, u, d)))
+        torch.cuda.synchronize()
+        src[bits] = blk.data.cpu()
+        del blk
+    t0 = time.time()
+    host = []  # per layer: (int4 blocks [hot], int2 blocks [E - hot]) pinned
+    for layer in range(Lr):
+        h4 = torch.empty((hot, b4), dtype=torch.uint8, pin_memory=True)
+        h2 = torch.empty((E - hot, b2), dtype=torch.uint8, pin_memory=True)
+        for i in range(hot):
+            h4[i].copy_(src[4][(layer + i) % nsrc])
+        for i in range(E - hot):
+            h2[i].copy_(src[2][(layer + i) % nsrc])
+        host.append((h4, h2))
+    host_bytes = Lr * (hot * b4 + (E - hot) * b2)
+    log(f"[stack] {Lr} layers, {host_bytes / 1e9:.1f} GB of pinned expert blocks ready in {time.time() - t0:.1f}s")
+    pool = moe.MoePool(ctx, int(args.stack_pool_gb * 1e9), Lr, E, H, I)
+    for layer in range(Lr):
+        rank_of = wl.zipf_rank(w.seed, layer, E)
+        n4 = n2 = 0
+        for e in range(E):
+            if rank_of[e] <= hot:
+                pool.register(layer, e, 4, host[layer][0][n4])
+                n4 += 1
+            else:
+                pool.register(layer, e, 2, host[layer][1][n2])
+                n2 += 1
+    shared = moe.ExpertBlocks(Lr, 4, H, I)
+    for layer in range(Lr):
+        g, u, d = wl.shared_fp32(w, layer)
+        shared.pack_from_fp32(ctx, layer, *(torch.from_numpy(a).cuda() for a in (g, u, d)))
+    ntok = args.stack_warmup + args.stack_tokens
+    traces = [wl.correlated_trace(w.seed, layer, ntok, E, k) for layer in range(Lr)]
+    trace_dev = [torch.from_numpy(tr).cuda() for tr in traces]
+    wts = torch.full((1, k), 1.0 / k, dtype=torch.float32, device="cuda")
+    xs = [torch.from_numpy(wl.hidden_fp32(w, 1, batch=i)).cuda() for i in range(16)]
+    tables = [torch.zeros((E, 6), dtype=torch.int64, device="cuda") for _ in range(Lr)]
+    widths = [torch.zeros((E,), dtype=torch.uint8, device="cuda") for _ in range(Lr)]
+    xq = torch.empty((1, H), dtype=torch.int8, device="cuda")
+    sx = torch.empty((1,), dtype=torch.float32, device="cuda")
+    y = torch.zeros((1, k + 1, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def run(t0_, t1_):
+        for t in range(t0_, t1_):
+            for layer in range(Lr):
+                idx = trace_dev[layer][t:t + 1]
+                moe.moe_quantize_act_i8(ctx, xs[(t + layer) % 16], xq, sx)
+                pool.prepare(layer, traces[layer][t:t + 1], tables[layer], widths[layer])
+                moe.moe_expert_ffn_q4(ctx, tables[layer], shared.struct(layer), widths[layer], xq, sx, idx, H, I, E, y)
+                moe.moe_expert_ffn_q2(ctx, tables[layer], None, widths[layer], xq, sx, idx, H, I, E, y)
+                moe.moe_combine(ctx, y, wts, True, out)
+
+    tc = time.perf_counter()
+    run(0, args.stack_warmup)
+    torch.cuda.synchronize()
+    cold_s = time.perf_counter() - tc
+    st0 = pool.stats()
+    tm = time.perf_counter()
+    run(args.stack_warmup, ntok)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - tm
+    ctx.check()
+    st1 = pool.stats()
+    n = args.stack_tokens
+    hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
+    h2d = st1["bytes_h2d"] - st0["bytes_h2d"]
+    # H2D probe: one pinned 1 GB host-to-device copy
+    hp = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dp = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dp.copy_(hp, non_blocking=True)
+    torch.cuda.synchronize()
+    tp = time.perf_counter()
+    for _ in range(4):
+        dp.copy_(hp, non_blocking=True)
+    torch.cuda.synchronize()
+    probe = 4 * (1 << 30) / (time.perf_counter() - tp) / 1e9
+    res = {
+        "metric": "MoE stack decode tokens/s through the expert pool (int4 hot / int2 cold, 1 GPU)",
+        "value": round(n / dt, 2), "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": args.stack_warmup,
+        "ms_per_step": round(dt / n * 1e3, 4), "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": "glm_stack_pool", "layers": Lr, "hidden": H, "intermediate": I, "routed_experts": E,
+                   "top_k": k, "hot_experts_int4": hot, "pool_bytes": int(args.stack_pool_gb * 1e9),
+                   "host_expert_bytes": host_bytes, "routing": "correlated Zipf trace (reuse 0.6, s 1.1)"},
+        "cold_start_tokens_per_s": round(args.stack_warmup / cold_s, 2),
+        "hit_rate": round(hits / max(1, hits + misses), 5),
+        "misses_per_token": round(misses / n, 3),
+        "h2d_GBps": round(h2d / dt / 1e9, 2),
+        "h2d_probe_GBps": round(probe, 2),
+    }
+    log(f"[stack] {n} tokens in {dt:.2f}s: {n / dt:.1f} tokens/s, hit rate {res['hit_rate']}, "
+        f"{res['misses_per_token']} misses/token, H2D {res['h2d_GBps']} GB/s (probe {res['h2d_probe_GBps']} GB/s)")
+    print(json.dumps(res), flush=True)
+    pool.close()
+    ctx.close()
+
+
 def load_traffic():
     """Scaled HBM bytes per launch from the committed counter summary, or None
     when it is missing or was measured on other kernel sources."""
@@ -197,6 +323,11 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--cpu-repeats", type=int, default=8)
     ap.add_argument("--copy-probe", type=float, default=0.0, help="only run a device copy of this many MB")
+    ap.add_argument("--stack-layers", type=int, default=10)
+    ap.add_argument("--stack-pool-gb", type=float, default=40.0)
+    ap.add_argument("--stack-hot", type=int, default=192)
+    ap.add_argument("--stack-tokens", type=int, default=1000)
+    ap.add_argument("--stack-warmup", type=int, default=300)
     ap.add_argument("--pmc-summary", nargs=5, default=None,
                     metavar=("BENCH_FETCH", "BENCH_WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"))
     args = ap.parse_args()
@@ -218,6 +349,9 @@ def main():
         sys.exit(2)
     if args.copy_probe > 0:
         copy_probe(args.copy_probe)
+        return
+    if args.workload == "glm_stack_pool":
+        stack_pool_bench(args)
         return
     moe.lib()
     w = wl.ALL[args.workload]

@@ -22,7 +22,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import expert_weights, hidden, router_bias, router_weights, zipf_logits
+from . import (K_TRACE, expert_weights, gumbel, hidden, router_bias, router_weights, stream_id, uniform, zipf_logits,
+               zipf_rank)
 
 
 @dataclass(frozen=True)
@@ -93,3 +94,35 @@ def iter_experts(w: Workload, experts, layer: int = 0, prefetch: int = 2):
             break
         yield item
     th.join()
+
+
+def correlated_trace(seed: int, layer: int, T: int, E: int, k: int, reuse: float = 0.6, s: float = 1.1):
+    """Routing trace int32 [T][k] of one layer of a decoding stack: each slot
+    keeps the previous token's expert in that slot with probability `reuse`
+    (when this token has not taken it already); the other slots draw from the
+    layer's Zipf(s) popularity without replacement (Gumbel-top-k over
+    ln p_rank + Gumbel noise, one noise vector per token)."""
+    rank_of = zipf_rank(seed, layer, E)
+    logp = -s * np.log(rank_of.astype(np.float64))
+    g = gumbel(seed, stream_id(K_TRACE, layer, 0), T * E).reshape(T, E)
+    u = uniform(seed, stream_id(K_TRACE, layer, 1), T * k).reshape(T, k)
+    out = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        taken = np.zeros(E, dtype=bool)
+        row = np.full(k, -1, dtype=np.int64)
+        if t > 0:
+            for j in range(k):
+                e = out[t - 1, j]
+                if u[t, j] < reuse and not taken[e]:
+                    row[j] = e
+                    taken[e] = True
+        order = np.argsort(-(logp + g[t]), kind="stable")
+        pos = 0
+        for j in range(k):
+            if row[j] < 0:
+                while taken[order[pos]]:
+                    pos += 1
+                row[j] = order[pos]
+                taken[row[j]] = True
+        out[t] = row
+    return out
