@@ -99,7 +99,7 @@ def pmc_summary(bench_fetch, bench_write, copy_fetch, copy_write, out_md) -> Non
     bf, bw = _pmc_means(bench_fetch, "FETCH_SIZE"), _pmc_means(bench_write, "WRITE_SIZE")
     rows, traffic = [], {}
     for short, key in (("router", "router_gemv_t1_kernel"), ("gateup", "gateup_t1_kernel"),
-                       ("down", "down_combine_t1_kernel")):
+                       ("requant", "requant_t1_kernel"), ("down", "down_combine_t1_kernel")):
         kf, kw = pick(bf, key), pick(bw, key)
         fb = bf[kf][0] * 1024.0 * f_scale
         wb = bw[kw][0] * 1024.0 * w_scale
