@@ -24,6 +24,7 @@ _lock = threading.Lock()
 _lib = None
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_EUNSUPPORTED, MOE_EPOOL, MOE_ETIMEOUT = 0, -1, -2, -3, -4, -5, -6
+MOE_FFN_AUTO, MOE_FFN_DOT4, MOE_FFN_MFMA = 0, 1, 2
 _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_EUNSUPPORTED",
            -5: "MOE_EPOOL", -6: "MOE_ETIMEOUT"}
 
@@ -73,6 +74,7 @@ _SIGS = {
     "moe_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "moe_ctx_set_debug": (_i32, [_vp, ctypes.POINTER(DebugBufs)]),
     "moe_ctx_enable_timing": (_i32, [_vp, _i32]),
+    "moe_ctx_set_ffn_kernels": (_i32, [_vp, _i32]),
     "moe_ctx_read_timing": (_i32, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
     "moe_layer_forward": (_i32, [_vp, _i32, ctypes.POINTER(RouterCfg), _vp, _vp, _vp, _vp, _vp,
                                  ctypes.POINTER(ExpertW), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -161,6 +163,12 @@ class MoeCtx:
         _ck(lib().moe_ctx_check(self.handle))
 
     STAGES = ("router", "bucket", "gateup", "requant", "down", "combine")
+
+    def set_ffn_kernels(self, which):
+        """"auto", "dot4" or "mfma" (or MOE_FFN_*): kernels of the expert FFN."""
+        if isinstance(which, str):
+            which = {"auto": MOE_FFN_AUTO, "dot4": MOE_FFN_DOT4, "mfma": MOE_FFN_MFMA}[which]
+        _ck(lib().moe_ctx_set_ffn_kernels(self.handle, int(which)))
 
     def enable_timing(self, on: bool = True):
         _ck(lib().moe_ctx_enable_timing(self.handle, 1 if on else 0))

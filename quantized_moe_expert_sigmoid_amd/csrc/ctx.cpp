@@ -114,6 +114,14 @@ MoeTimer::~MoeTimer() {
   }
 }
 
+extern "C" moe_status moe_ctx_set_ffn_kernels(moe_ctx *ctx, int which) {
+  if (!ctx) return moe_fail(MOE_EINVAL, "moe_ctx_set_ffn_kernels: ctx is NULL");
+  if (which != MOE_FFN_AUTO && which != MOE_FFN_DOT4 && which != MOE_FFN_MFMA)
+    return moe_fail(MOE_EINVAL, "moe_ctx_set_ffn_kernels: %d is not MOE_FFN_AUTO, _DOT4 or _MFMA", which);
+  ctx->ffn_kernels = which;
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_ctx_enable_timing(moe_ctx *ctx, int enable) {
   if (!ctx) return moe_fail(MOE_EINVAL, "moe_ctx_enable_timing: ctx is NULL");
   ctx->timing = enable != 0;

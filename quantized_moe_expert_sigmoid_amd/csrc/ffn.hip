@@ -26,10 +26,6 @@
 
 #include "moe_internal.h"
 
-moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
-                         int32_t *perm, const uint8_t *expert_bits, int want_bits, int32_t *active,
-                         int32_t *n_active);
-
 namespace {
 
 constexpr int kThreads = 256;
@@ -455,6 +451,12 @@ int rows_per_wg_d(int bits) { return kWaves * (bits == 8 ? Shape<8>::kRwD : bits
 moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                              const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
                              int T, int H, int I, int E, int k, float *y_slots) {
+  const bool mfma_ok = expert_ffn_mfma_supported(bits, H, I);
+  if (ctx->ffn_kernels == MOE_FFN_MFMA && !mfma_ok)
+    return moe_fail(MOE_EUNSUPPORTED, "expert FFN: the matrix-core kernels do not take H %d, I %d at %d bits", H, I,
+                    bits);
+  if (mfma_ok && (ctx->ffn_kernels == MOE_FFN_MFMA || (ctx->ffn_kernels == MOE_FFN_AUTO && T >= 2)))
+    return launch_expert_ffn_mfma(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots);
   const int64_t P = (int64_t)T * (k + 1);
   FfnArgs a{};
   a.tiles1 = I / rows_per_wg_gu(bits);
@@ -496,7 +498,7 @@ moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts
   a.dbg_on = ctx->dbg_on ? 1 : 0;
   st = launch_bucket(ctx, topk_idx, T, k, E, const_cast<int32_t *>(a.counts), const_cast<int32_t *>(a.offsets),
                      const_cast<int32_t *>(a.perm), expert_bits, bits, const_cast<int32_t *>(a.active),
-                     const_cast<int32_t *>(a.n_active));
+                     const_cast<int32_t *>(a.n_active), nullptr, nullptr, 0, 0);
   if (st) return st;
   const int dmax = (int)std::min<int64_t>(E, (int64_t)T * k) + a.has_shared;
   switch (bits) {

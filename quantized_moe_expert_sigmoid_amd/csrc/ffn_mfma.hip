@@ -1,0 +1,576 @@
+// Multi-token SwiGLU expert FFN on the int8 matrix cores
+// (v_mfma_i32_16x16x64_i8: 16 x 16 int32 results over 64 int8 products).
+//
+// agentlenshq.com, "Colibri: running GLM-5.2 744B MoE on consumer hardware",
+// section "Key features": packed int4/int8/int2 weights with per-row scales,
+// dequantised on use, and int8 matmuls as integer dot products (here the
+// matrix cores' exact int32 accumulation). remio.ai, "Colibri shows how to run
+// GLM-5.2 on a low-spec PC", section "The RAM wall became a storage problem":
+// an expert needed by several batch positions is read once -- here once per
+// tile of up to 64 of them.
+//
+// After bucket_kernel has built the per-expert token lists and their tiles:
+//  1. act_field_kernel (int4 and int2 only): every token's int8 codes
+//     reordered into the packed weights' field order -- per 32 elements the 16
+//     even ones then the 16 odd ones (int4), per 64 elements the four 2-bit
+//     fields of 16 elements each (int2) -- and the sum of the codes.
+//  2. gu_mfma_kernel: one workgroup per (token tile, 64 rows of gate and of
+//     up); wave w owns rows 16w..16w+15 of both. A row is read as 16-byte
+//     pieces; per step lane l takes piece 4c + l/16 of row l%16 and splits it
+//     into its 1, 2 or 4 fields (int8 bytes, or offset-binary values 0..15 /
+//     0..3 held as int8). The matrix core pairs byte j of lane l's activation
+//     operand with byte j of its weight operand, so the field order of the
+//     activations makes each weight field meet its own element. The offset is
+//     removed once per token with its code sum. Epilogue: the scales, SiLU,
+//     a = silu(g) * u into the (token, slot) row of the intermediate.
+//  3. requant_mfma_kernel: per (token, slot) pair: sa = max|a| / 127 and the
+//     codes rint(a / sa), written in field order, and their sum.
+//  4. dn_mfma_kernel: one workgroup per (token tile, 128 down rows), each wave
+//     32 rows; y = acc * s_down * sa into the slot buffer.
+// A tile holds up to 64 tokens of one expert, run as 4 blocks of 16 through
+// the matrix core (rows past the expert's last token repeat it and are not
+// stored); an expert's remainder of 1..16 tokens is a one-block tile. Both
+// kinds are workgroups of the same launch. Weight rows stream from HBM once
+// per tile; the activation rows are re-read from L2.
+#include <algorithm>
+
+#include "gemv_common.h"
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kGuRows = 64;   // gate (and up) rows per workgroup
+constexpr int kDnRows = 128;  // down rows per workgroup
+constexpr int kMaxI = 8192;
+
+struct MArgs {
+  const moe_expert_w *experts;
+  moe_expert_w shared;
+  int has_shared;
+  const int8_t *xa;      // [T][H] token codes in field order (xq itself for int8)
+  const int32_t *xsum;   // [T] code sums (int4, int2)
+  const float *sx;       // [T]
+  const int32_t *topk_idx;
+  const uint8_t *expert_bits;
+  int bits, T, H, I, E, k;
+  const int32_t *counts, *offsets, *perm, *active, *n_active;
+  const int2 *units;      // tiles: [ubig_max] of up to 64 tokens, then the one-block tiles
+  const int32_t *n_units;  // [2] tiles of each kind
+  int ubig_max;
+  float *A;      // [P][I] SwiGLU intermediate, P = T (k + 1)
+  int8_t *aq;    // [P][I] its codes, field order
+  int32_t *aqs;  // [P] code sums
+  float *sa;     // [P]
+  float *y;      // [T][k+1][H]
+  moe_debug_bufs dbg;
+  int dbg_on;
+};
+
+struct Ex {
+  moe_expert_w w;
+  int ntok, base, is_shared;
+};
+
+__device__ __forceinline__ bool resolve_ex(const MArgs &a, int d, Ex &r) {
+  const int na = *a.n_active;
+  if (d < na) {
+    const int e = a.active[d];
+    r.w = a.experts[e];
+    r.ntok = a.counts[e];
+    r.base = a.offsets[e];
+    r.is_shared = 0;
+    return true;
+  }
+  if (a.has_shared && d == na) {
+    r.w = a.shared;
+    r.ntok = a.T;
+    r.base = 0;
+    r.is_shared = 1;
+    return true;
+  }
+  return false;
+}
+
+// token and (token, slot) row of the expert's g-th entry
+__device__ __forceinline__ void pair_of(const MArgs &a, const Ex &ex, int g, int &t, int &p) {
+  if (ex.is_shared) {
+    t = g;
+    p = g * (a.k + 1) + a.k;
+  } else {
+    const int ent = a.perm[ex.base + g];
+    t = ent / a.k;
+    p = t * (a.k + 1) + (ent - t * a.k);
+  }
+}
+
+// field S of a 16-byte piece of packed weights as an int8 operand
+template <int BITS, int S>
+__device__ __forceinline__ v4i wfield(uint4 w) {
+  if constexpr (BITS == 8) {
+    return v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+  } else if constexpr (BITS == 4) {
+    constexpr uint32_t M = 0x0f0f0f0fu;
+    return v4i{(int)((w.x >> (4 * S)) & M), (int)((w.y >> (4 * S)) & M), (int)((w.z >> (4 * S)) & M),
+               (int)((w.w >> (4 * S)) & M)};
+  } else {
+    constexpr uint32_t M = 0x03030303u;
+    return v4i{(int)((w.x >> (2 * S)) & M), (int)((w.y >> (2 * S)) & M), (int)((w.z >> (2 * S)) & M),
+               (int)((w.w >> (2 * S)) & M)};
+  }
+}
+
+__device__ __forceinline__ v4i as_v4i(uint4 v, bool keep) {
+  return keep ? v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w} : v4i{0, 0, 0, 0};
+}
+
+__device__ __forceinline__ v4i mfma(v4i x, v4i w, v4i acc) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w, acc, 0, 0, 0);
+}
+
+struct TileTokens {
+  int tok[64], pair[64], osum[64];
+  float scale[64];
+};
+
+// ---------------------------------------------------------------------------
+// token codes in field order
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void act_field_kernel(const int8_t *xq, int H, int8_t *xa, int32_t *xsum) {
+  constexpr int EPC = QFmt<BITS>::kEpc, ND = EPC / 4;
+  __shared__ int red[kThreads / MOE_WAVE];
+  const int t = blockIdx.x;
+  const uint32_t *src = reinterpret_cast<const uint32_t *>(xq + (int64_t)t * H);
+  uint32_t *dst = reinterpret_cast<uint32_t *>(xa + (int64_t)t * H);
+  int sum = 0;
+  for (int blk = threadIdx.x; blk < H / EPC; blk += kThreads) {
+    uint32_t d[ND], o[ND];
+#pragma unroll
+    for (int q = 0; q < ND / 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4 *>(src + blk * ND)[q];
+      d[4 * q] = v.x;
+      d[4 * q + 1] = v.y;
+      d[4 * q + 2] = v.z;
+      d[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int q = 0; q < ND; ++q) sum = sdot4((int)d[q], 0x01010101, sum);
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) act_order_q4(d[2 * j], d[2 * j + 1], o[j], o[4 + j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t f[4];
+        act_order_q2(d + 4 * j, f);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) o[4 * s + j] = f[s];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < ND / 4; ++q)
+      reinterpret_cast<uint4 *>(dst + blk * ND)[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  }
+  sum = wave_sum_i32(sum);
+  if ((threadIdx.x & (MOE_WAVE - 1)) == 0) red[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) xsum[t] = red[0] + red[1] + red[2] + red[3];
+}
+
+// ---------------------------------------------------------------------------
+// gate + up
+// ---------------------------------------------------------------------------
+template <int BITS, int MB>
+__device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, int d, int m0) {
+  constexpr int EPC = QFmt<BITS>::kEpc, OFF = QFmt<BITS>::kOff, NS = EPC / 16;
+  Ex ex;
+  if (!resolve_ex(a, d, ex)) return;
+  const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wave = tid >> 6;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int nt = min(MB * 16, ex.ntok - m0);  // >= 1 for a listed tile
+  if (tid < MB * 16) {
+    int t, p;
+    pair_of(a, ex, m0 + min(tid, nt - 1), t, p);
+    tt_s.tok[tid] = t;
+    tt_s.pair[tid] = p;
+    tt_s.scale[tid] = a.sx[t];
+    if constexpr (OFF != 0) tt_s.osum[tid] = OFF * a.xsum[t];
+  }
+  const int rowbytes = a.H * BITS / 8;
+  const int nq = rowbytes / 16;       // 16-byte pieces per row
+  const int nch = (nq + 3) / 4;       // steps of 4 pieces
+  const int row = blockIdx.y * kGuRows + wave * 16 + r16;
+  const uint8_t *pg = ex.w.gate + (int64_t)row * rowbytes;
+  const uint8_t *pu = ex.w.up + (int64_t)row * rowbytes;
+  const float sg = ex.w.s_gate[row], su = ex.w.s_up[row];
+  __syncthreads();
+  const int8_t *px[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) px[mb] = a.xa + (int64_t)tt_s.tok[mb * 16 + r16] * a.H;
+
+  uint4 bg[2], bu[2], xv[2][MB][NS];
+  bool kv[2];
+  auto load = [&](int c, int b) {
+    const int q = c * 4 + grp;
+    kv[b] = q < nq;
+    const int qc = min(q, nq - 1);
+    bg[b] = ldg16(pg + qc * 16, 0);
+    bu[b] = ldg16(pu + qc * 16, 0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) xv[b][mb][s] = ldg16(px[mb] + qc * EPC, s);
+    asm volatile("" ::: "memory");  // issue here, one step ahead of the use
+  };
+  v4i accg[MB], accu[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) accg[mb] = accu[mb] = v4i{0, 0, 0, 0};
+  load(0, 0);
+  load(1, 1);
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        v4i wg, wu;
+        if (s == 0) { wg = wfield<BITS, 0>(bg[b]); wu = wfield<BITS, 0>(bu[b]); }
+        else if (s == 1) { wg = wfield<BITS, 1>(bg[b]); wu = wfield<BITS, 1>(bu[b]); }
+        else if (s == 2) { wg = wfield<BITS, 2>(bg[b]); wu = wfield<BITS, 2>(bu[b]); }
+        else { wg = wfield<BITS, 3>(bg[b]); wu = wfield<BITS, 3>(bu[b]); }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const v4i x = as_v4i(xv[b][mb][s], kv[b]);
+          accg[mb] = mfma(x, wg, accg[mb]);
+          accu[mb] = mfma(x, wu, accu[mb]);
+        }
+      }
+      load(c + b + 2, b);
+    }
+  }
+  // lane holds tokens 4*grp + r of each block, row `row`
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = mb * 16 + grp * 4 + r;
+      if (tt < nt) {
+        const int64_t p = tt_s.pair[tt];
+        int gi = accg[mb][r], ui = accu[mb][r];
+        if constexpr (OFF != 0) {
+          gi -= tt_s.osum[tt];
+          ui -= tt_s.osum[tt];
+        }
+        const float g = (float)gi * sg * tt_s.scale[tt];
+        const float u = (float)ui * su * tt_s.scale[tt];
+        const float av = moe_silu_f32(g) * u;
+        a.A[p * a.I + row] = av;
+        if (a.dbg_on) {
+          if (a.dbg.accg) a.dbg.accg[p * a.I + row] = gi;
+          if (a.dbg.accu) a.dbg.accu[p * a.I + row] = ui;
+          if (a.dbg.a) a.dbg.a[p * a.I + row] = av;
+        }
+      }
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a) {
+  __shared__ TileTokens tt_s;
+  const int u = blockIdx.x;
+  if (u < a.ubig_max) {
+    if (u >= a.n_units[0]) return;
+    const int2 un = a.units[u];
+    gu_tile<BITS, 4>(a, tt_s, un.x, un.y);
+  } else {
+    if (u - a.ubig_max >= a.n_units[1]) return;
+    const int2 un = a.units[u];
+    gu_tile<BITS, 1>(a, tt_s, un.x, un.y);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// requantisation of a, one workgroup per (token, slot) pair
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void requant_mfma_kernel(MArgs a) {
+  constexpr int G = (BITS == 8) ? 4 : (BITS == 4 ? 8 : 16);  // consecutive elements per thread and group
+  constexpr int GD = G / 4;
+  constexpr int kIt = (kMaxI / G + kThreads - 1) / kThreads;
+  __shared__ float red_m[kThreads / MOE_WAVE];
+  __shared__ int red_s[kThreads / MOE_WAVE];
+  const int64_t p = blockIdx.x;
+  const int t = (int)(p / (a.k + 1));
+  const int slot = (int)(p - (int64_t)t * (a.k + 1));
+  if (slot < a.k) {
+    const int e = a.topk_idx[(int64_t)t * a.k + slot];
+    if (e < 0 || e >= a.E) return;
+    if (a.expert_bits && a.expert_bits[e] != a.bits) return;
+    for (int j = 0; j < slot; ++j)  // a repeated expert is computed for its first slot only
+      if (a.topk_idx[(int64_t)t * a.k + j] == e) return;
+  } else if (!a.has_shared) {
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wave = tid >> 6;
+  const int ng = a.I / G;
+  const float4 *src = reinterpret_cast<const float4 *>(a.A + p * a.I);
+  float4 v[kIt][GD];
+  float m = 0.0f;
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int g = min(tid + it * kThreads, ng - 1);  // past the end: a re-read group, same maximum
+#pragma unroll
+    for (int q = 0; q < GD; ++q) {
+      v[it][q] = src[g * GD + q];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[it][q].x), fabsf(v[it][q].y)), fmaxf(fabsf(v[it][q].z), fabsf(v[it][q].w))));
+    }
+  }
+  m = wave_max_f32(m);
+  if (lane == 0) red_m[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  const float sc = (m == 0.0f) ? 0.0f : m / 127.0f;
+  int csum = 0;
+  uint8_t *dst = reinterpret_cast<uint8_t *>(a.aq + p * a.I);
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int g = tid + it * kThreads;
+    if (g >= ng) break;
+    uint32_t nat[GD];
+#pragma unroll
+    for (int q = 0; q < GD; ++q) {
+      const float e4[4] = {v[it][q].x, v[it][q].y, v[it][q].z, v[it][q].w};
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int c = 0;
+        if (m != 0.0f) c = (int)fminf(fmaxf(__builtin_rintf(e4[j] / sc), -127.0f), 127.0f);
+        w |= (uint32_t)(uint8_t)(int8_t)c << (8 * j);
+      }
+      nat[q] = w;
+      csum = sdot4((int)w, 0x01010101, csum);
+    }
+    if (a.dbg_on && a.dbg.aq) {
+#pragma unroll
+      for (int q = 0; q < GD; ++q) reinterpret_cast<uint32_t *>(a.dbg.aq + p * a.I + g * G)[q] = nat[q];
+    }
+    if constexpr (BITS == 8) {
+      *reinterpret_cast<uint32_t *>(dst + g * 4) = nat[0];
+    } else if constexpr (BITS == 4) {
+      uint32_t ev, od;
+      act_order_q4(nat[0], nat[1], ev, od);
+      const int base = (g >> 2) * 32 + (g & 3) * 4;
+      *reinterpret_cast<uint32_t *>(dst + base) = ev;
+      *reinterpret_cast<uint32_t *>(dst + base + 16) = od;
+    } else {
+      uint32_t f[4];
+      act_order_q2(nat, f);
+      const int base = (g >> 2) * 64 + (g & 3) * 4;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) *reinterpret_cast<uint32_t *>(dst + base + 16 * s) = f[s];
+    }
+  }
+  csum = wave_sum_i32(csum);
+  if (lane == 0) red_s[wave] = csum;
+  __syncthreads();
+  if (tid == 0) {
+    a.aqs[p] = red_s[0] + red_s[1] + red_s[2] + red_s[3];
+    a.sa[p] = sc;
+    if (a.dbg_on && a.dbg.sa) a.dbg.sa[p] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down
+// ---------------------------------------------------------------------------
+template <int BITS, int MB>
+__device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, int d, int m0) {
+  constexpr int EPC = QFmt<BITS>::kEpc, OFF = QFmt<BITS>::kOff, NS = EPC / 16;
+  Ex ex;
+  if (!resolve_ex(a, d, ex)) return;
+  const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wave = tid >> 6;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int nt = min(MB * 16, ex.ntok - m0);
+  if (tid < MB * 16) {
+    int t, p;
+    pair_of(a, ex, m0 + min(tid, nt - 1), t, p);
+    tt_s.tok[tid] = t;
+    tt_s.pair[tid] = p;
+    tt_s.scale[tid] = a.sa[p];
+    if constexpr (OFF != 0) tt_s.osum[tid] = OFF * a.aqs[p];
+  }
+  const int rowbytes = a.I * BITS / 8;
+  const int nq = rowbytes / 16;
+  const int nch = (nq + 3) / 4;
+  const int row0 = blockIdx.y * kDnRows + wave * 32 + r16, row1 = row0 + 16;
+  const uint8_t *pd0 = ex.w.down + (int64_t)row0 * rowbytes;
+  const uint8_t *pd1 = ex.w.down + (int64_t)row1 * rowbytes;
+  const float sd0 = ex.w.s_down[row0], sd1 = ex.w.s_down[row1];
+  __syncthreads();
+  const int8_t *px[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) px[mb] = a.aq + (int64_t)tt_s.pair[mb * 16 + r16] * a.I;
+
+  uint4 b0[2], b1[2], xv[2][MB][NS];
+  bool kv[2];
+  auto load = [&](int c, int b) {
+    const int q = c * 4 + grp;
+    kv[b] = q < nq;
+    const int qc = min(q, nq - 1);
+    b0[b] = ldg16(pd0 + qc * 16, 0);
+    b1[b] = ldg16(pd1 + qc * 16, 0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) xv[b][mb][s] = ldg16(px[mb] + qc * EPC, s);
+    asm volatile("" ::: "memory");  // issue here, one step ahead of the use
+  };
+  v4i acc0[MB], acc1[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc0[mb] = acc1[mb] = v4i{0, 0, 0, 0};
+  load(0, 0);
+  load(1, 1);
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        v4i w0, w1;
+        if (s == 0) { w0 = wfield<BITS, 0>(b0[b]); w1 = wfield<BITS, 0>(b1[b]); }
+        else if (s == 1) { w0 = wfield<BITS, 1>(b0[b]); w1 = wfield<BITS, 1>(b1[b]); }
+        else if (s == 2) { w0 = wfield<BITS, 2>(b0[b]); w1 = wfield<BITS, 2>(b1[b]); }
+        else { w0 = wfield<BITS, 3>(b0[b]); w1 = wfield<BITS, 3>(b1[b]); }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const v4i x = as_v4i(xv[b][mb][s], kv[b]);
+          acc0[mb] = mfma(x, w0, acc0[mb]);
+          acc1[mb] = mfma(x, w1, acc1[mb]);
+        }
+      }
+      load(c + b + 2, b);
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = mb * 16 + grp * 4 + r;
+      if (tt < nt) {
+        const int64_t p = tt_s.pair[tt];
+        int d0 = acc0[mb][r], d1 = acc1[mb][r];
+        if constexpr (OFF != 0) {
+          d0 -= tt_s.osum[tt];
+          d1 -= tt_s.osum[tt];
+        }
+        a.y[p * a.H + row0] = (float)d0 * sd0 * tt_s.scale[tt];
+        a.y[p * a.H + row1] = (float)d1 * sd1 * tt_s.scale[tt];
+        if (a.dbg_on && a.dbg.accd) {
+          a.dbg.accd[p * a.H + row0] = d0;
+          a.dbg.accd[p * a.H + row1] = d1;
+        }
+      }
+    }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void dn_mfma_kernel(MArgs a) {
+  __shared__ TileTokens tt_s;
+  const int u = blockIdx.x;
+  if (u < a.ubig_max) {
+    if (u >= a.n_units[0]) return;
+    const int2 un = a.units[u];
+    dn_tile<BITS, 4>(a, tt_s, un.x, un.y);
+  } else {
+    if (u - a.ubig_max >= a.n_units[1]) return;
+    const int2 un = a.units[u];
+    dn_tile<BITS, 1>(a, tt_s, un.x, un.y);
+  }
+}
+
+template <int BITS>
+moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *xa, int32_t *xsum, int nunits) {
+  if constexpr (BITS != 8) {
+    moe_launch(ctx, MOE_STAGE_BUCKET, act_field_kernel<BITS>, dim3(a.T), dim3(kThreads), xq, a.H, xa, xsum);
+    MOE_CHECK_LAUNCH("act_field_kernel");
+  }
+  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS>, dim3(nunits, a.I / kGuRows), dim3(kThreads), a);
+  MOE_CHECK_LAUNCH("gu_mfma_kernel");
+  moe_launch(ctx, MOE_STAGE_REQUANT, requant_mfma_kernel<BITS>, dim3(a.T * (a.k + 1)), dim3(kThreads), a);
+  MOE_CHECK_LAUNCH("requant_mfma_kernel");
+  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS>, dim3(nunits, a.H / kDnRows), dim3(kThreads), a);
+  MOE_CHECK_LAUNCH("dn_mfma_kernel");
+  return MOE_OK;
+}
+
+}  // namespace
+
+bool expert_ffn_mfma_supported(int bits, int H, int I) {
+  return H % kDnRows == 0 && I % kGuRows == 0 && I <= kMaxI && (H * bits / 8) % 16 == 0 && (I * bits / 8) % 16 == 0;
+}
+
+moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
+                                  const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                                  const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots) {
+  const int64_t P = (int64_t)T * (k + 1);
+  const int has_shared = shared ? 1 : 0;
+  const int dact = (int)std::min<int64_t>(E, (int64_t)T * k);
+  // sum over experts of ceil(n_e / 64) <= T k / 64 + (active experts), plus the shared expert's tiles
+  const int ubig = (int)(((int64_t)T * k) / kUnitM + dact + 1 + (has_shared ? (T + kUnitM - 1) / kUnitM : 0));
+  const int usmall = dact + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = moe_round_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_counts = take(4 * (size_t)E), o_offsets = take(4 * (size_t)(E + 1)), o_perm = take(4 * (size_t)T * k),
+               o_active = take(4 * (size_t)E), o_nact = take(4), o_units = take(8 * (size_t)(ubig + usmall)),
+               o_nunits = take(8), o_xa = take(bits == 8 ? 0 : (size_t)T * H), o_xsum = take(4 * (size_t)T),
+               o_A = take(4 * (size_t)P * I), o_aq = take((size_t)P * I), o_aqs = take(4 * (size_t)P),
+               o_sa = take(4 * (size_t)P);
+  void *scr = nullptr;
+  moe_status st = moe_scratch(ctx, off, &scr);
+  if (st) return st;
+  char *base = static_cast<char *>(scr);
+  MArgs a{};
+  a.experts = experts;
+  a.has_shared = has_shared;
+  if (shared) a.shared = *shared;
+  int8_t *xa = bits == 8 ? const_cast<int8_t *>(xq) : reinterpret_cast<int8_t *>(base + o_xa);
+  int32_t *xsum = reinterpret_cast<int32_t *>(base + o_xsum);
+  a.xa = xa;
+  a.xsum = xsum;
+  a.sx = sx;
+  a.topk_idx = topk_idx;
+  a.expert_bits = expert_bits;
+  a.bits = bits;
+  a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
+  int32_t *counts = reinterpret_cast<int32_t *>(base + o_counts);
+  int32_t *offsets = reinterpret_cast<int32_t *>(base + o_offsets);
+  int32_t *perm = reinterpret_cast<int32_t *>(base + o_perm);
+  int32_t *active = reinterpret_cast<int32_t *>(base + o_active);
+  int32_t *nact = reinterpret_cast<int32_t *>(base + o_nact);
+  int2 *units = reinterpret_cast<int2 *>(base + o_units);
+  int32_t *nunits = reinterpret_cast<int32_t *>(base + o_nunits);
+  a.counts = counts; a.offsets = offsets; a.perm = perm; a.active = active; a.n_active = nact;
+  a.units = units;
+  a.n_units = nunits;
+  a.ubig_max = ubig;
+  a.A = reinterpret_cast<float *>(base + o_A);
+  a.aq = reinterpret_cast<int8_t *>(base + o_aq);
+  a.aqs = reinterpret_cast<int32_t *>(base + o_aqs);
+  a.sa = reinterpret_cast<float *>(base + o_sa);
+  a.y = y_slots;
+  a.dbg = ctx->dbg;
+  a.dbg_on = ctx->dbg_on ? 1 : 0;
+  st = launch_bucket(ctx, topk_idx, T, k, E, counts, offsets, perm, expert_bits, bits, active, nact, units, nunits,
+                     ubig, has_shared);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  switch (bits) {
+    case 8: return launch_bits<8>(ctx, a, xq, xa, xsum, ubig + usmall);
+    case 4: return launch_bits<4>(ctx, a, xq, xa, xsum, ubig + usmall);
+    default: return launch_bits<2>(ctx, a, xq, xa, xsum, ubig + usmall);
+  }
+}

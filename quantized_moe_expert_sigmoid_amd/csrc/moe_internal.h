@@ -33,6 +33,7 @@ struct moe_ctx {
   size_t io_bytes = 0;
   // small persistent device block: error flags and counters
   uint32_t *dev_small = nullptr;  // [0] error flags, [1..] counters
+  int ffn_kernels = MOE_FFN_AUTO;
   bool dbg_on = false;
   moe_debug_bufs dbg{};
   // per-kernel timing (measurement only)
@@ -104,6 +105,17 @@ moe_status launch_bucket_public(moe_ctx *ctx, const int32_t *topk_idx, int T, in
 moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                              const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
                              int T, int H, int I, int E, int k, float *y_slots);
+// Token tiles of the matrix-core expert FFN: up to kUnitM tokens of one
+// expert per tile; a remainder of at most kUnitSmall tokens is a one-block tile.
+constexpr int kUnitM = 64;
+constexpr int kUnitSmall = 16;
+moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
+                         int32_t *perm, const uint8_t *expert_bits, int want_bits, int32_t *active,
+                         int32_t *n_active, int2 *units, int32_t *n_units, int ubig_max, int has_shared);
+bool expert_ffn_mfma_supported(int bits, int H, int I);
+moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
+                                  const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                                  const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots);
 moe_status launch_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, int T, int k, int H,
                           int has_shared, float *out);
 bool decode_t1_supported(int bits, int H, int I, int k, int has_shared, int n_cu);

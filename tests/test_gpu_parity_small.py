@@ -184,14 +184,12 @@ def random_routing(syn, T, E, k, seed):
     return np.argsort(-z, axis=1, kind="stable")[:, :k].astype(np.int32)
 
 
-@pytest.mark.parametrize("bits", [4, 8, 2])
-@pytest.mark.parametrize("T,H,I,E,k", [(32, 128, 64, 8, 2), (37, 256, 192, 8, 2), (3, 512, 128, 16, 4)])
-def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, bits, T, H, I, E, k):
-    log(f"ffn bits={bits} T={T} H={H} I={I} E={E} k={k}")
-    blocks, shared, oexp, osh = make_experts(moe, orc, syn, bits, H, I, E, seed=40 + bits)
-    x = syn.hidden(41, T, H)
+def check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, seed):
+    """Every intermediate of every (token, slot) pair bit-equal to the oracle's."""
+    log(f"ffn kernels={kern} bits={bits} T={T} H={H} I={I} E={E} k={k}")
+    blocks, shared, oexp, osh = make_experts(moe, orc, syn, bits, H, I, E, seed=seed)
+    x = syn.hidden(seed + 1, T, H)
     xq_o, sx_o = orc.quantize_act(x)
-    idx = random_routing(syn, T, E, k, 42)
     P = T * (k + 1)
     dbg = dict(accg=torch.zeros((P, I), dtype=torch.int32, device="cuda"),
                accu=torch.zeros((P, I), dtype=torch.int32, device="cuda"),
@@ -201,11 +199,13 @@ def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, bits, T, H, I, E, k):
                accd=torch.zeros((P, H), dtype=torch.int32, device="cuda"))
     y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
     ctx.set_debug(dbg)
+    ctx.set_ffn_kernels(kern)
     try:
         moe.FFN_BY_BITS[bits](ctx, blocks.table, shared.struct(0), None, dev(xq_o), dev(sx_o), dev(idx), H, I, E, y)
         ctx.check()
     finally:
         ctx.set_debug(None)
+        ctx.set_ffn_kernels("auto")
     got = {n: host(t) for n, t in dbg.items()}
     yg = host(y)
     for t in range(T):
@@ -220,6 +220,47 @@ def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, bits, T, H, I, E, k):
             assert got["sa"][p] == np.float32(r["sa"]), (t, j)
             assert np.array_equal(got["accd"][p], r["accd"]), (t, j)
             assert np.array_equal(yg[t, j].view(np.uint32), r["y"].view(np.uint32)), (t, j)
+
+
+@pytest.mark.parametrize("kern", ["dot4", "mfma"])
+@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("T,H,I,E,k", [(32, 128, 64, 8, 2), (37, 256, 192, 8, 2), (3, 512, 128, 16, 4),
+                                       (150, 256, 128, 4, 2)])
+def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, kern, bits, T, H, I, E, k):
+    idx = random_routing(syn, T, E, k, 42)
+    check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, seed=40 + bits)
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+def test_ffn_mfma_tile_boundaries(moe, ctx, orc, syn, bits):
+    """Per-expert token counts on both sides of every tile boundary of the
+    matrix-core kernels (tiles of 64 tokens, one-block tiles for remainders of
+    up to 16): 16, 17, 64, 65, 80, 81, 1 and 0 tokens; the shared expert takes
+    all 324 (5 full tiles and a remainder of 4)."""
+    counts = [16, 17, 64, 65, 80, 81, 1, 0]
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    rng = np.random.default_rng(7)
+    idx = rng.permutation(ids).reshape(-1, 1).astype(np.int32)
+    check_ffn_intermediates(moe, ctx, orc, syn, "mfma", bits, idx.shape[0], 128, 64, 8, 1, idx, seed=45 + bits)
+
+
+def test_ffn_mfma_unsupported_shape_refused(moe, ctx, syn):
+    """Forcing the matrix-core kernels on a shape they do not take (H not a
+    multiple of 128) is refused, not silently rerouted."""
+    H, I, E, k, T = 192, 64, 4, 2, 3
+    blocks = moe.ExpertBlocks(E, 4, H, I)
+    xq = torch.zeros((T, H), dtype=torch.int8, device="cuda")
+    sx = torch.ones((T,), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((T, k), dtype=torch.int32, device="cuda")
+    idx[:, 1] = 1
+    y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
+    ctx.set_ffn_kernels("mfma")
+    try:
+        with pytest.raises(moe.MoeError) as ex:
+            moe.moe_expert_ffn_q4(ctx, blocks.table, None, None, xq, sx, idx, H, I, E, y)
+        assert ex.value.status == moe.MOE_EUNSUPPORTED
+    finally:
+        ctx.set_ffn_kernels("auto")
 
 
 def test_ffn_without_shared_leaves_slot(moe, ctx, orc, syn):
