@@ -112,13 +112,12 @@ const char *moe_last_error(void);
 int moe_abi_version(void);
 /* Which kernels compute the expert FFN of moe_expert_ffn_q* and of the
  * multi-token path of moe_layer_forward. MOE_FFN_AUTO (the default): the
- * int8 matrix-core kernels for two or more tokens when the shape allows them
- * (H a multiple of 128, I of 64, both rows a multiple of 16 bytes at the
- * width), else the vector dot-product kernels. MOE_FFN_DOT4: always the
- * vector kernels. MOE_FFN_MFMA: always the matrix-core kernels; a call whose
- * shape they do not take then fails with MOE_EUNSUPPORTED. Both compute the
- * same exact integer sums and the same fp32 epilogue, so their results are
- * bit-identical. Host-only setting; enqueues nothing. */
+ * int8 matrix-core kernels for two or more tokens, the vector dot-product
+ * kernels for one. MOE_FFN_DOT4: always the vector kernels. MOE_FFN_MFMA:
+ * always the matrix-core kernels. Both take every shape the FFN entry points
+ * accept and compute the same exact integer sums and the same fp32 epilogue,
+ * so their results are bit-identical. Any other value: MOE_EINVAL.
+ * Host-only setting; enqueues nothing. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_DOT4 = 1, MOE_FFN_MFMA = 2 };
 moe_status moe_ctx_set_ffn_kernels(moe_ctx *ctx, int which);
 /* Synchronise the stream and report device-side errors recorded by earlier

@@ -29,9 +29,10 @@
 //     32 rows; y = acc * s_down * sa into the slot buffer.
 // A tile holds up to 64 tokens of one expert, run as 4 blocks of 16 through
 // the matrix core (rows past the expert's last token repeat it and are not
-// stored); an expert's remainder of 1..16 tokens is a one-block tile. Both
-// kinds are workgroups of the same launch. Weight rows stream from HBM once
-// per tile; the activation rows are re-read from L2.
+// stored); an expert's remainder of 1..16 tokens is a one-block tile. Each
+// kind has its own launch (the one-block kernel needs fewer registers and
+// keeps four steps of loads in flight instead of two). Weight rows stream
+// from HBM once per tile; the activation rows are re-read from L2.
 #include <algorithm>
 
 #include "gemv_common.h"
@@ -41,8 +42,6 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kGuRows = 64;   // gate (and up) rows per workgroup
-constexpr int kDnRows = 128;  // down rows per workgroup
 constexpr int kMaxI = 8192;
 
 struct MArgs {
@@ -180,114 +179,162 @@ __global__ __launch_bounds__(kThreads) void act_field_kernel(const int8_t *xq, i
 }
 
 // ---------------------------------------------------------------------------
-// gate + up
+// acc[m][mat][nb] += the tokens of block m times rows of block nb of matrix
+// mat, over whole rows of rowbytes packed bytes. wrow: this lane's row (l%16
+// of the block) of each matrix and block; px: this lane's token row (l%16 of
+// the block) of field-ordered codes. D steps of loads in flight.
 // ---------------------------------------------------------------------------
-template <int BITS, int MB>
-__device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, int d, int m0) {
-  constexpr int EPC = QFmt<BITS>::kEpc, OFF = QFmt<BITS>::kOff, NS = EPC / 16;
-  Ex ex;
-  if (!resolve_ex(a, d, ex)) return;
-  const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wave = tid >> 6;
-  const int grp = lane >> 4, r16 = lane & 15;
+template <int BITS, int MB, int NM, int NB, int D>
+__device__ __forceinline__ void tile_mma(const uint8_t *const (&wrow)[NM][NB], const int8_t *const (&px)[MB],
+                                         int rowbytes, v4i (&acc)[MB][NM][NB]) {
+  constexpr int EPC = QFmt<BITS>::kEpc, NS = EPC / 16;
+  const int grp = (threadIdx.x & (MOE_WAVE - 1)) >> 4;
+  const int nq = rowbytes / 16;  // 16-byte pieces per row
+  const int nch = (nq + 3) / 4;  // steps of 4 pieces (one per lane group)
+  uint4 wv[D][NM][NB], xv[D][MB][NS];
+  bool kv[D];
+  auto load = [&](int c, int b) {
+    const int q = c * 4 + grp;
+    kv[b] = q < nq;  // past the row end: a re-read piece, multiplied by zeros
+    const int qc = min(q, nq - 1);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) wv[b][m][nb] = ldg16(wrow[m][nb] + qc * 16, 0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) xv[b][mb][s] = ldg16(px[mb] + qc * EPC, s);
+    asm volatile("" ::: "memory");  // issue here, D steps ahead of the use
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int b = 0; b < D; ++b) load(b, b);
+  for (int c = 0; c < nch; c += D) {
+#pragma unroll
+    for (int b = 0; b < D; ++b) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        v4i x[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) x[mb] = as_v4i(xv[b][mb][s], kv[b]);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            v4i w;
+            if (s == 0) w = wfield<BITS, 0>(wv[b][m][nb]);
+            else if (s == 1) w = wfield<BITS, 1>(wv[b][m][nb]);
+            else if (s == 2) w = wfield<BITS, 2>(wv[b][m][nb]);
+            else w = wfield<BITS, 3>(wv[b][m][nb]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb][m][nb] = mfma(x[mb], w, acc[mb][m][nb]);
+          }
+      }
+      load(c + b + D, b);
+    }
+  }
+}
+
+// the tile's tokens (entries past the expert's last token repeat it)
+template <int MB>
+__device__ __forceinline__ int stage_tokens(const MArgs &a, const Ex &ex, int m0, bool down, int off,
+                                            TileTokens &tt_s) {
   const int nt = min(MB * 16, ex.ntok - m0);  // >= 1 for a listed tile
+  const int tid = threadIdx.x;
   if (tid < MB * 16) {
     int t, p;
     pair_of(a, ex, m0 + min(tid, nt - 1), t, p);
     tt_s.tok[tid] = t;
     tt_s.pair[tid] = p;
-    tt_s.scale[tid] = a.sx[t];
-    if constexpr (OFF != 0) tt_s.osum[tid] = OFF * a.xsum[t];
+    tt_s.scale[tid] = down ? a.sa[p] : a.sx[t];
+    if (off != 0) tt_s.osum[tid] = off * (down ? a.aqs[p] : a.xsum[t]);
   }
+  return nt;
+}
+
+// ---------------------------------------------------------------------------
+// gate + up: a workgroup takes 64 NB rows of each, a wave 16 NB
+// ---------------------------------------------------------------------------
+template <int BITS, int MB, int NB, int D>
+__device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, int d, int m0) {
+  constexpr int OFF = QFmt<BITS>::kOff;
+  Ex ex;
+  if (!resolve_ex(a, d, ex)) return;
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int nt = stage_tokens<MB>(a, ex, m0, false, OFF, tt_s);
   const int rowbytes = a.H * BITS / 8;
-  const int nq = rowbytes / 16;       // 16-byte pieces per row
-  const int nch = (nq + 3) / 4;       // steps of 4 pieces
-  const int row = blockIdx.y * kGuRows + wave * 16 + r16;
-  const uint8_t *pg = ex.w.gate + (int64_t)row * rowbytes;
-  const uint8_t *pu = ex.w.up + (int64_t)row * rowbytes;
-  const float sg = ex.w.s_gate[row], su = ex.w.s_up[row];
+  int row[NB];
+  const uint8_t *wrow[2][NB];
+  float sg[NB], su[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    row[nb] = blockIdx.y * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
+    const int rc = min(row[nb], a.I - 1);  // rows past I: re-read, not stored
+    wrow[0][nb] = ex.w.gate + (int64_t)rc * rowbytes;
+    wrow[1][nb] = ex.w.up + (int64_t)rc * rowbytes;
+    sg[nb] = ex.w.s_gate[rc];
+    su[nb] = ex.w.s_up[rc];
+  }
   __syncthreads();
   const int8_t *px[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) px[mb] = a.xa + (int64_t)tt_s.tok[mb * 16 + r16] * a.H;
-
-  uint4 bg[2], bu[2], xv[2][MB][NS];
-  bool kv[2];
-  auto load = [&](int c, int b) {
-    const int q = c * 4 + grp;
-    kv[b] = q < nq;
-    const int qc = min(q, nq - 1);
-    bg[b] = ldg16(pg + qc * 16, 0);
-    bu[b] = ldg16(pu + qc * 16, 0);
+  v4i acc[MB][2][NB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int s = 0; s < NS; ++s) xv[b][mb][s] = ldg16(px[mb] + qc * EPC, s);
-    asm volatile("" ::: "memory");  // issue here, one step ahead of the use
-  };
-  v4i accg[MB], accu[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) accg[mb] = accu[mb] = v4i{0, 0, 0, 0};
-  load(0, 0);
-  load(1, 1);
-  for (int c = 0; c < nch; c += 2) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        v4i wg, wu;
-        if (s == 0) { wg = wfield<BITS, 0>(bg[b]); wu = wfield<BITS, 0>(bu[b]); }
-        else if (s == 1) { wg = wfield<BITS, 1>(bg[b]); wu = wfield<BITS, 1>(bu[b]); }
-        else if (s == 2) { wg = wfield<BITS, 2>(bg[b]); wu = wfield<BITS, 2>(bu[b]); }
-        else { wg = wfield<BITS, 3>(bg[b]); wu = wfield<BITS, 3>(bu[b]); }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const v4i x = as_v4i(xv[b][mb][s], kv[b]);
-          accg[mb] = mfma(x, wg, accg[mb]);
-          accu[mb] = mfma(x, wu, accu[mb]);
-        }
-      }
-      load(c + b + 2, b);
-    }
-  }
-  // lane holds tokens 4*grp + r of each block, row `row`
+    for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = acc[mb][1][nb] = v4i{0, 0, 0, 0};
+  tile_mma<BITS, MB, 2, NB, D>(wrow, px, rowbytes, acc);
+  // lane holds tokens 4*grp + r of each block, row row[nb]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tt = mb * 16 + grp * 4 + r;
-      if (tt < nt) {
-        const int64_t p = tt_s.pair[tt];
-        int gi = accg[mb][r], ui = accu[mb][r];
+      if (tt >= nt) continue;
+      const int64_t p = tt_s.pair[tt];
+      const float sxt = tt_s.scale[tt];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (row[nb] >= a.I) continue;
+        int gi = acc[mb][0][nb][r], ui = acc[mb][1][nb][r];
         if constexpr (OFF != 0) {
           gi -= tt_s.osum[tt];
           ui -= tt_s.osum[tt];
         }
-        const float g = (float)gi * sg * tt_s.scale[tt];
-        const float u = (float)ui * su * tt_s.scale[tt];
+        const float g = (float)gi * sg[nb] * sxt;
+        const float u = (float)ui * su[nb] * sxt;
         const float av = moe_silu_f32(g) * u;
-        a.A[p * a.I + row] = av;
+        const int64_t o = p * a.I + row[nb];
+        a.A[o] = av;
         if (a.dbg_on) {
-          if (a.dbg.accg) a.dbg.accg[p * a.I + row] = gi;
-          if (a.dbg.accu) a.dbg.accu[p * a.I + row] = ui;
-          if (a.dbg.a) a.dbg.a[p * a.I + row] = av;
+          if (a.dbg.accg) a.dbg.accg[o] = gi;
+          if (a.dbg.accu) a.dbg.accu[o] = ui;
+          if (a.dbg.a) a.dbg.a[o] = av;
         }
       }
     }
 }
 
-template <int BITS>
+// MB = 4: the tiles of more than 16 tokens; MB = 1: the one-block tiles
+template <int MB>
+struct GuShape {
+  static constexpr int NB = MB == 4 ? 2 : 1, D = MB == 4 ? 2 : 4;
+};
+template <int MB>
+struct DnShape {
+  static constexpr int NB = 2, D = MB == 4 ? 2 : 4;
+};
+
+template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a) {
   __shared__ TileTokens tt_s;
   const int u = blockIdx.x;
-  if (u < a.ubig_max) {
-    if (u >= a.n_units[0]) return;
-    const int2 un = a.units[u];
-    gu_tile<BITS, 4>(a, tt_s, un.x, un.y);
-  } else {
-    if (u - a.ubig_max >= a.n_units[1]) return;
-    const int2 un = a.units[u];
-    gu_tile<BITS, 1>(a, tt_s, un.x, un.y);
-  }
+  if (u >= a.n_units[MB == 4 ? 0 : 1]) return;
+  const int2 un = a.units[MB == 4 ? u : a.ubig_max + u];
+  gu_tile<BITS, MB, GuShape<MB>::NB, GuShape<MB>::D>(a, tt_s, un.x, un.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -382,123 +429,85 @@ __global__ __launch_bounds__(kThreads) void requant_mfma_kernel(MArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// down
+// down: a workgroup takes 64 NB rows, a wave 16 NB
 // ---------------------------------------------------------------------------
-template <int BITS, int MB>
+template <int BITS, int MB, int NB, int D>
 __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, int d, int m0) {
-  constexpr int EPC = QFmt<BITS>::kEpc, OFF = QFmt<BITS>::kOff, NS = EPC / 16;
+  constexpr int OFF = QFmt<BITS>::kOff;
   Ex ex;
   if (!resolve_ex(a, d, ex)) return;
-  const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wave = tid >> 6;
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x >> 6;
   const int grp = lane >> 4, r16 = lane & 15;
-  const int nt = min(MB * 16, ex.ntok - m0);
-  if (tid < MB * 16) {
-    int t, p;
-    pair_of(a, ex, m0 + min(tid, nt - 1), t, p);
-    tt_s.tok[tid] = t;
-    tt_s.pair[tid] = p;
-    tt_s.scale[tid] = a.sa[p];
-    if constexpr (OFF != 0) tt_s.osum[tid] = OFF * a.aqs[p];
-  }
+  const int nt = stage_tokens<MB>(a, ex, m0, true, OFF, tt_s);
   const int rowbytes = a.I * BITS / 8;
-  const int nq = rowbytes / 16;
-  const int nch = (nq + 3) / 4;
-  const int row0 = blockIdx.y * kDnRows + wave * 32 + r16, row1 = row0 + 16;
-  const uint8_t *pd0 = ex.w.down + (int64_t)row0 * rowbytes;
-  const uint8_t *pd1 = ex.w.down + (int64_t)row1 * rowbytes;
-  const float sd0 = ex.w.s_down[row0], sd1 = ex.w.s_down[row1];
+  int row[NB];
+  const uint8_t *wrow[1][NB];
+  float sd[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    row[nb] = blockIdx.y * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
+    const int rc = min(row[nb], a.H - 1);
+    wrow[0][nb] = ex.w.down + (int64_t)rc * rowbytes;
+    sd[nb] = ex.w.s_down[rc];
+  }
   __syncthreads();
   const int8_t *px[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) px[mb] = a.aq + (int64_t)tt_s.pair[mb * 16 + r16] * a.I;
-
-  uint4 b0[2], b1[2], xv[2][MB][NS];
-  bool kv[2];
-  auto load = [&](int c, int b) {
-    const int q = c * 4 + grp;
-    kv[b] = q < nq;
-    const int qc = min(q, nq - 1);
-    b0[b] = ldg16(pd0 + qc * 16, 0);
-    b1[b] = ldg16(pd1 + qc * 16, 0);
+  v4i acc[MB][1][NB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int s = 0; s < NS; ++s) xv[b][mb][s] = ldg16(px[mb] + qc * EPC, s);
-    asm volatile("" ::: "memory");  // issue here, one step ahead of the use
-  };
-  v4i acc0[MB], acc1[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc0[mb] = acc1[mb] = v4i{0, 0, 0, 0};
-  load(0, 0);
-  load(1, 1);
-  for (int c = 0; c < nch; c += 2) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        v4i w0, w1;
-        if (s == 0) { w0 = wfield<BITS, 0>(b0[b]); w1 = wfield<BITS, 0>(b1[b]); }
-        else if (s == 1) { w0 = wfield<BITS, 1>(b0[b]); w1 = wfield<BITS, 1>(b1[b]); }
-        else if (s == 2) { w0 = wfield<BITS, 2>(b0[b]); w1 = wfield<BITS, 2>(b1[b]); }
-        else { w0 = wfield<BITS, 3>(b0[b]); w1 = wfield<BITS, 3>(b1[b]); }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const v4i x = as_v4i(xv[b][mb][s], kv[b]);
-          acc0[mb] = mfma(x, w0, acc0[mb]);
-          acc1[mb] = mfma(x, w1, acc1[mb]);
-        }
-      }
-      load(c + b + 2, b);
-    }
-  }
+    for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = v4i{0, 0, 0, 0};
+  tile_mma<BITS, MB, 1, NB, D>(wrow, px, rowbytes, acc);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tt = mb * 16 + grp * 4 + r;
-      if (tt < nt) {
-        const int64_t p = tt_s.pair[tt];
-        int d0 = acc0[mb][r], d1 = acc1[mb][r];
-        if constexpr (OFF != 0) {
-          d0 -= tt_s.osum[tt];
-          d1 -= tt_s.osum[tt];
-        }
-        a.y[p * a.H + row0] = (float)d0 * sd0 * tt_s.scale[tt];
-        a.y[p * a.H + row1] = (float)d1 * sd1 * tt_s.scale[tt];
-        if (a.dbg_on && a.dbg.accd) {
-          a.dbg.accd[p * a.H + row0] = d0;
-          a.dbg.accd[p * a.H + row1] = d1;
-        }
+      if (tt >= nt) continue;
+      const int64_t p = tt_s.pair[tt];
+      const float sat = tt_s.scale[tt];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (row[nb] >= a.H) continue;
+        int di = acc[mb][0][nb][r];
+        if constexpr (OFF != 0) di -= tt_s.osum[tt];
+        a.y[p * a.H + row[nb]] = (float)di * sd[nb] * sat;
+        if (a.dbg_on && a.dbg.accd) a.dbg.accd[p * a.H + row[nb]] = di;
       }
     }
 }
 
-template <int BITS>
+template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads) void dn_mfma_kernel(MArgs a) {
   __shared__ TileTokens tt_s;
   const int u = blockIdx.x;
-  if (u < a.ubig_max) {
-    if (u >= a.n_units[0]) return;
-    const int2 un = a.units[u];
-    dn_tile<BITS, 4>(a, tt_s, un.x, un.y);
-  } else {
-    if (u - a.ubig_max >= a.n_units[1]) return;
-    const int2 un = a.units[u];
-    dn_tile<BITS, 1>(a, tt_s, un.x, un.y);
-  }
+  if (u >= a.n_units[MB == 4 ? 0 : 1]) return;
+  const int2 un = a.units[MB == 4 ? u : a.ubig_max + u];
+  dn_tile<BITS, MB, DnShape<MB>::NB, DnShape<MB>::D>(a, tt_s, un.x, un.y);
 }
 
 template <int BITS>
-moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *xa, int32_t *xsum, int nunits) {
+moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *xa, int32_t *xsum, int usmall) {
   if constexpr (BITS != 8) {
     moe_launch(ctx, MOE_STAGE_BUCKET, act_field_kernel<BITS>, dim3(a.T), dim3(kThreads), xq, a.H, xa, xsum);
     MOE_CHECK_LAUNCH("act_field_kernel");
   }
-  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS>, dim3(nunits, a.I / kGuRows), dim3(kThreads), a);
+  auto tiles = [](int n, int rows) { return (n + rows - 1) / rows; };
+  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max, tiles(a.I, 64 * GuShape<4>::NB)),
+             dim3(kThreads), a);
+  MOE_CHECK_LAUNCH("gu_mfma_kernel");
+  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 1>, dim3(usmall, tiles(a.I, 64 * GuShape<1>::NB)),
+             dim3(kThreads), a);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
   moe_launch(ctx, MOE_STAGE_REQUANT, requant_mfma_kernel<BITS>, dim3(a.T * (a.k + 1)), dim3(kThreads), a);
   MOE_CHECK_LAUNCH("requant_mfma_kernel");
-  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS>, dim3(nunits, a.H / kDnRows), dim3(kThreads), a);
+  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max, tiles(a.H, 64 * DnShape<4>::NB)),
+             dim3(kThreads), a);
+  MOE_CHECK_LAUNCH("dn_mfma_kernel");
+  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 1>, dim3(usmall, tiles(a.H, 64 * DnShape<1>::NB)),
+             dim3(kThreads), a);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
   return MOE_OK;
 }
@@ -506,7 +515,7 @@ moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *x
 }  // namespace
 
 bool expert_ffn_mfma_supported(int bits, int H, int I) {
-  return H % kDnRows == 0 && I % kGuRows == 0 && I <= kMaxI && (H * bits / 8) % 16 == 0 && (I * bits / 8) % 16 == 0;
+  return H % 16 == 0 && I % 16 == 0 && I <= kMaxI && (H * bits / 8) % 16 == 0 && (I * bits / 8) % 16 == 0;
 }
 
 moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
@@ -569,8 +578,8 @@ moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *ex
   if (st) return st;
   if (T == 0) return MOE_OK;
   switch (bits) {
-    case 8: return launch_bits<8>(ctx, a, xq, xa, xsum, ubig + usmall);
-    case 4: return launch_bits<4>(ctx, a, xq, xa, xsum, ubig + usmall);
-    default: return launch_bits<2>(ctx, a, xq, xa, xsum, ubig + usmall);
+    case 8: return launch_bits<8>(ctx, a, xq, xa, xsum, usmall);
+    case 4: return launch_bits<4>(ctx, a, xq, xa, xsum, usmall);
+    default: return launch_bits<2>(ctx, a, xq, xa, xsum, usmall);
   }
 }

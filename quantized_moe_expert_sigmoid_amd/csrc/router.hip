@@ -234,17 +234,31 @@ __device__ int block_exclusive_scan(int v, int *tmp) {
   return incl - v;
 }
 
+// ids of token t with repeats dropped (a repeated id counts once, at its
+// first slot); returns false when an id is out of range or repeated
+__device__ __forceinline__ bool token_ids(const BucketArgs &a, int64_t t, int ids[16]) {
+  bool ok = true;
+  for (int j = 0; j < a.k; ++j) ids[j] = a.idx[t * a.k + j];
+  for (int j = 0; j < a.k; ++j) {
+    bool dup = false;
+    for (int i = 0; i < j; ++i) dup |= ids[i] == ids[j];
+    if (ids[j] < 0 || ids[j] >= a.E || dup) {
+      ok = false;
+      ids[j] = -1;
+    }
+  }
+  return ok;
+}
+
 __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
   __shared__ int cnt[1024];
   __shared__ int off[1025];
   __shared__ int cursor[1024];
   __shared__ int tmp[kBThreads];
   __shared__ uint32_t bitmap[kBitmapWords];
+  __shared__ int before[kBitmapWords];  // entries of the expert in earlier words of the chunk
   const int tid = threadIdx.x;
-  const int lane = tid & (MOE_WAVE - 1);
-  const int wave = tid >> 6;
   const int E = a.E, k = a.k, T = a.T;
-  const int64_t n = (int64_t)T * k;
 
   for (int e = tid; e < 1024; e += kBThreads) {
     cnt[e] = 0;
@@ -252,14 +266,11 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
   }
   __syncthreads();
   bool bad = false;
-  for (int64_t i = tid; i < n; i += kBThreads) {
-    const int e = a.idx[i];
-    bool dup = false;  // an expert repeated inside one token counts once (first slot)
-    for (int64_t j = i - i % k; j < i; ++j) dup |= (a.idx[j] == e);
-    if (e < 0 || e >= E || dup)
-      bad = true;
-    else
-      atomicAdd(&cnt[e], 1);
+  for (int t = tid; t < T; t += kBThreads) {
+    int ids[16];
+    bad |= !token_ids(a, t, ids);
+    for (int j = 0; j < k; ++j)
+      if (ids[j] >= 0) atomicAdd(&cnt[ids[j]], 1);
   }
   if (bad) atomicOr(a.err, (uint32_t)ERRF_BAD_INDEX);
   __syncthreads();
@@ -310,7 +321,9 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
   }
   if (T == 0) return;
 
-  // stable placement, tokens in chunks that fit the LDS bitmap
+  // stable placement, tokens in chunks of 32 W (one bit per token and expert
+  // in LDS): an entry's rank in its expert's list is the expert's count from
+  // earlier chunks, plus its set bits in earlier words, plus those below it
   int W = kBitmapWords / E;  // words per expert
   if (W > 64) W = 64;
   const int TC = 32 * W;
@@ -318,39 +331,33 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
     const int nt = min(TC, T - c0);
     for (int i = tid; i < E * W; i += kBThreads) bitmap[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < nt * k; i += kBThreads) {
-      const int tl = i / k;
-      const int e = a.idx[(int64_t)(c0 + tl) * k + (i % k)];
-      if (e >= 0 && e < E) atomicOr(&bitmap[e * W + (tl >> 5)], 1u << (tl & 31));
+    for (int tl = tid; tl < nt; tl += kBThreads) {
+      int ids[16];
+      token_ids(a, c0 + tl, ids);
+      for (int j = 0; j < k; ++j)
+        if (ids[j] >= 0) atomicOr(&bitmap[ids[j] * W + (tl >> 5)], 1u << (tl & 31));
     }
     __syncthreads();
-    for (int e = wave; e < E; e += kBThreads / MOE_WAVE) {
-      if (cnt[e] == 0) continue;
-      int base = cursor[e];
-      for (int w0 = 0; w0 < W; w0 += MOE_WAVE) {
-        uint32_t word = (w0 + lane < W) ? bitmap[e * W + w0 + lane] : 0u;
-        const int pc = __popc(word);
-        int incl = pc;
-#pragma unroll
-        for (int o = 1; o < MOE_WAVE; o <<= 1) {
-          const int v = __shfl_up(incl, o, MOE_WAVE);
-          if (lane >= o) incl += v;
-        }
-        const int total = __shfl(incl, MOE_WAVE - 1, MOE_WAVE);
-        int r = base + incl - pc;
-        while (word) {
-          const int b = __ffs(word) - 1;
-          word &= word - 1;
-          const int t = c0 + 32 * (w0 + lane) + b;
-          int jj = k - 1;
-          for (int j = k - 1; j >= 0; --j)
-            if (a.idx[(int64_t)t * k + j] == e) jj = j;
-          a.perm[off[e] + r] = t * k + jj;
-          ++r;
-        }
-        base += total;
+    for (int e = tid; e < E; e += kBThreads) {
+      int run = cursor[e];
+      for (int w = 0; w < W; ++w) {
+        before[e * W + w] = run;
+        run += __popc(bitmap[e * W + w]);
       }
-      if (lane == 0) cursor[e] = base;
+      cursor[e] = run;
+    }
+    __syncthreads();
+    for (int tl = tid; tl < nt; tl += kBThreads) {
+      int ids[16];
+      token_ids(a, c0 + tl, ids);
+      const int w = tl >> 5;
+      const uint32_t below = (1u << (tl & 31)) - 1u;
+      for (int j = 0; j < k; ++j) {
+        const int e = ids[j];
+        if (e < 0) continue;
+        const int r = before[e * W + w] + __popc(bitmap[e * W + w] & below);
+        a.perm[off[e] + r] = (c0 + tl) * k + j;
+      }
     }
     __syncthreads();
   }

@@ -244,23 +244,12 @@ def test_ffn_mfma_tile_boundaries(moe, ctx, orc, syn, bits):
     check_ffn_intermediates(moe, ctx, orc, syn, "mfma", bits, idx.shape[0], 128, 64, 8, 1, idx, seed=45 + bits)
 
 
-def test_ffn_mfma_unsupported_shape_refused(moe, ctx, syn):
-    """Forcing the matrix-core kernels on a shape they do not take (H not a
-    multiple of 128) is refused, not silently rerouted."""
-    H, I, E, k, T = 192, 64, 4, 2, 3
-    blocks = moe.ExpertBlocks(E, 4, H, I)
-    xq = torch.zeros((T, H), dtype=torch.int8, device="cuda")
-    sx = torch.ones((T,), dtype=torch.float32, device="cuda")
-    idx = torch.zeros((T, k), dtype=torch.int32, device="cuda")
-    idx[:, 1] = 1
-    y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
-    ctx.set_ffn_kernels("mfma")
-    try:
+def test_ffn_kernel_selector_rejects_unknown_values(moe, ctx):
+    for bad in (-1, 3, 7):
         with pytest.raises(moe.MoeError) as ex:
-            moe.moe_expert_ffn_q4(ctx, blocks.table, None, None, xq, sx, idx, H, I, E, y)
-        assert ex.value.status == moe.MOE_EUNSUPPORTED
-    finally:
-        ctx.set_ffn_kernels("auto")
+            ctx.set_ffn_kernels(bad)
+        assert ex.value.status == moe.MOE_EINVAL
+    ctx.set_ffn_kernels("auto")
 
 
 def test_ffn_without_shared_leaves_slot(moe, ctx, orc, syn):
