@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s + effective expert-weight HBM GB/s (int4 decode, 1 GPU)"
 HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak (5.0 POP/s)
 COPY_PROBE_MB = 512  # larger than the 256 MB last-level cache: the copy streams HBM
 # sources of the single-token kernels: a traffic figure measured on other
 # sources is stale and is not reported
@@ -447,8 +448,11 @@ def main():
         k_ = tr["kernels"]["gateup"]
         traffic_gu = k_["fetch_bytes"] + k_["write_bytes"]
     kernel_names = {"router": "router_gemv_t1_kernel" if T == 1 else "router kernels",
-                    "gateup": "gateup_t1_kernel" if T == 1 else "ffn_gateup_kernel",
-                    "down": "down_combine_t1_kernel" if T == 1 else "ffn_down_kernel"}
+                    "gateup": "gateup_t1_kernel" if T == 1 else "gu_mfma_kernel (64-token and one-block tiles)",
+                    "down": "down_combine_t1_kernel" if T == 1 else "dn_mfma_kernel (64-token and one-block tiles)"}
+    # int8 products of the gate/up launches: every (token, slot) pair and the
+    # shared expert's, 2 I rows of H each (multiply and add counted as 2 ops)
+    gu_ops = 2.0 * T * (w.k + (1 if w.has_shared else 0)) * 2 * I * H
 
     result = {
         "metric": METRIC,
@@ -470,7 +474,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel_names["gateup"], "achieved": round(gu_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_gu, "algorithmic_bytes_per_launch": round(n_avg * gu_bytes),
-                     "avg_launch_us": round(gu_ms * 1e3, 2)},
+                     "avg_launch_us": round(gu_ms * 1e3, 2),
+                     "int8_ops_per_launch": gu_ops, "int8_TOPS": round(gu_ops / (gu_ms / 1e3) / 1e12, 1),
+                     "int8_peak_TOPS": INT8_PEAK_TOPS,
+                     "mfma_frac": round(gu_ops / (gu_ms / 1e3) / 1e12 / INT8_PEAK_TOPS, 4) if T > 1 else None},
         "kernels": {k_: {"avg_us": round(v[0] * 1e3, 2), "launches_per_call": v[1]} for k_, v in per_call.items()},
         "expert_ffn": {"kernels": kernel_names["gateup"] + " + " + kernel_names["down"],
                        "algorithmic_bytes": round(avg_bytes), "avg_us": round(ffn_ms * 1e3, 2),

@@ -221,9 +221,9 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, 
  * the shared expert at `bits` (8, 4 or 2; every expert at that width), and
  * the combine. Results equal moe_quantize_act_i8 -> moe_router_topk ->
  * moe_expert_ffn_q* -> moe_combine on the same inputs (the same arithmetic
- * in the same order; a single token runs three fused kernels: router with
- * top-k and activation quantisation, gate/up with requantisation, and down
- * fused with the combine).
+ * in the same order; a single token runs four fused kernels: router logits
+ * with the activation quantisation, top-k with gate/up, requantisation of the
+ * intermediate, and down fused with the combine).
  *
  * x fp32 [T][H] hidden states; logits fp32 [T][E] (only with
  * cfg->logits_in, else NULL); w_router fp32 [E][H] (ignored with logits);
