@@ -13,7 +13,9 @@
 //  1. act_field_kernel (int4 and int2 only): every token's int8 codes
 //     reordered into the packed weights' field order -- per 32 elements the 16
 //     even ones then the 16 odd ones (int4), per 64 elements the four 2-bit
-//     fields of 16 elements each (int2) -- and the sum of the codes.
+//     fields of 16 elements each (int2), each such 16-byte step stored next
+//     to the same step of the three neighbouring pieces (field_pos) -- and
+//     the sum of the codes.
 //  2. gu_mfma_kernel: one workgroup per (token tile, 64 rows of gate and of
 //     up); wave w owns rows 16w..16w+15 of both. A row is read as 16-byte
 //     pieces; per step lane l takes piece 4c + l/16 of row l%16 and splits it
@@ -48,7 +50,8 @@ struct MArgs {
   const moe_expert_w *experts;
   moe_expert_w shared;
   int has_shared;
-  const int8_t *xa;      // [T][H] token codes in field order (xq itself for int8)
+  const int8_t *xa;      // [T][xstride] token codes in field order (xq itself for int8)
+  int xstride, astride;  // row strides of xa and aq: whole groups of four pieces
   const int32_t *xsum;   // [T] code sums (int4, int2)
   const float *sx;       // [T]
   const int32_t *topk_idx;
@@ -59,7 +62,7 @@ struct MArgs {
   const int32_t *n_units;  // [2] tiles of each kind
   int ubig_max;
   float *A;      // [P][I] SwiGLU intermediate, P = T (k + 1)
-  int8_t *aq;    // [P][I] its codes, field order
+  int8_t *aq;    // [P][astride] its codes, field order
   int32_t *aqs;  // [P] code sums
   float *sa;     // [P]
   float *y;      // [T][k+1][H]
@@ -128,6 +131,15 @@ __device__ __forceinline__ v4i mfma(v4i x, v4i w, v4i acc) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w, acc, 0, 0, 0);
 }
 
+// Byte offset, in a row of field-ordered codes, of step s (16 bytes) of the
+// lane-group piece b (EPC elements): pieces go in groups of four (one per
+// lane group of a load), and within a group step s of the four pieces is 64
+// contiguous bytes, so one load instruction reads a token's 64 bytes.
+template <int BITS>
+__device__ __forceinline__ int field_pos(int b, int s) {
+  return (b >> 2) * 4 * QFmt<BITS>::kEpc + s * 64 + (b & 3) * 16;
+}
+
 struct TileTokens {
   int tok[64], pair[64], osum[64];
   float scale[64];
@@ -137,12 +149,13 @@ struct TileTokens {
 // token codes in field order
 // ---------------------------------------------------------------------------
 template <int BITS>
-__global__ __launch_bounds__(kThreads) void act_field_kernel(const int8_t *xq, int H, int8_t *xa, int32_t *xsum) {
+__global__ __launch_bounds__(kThreads) void act_field_kernel(const int8_t *xq, int H, int8_t *xa, int xstride,
+                                                              int32_t *xsum) {
   constexpr int EPC = QFmt<BITS>::kEpc, ND = EPC / 4;
   __shared__ int red[kThreads / MOE_WAVE];
   const int t = blockIdx.x;
   const uint32_t *src = reinterpret_cast<const uint32_t *>(xq + (int64_t)t * H);
-  uint32_t *dst = reinterpret_cast<uint32_t *>(xa + (int64_t)t * H);
+  uint8_t *dst = reinterpret_cast<uint8_t *>(xa + (int64_t)t * xstride);
   int sum = 0;
   for (int blk = threadIdx.x; blk < H / EPC; blk += kThreads) {
     uint32_t d[ND], o[ND];
@@ -170,7 +183,8 @@ __global__ __launch_bounds__(kThreads) void act_field_kernel(const int8_t *xq, i
     }
 #pragma unroll
     for (int q = 0; q < ND / 4; ++q)
-      reinterpret_cast<uint4 *>(dst + blk * ND)[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+      *reinterpret_cast<uint4 *>(dst + field_pos<BITS>(blk, q)) =
+          make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
   }
   sum = wave_sum_i32(sum);
   if ((threadIdx.x & (MOE_WAVE - 1)) == 0) red[threadIdx.x >> 6] = sum;
@@ -204,7 +218,7 @@ __device__ __forceinline__ void tile_mma(const uint8_t *const (&wrow)[NM][NB], c
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int s = 0; s < NS; ++s) xv[b][mb][s] = ldg16(px[mb] + qc * EPC, s);
+      for (int s = 0; s < NS; ++s) xv[b][mb][s] = ldg16(px[mb] + field_pos<BITS>(qc, s), 0);
     asm volatile("" ::: "memory");  // issue here, D steps ahead of the use
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -236,6 +250,104 @@ __device__ __forceinline__ void tile_mma(const uint8_t *const (&wrow)[NM][NB], c
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same product for a 64-token tile with the tokens' codes staged in LDS,
+// once per workgroup instead of once per wave: slices of 512 bytes per token
+// (double-buffered, 64 KB), loaded one slice ahead into registers and written
+// to LDS after the current slice is consumed, one barrier per slice. In LDS
+// the 16-byte unit u of token t sits at unit u ^ (t & 7) of the token's row,
+// so the 16 tokens a read instruction spans hit distinct banks. The weight
+// rows stream through registers D steps ahead as in tile_mma.
+// ---------------------------------------------------------------------------
+constexpr int kSlice = 512;  // bytes of codes per token and slice
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ void lds_st16(lds_u8 *p, uint4 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) moe_u32x4 *>(p) = moe_u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ uint4 lds_ld16(const lds_u8 *p) {
+  const moe_u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) moe_u32x4 *>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int BITS, int NM, int NB, int D>
+__device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB], const int8_t *abase, int astride,
+                                             const int *ids, int rowbytes, lds_u8 *lds, v4i (&acc)[4][NM][NB]) {
+  constexpr int EPC = QFmt<BITS>::kEpc, NS = EPC / 16, MB = 4;
+  constexpr int SC = kSlice / (4 * EPC);  // steps per slice
+  static_assert(SC % D == 0, "the weight buffers rotate within a slice");
+  const int tid = threadIdx.x, grp = (tid & (MOE_WAVE - 1)) >> 4, r16 = tid & 15;
+  const int nq = rowbytes / 16;
+  const int nch = (nq + 3) / 4;
+  const int nsl = (nch + SC - 1) / SC;
+  // staging: this thread moves unit su of tokens (tid >> 5) + 8 i
+  const int su = tid & 31;
+  const int8_t *srow[8];
+  int sdst[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = (tid >> 5) + 8 * i;
+    srow[i] = abase + (int64_t)ids[t] * astride;
+    sdst[i] = t * kSlice + ((su ^ (t & 7)) << 4);
+  }
+  uint4 st[8];
+  auto aload = [&](int sl) {
+    const int o = min(sl * kSlice + su * 16, astride - 16);  // past the row: a re-read, never used
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st[i] = ldg16(srow[i] + o, 0);
+  };
+  auto astore = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lds_st16(lds + b * (64 * kSlice) + sdst[i], st[i]);
+  };
+  uint4 wv[D][NM][NB];
+  auto bload = [&](int c, int b) {
+    const int qc = min(c * 4 + grp, nq - 1);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) wv[b][m][nb] = ldg16(wrow[m][nb] + qc * 16, 0);
+  };
+#pragma unroll
+  for (int b = 0; b < D; ++b) bload(b, b);
+  aload(0);
+  astore(0);
+  aload(1);
+  __syncthreads();
+  for (int sl = 0; sl < nsl; ++sl) {
+    const lds_u8 *cur = lds + (sl & 1) * (64 * kSlice);
+#pragma unroll
+    for (int cc = 0; cc < SC; ++cc) {
+      const int c = sl * SC + cc, b = cc % D;
+      const bool kv = c * 4 + grp < nq;  // pieces past the row end multiply zeros
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        v4i x[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int t = mb * 16 + r16, u = cc * NS * 4 + s * 4 + grp;
+          x[mb] = as_v4i(lds_ld16(cur + t * kSlice + ((u ^ (t & 7)) << 4)), kv);
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            v4i w;
+            if (s == 0) w = wfield<BITS, 0>(wv[b][m][nb]);
+            else if (s == 1) w = wfield<BITS, 1>(wv[b][m][nb]);
+            else if (s == 2) w = wfield<BITS, 2>(wv[b][m][nb]);
+            else w = wfield<BITS, 3>(wv[b][m][nb]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb][m][nb] = mfma(x[mb], w, acc[mb][m][nb]);
+          }
+      }
+      bload(c + D, b);
+    }
+    astore((sl + 1) & 1);  // the buffer read in the previous slice; every wave has passed the barrier after it
+    aload(sl + 2);
+    __syncthreads();
+  }
+}
+
 // the tile's tokens (entries past the expert's last token repeat it)
 template <int MB>
 __device__ __forceinline__ int stage_tokens(const MArgs &a, const Ex &ex, int m0, bool down, int off,
@@ -257,7 +369,7 @@ __device__ __forceinline__ int stage_tokens(const MArgs &a, const Ex &ex, int m0
 // gate + up: a workgroup takes 64 NB rows of each, a wave 16 NB
 // ---------------------------------------------------------------------------
 template <int BITS, int MB, int NB, int D>
-__device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, int d, int m0) {
+__device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8 *lds, int d, int m0, int ntile) {
   constexpr int OFF = QFmt<BITS>::kOff;
   Ex ex;
   if (!resolve_ex(a, d, ex)) return;
@@ -270,23 +382,29 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, int d,
   float sg[NB], su[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    row[nb] = blockIdx.y * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
+    row[nb] = ntile * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
     const int rc = min(row[nb], a.I - 1);  // rows past I: re-read, not stored
     wrow[0][nb] = ex.w.gate + (int64_t)rc * rowbytes;
     wrow[1][nb] = ex.w.up + (int64_t)rc * rowbytes;
-    sg[nb] = ex.w.s_gate[rc];
-    su[nb] = ex.w.s_up[rc];
+    // global-space loads: a pending flat load would make every wait in the
+    // K loop below a wait for all loads
+    sg[nb] = gptr(ex.w.s_gate)[rc];
+    su[nb] = gptr(ex.w.s_up)[rc];
   }
   __syncthreads();
-  const int8_t *px[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) px[mb] = a.xa + (int64_t)tt_s.tok[mb * 16 + r16] * a.H;
   v4i acc[MB][2][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = acc[mb][1][nb] = v4i{0, 0, 0, 0};
-  tile_mma<BITS, MB, 2, NB, D>(wrow, px, rowbytes, acc);
+  if constexpr (MB == 4) {
+    tile_mma_lds<BITS, 2, NB, D>(wrow, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
+  } else {
+    const int8_t *px[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) px[mb] = a.xa + (int64_t)tt_s.tok[mb * 16 + r16] * a.xstride;
+    tile_mma<BITS, MB, 2, NB, D>(wrow, px, rowbytes, acc);
+  }
   // lane holds tokens 4*grp + r of each block, row row[nb]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -328,13 +446,31 @@ struct DnShape {
   static constexpr int NB = 2, D = MB == 4 ? 2 : 4;
 };
 
+// Workgroup -> (tile, row tile). Workgroups go to the 8 XCDs in turn (id mod
+// 8), each XCD with its own L2; the mapping gives every XCD a contiguous range
+// of the (tile, row tile) order, row tiles fastest, so the workgroups that
+// read one tile's activations run together on one XCD and find them in its L2
+// (and those of an expert's next tile share its weight rows there).
+__device__ __forceinline__ bool xcd_work(int n_units, int ntiles, int &unit, int &ntile) {
+  const int total = n_units * ntiles;
+  const int b = blockIdx.x;
+  if (b >= total) return false;
+  const int x = b & 7, slot = b >> 3, q = total >> 3, r = total & 7;
+  const int L = x * q + min(x, r) + slot;  // a bijection of [0, total)
+  unit = L / ntiles;
+  ntile = L - unit * ntiles;
+  return true;
+}
+
 template <int BITS, int MB>
-__global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a) {
+__global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
-  const int u = blockIdx.x;
-  if (u >= a.n_units[MB == 4 ? 0 : 1]) return;
+  __shared__ __align__(16) uint8_t abuf_s[MB == 4 ? 2 * 64 * kSlice : 16];
+  lds_u8 *abuf = (lds_u8 *)abuf_s;
+  int u, nt;
+  if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
   const int2 un = a.units[MB == 4 ? u : a.ubig_max + u];
-  gu_tile<BITS, MB, GuShape<MB>::NB, GuShape<MB>::D>(a, tt_s, un.x, un.y);
+  gu_tile<BITS, MB, GuShape<MB>::NB, GuShape<MB>::D>(a, tt_s, abuf, un.x, un.y, nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -379,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void requant_mfma_kernel(MArgs a) {
   m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   const float sc = (m == 0.0f) ? 0.0f : m / 127.0f;
   int csum = 0;
-  uint8_t *dst = reinterpret_cast<uint8_t *>(a.aq + p * a.I);
+  uint8_t *dst = reinterpret_cast<uint8_t *>(a.aq + p * a.astride);
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
     const int g = tid + it * kThreads;
@@ -407,15 +543,13 @@ __global__ __launch_bounds__(kThreads) void requant_mfma_kernel(MArgs a) {
     } else if constexpr (BITS == 4) {
       uint32_t ev, od;
       act_order_q4(nat[0], nat[1], ev, od);
-      const int base = (g >> 2) * 32 + (g & 3) * 4;
-      *reinterpret_cast<uint32_t *>(dst + base) = ev;
-      *reinterpret_cast<uint32_t *>(dst + base + 16) = od;
+      *reinterpret_cast<uint32_t *>(dst + field_pos<4>(g >> 2, 0) + (g & 3) * 4) = ev;
+      *reinterpret_cast<uint32_t *>(dst + field_pos<4>(g >> 2, 1) + (g & 3) * 4) = od;
     } else {
       uint32_t f[4];
       act_order_q2(nat, f);
-      const int base = (g >> 2) * 64 + (g & 3) * 4;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) *reinterpret_cast<uint32_t *>(dst + base + 16 * s) = f[s];
+      for (int s = 0; s < 4; ++s) *reinterpret_cast<uint32_t *>(dst + field_pos<2>(g >> 2, s) + (g & 3) * 4) = f[s];
     }
   }
   csum = wave_sum_i32(csum);
@@ -432,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void requant_mfma_kernel(MArgs a) {
 // down: a workgroup takes 64 NB rows, a wave 16 NB
 // ---------------------------------------------------------------------------
 template <int BITS, int MB, int NB, int D>
-__device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, int d, int m0) {
+__device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8 *lds, int d, int m0, int ntile) {
   constexpr int OFF = QFmt<BITS>::kOff;
   Ex ex;
   if (!resolve_ex(a, d, ex)) return;
@@ -445,21 +579,25 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, int d,
   float sd[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    row[nb] = blockIdx.y * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
+    row[nb] = ntile * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
     const int rc = min(row[nb], a.H - 1);
     wrow[0][nb] = ex.w.down + (int64_t)rc * rowbytes;
-    sd[nb] = ex.w.s_down[rc];
+    sd[nb] = gptr(ex.w.s_down)[rc];
   }
   __syncthreads();
-  const int8_t *px[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) px[mb] = a.aq + (int64_t)tt_s.pair[mb * 16 + r16] * a.I;
   v4i acc[MB][1][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = v4i{0, 0, 0, 0};
-  tile_mma<BITS, MB, 1, NB, D>(wrow, px, rowbytes, acc);
+  if constexpr (MB == 4) {
+    tile_mma_lds<BITS, 1, NB, D>(wrow, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
+  } else {
+    const int8_t *px[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) px[mb] = a.aq + (int64_t)tt_s.pair[mb * 16 + r16] * a.astride;
+    tile_mma<BITS, MB, 1, NB, D>(wrow, px, rowbytes, acc);
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -480,34 +618,37 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, int d,
 }
 
 template <int BITS, int MB>
-__global__ __launch_bounds__(kThreads) void dn_mfma_kernel(MArgs a) {
+__global__ __launch_bounds__(kThreads) void dn_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
-  const int u = blockIdx.x;
-  if (u >= a.n_units[MB == 4 ? 0 : 1]) return;
+  __shared__ __align__(16) uint8_t abuf_s[MB == 4 ? 2 * 64 * kSlice : 16];
+  lds_u8 *abuf = (lds_u8 *)abuf_s;
+  int u, nt;
+  if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
   const int2 un = a.units[MB == 4 ? u : a.ubig_max + u];
-  dn_tile<BITS, MB, DnShape<MB>::NB, DnShape<MB>::D>(a, tt_s, un.x, un.y);
+  dn_tile<BITS, MB, DnShape<MB>::NB, DnShape<MB>::D>(a, tt_s, abuf, un.x, un.y, nt);
 }
 
 template <int BITS>
 moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *xa, int32_t *xsum, int usmall) {
   if constexpr (BITS != 8) {
-    moe_launch(ctx, MOE_STAGE_BUCKET, act_field_kernel<BITS>, dim3(a.T), dim3(kThreads), xq, a.H, xa, xsum);
+    moe_launch(ctx, MOE_STAGE_BUCKET, act_field_kernel<BITS>, dim3(a.T), dim3(kThreads), xq, a.H, xa, a.xstride,
+               xsum);
     MOE_CHECK_LAUNCH("act_field_kernel");
   }
   auto tiles = [](int n, int rows) { return (n + rows - 1) / rows; };
-  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max, tiles(a.I, 64 * GuShape<4>::NB)),
-             dim3(kThreads), a);
+  const int g4 = tiles(a.I, 64 * GuShape<4>::NB), g1 = tiles(a.I, 64 * GuShape<1>::NB);
+  const int d4 = tiles(a.H, 64 * DnShape<4>::NB), d1 = tiles(a.H, 64 * DnShape<1>::NB);
+  // 1-D grids sized for the most tiles the bucket can list; the surplus
+  // workgroups return at once
+  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max * g4), dim3(kThreads), a, g4);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
-  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 1>, dim3(usmall, tiles(a.I, 64 * GuShape<1>::NB)),
-             dim3(kThreads), a);
+  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 1>, dim3(usmall * g1), dim3(kThreads), a, g1);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
   moe_launch(ctx, MOE_STAGE_REQUANT, requant_mfma_kernel<BITS>, dim3(a.T * (a.k + 1)), dim3(kThreads), a);
   MOE_CHECK_LAUNCH("requant_mfma_kernel");
-  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max, tiles(a.H, 64 * DnShape<4>::NB)),
-             dim3(kThreads), a);
+  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max * d4), dim3(kThreads), a, d4);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
-  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 1>, dim3(usmall, tiles(a.H, 64 * DnShape<1>::NB)),
-             dim3(kThreads), a);
+  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 1>, dim3(usmall * d1), dim3(kThreads), a, d1);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
   return MOE_OK;
 }
@@ -527,6 +668,10 @@ moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *ex
   // sum over experts of ceil(n_e / 64) <= T k / 64 + (active experts), plus the shared expert's tiles
   const int ubig = (int)(((int64_t)T * k) / kUnitM + dact + 1 + (has_shared ? (T + kUnitM - 1) / kUnitM : 0));
   const int usmall = dact + 1;
+  // rows of field-ordered codes hold whole groups of four lane pieces
+  const int grp_bytes = 4 * (128 / bits);
+  const int xstride = bits == 8 ? H : (int)moe_round_up(H, grp_bytes);
+  const int astride = (int)moe_round_up(I, grp_bytes);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -535,8 +680,8 @@ moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *ex
   };
   const size_t o_counts = take(4 * (size_t)E), o_offsets = take(4 * (size_t)(E + 1)), o_perm = take(4 * (size_t)T * k),
                o_active = take(4 * (size_t)E), o_nact = take(4), o_units = take(8 * (size_t)(ubig + usmall)),
-               o_nunits = take(8), o_xa = take(bits == 8 ? 0 : (size_t)T * H), o_xsum = take(4 * (size_t)T),
-               o_A = take(4 * (size_t)P * I), o_aq = take((size_t)P * I), o_aqs = take(4 * (size_t)P),
+               o_nunits = take(8), o_xa = take(bits == 8 ? 0 : (size_t)T * xstride), o_xsum = take(4 * (size_t)T),
+               o_A = take(4 * (size_t)P * I), o_aq = take((size_t)P * astride), o_aqs = take(4 * (size_t)P),
                o_sa = take(4 * (size_t)P);
   void *scr = nullptr;
   moe_status st = moe_scratch(ctx, off, &scr);
@@ -549,6 +694,8 @@ moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *ex
   int8_t *xa = bits == 8 ? const_cast<int8_t *>(xq) : reinterpret_cast<int8_t *>(base + o_xa);
   int32_t *xsum = reinterpret_cast<int32_t *>(base + o_xsum);
   a.xa = xa;
+  a.xstride = xstride;
+  a.astride = astride;
   a.xsum = xsum;
   a.sx = sx;
   a.topk_idx = topk_idx;
