@@ -193,71 +193,16 @@ __global__ __launch_bounds__(kThreads) void act_field_kernel(const int8_t *xq, i
 }
 
 // ---------------------------------------------------------------------------
-// acc[m][mat][nb] += the tokens of block m times rows of block nb of matrix
-// mat, over whole rows of rowbytes packed bytes. wrow: this lane's row (l%16
-// of the block) of each matrix and block; px: this lane's token row (l%16 of
-// the block) of field-ordered codes. D steps of loads in flight.
-// ---------------------------------------------------------------------------
-template <int BITS, int MB, int NM, int NB, int D>
-__device__ __forceinline__ void tile_mma(const uint8_t *const (&wrow)[NM][NB], const int8_t *const (&px)[MB],
-                                         int rowbytes, v4i (&acc)[MB][NM][NB]) {
-  constexpr int EPC = QFmt<BITS>::kEpc, NS = EPC / 16;
-  const int grp = (threadIdx.x & (MOE_WAVE - 1)) >> 4;
-  const int nq = rowbytes / 16;  // 16-byte pieces per row
-  const int nch = (nq + 3) / 4;  // steps of 4 pieces (one per lane group)
-  uint4 wv[D][NM][NB], xv[D][MB][NS];
-  bool kv[D];
-  auto load = [&](int c, int b) {
-    const int q = c * 4 + grp;
-    kv[b] = q < nq;  // past the row end: a re-read piece, multiplied by zeros
-    const int qc = min(q, nq - 1);
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) wv[b][m][nb] = ldg16(wrow[m][nb] + qc * 16, 0);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) xv[b][mb][s] = ldg16(px[mb] + field_pos<BITS>(qc, s), 0);
-    asm volatile("" ::: "memory");  // issue here, D steps ahead of the use
-    __builtin_amdgcn_sched_barrier(0);
-  };
-#pragma unroll
-  for (int b = 0; b < D; ++b) load(b, b);
-  for (int c = 0; c < nch; c += D) {
-#pragma unroll
-    for (int b = 0; b < D; ++b) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        v4i x[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) x[mb] = as_v4i(xv[b][mb][s], kv[b]);
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            v4i w;
-            if (s == 0) w = wfield<BITS, 0>(wv[b][m][nb]);
-            else if (s == 1) w = wfield<BITS, 1>(wv[b][m][nb]);
-            else if (s == 2) w = wfield<BITS, 2>(wv[b][m][nb]);
-            else w = wfield<BITS, 3>(wv[b][m][nb]);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb][m][nb] = mfma(x[mb], w, acc[mb][m][nb]);
-          }
-      }
-      load(c + b + D, b);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// The same product for a 64-token tile with the tokens' codes staged in LDS,
-// once per workgroup instead of once per wave: slices of 512 bytes per token
-// (double-buffered, 64 KB), loaded one slice ahead into registers and written
-// to LDS after the current slice is consumed, one barrier per slice. In LDS
-// the 16-byte unit u of token t sits at unit u ^ (t & 7) of the token's row,
-// so the 16 tokens a read instruction spans hit distinct banks. The weight
-// rows stream through registers D steps ahead as in tile_mma.
+// acc[m][mat][nb] += the tokens of block m (16 each) times rows of block nb
+// (16 each) of matrix mat, over whole rows of rowbytes packed bytes. wrow:
+// this lane's row (l%16 of the block) of each matrix and block. Per step lane
+// l takes piece 4c + l/16 of its row. The tokens' field-ordered codes (rows
+// abase + ids[t] * astride) are staged in LDS once per workgroup: slices of
+// 512 bytes per token, double-buffered, loaded one slice ahead into registers
+// and written to LDS after the current slice is consumed, one barrier per
+// slice. In LDS the 16-byte unit u of token t sits at unit u ^ (t & 7) of the
+// token's row, so the 16 tokens a read instruction spans hit distinct banks.
+// The weight pieces stream through registers D steps ahead.
 // ---------------------------------------------------------------------------
 constexpr int kSlice = 512;  // bytes of codes per token and slice
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -269,11 +214,14 @@ __device__ __forceinline__ uint4 lds_ld16(const lds_u8 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int BITS, int NM, int NB, int D>
+template <int BITS, int MB, int NM, int NB, int D0>
 __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB], const int8_t *abase, int astride,
-                                             const int *ids, int rowbytes, lds_u8 *lds, v4i (&acc)[4][NM][NB]) {
-  constexpr int EPC = QFmt<BITS>::kEpc, NS = EPC / 16, MB = 4;
+                                             const int *ids, int rowbytes, lds_u8 *lds, v4i (&acc)[MB][NM][NB]) {
+  constexpr int EPC = QFmt<BITS>::kEpc, NS = EPC / 16;
   constexpr int SC = kSlice / (4 * EPC);  // steps per slice
+  constexpr int D = D0 < SC ? D0 : SC;    // weight steps in flight (a divisor of SC)
+  constexpr int NI = MB * 2;              // staged units per thread and slice
+  constexpr int BUF = MB * 16 * kSlice;   // bytes per slice buffer
   static_assert(SC % D == 0, "the weight buffers rotate within a slice");
   const int tid = threadIdx.x, grp = (tid & (MOE_WAVE - 1)) >> 4, r16 = tid & 15;
   const int nq = rowbytes / 16;
@@ -281,23 +229,23 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB
   const int nsl = (nch + SC - 1) / SC;
   // staging: this thread moves unit su of tokens (tid >> 5) + 8 i
   const int su = tid & 31;
-  const int8_t *srow[8];
-  int sdst[8];
+  const int8_t *srow[NI];
+  int sdst[NI];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int t = (tid >> 5) + 8 * i;
     srow[i] = abase + (int64_t)ids[t] * astride;
     sdst[i] = t * kSlice + ((su ^ (t & 7)) << 4);
   }
-  uint4 st[8];
+  uint4 st[NI];
   auto aload = [&](int sl) {
     const int o = min(sl * kSlice + su * 16, astride - 16);  // past the row: a re-read, never used
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st[i] = ldg16(srow[i] + o, 0);
+    for (int i = 0; i < NI; ++i) st[i] = ldg16(srow[i] + o, 0);
   };
   auto astore = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lds_st16(lds + b * (64 * kSlice) + sdst[i], st[i]);
+    for (int i = 0; i < NI; ++i) lds_st16(lds + b * BUF + sdst[i], st[i]);
   };
   uint4 wv[D][NM][NB];
   auto bload = [&](int c, int b) {
@@ -306,6 +254,7 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) wv[b][m][nb] = ldg16(wrow[m][nb] + qc * 16, 0);
+    __builtin_amdgcn_sched_barrier(0);  // issue here, D steps ahead of the use
   };
 #pragma unroll
   for (int b = 0; b < D; ++b) bload(b, b);
@@ -314,7 +263,7 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB
   aload(1);
   __syncthreads();
   for (int sl = 0; sl < nsl; ++sl) {
-    const lds_u8 *cur = lds + (sl & 1) * (64 * kSlice);
+    const lds_u8 *cur = lds + (sl & 1) * BUF;
 #pragma unroll
     for (int cc = 0; cc < SC; ++cc) {
       const int c = sl * SC + cc, b = cc % D;
@@ -397,14 +346,7 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = acc[mb][1][nb] = v4i{0, 0, 0, 0};
-  if constexpr (MB == 4) {
-    tile_mma_lds<BITS, 2, NB, D>(wrow, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
-  } else {
-    const int8_t *px[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) px[mb] = a.xa + (int64_t)tt_s.tok[mb * 16 + r16] * a.xstride;
-    tile_mma<BITS, MB, 2, NB, D>(wrow, px, rowbytes, acc);
-  }
+  tile_mma_lds<BITS, MB, 2, NB, D>(wrow, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
   // lane holds tokens 4*grp + r of each block, row row[nb]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -465,7 +407,7 @@ __device__ __forceinline__ bool xcd_work(int n_units, int ntiles, int &unit, int
 template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
-  __shared__ __align__(16) uint8_t abuf_s[MB == 4 ? 2 * 64 * kSlice : 16];
+  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * kSlice];
   lds_u8 *abuf = (lds_u8 *)abuf_s;
   int u, nt;
   if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
@@ -590,14 +532,7 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = v4i{0, 0, 0, 0};
-  if constexpr (MB == 4) {
-    tile_mma_lds<BITS, 1, NB, D>(wrow, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
-  } else {
-    const int8_t *px[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) px[mb] = a.aq + (int64_t)tt_s.pair[mb * 16 + r16] * a.astride;
-    tile_mma<BITS, MB, 1, NB, D>(wrow, px, rowbytes, acc);
-  }
+  tile_mma_lds<BITS, MB, 1, NB, D>(wrow, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -620,7 +555,7 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
 template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads) void dn_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
-  __shared__ __align__(16) uint8_t abuf_s[MB == 4 ? 2 * 64 * kSlice : 16];
+  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * kSlice];
   lds_u8 *abuf = (lds_u8 *)abuf_s;
   int u, nt;
   if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
