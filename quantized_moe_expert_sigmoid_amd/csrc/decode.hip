@@ -69,9 +69,6 @@ struct SlotEntry {
 static_assert(sizeof(SlotEntry) == 64, "slot entries are 64 bytes");
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
 template <typename P>
 __device__ __forceinline__ P readlane_p(P p, int l) {
   const uint64_t v = (uint64_t)p;
@@ -196,97 +193,6 @@ struct GateUpT1Args {
   moe_debug_bufs dbg;
   int dbg_on;
 };
-
-// Order-preserving integer image of a float: a > b as floats (no NaN, no -0)
-// if and only if key_bits(a) > key_bits(b) as signed integers.
-__device__ __forceinline__ int key_bits(float f) {
-  const int i = __float_as_int(f);
-  return i ^ ((i >> 31) & 0x7fffffff);
-}
-// wave-uniform maximum of an int (DPP; lanes of masked rows keep their value)
-__device__ __forceinline__ int wave_max_i32(int v) {
-  v = max(v, dpp_keep<0xB1>(v));
-  v = max(v, dpp_keep<0x4E>(v));
-  v = max(v, dpp_keep<0x141>(v));
-  v = max(v, dpp_keep<0x140>(v));
-  v = max(v, dpp_keep<0x142, 0xa>(v));
-  v = max(v, dpp_keep<0x143, 0xc>(v));
-  return __builtin_amdgcn_readlane(v, 63);
-}
-__device__ __forceinline__ int64_t cat_key(int kb, int id) {
-  return (int64_t)(((uint64_t)(uint32_t)kb << 32) | (uint32_t)~id);
-}
-__device__ __forceinline__ void cex(int64_t &a, int64_t &b) {  // (a, b) <- (max, min)
-  const bool sw = b > a;
-  const int64_t t = a;
-  a = sw ? b : a;
-  b = sw ? t : b;
-}
-
-// Top-k over the keys in LDS (descending key, then ascending id), run by one
-// wave; lane r < k returns the id of rank r. Lane l holds keys l*4 .. l*4+3
-// (E <= 256) as 64-bit (key, ~id) entries sorted in descending order, so
-// every lane's head is its best and, since lanes hold ascending id ranges,
-// the lowest lane whose head equals the wave maximum holds the lowest id among
-// equal keys. Each round takes that head and shifts the winner's list.
-__device__ __forceinline__ int wave_topk4(const float *key_s, int E, int k, int lane) {
-  constexpr int64_t kNone = INT64_MIN;
-  int64_t h[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int e = lane * 4 + m;
-    h[m] = e < E ? cat_key(key_bits(key_s[e]), e) : kNone;
-  }
-  cex(h[0], h[1]);
-  cex(h[2], h[3]);
-  cex(h[0], h[2]);
-  cex(h[1], h[3]);
-  cex(h[1], h[2]);
-  int my_id = 0;
-  for (int r = 0; r < k; ++r) {
-    const int hk = (int)(h[0] >> 32);
-    const int wm = wave_max_i32(hk);
-    const uint64_t mask = __ballot(hk == wm);
-    const int wl = (int)__builtin_ctzll(mask);
-    const int id = ~__builtin_amdgcn_readlane((int)(uint32_t)h[0], wl);
-    if (lane == r) my_id = id;
-    if (lane == wl) {
-      h[0] = h[1];
-      h[1] = h[2];
-      h[2] = h[3];
-      h[3] = kNone;
-    }
-  }
-  return my_id;
-}
-// The same for E <= 1024: 16 keys per lane, each round recomputes the lane's
-// best among the keys not yet taken.
-__device__ __forceinline__ int wave_topk16(const float *key_s, int E, int k, int lane) {
-  constexpr int64_t kNone = INT64_MIN;
-  int64_t h[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int e = lane * 16 + m;
-    h[m] = e < E ? cat_key(key_bits(key_s[e]), e) : kNone;
-  }
-  int my_id = 0;
-  for (int r = 0; r < k; ++r) {
-    int64_t best = h[0];
-#pragma unroll
-    for (int m = 1; m < 16; ++m) best = h[m] > best ? h[m] : best;
-    const int hk = (int)(best >> 32);
-    const int wm = wave_max_i32(hk);
-    const uint64_t mask = __ballot(hk == wm);
-    const int wl = (int)__builtin_ctzll(mask);
-    const int id = ~__builtin_amdgcn_readlane((int)(uint32_t)best, wl);
-    if (lane == r) my_id = id;
-    if (lane == wl) {
-#pragma unroll
-      for (int m = 0; m < 16; ++m) h[m] = h[m] == best ? kNone : h[m];
-    }
-  }
-  return my_id;
-}
 
 template <int BITS, int JG, int NB>
 struct GuBatch {

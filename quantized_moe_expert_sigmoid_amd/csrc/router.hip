@@ -11,7 +11,7 @@
 // sums are added in slice order (deterministic). Top-k runs one wave per
 // token: sigmoid via the library's fp32 exp, key = sigmoid + bias, k rounds
 // of a wave-wide (key desc, id asc) arg-max, weights = sigmoid / sum.
-#include "moe_internal.h"
+#include "gemv_common.h"
 
 namespace {
 
@@ -107,88 +107,42 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const float *__restric
   }
 }
 
-// (key, id) order: a before b iff key_a > key_b, or equal keys and id_a < id_b.
-// NaN keys never win against a number.
-__device__ __forceinline__ bool key_before(float ka, int ia, float kb, int ib) {
-  if (ia < 0) return false;
-  if (ib < 0) return true;
-  if (ka > kb) return true;
-  if (ka == kb) return ia < ib;
-  return (kb != kb) && (ka == ka);
-}
-
 // --- top-k: one wave per token ---------------------------------------------
-constexpr int kMaxPerLane = 1024 / MOE_WAVE;  // E <= 1024
+// Each lane sums its experts' logit slices in slice order, forms sigmoid and
+// key (a NaN key ranks last, -0 becomes +0) into the wave's LDS rows; the
+// wave then selects the k best (descending key, ties to the lower id) with
+// the DPP selection of the single-token path, and the weights are
+// routed_scale * sigmoid / (sum of the selected sigmoids, in rank order).
+constexpr int kTopkWaves = 4;
 
-__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ partial, int nslices, int T,
-                                                          int E, int k, const float *__restrict__ bias,
-                                                          float routed_scale, int32_t *__restrict__ topk_idx,
-                                                          float *__restrict__ topk_w) {
-  const int lane = threadIdx.x & (MOE_WAVE - 1);
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
-  float sig[kMaxPerLane], key[kMaxPerLane];
+template <int NSL>  // logit slices
+__global__ __launch_bounds__(kTopkWaves * MOE_WAVE) void router_topk_kernel(
+    const float *__restrict__ partial, int T, int E, int k, const float *__restrict__ bias,
+    float routed_scale, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w) {
+  __shared__ float key_s[kTopkWaves][1024], sig_s[kTopkWaves][1024];
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kTopkWaves + wave;
+  if (t >= T) return;  // whole waves; no workgroup barrier below
+  for (int e0 = 0; e0 < E; e0 += MOE_WAVE) {
+    const int e = min(e0 + lane, E - 1);
+    float zs[NSL];
 #pragma unroll
-  for (int m = 0; m < kMaxPerLane; ++m) {
-    sig[m] = 0.0f;
-    key[m] = 0.0f;
-    const int e = lane + m * MOE_WAVE;
-    if (m < per && e < E) {
-      // all slice loads issued together, then added in slice order
-      constexpr int kMaxSlices = 16;
-      float zs[kMaxSlices];
+    for (int sl = 0; sl < NSL; ++sl) zs[sl] = partial[((int64_t)sl * T + t) * E + e];  // all issued, then summed
+    float z = zs[0];
 #pragma unroll
-      for (int s = 0; s < kMaxSlices; ++s) zs[s] = (s < nslices) ? partial[((int64_t)s * T + t) * E + e] : 0.0f;
-      float z = 0.0f;
-#pragma unroll
-      for (int s = 0; s < kMaxSlices; ++s)
-        if (s < nslices) z += zs[s];
-      sig[m] = 1.0f / (1.0f + moe_exp_f32(-z));
-      key[m] = sig[m] + (bias ? bias[e] : 0.0f);
-      if (key[m] != key[m]) key[m] = -__builtin_inff();  // a NaN key ranks last
+    for (int sl = 1; sl < NSL; ++sl) z += zs[sl];
+    const float sg = 1.0f / (1.0f + moe_exp_f32(-z));
+    float key = sg + (bias ? bias[e] : 0.0f);
+    if (key != key) key = -__builtin_inff();
+    if (e0 + lane < E) {
+      key_s[wave][e] = key + 0.0f;
+      sig_s[wave][e] = sg;
     }
   }
-  unsigned taken = 0;  // bit m: element m of this lane already selected
-  float my_sig = 0.0f;
-  int my_id = -1;
-  float sum = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bk = 0.0f;
-    int bi = -1;
-#pragma unroll
-    for (int m = 0; m < kMaxPerLane; ++m) {
-      const int e = lane + m * MOE_WAVE;
-      if (m < per && e < E && !(taken & (1u << m)) && key_before(key[m], e, bk, bi)) {
-        bk = key[m];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ok = __shfl_xor(bk, o, MOE_WAVE);
-      const int oi = __shfl_xor(bi, o, MOE_WAVE);
-      if (key_before(ok, oi, bk, bi)) {
-        bk = ok;
-        bi = oi;
-      }
-    }
-    // bi is now the same on every lane; its owner marks it and shares sigmoid
-    float s = 0.0f;
-    if ((bi & (MOE_WAVE - 1)) == lane) {
-      const int m = bi / MOE_WAVE;
-      taken |= 1u << m;
-#pragma unroll
-      for (int mm = 0; mm < kMaxPerLane; ++mm)
-        if (mm == m) s = sig[mm];
-    }
-    s = __shfl(s, bi & (MOE_WAVE - 1), MOE_WAVE);
-    sum += s;
-    if (lane == j) {
-      my_sig = s;
-      my_id = bi;
-    }
-  }
+  const int my_id = E <= 4 * MOE_WAVE ? wave_topk4(key_s[wave], E, k, lane) : wave_topk16(key_s[wave], E, k, lane);
+  const float my_sig = lane < k ? sig_s[wave][my_id] : 0.0f;
+  float sum = 0.0f;  // in rank order
+  for (int j = 0; j < k; ++j) sum += readlane_f(my_sig, j);
   if (lane < k) {
     topk_idx[(int64_t)t * k + lane] = my_id;
     topk_w[(int64_t)t * k + lane] = routed_scale * (my_sig / sum);
@@ -426,8 +380,14 @@ moe_status launch_router(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x
   }
   {
     MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
-    hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, ctx->stream, partial, nslices, T, E, k,
-                       bias, cfg->routed_scale, topk_idx, topk_w);
+    const dim3 g((T + kTopkWaves - 1) / kTopkWaves), b(kTopkWaves * MOE_WAVE);
+    switch (nslices) {
+      case 1: hipLaunchKernelGGL(router_topk_kernel<1>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
+      case 2: hipLaunchKernelGGL(router_topk_kernel<2>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
+      case 4: hipLaunchKernelGGL(router_topk_kernel<4>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
+      case 8: hipLaunchKernelGGL(router_topk_kernel<8>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
+      default: hipLaunchKernelGGL(router_topk_kernel<16>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
+    }
   }
   MOE_CHECK_LAUNCH("router_topk_kernel");
   return MOE_OK;
