@@ -477,7 +477,10 @@ def main():
                      "avg_launch_us": round(gu_ms * 1e3, 2),
                      "int8_ops_per_launch": gu_ops, "int8_TOPS": round(gu_ops / (gu_ms / 1e3) / 1e12, 1),
                      "int8_peak_TOPS": INT8_PEAK_TOPS,
-                     "mfma_frac": round(gu_ops / (gu_ms / 1e3) / 1e12 / INT8_PEAK_TOPS, 4) if T > 1 else None},
+                     "mfma_frac": round(gu_ops / (gu_ms / 1e3) / 1e12 / INT8_PEAK_TOPS, 4) if T > 1 else None,
+                     "launch_time": "one launch" if T == 1 else
+                     "sum of the 64-token and one-block launches, which overlap on two streams (a lower bound on "
+                     "the rate)"},
         "kernels": {k_: {"avg_us": round(v[0] * 1e3, 2), "launches_per_call": v[1]} for k_, v in per_call.items()},
         "expert_ffn": {"kernels": kernel_names["gateup"] + " + " + kernel_names["down"],
                        "algorithmic_bytes": round(avg_bytes), "avg_us": round(ffn_ms * 1e3, 2),

@@ -83,6 +83,23 @@ extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out
   return MOE_OK;
 }
 
+moe_status moe_side_fork(moe_ctx *ctx) {
+  if (!ctx->side) {
+    MOE_HIP(hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
+    MOE_HIP(hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming));
+    MOE_HIP(hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming));
+  }
+  MOE_HIP(hipEventRecord(ctx->ev_fork, ctx->stream));
+  MOE_HIP(hipStreamWaitEvent(ctx->side, ctx->ev_fork, 0));
+  return MOE_OK;
+}
+
+moe_status moe_side_join(moe_ctx *ctx) {
+  MOE_HIP(hipEventRecord(ctx->ev_join, ctx->side));
+  MOE_HIP(hipStreamWaitEvent(ctx->stream, ctx->ev_join, 0));
+  return MOE_OK;
+}
+
 hipEvent_t moe_timing_event(moe_ctx *ctx) {
   if (!ctx->event_pool.empty()) {
     hipEvent_t e = ctx->event_pool.back();
@@ -158,6 +175,12 @@ extern "C" void moe_ctx_destroy(moe_ctx *ctx) {
   if (!ctx) return;
   (void)hipSetDevice(ctx->device);
   (void)hipStreamSynchronize(ctx->stream);
+  if (ctx->side) {
+    (void)hipStreamSynchronize(ctx->side);
+    (void)hipStreamDestroy(ctx->side);
+    (void)hipEventDestroy(ctx->ev_fork);
+    (void)hipEventDestroy(ctx->ev_join);
+  }
   for (auto &t : ctx->timed) {
     (void)hipEventDestroy(t.start);
     (void)hipEventDestroy(t.stop);

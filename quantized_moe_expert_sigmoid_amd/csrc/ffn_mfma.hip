@@ -574,18 +574,25 @@ moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *x
   const int g4 = tiles(a.I, 64 * GuShape<4>::NB), g1 = tiles(a.I, 64 * GuShape<1>::NB);
   const int d4 = tiles(a.H, 64 * DnShape<4>::NB), d1 = tiles(a.H, 64 * DnShape<1>::NB);
   // 1-D grids sized for the most tiles the bucket can list; the surplus
-  // workgroups return at once
-  moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max * g4), dim3(kThreads), a, g4);
+  // workgroups return at once. The two tile kinds write disjoint rows: the
+  // 64-token tiles run on the side stream, overlapping the one-block tiles.
+  moe_status st;
+  if ((st = moe_side_fork(ctx))) return st;
+  moe_launch_on(ctx, ctx->side, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max * g4), dim3(kThreads), a,
+                g4);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
   moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 1>, dim3(usmall * g1), dim3(kThreads), a, g1);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
+  if ((st = moe_side_join(ctx))) return st;
   moe_launch(ctx, MOE_STAGE_REQUANT, requant_mfma_kernel<BITS>, dim3(a.T * (a.k + 1)), dim3(kThreads), a);
   MOE_CHECK_LAUNCH("requant_mfma_kernel");
-  moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max * d4), dim3(kThreads), a, d4);
+  if ((st = moe_side_fork(ctx))) return st;
+  moe_launch_on(ctx, ctx->side, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max * d4), dim3(kThreads), a,
+                d4);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
   moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 1>, dim3(usmall * d1), dim3(kThreads), a, d1);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
-  return MOE_OK;
+  return moe_side_join(ctx);
 }
 
 }  // namespace

@@ -34,6 +34,10 @@ struct moe_ctx {
   // small persistent device block: error flags and counters
   uint32_t *dev_small = nullptr;  // [0] error flags, [1..] counters
   int ffn_kernels = MOE_FFN_AUTO;
+  // a second stream for work that may overlap the context stream's, forked
+  // from and joined back into it with events (created on first use)
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool dbg_on = false;
   moe_debug_bufs dbg{};
   // per-kernel timing (measurement only)
@@ -61,17 +65,26 @@ hipEvent_t moe_timing_event(moe_ctx *ctx);
 // carries the start/stop events (hipExtLaunchKernelGGL), so the recorded time
 // is the kernel's own execution, not that of extra event packets around it.
 template <typename K, typename... Args>
-void moe_launch(moe_ctx *ctx, int stage, K kernel, dim3 grid, dim3 block, Args... args) {
+void moe_launch_on(moe_ctx *ctx, hipStream_t stream, int stage, K kernel, dim3 grid, dim3 block, Args... args) {
   hipEvent_t s = ctx->timing ? moe_timing_event(ctx) : nullptr;
   hipEvent_t e = s ? moe_timing_event(ctx) : nullptr;
   if (s && e) {
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, ctx->stream, s, e, 0, args...);
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, s, e, 0, args...);
     ctx->timed.push_back({s, e, stage});
     return;
   }
   if (s) ctx->event_pool.push_back(s);
-  hipLaunchKernelGGL(kernel, grid, block, 0, ctx->stream, args...);
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
 }
+template <typename K, typename... Args>
+void moe_launch(moe_ctx *ctx, int stage, K kernel, dim3 grid, dim3 block, Args... args) {
+  moe_launch_on(ctx, ctx->stream, stage, kernel, grid, block, args...);
+}
+// Fork: work enqueued on ctx->side after this call starts after everything
+// enqueued on ctx->stream so far. Join: work enqueued on ctx->stream after
+// this call starts after everything enqueued on ctx->side so far.
+moe_status moe_side_fork(moe_ctx *ctx);
+moe_status moe_side_join(moe_ctx *ctx);
 
 moe_status moe_fail(moe_status st, const char *fmt, ...);
 moe_status moe_hip_fail(hipError_t e, const char *what);

@@ -172,20 +172,33 @@ struct BucketArgs {
   int ubig_max, has_shared;
 };
 
+// Exclusive prefix sum over the workgroup's threads (in thread order): an
+// inclusive scan inside each wave (shuffles), the wave totals scanned by
+// wave 0 through LDS, two barriers. tmp holds at least one int per wave.
 __device__ int block_exclusive_scan(int v, int *tmp) {
-  // Hillis-Steele over kBThreads entries in LDS
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < kBThreads; o <<= 1) {
-    const int add = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  constexpr int kW = kBThreads / MOE_WAVE;
+  const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < MOE_WAVE; o <<= 1) {
+    const int u = __shfl_up(incl, o, MOE_WAVE);
+    if (lane >= o) incl += u;
   }
-  const int incl = tmp[tid];
+  if (lane == MOE_WAVE - 1) tmp[wave] = incl;
   __syncthreads();
-  return incl - v;
+  if (wave == 0) {
+    int w = lane < kW ? tmp[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < kW; o <<= 1) {
+      const int u = __shfl_up(w, o, MOE_WAVE);
+      if (lane >= o) w += u;
+    }
+    if (lane < kW) tmp[kW + lane] = w - (lane < kW ? tmp[lane] : 0);  // exclusive wave offsets
+  }
+  __syncthreads();
+  const int r = tmp[kW + wave] + incl - v;
+  __syncthreads();  // tmp is reused by the next scan
+  return r;
 }
 
 // ids of token t with repeats dropped (a repeated id counts once, at its

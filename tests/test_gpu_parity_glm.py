@@ -178,3 +178,37 @@ def test_glm_graph_replay_matches_eager(glm):
         L.forward(xs[rep])  # eager work between replays
         torch.cuda.synchronize()
     ctx.check()
+
+
+def test_glm_graph_replay_multi_token(glm):
+    """Multi-token calls fork the 64-token tiles onto a side stream and join
+    back; captured in a graph, every replay (eager work in between) equals the
+    eager result, slot by slot and combined."""
+    from synth import workloads as wl
+    moe, ctx, L = glm
+    xs = [torch.from_numpy(wl.hidden_fp32(wl.DECODE64, 64, batch=b)).cuda() for b in range(2)]
+    zs = [torch.from_numpy(wl.logits_fp32(wl.DECODE64, 64, batch=b)).cuda() for b in range(2)]
+    eager = []
+    for x, z in zip(xs, zs):
+        r = L.forward(x, z)
+        torch.cuda.synchronize()
+        eager.append((r["y"].clone(), r["out"].clone()))
+    cap = torch.cuda.Stream()
+    old = ctx.stream
+    ctx.set_stream(cap)
+    g = torch.cuda.CUDAGraph()
+    outs = []
+    with torch.cuda.graph(g, stream=cap):
+        for x, z in zip(xs, zs):
+            r = L.forward(x, z)
+            outs.append((r["y"].clone(), r["out"].clone()))
+    ctx.set_stream(old)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i][0], eager[i][0]), (rep, i)
+            assert torch.equal(outs[i][1], eager[i][1]), (rep, i)
+        L.forward(xs[rep % 2], zs[rep % 2])
+        torch.cuda.synchronize()
+    ctx.check()
