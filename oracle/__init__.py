@@ -68,7 +68,8 @@ def _load():
                                              vp, vp, vp, vp, vp, vp, vp]
             lib.orc_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp]
             lib.orc_layer.argtypes = [vp, vp, vp, vp, dbl, vp, vp, ctypes.POINTER(_Expert), i32,
-                                      i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+                                      i32, i32, i32, i32, i32, dbl, vp, vp, vp, vp, vp, vp]
+            lib.orc_topp.argtypes = [i32, i32, i32, vp, dbl, dbl, vp, vp, vp]
             lib.orc_swiglu_f64.argtypes = [vp, vp, vp, vp, i32, i32, vp]
             _lib = lib
     return _lib
@@ -153,6 +154,19 @@ def router(x: np.ndarray, wr: np.ndarray | None, bias: np.ndarray | None, k: int
     if want_keys:
         return idx, w, keys, sig
     return idx, w
+
+
+def topp(idx: np.ndarray, sig: np.ndarray, top_p: float, routed_scale: float = 1.0):
+    """Top-p truncation of a top-k selection (orc_topp): returns (idx with -1
+    for dropped slots, w, cumulative normalised weights fp64 [T][k])."""
+    idx = np.array(idx, dtype=np.int32, order="C")
+    sig = np.ascontiguousarray(sig, dtype=np.float64)
+    T, k = idx.shape
+    E = sig.shape[1]
+    w = np.zeros((T, k), dtype=np.float32)
+    cum = np.empty((T, k), dtype=np.float64)
+    _check(_load().orc_topp(T, E, k, _p(sig), float(routed_scale), float(top_p), _p(idx), _p(w), _p(cum)), "topp")
+    return idx, w, cum
 
 
 # --- O4 ----------------------------------------------------------------------
@@ -244,8 +258,10 @@ class ExpertTable:
 
 
 def layer(x: np.ndarray, table: ExpertTable, shared: Expert | None, k: int, wr: np.ndarray | None = None,
-          bias: np.ndarray | None = None, logits: np.ndarray | None = None, routed_scale: float = 1.0):
-    """Full layer. Returns dict xq, sx, idx, w, y_slots, out.
+          bias: np.ndarray | None = None, logits: np.ndarray | None = None, routed_scale: float = 1.0,
+          top_p: float = 0.0):
+    """Full layer. Returns dict xq, sx, idx, w, y_slots, out. top_p > 0 applies
+    the top-p truncation (orc_topp); dropped slots have id -1 and zero y.
 
     Experts referenced by the routing must be present in ``table``; the call
     raises if one is missing.
@@ -272,7 +288,7 @@ def layer(x: np.ndarray, table: ExpertTable, shared: Expert | None, k: int, wr: 
     b_ = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     _check(_load().orc_layer(_p(x), _p(lg), _p(wr_), _p(b_), float(routed_scale), ctypes.addressof(table._arr),
                              _p(table.bits), ctypes.byref(sh) if sh is not None else None,
-                             shared.bits if shared is not None else 0, T, H, I, E, k,
+                             shared.bits if shared is not None else 0, T, H, I, E, k, float(top_p),
                              _p(res["xq"]), _p(res["sx"]), _p(res["idx"]), _p(res["w"]), _p(res["y_slots"]),
                              _p(res["out"])), "layer")
     return res

@@ -211,6 +211,45 @@ int orc_router(int logits_in, const float *x, const float *wr, const float *bias
   return 0;
 }
 
+/* Top-p truncation of a top-k selection (agentlenshq.com, "Colibri: running
+ * GLM-5.2 744B MoE on consumer hardware", sections "Measured benchmarks" and
+ * community insights: the --topp 0.7 setting that loads fewer experts per
+ * token). Reading: in rank order, the normalised weights sigma_j / sum_k sigma
+ * accumulate; the shortest prefix whose cumulative weight reaches top_p is
+ * kept (all k if none does), its weights renormalised over the kept experts;
+ * dropped slots get id -1 and weight 0. top_p <= 0 leaves the selection as it
+ * is. sig: [T][E] sigmoids (fp64) as orc_router returns them; idx [T][k] in,
+ * out; w [T][k] out; cum_out [T][k] (nullable) the cumulative weights. */
+int orc_topp(int T, int E, int k, const double *sig, double routed_scale, double top_p, int32_t *idx, float *w,
+             double *cum_out) {
+  if (T < 0 || E <= 0 || k <= 0 || !sig || !idx || !w) return -1;
+  for (int t = 0; t < T; ++t) {
+    int32_t *id = idx + (int64_t)t * k;
+    const double *sg = sig + (int64_t)t * E;
+    double total = 0.0;
+    for (int j = 0; j < k; ++j) total += sg[id[j]];
+    double cum = 0.0;
+    int keep = k;
+    for (int j = 0; j < k; ++j) {
+      cum += sg[id[j]] / total;
+      if (cum_out) cum_out[(int64_t)t * k + j] = cum;
+      if (keep == k && top_p > 0.0 && cum >= top_p) keep = j + 1;
+    }
+    if (top_p <= 0.0) continue;
+    double kept = 0.0;
+    for (int j = 0; j < keep; ++j) kept += sg[id[j]];
+    for (int j = 0; j < k; ++j) {
+      if (j < keep) {
+        w[(int64_t)t * k + j] = (float)(routed_scale * sg[id[j]] / kept);
+      } else {
+        id[j] = -1;
+        w[(int64_t)t * k + j] = 0.0f;
+      }
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* O4: bucketing                                                            */
 /* ------------------------------------------------------------------------ */
@@ -313,8 +352,10 @@ int orc_combine(const float *y_slots, const float *w, int T, int k, int H, int h
 
 int orc_layer(const float *x, const float *logits, const float *wr, const float *bias, double routed_scale,
               const orc_expert *experts, const uint8_t *bits, const orc_expert *shared, int shared_bits, int T, int H,
-              int I, int E, int k, int8_t *xq, float *sx, int32_t *idx, float *w, float *y_slots, float *out) {
+              int I, int E, int k, double top_p, int8_t *xq, float *sx, int32_t *idx, float *w, float *y_slots,
+              float *out) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || k > E || !out) return -1;
+  double *sig = NULL;
   const int S = k + (shared ? 1 : 0);
   int8_t *xq_ = xq ? xq : (int8_t *)malloc((size_t)T * H);
   float *sx_ = sx ? sx : (float *)malloc(sizeof(float) * (size_t)T);
@@ -324,14 +365,20 @@ int orc_layer(const float *x, const float *logits, const float *wr, const float 
   int rc = 0;
   if (!xq_ || !sx_ || !idx_ || !w_ || !ys_) { rc = -2; goto done; }
   if ((rc = orc_quantize_act(x, T, H, xq_, sx_)) != 0) goto done;
+  if (top_p > 0.0 && !(sig = (double *)malloc(sizeof(double) * (size_t)T * E))) { rc = -2; goto done; }
   if (logits)
-    rc = orc_router(1, logits, NULL, bias, T, H, E, k, routed_scale, idx_, w_, NULL, NULL);
+    rc = orc_router(1, logits, NULL, bias, T, H, E, k, routed_scale, idx_, w_, NULL, sig);
   else
-    rc = orc_router(0, x, wr, bias, T, H, E, k, routed_scale, idx_, w_, NULL, NULL);
+    rc = orc_router(0, x, wr, bias, T, H, E, k, routed_scale, idx_, w_, NULL, sig);
   if (rc) goto done;
+  if (top_p > 0.0 && (rc = orc_topp(T, E, k, sig, routed_scale, top_p, idx_, w_, NULL)) != 0) goto done;
   for (int t = 0; t < T; ++t) {
     for (int j = 0; j < k; ++j) {
       int e = idx_[(int64_t)t * k + j];
+      if (e < 0) { /* dropped by top-p: no expert, a zero slot */
+        memset(ys_ + ((int64_t)t * S + j) * H, 0, sizeof(float) * (size_t)H);
+        continue;
+      }
       rc = orc_expert_token(bits[e], &experts[e], xq_ + (int64_t)t * H, sx_[t], H, I, NULL, NULL, NULL, NULL, NULL,
                             NULL, ys_ + ((int64_t)t * S + j) * H);
       if (rc) goto done;
@@ -344,6 +391,7 @@ int orc_layer(const float *x, const float *logits, const float *wr, const float 
   }
   rc = orc_combine(ys_, w_, T, k, H, shared ? 1 : 0, out);
 done:
+  free(sig);
   if (!xq) free(xq_);
   if (!sx) free(sx_);
   if (!idx) free(idx_);

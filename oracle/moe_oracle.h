@@ -98,9 +98,15 @@ int orc_combine(const float *y_slots, const float *w, int T, int k, int H, int h
  * logits: [T][E] when logits_in, else NULL (router runs on x with wr).
  * Outputs: xq [T][H], sx [T], idx [T][k], w [T][k], y_slots [T][S][H],
  * out [T][H] (any output except out may be NULL). */
+/* Top-p truncation of a top-k selection: the shortest rank-order prefix whose
+ * cumulative normalised weight reaches top_p is kept and renormalised;
+ * dropped slots get id -1 and weight 0; top_p <= 0 changes nothing. */
+int orc_topp(int T, int E, int k, const double *sig, double routed_scale, double top_p, int32_t *idx, float *w,
+             double *cum_out);
 int orc_layer(const float *x, const float *logits, const float *wr, const float *bias, double routed_scale,
               const orc_expert *experts, const uint8_t *bits, const orc_expert *shared, int shared_bits, int T, int H,
-              int I, int E, int k, int8_t *xq, float *sx, int32_t *idx, float *w, float *y_slots, float *out);
+              int I, int E, int k, double top_p, int8_t *xq, float *sx, int32_t *idx, float *w, float *y_slots,
+              float *out);
 
 /* Unquantised reference SwiGLU in fp64 (for the quantisation-error sanity
  * figure only): y = Wd (silu(Wg x) * (Wu x)). wg, wu [I][H]; wd [H][I]. */
