@@ -286,7 +286,7 @@ def build_gpu_layer(ctx, w, bits):
     return L
 
 
-def cpu_baseline(w, bits, n_tokens, repeats):
+def cpu_baseline(w, bits, n_tokens, repeats, top_p=0.0):
     """Time the oracle's full layer on n_tokens distinct tokens x repeats."""
     import oracle as orc
     from synth import workloads as wl
@@ -305,7 +305,7 @@ def cpu_baseline(w, bits, n_tokens, repeats):
     table = orc.ExpertTable(exps)
     t0 = time.perf_counter()
     for _ in range(repeats):
-        orc.layer(x, table, sh, w.k, wr=wr, bias=b, logits=logits)
+        orc.layer(x, table, sh, w.k, wr=wr, bias=b, logits=logits, top_p=top_p)
     dt = time.perf_counter() - t0
     return {"value": round(T * repeats / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{T} distinct tokens x {repeats} repeats of the full layer ({len(need)} routed experts "
@@ -320,6 +320,8 @@ def main():
     ap.add_argument("--workload", default="glm_decode_t1")
     ap.add_argument("--bits", type=int, default=4)
     ap.add_argument("--pool", type=int, default=64, help="distinct input batches rotated through")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="top-p truncation of the top-k experts (0: keep all k; the pages' setting is 0.7)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--cpu-repeats", type=int, default=8)
@@ -359,6 +361,7 @@ def main():
     bits = args.bits
     ctx = moe.MoeCtx(0)
     L = build_gpu_layer(ctx, w, bits)
+    L.top_p = args.top_p
 
     # input pool in HBM
     T = w.T
@@ -382,7 +385,8 @@ def main():
     for i in range(npool):
         step(i)
         torch.cuda.synchronize()
-        distinct.append(len(np.unique(b["idx"].cpu().numpy())) + (1 if w.has_shared else 0))
+        ids = b["idx"].cpu().numpy()
+        distinct.append(len(np.unique(ids[ids >= 0])) + (1 if w.has_shared else 0))
     H, I = w.H, w.I
     o = L.experts.offsets
     gu_bytes = 2 * (o[1] - o[0]) + 8 * I          # packed gate + up rows and their fp32 scales
@@ -469,7 +473,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "hidden": w.H, "intermediate": w.I, "routed_experts": w.E, "top_k": w.k,
                    "shared_experts": 1 if w.has_shared else 0, "tokens_per_step": T, "weight_bits": bits,
-                   "routing": w.routing, "input_pool": npool},
+                   "routing": w.routing, "input_pool": npool, "top_p": args.top_p},
         "effective_weight_GBps": round(eff_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": kernel_names["gateup"], "achieved": round(gu_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
@@ -490,7 +494,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         t0 = time.time()
-        result["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_tokens, args.cpu_repeats)
+        result["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_tokens, args.cpu_repeats, args.top_p)
         log(f"[bench] cpu baseline done in {time.time() - t0:.1f}s")
     print(json.dumps(result), flush=True)
     ctx.close()

@@ -27,6 +27,10 @@
  *  [P-dedup] same page, section "The RAM wall became a storage problem": an
  *            expert requested by several batch positions is read once; an
  *            expert's matrices are stored together and fetched in one go.
+ *  [P-topp]  agentlenshq.com, "Colibri: running GLM-5.2 744B MoE on consumer
+ *            hardware", measured-benchmark table and community remarks: the
+ *            --topp 0.7 setting loads fewer experts per token (1.6x end to
+ *            end on a RAM-bound machine).
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
@@ -63,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -88,12 +92,18 @@ typedef struct {
  * n_experts: E routed experts (1..1024); top_k: k (1..min(E, 16));
  * routed_scale: factor applied to the normalised weights (1.0 for plain
  * normalisation); logits_in: 0 = the router computes logits from hidden
- * states, 1 = the caller passes logits [T][E]. */
+ * states, 1 = the caller passes logits [T][E]; top_p ([P-topp]): 0 (or less)
+ * keeps all k experts; otherwise, in rank order, the normalised weights
+ * sig_j / sum_k sig accumulate (fp32, in that order) and only the shortest
+ * prefix whose cumulative weight reaches top_p is kept (all k if none does),
+ * its weights renormalised over the kept experts; the other slots get id -1
+ * and weight 0. */
 typedef struct {
   int n_experts;
   int top_k;
   float routed_scale;
   int logits_in;
+  float top_p;
 } moe_router_cfg;
 
 /* ---------------------------------------------------------------------- */
@@ -158,7 +168,8 @@ moe_status moe_quantize_act_i8(moe_ctx *ctx, const float *x, int T, int H, int8_
  * [E] or NULL); topk_idx int32 [T][k] = experts with the k largest keys in
  * descending key order (equal keys: lower id first); topk_w fp32 [T][k] =
  * routed_scale * sig / sum of the selected sig (the bias selects, it does not
- * weight). */
+ * weight). With cfg->top_p > 0 the selection is truncated as described at
+ * moe_router_cfg: dropped slots hold id -1 and weight 0. */
 moe_status moe_router_topk(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x, const float *w_router,
                            const float *bias, int T, int H, int32_t *topk_idx, float *topk_w);
 
@@ -189,8 +200,10 @@ moe_status moe_bucket_tokens(moe_ctx *ctx, const int32_t *topk_idx, int T, int k
  * entry equals this entry point's width are computed (slots of the others
  * are left untouched), so a mixed-precision layer is one call per width.
  * xq int8 [T][H], sx fp32 [T]: from moe_quantize_act_i8. topk_idx int32
- * [T][k]. y_slots fp32 [T][k+1][H] (slot k is the shared expert's; it is
- * written only when shared != NULL). */
+ * [T][k]; an id of -1 (a slot dropped by top-p) names no expert: its slot is
+ * not computed and not written; any other id outside [0, E) is an error
+ * reported by moe_ctx_check. y_slots fp32 [T][k+1][H] (slot k is the shared
+ * expert's; it is written only when shared != NULL). */
 moe_status moe_expert_ffn_q4(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
                              const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
                              int T, int H, int I, int E, int k, float *y_slots);
@@ -206,8 +219,9 @@ moe_status moe_expert_ffn_q2(moe_ctx *ctx, const moe_expert_w *experts, const mo
 /* ---------------------------------------------------------------------- */
 
 /* out fp32 [T][H] = (has_shared ? y_slots[t][k] : 0) + sum_{j<k}
- * topk_w[t][j] * y_slots[t][j], accumulated in fp32 in that order.
- * y_slots fp32 [T][k+1][H]. */
+ * topk_w[t][j] * y_slots[t][j], accumulated in fp32 in that order; slots of
+ * zero weight are skipped (their y is not read, so slots dropped by top-p may
+ * hold anything). y_slots fp32 [T][k+1][H]. */
 moe_status moe_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, int T, int k, int H, int has_shared,
                        float *out);
 
@@ -279,7 +293,8 @@ moe_status moe_pool_register(moe_pool *pool, int layer, int expert, int bits, co
  * experts point into the slab, the others are zero) and bits_dev DEVICE
  * uint8 [E] (the experts' widths, 0 when absent; nullable) -- ready for
  * moe_expert_ffn_q* with expert_bits = bits_dev. n_miss_host (nullable): this
- * call's misses. MOE_EINVAL for an id outside [0, E) or an unregistered
+ * call's misses; an id of -1 (a slot dropped by top-p) is skipped.
+ * MOE_EINVAL for another id outside [0, E) or an unregistered
  * expert; MOE_EPOOL when the slab cannot hold this call's experts beside the
  * pinned ones (the pool stays consistent). A bookkeeping-only pool takes
  * table_dev = bits_dev = NULL. */

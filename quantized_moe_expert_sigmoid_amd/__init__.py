@@ -43,7 +43,7 @@ class ExpertW(ctypes.Structure):
 
 class RouterCfg(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int), ("top_k", ctypes.c_int), ("routed_scale", ctypes.c_float),
-                ("logits_in", ctypes.c_int)]
+                ("logits_in", ctypes.c_int), ("top_p", ctypes.c_float)]
 
 
 class DebugBufs(ctypes.Structure):
@@ -223,7 +223,7 @@ def moe_quantize_act_i8(ctx: MoeCtx, x: torch.Tensor, xq: torch.Tensor, sx: torc
 
 def moe_router_topk(ctx: MoeCtx, x: torch.Tensor, w_router: torch.Tensor | None, bias: torch.Tensor | None, k: int,
                     topk_idx: torch.Tensor, topk_w: torch.Tensor, routed_scale: float = 1.0,
-                    logits_in: bool = False, n_experts: int | None = None):
+                    logits_in: bool = False, n_experts: int | None = None, top_p: float = 0.0):
     T = x.shape[0]
     _dev(x, torch.float32, "x")
     if logits_in:
@@ -237,7 +237,7 @@ def moe_router_topk(ctx: MoeCtx, x: torch.Tensor, w_router: torch.Tensor | None,
         _dev(bias, torch.float32, "bias", (E,))
     _dev(topk_idx, torch.int32, "topk_idx", (T, k))
     _dev(topk_w, torch.float32, "topk_w", (T, k))
-    cfg = RouterCfg(E, k, float(routed_scale), 1 if logits_in else 0)
+    cfg = RouterCfg(E, k, float(routed_scale), 1 if logits_in else 0, float(top_p))
     _ck(lib().moe_router_topk(ctx.handle, ctypes.byref(cfg), x.data_ptr(),
                               None if logits_in else w_router.data_ptr(), _ptr(bias), T, H,
                               topk_idx.data_ptr(), topk_w.data_ptr()))
@@ -302,7 +302,8 @@ def moe_combine(ctx: MoeCtx, y_slots: torch.Tensor, topk_w: torch.Tensor, has_sh
 def moe_layer_forward(ctx: MoeCtx, bits: int, x: torch.Tensor, table: torch.Tensor, shared: ExpertW | None,
                       k: int, I: int, out: torch.Tensor, w_router: torch.Tensor | None = None,
                       bias: torch.Tensor | None = None, logits: torch.Tensor | None = None,
-                      routed_scale: float = 1.0, topk_idx=None, topk_w=None, xq=None, sx=None, y_slots=None):
+                      routed_scale: float = 1.0, topk_idx=None, topk_w=None, xq=None, sx=None, y_slots=None,
+                      top_p: float = 0.0):
     """Whole layer in one call (see include/moe.h). Optional outputs may be None."""
     T, H = x.shape
     E = table.shape[0]
@@ -320,7 +321,7 @@ def moe_layer_forward(ctx: MoeCtx, bits: int, x: torch.Tensor, table: torch.Tens
                            (y_slots, torch.float32, (T, k + 1, H), "y_slots")):
         if t is not None:
             _dev(t, dt, nm, shp)
-    cfg = RouterCfg(E, k, float(routed_scale), 1 if logits is not None else 0)
+    cfg = RouterCfg(E, k, float(routed_scale), 1 if logits is not None else 0, float(top_p))
     sh = ctypes.byref(shared) if shared is not None else None
     _ck(lib().moe_layer_forward(ctx.handle, bits, ctypes.byref(cfg), x.data_ptr(), _ptr(logits),
                                 None if logits is not None else w_router.data_ptr(), _ptr(bias), table.data_ptr(), sh,

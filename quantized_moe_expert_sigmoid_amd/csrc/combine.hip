@@ -21,6 +21,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   if (has_shared) acc = *reinterpret_cast<const float4 *>(ys + (int64_t)k * H + hh);
   for (int j = 0; j < k; ++j) {
     const float wj = w[(int64_t)t * k + j];
+    if (wj == 0.0f) continue;  // a slot dropped by top-p: its y is not read (fma(0, y, acc) = acc for finite y)
     const float4 v = *reinterpret_cast<const float4 *>(ys + (int64_t)j * H + hh);
     acc.x = __builtin_fmaf(wj, v.x, acc.x);
     acc.y = __builtin_fmaf(wj, v.y, acc.y);

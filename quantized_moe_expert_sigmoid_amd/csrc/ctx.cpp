@@ -277,6 +277,7 @@ extern "C" moe_status moe_router_topk(moe_ctx *ctx, const moe_router_cfg *cfg, c
   if (st) return st;
   REQUIRE(cfg, "moe_router_topk: cfg is NULL");
   REQUIRE(cfg->n_experts >= 1 && cfg->n_experts <= 1024, "moe_router_topk: n_experts %d", cfg->n_experts);
+  REQUIRE(cfg->top_p == cfg->top_p, "moe_router_topk: top_p is NaN");
   REQUIRE(cfg->top_k >= 1 && cfg->top_k <= 16 && cfg->top_k <= cfg->n_experts, "moe_router_topk: top_k %d",
           cfg->top_k);
   REQUIRE(T >= 0, "moe_router_topk: T %d", T);
@@ -374,6 +375,7 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, int bits, const moe_router
   if (st) return st;
   REQUIRE(bits == 8 || bits == 4 || bits == 2, "moe_layer_forward: bits %d not in {8,4,2}", bits);
   REQUIRE(cfg, "moe_layer_forward: cfg is NULL");
+  REQUIRE(cfg->top_p == cfg->top_p, "moe_layer_forward: top_p is NaN");
   const int E = cfg->n_experts, k = cfg->top_k;
   REQUIRE(E >= 1 && E <= 1024 && k >= 1 && k <= 16 && k <= E, "moe_layer_forward: E %d k %d", E, k);
   REQUIRE(T >= 0 && (int64_t)T * (k + 1) <= (1 << 22), "moe_layer_forward: T %d", T);

@@ -63,7 +63,7 @@ constexpr int kMaxPairsWg = kFfnThreads;  // routed row pairs per gate/up workgr
 struct SlotEntry {
   moe_expert_w w;
   float weight;  // routing weight (1 for the shared expert)
-  int expert;    // expert id (-1 for the shared expert)
+  int expert;    // expert id (-1 for the shared expert and for slots dropped by top-p)
   int pad[2];
 };
 static_assert(sizeof(SlotEntry) == 64, "slot entries are 64 bytes");
@@ -177,7 +177,7 @@ struct GateUpT1Args {
   const float *logits;   // [E] or null
   const float *bias;     // [E] or null
   int E, k, ks;
-  float routed_scale;
+  float routed_scale, top_p;
   const moe_expert_w *experts;
   moe_expert_w shared;
   int has_shared;
@@ -293,11 +293,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   // this wave's shared pairs [sh0, sh0 + ns); lanes [0, ns) keep their sums
   const int sh0 = a.has_shared ? uniform((int)((int64_t)gw * a.I / nw)) : 0;
   const int ns = a.has_shared ? uniform((int)((int64_t)(gw + 1) * a.I / nw)) - sh0 : 0;
-  const int R = a.k * a.I;
-  // the workgroup's routed pairs [Q0, Q0 + np), taken one at a time by its
-  // waves from an LDS counter: a wave whose loads are served late takes fewer
-  const int Q0 = uniform((int)((int64_t)blockIdx.x * R / gridDim.x));
-  const int np = uniform((int)((int64_t)(blockIdx.x + 1) * R / gridDim.x)) - Q0;
+  __shared__ int nkeep_s;  // routed slots kept (k, or fewer under top-p)
   if (tid == 0) next_s = 0;
 
   // ---- loads first: the routing inputs, the expert table, the token's int8
@@ -402,18 +398,25 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
     const float my_sig = lane < a.k ? sig_s[my_id] : 0.0f;
     float sum = 0.0f;  // in rank order
     for (int j = 0; j < a.k; ++j) sum += readlane_f(my_sig, j);
+    float kept = sum;
+    const int keep = a.top_p > 0.0f ? topp_keep(my_sig, sum, a.k, a.top_p, kept) : a.k;
+    if (lane == 0) nkeep_s = keep;
     uint4 row[4];
     bool have = false;
     if (lane < a.k) {
-      const float wgt = a.routed_scale * (my_sig / sum);
-      const uint4 *src = reinterpret_cast<const uint4 *>(exp_s + my_id);
+      // a dropped slot keeps the first expert's pointers (valid rows for the
+      // down kernel, whose result for it is zero), weight 0 and id -1
+      const bool kp = lane < keep;
+      const int id0 = __builtin_amdgcn_readlane(my_id, 0);
+      const float wgt = kp ? a.routed_scale * (my_sig / kept) : 0.0f;
+      const uint4 *src = reinterpret_cast<const uint4 *>(exp_s + (kp ? my_id : id0));
       row[0] = src[0];
       row[1] = src[1];
       row[2] = src[2];
-      row[3] = make_uint4(__float_as_uint(wgt), (uint32_t)my_id, 0u, 0u);
+      row[3] = make_uint4(__float_as_uint(wgt), (uint32_t)(kp ? my_id : -1), 0u, 0u);
       have = true;
       if (blockIdx.x == 0) {
-        a.topk_idx[lane] = my_id;
+        a.topk_idx[lane] = kp ? my_id : -1;
         a.topk_w[lane] = wgt;
       }
     } else if (lane == a.k && a.has_shared) {
@@ -438,6 +441,13 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
     }
   }
   __syncthreads();
+
+  // the workgroup's routed pairs [Q0, Q0 + np) of the kept slots' keep * I,
+  // taken one at a time by its waves from an LDS counter: a wave whose loads
+  // are served late takes fewer
+  const int R = uniform(nkeep_s) * a.I;
+  const int Q0 = uniform((int)((int64_t)blockIdx.x * R / gridDim.x));
+  const int np = uniform((int)((int64_t)(blockIdx.x + 1) * R / gridDim.x)) - Q0;
 
   // ---- the workgroup's routed slots (a contiguous range spans at most two) ----
   WaveSlots ws;
@@ -576,7 +586,8 @@ constexpr int kRqThreads = 256;
 
 struct RequantT1Args {
   const float *A;  // [S][I]
-  int I, S;
+  const SlotEntry *slots;  // a routed slot with expert -1 was dropped by top-p
+  int I, S, k;
   uint32_t *aqf;   // [S][I/4] int8 codes, in the packed weights' field order
   int *sums;       // [S] sum of the codes per slot
   float *sa;       // [S] per-slot scale
@@ -621,7 +632,9 @@ __global__ __launch_bounds__(kRqThreads) void requant_t1_kernel(RequantT1Args a)
   if (lane == 0) red_m[wave] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-  const bool zero = m == 0.0f;
+  // a dropped slot (its a was never written): zero codes and scale, so the
+  // down kernel's y for it is exactly zero
+  const bool zero = m == 0.0f || (s < a.k && a.slots[s].expert == -1);
   const float sc = zero ? 0.0f : m / 127.0f;
   const float inv = zero ? 0.0f : 1.0f / sc;
   const bool fast = sc >= 0x1p-126f && sc <= 0x1.fffffep127f;
@@ -929,6 +942,7 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
   g.bias = bias;
   g.E = E; g.k = k; g.ks = ks;
   g.routed_scale = cfg->routed_scale;
+  g.top_p = cfg->top_p;
   g.experts = experts;
   if (shared) g.shared = *shared;
   g.has_shared = shared ? 1 : 0;
@@ -951,6 +965,8 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
 
   RequantT1Args q{};
   q.A = g.A;
+  q.slots = slots;
+  q.k = k;
   q.I = I;
   q.S = S;
   q.aqf = reinterpret_cast<uint32_t *>(base + o_aq);

@@ -261,3 +261,26 @@ __device__ __forceinline__ int wave_topk16(const float *key_s, int E, int k, int
   }
   return my_id;
 }
+
+// Top-p truncation (agentlenshq.com, "Colibri: running GLM-5.2 744B MoE on
+// consumer hardware", the --topp setting): lane j < k holds the sigmoid of the
+// rank-j expert, sum their total. In rank order the normalised weights
+// sig_j / sum accumulate in fp32; returns the length of the shortest prefix
+// whose cumulative weight reaches top_p (k if none does, or top_p <= 0) and
+// sets kept to the sum of the kept sigmoids in rank order. Wave-uniform.
+__device__ __forceinline__ int topp_keep(float my_sig, float sum, int k, float top_p, float &kept) {
+  int keep = k;
+  if (top_p > 0.0f) {
+    float cum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      cum += readlane_f(my_sig, j) / sum;
+      if (cum >= top_p) {
+        keep = j + 1;
+        break;
+      }
+    }
+  }
+  kept = 0.0f;
+  for (int j = 0; j < keep; ++j) kept += readlane_f(my_sig, j);
+  return keep;
+}

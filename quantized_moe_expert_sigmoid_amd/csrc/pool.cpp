@@ -214,6 +214,7 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   std::vector<uint8_t> want(E, 0);
   for (int64_t i = 0; i < (int64_t)T * k; ++i) {
     const int e = topk_idx_host[i];
+    if (e == -1) continue;  // a slot dropped by top-p needs no expert
     if (e < 0 || e >= E) return moe_fail(MOE_EINVAL, "moe_pool_prepare: expert id %d at %lld", e, (long long)i);
     if (!row[e].registered)
       return moe_fail(MOE_EINVAL, "moe_pool_prepare: (layer %d, expert %d) is not registered", layer, e);

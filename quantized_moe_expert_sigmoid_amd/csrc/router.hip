@@ -113,12 +113,14 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const float *__restric
 // wave then selects the k best (descending key, ties to the lower id) with
 // the DPP selection of the single-token path, and the weights are
 // routed_scale * sigmoid / (sum of the selected sigmoids, in rank order).
+// With top_p > 0 only the prefix topp_keep returns is kept (renormalised);
+// the other slots get id -1 and weight 0.
 constexpr int kTopkWaves = 4;
 
 template <int NSL>  // logit slices
 __global__ __launch_bounds__(kTopkWaves * MOE_WAVE) void router_topk_kernel(
     const float *__restrict__ partial, int T, int E, int k, const float *__restrict__ bias,
-    float routed_scale, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w) {
+    float routed_scale, float top_p, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w) {
   __shared__ float key_s[kTopkWaves][1024], sig_s[kTopkWaves][1024];
   const int lane = threadIdx.x & (MOE_WAVE - 1), wave = threadIdx.x >> 6;
   const int t = blockIdx.x * kTopkWaves + wave;
@@ -143,9 +145,11 @@ __global__ __launch_bounds__(kTopkWaves * MOE_WAVE) void router_topk_kernel(
   const float my_sig = lane < k ? sig_s[wave][my_id] : 0.0f;
   float sum = 0.0f;  // in rank order
   for (int j = 0; j < k; ++j) sum += readlane_f(my_sig, j);
+  float kept = sum;
+  const int keep = top_p > 0.0f ? topp_keep(my_sig, sum, k, top_p, kept) : k;
   if (lane < k) {
-    topk_idx[(int64_t)t * k + lane] = my_id;
-    topk_w[(int64_t)t * k + lane] = routed_scale * (my_sig / sum);
+    topk_idx[(int64_t)t * k + lane] = lane < keep ? my_id : -1;
+    topk_w[(int64_t)t * k + lane] = lane < keep ? routed_scale * (my_sig / kept) : 0.0f;
   }
 }
 
@@ -202,11 +206,13 @@ __device__ int block_exclusive_scan(int v, int *tmp) {
 }
 
 // ids of token t with repeats dropped (a repeated id counts once, at its
-// first slot); returns false when an id is out of range or repeated
+// first slot) and -1 (a slot dropped by top-p) skipped; returns false when an
+// id is otherwise out of range or repeated
 __device__ __forceinline__ bool token_ids(const BucketArgs &a, int64_t t, int ids[16]) {
   bool ok = true;
   for (int j = 0; j < a.k; ++j) ids[j] = a.idx[t * a.k + j];
   for (int j = 0; j < a.k; ++j) {
+    if (ids[j] == -1) continue;
     bool dup = false;
     for (int i = 0; i < j; ++i) dup |= ids[i] == ids[j];
     if (ids[j] < 0 || ids[j] >= a.E || dup) {
@@ -395,11 +401,11 @@ moe_status launch_router(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x
     MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
     const dim3 g((T + kTopkWaves - 1) / kTopkWaves), b(kTopkWaves * MOE_WAVE);
     switch (nslices) {
-      case 1: hipLaunchKernelGGL(router_topk_kernel<1>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
-      case 2: hipLaunchKernelGGL(router_topk_kernel<2>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
-      case 4: hipLaunchKernelGGL(router_topk_kernel<4>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
-      case 8: hipLaunchKernelGGL(router_topk_kernel<8>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
-      default: hipLaunchKernelGGL(router_topk_kernel<16>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, topk_idx, topk_w); break;
+      case 1: hipLaunchKernelGGL(router_topk_kernel<1>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, cfg->top_p, topk_idx, topk_w); break;
+      case 2: hipLaunchKernelGGL(router_topk_kernel<2>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, cfg->top_p, topk_idx, topk_w); break;
+      case 4: hipLaunchKernelGGL(router_topk_kernel<4>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, cfg->top_p, topk_idx, topk_w); break;
+      case 8: hipLaunchKernelGGL(router_topk_kernel<8>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, cfg->top_p, topk_idx, topk_w); break;
+      default: hipLaunchKernelGGL(router_topk_kernel<16>, g, b, 0, ctx->stream, partial, T, E, k, bias, cfg->routed_scale, cfg->top_p, topk_idx, topk_w); break;
     }
   }
   MOE_CHECK_LAUNCH("router_topk_kernel");

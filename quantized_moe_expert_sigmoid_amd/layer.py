@@ -23,9 +23,10 @@ def _to_dev(a, device):
 
 class MoeLayer:
     def __init__(self, ctx: MoeCtx, H: int, I: int, E: int, k: int, bits: int = 4, has_shared: bool = True,
-                 routed_scale: float = 1.0, device: str = "cuda"):
+                 routed_scale: float = 1.0, device: str = "cuda", top_p: float = 0.0):
         self.ctx, self.H, self.I, self.E, self.k, self.bits = ctx, H, I, E, k, bits
         self.routed_scale = routed_scale
+        self.top_p = top_p  # 0: keep all k experts (see moe_router_cfg)
         self.device = device
         self.experts = ExpertBlocks(E, bits, H, I, device)
         self.shared = ExpertBlocks(1, bits, H, I, device) if has_shared else None
@@ -71,7 +72,8 @@ class MoeLayer:
         sh = self.shared.struct(0) if self.shared is not None else None
         moe_layer_forward(self.ctx, self.bits, x, self.experts.table, sh, self.k, self.I, b["out"],
                           w_router=None if logits is not None else self.w_router, bias=self.bias, logits=logits,
-                          routed_scale=self.routed_scale, topk_idx=b["idx"], topk_w=b["w"], xq=b["xq"], sx=b["sx"],
+                          routed_scale=self.routed_scale, top_p=self.top_p, topk_idx=b["idx"], topk_w=b["w"],
+                          xq=b["xq"], sx=b["sx"],
                           y_slots=b["y"])
         return b
 
@@ -84,9 +86,10 @@ class MoeLayer:
         moe_quantize_act_i8(ctx, x, b["xq"], b["sx"])
         if logits is not None:
             moe_router_topk(ctx, logits, None, self.bias, self.k, b["idx"], b["w"], self.routed_scale,
-                            logits_in=True)
+                            logits_in=True, top_p=self.top_p)
         else:
-            moe_router_topk(ctx, x, self.w_router, self.bias, self.k, b["idx"], b["w"], self.routed_scale)
+            moe_router_topk(ctx, x, self.w_router, self.bias, self.k, b["idx"], b["w"], self.routed_scale,
+                            top_p=self.top_p)
         sh = self.shared.struct(0) if self.shared is not None else None
         FFN_BY_BITS[self.bits](ctx, self.experts.table, sh, None, b["xq"], b["sx"], b["idx"], self.H, self.I, self.E,
                                b["y"])

@@ -57,3 +57,34 @@ def rel_row_err(out, ref):
     num = np.abs(out - ref).max(axis=-1)
     den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
     return num / den
+
+
+def compare_topp(idx_g, w_g, idx_o, keys_o, sig_o, top_p, orc, tau=TAU, tau_cum=1e-5, w_rtol=2e-5):
+    """Compare GPU top-p routing with the oracle's plain top-k plus its top-p
+    truncation. Kept slots are a prefix, dropped ones hold id -1 and weight 0.
+    Where the oracle's ranking and its cumulative weight at the cut are clear
+    of ties (keys by tau, cumulative weights by tau_cum), the kept count, ids
+    and weights must match; otherwise any cut within the tie is accepted and
+    counted. Returns that count."""
+    idx_g, w_g = np.asarray(idx_g), np.asarray(w_g)
+    T, k = idx_o.shape
+    ti, tw, cum = orc.topp(idx_o, sig_o, top_p)
+    near = 0
+    for t in range(T):
+        m_g = int((idx_g[t] >= 0).sum())
+        assert m_g >= 1 and (idx_g[t, :m_g] >= 0).all() and (idx_g[t, m_g:] == -1).all(), (t, idx_g[t])
+        assert (w_g[t, m_g:] == 0).all(), (t, w_g[t])
+        m_o = int((ti[t] >= 0).sum())
+        ko = keys_o[t][idx_o[t]]
+        rest = np.delete(keys_o[t], idx_o[t])
+        clear_keys = np.all(ko[:-1] - ko[1:] > tau) and (ko[-1] - (rest.max() if rest.size else -np.inf) > tau)
+        clear_cut = abs(cum[t, m_o - 1] - top_p) > tau_cum and (m_o < 2 or abs(cum[t, m_o - 2] - top_p) > tau_cum)
+        if clear_keys and clear_cut:
+            assert m_g == m_o, (t, m_g, m_o, cum[t])
+            assert np.array_equal(idx_g[t, :m_g], ti[t, :m_o]), (t, idx_g[t], ti[t])
+            np.testing.assert_allclose(w_g[t, :m_g], tw[t, :m_o], rtol=w_rtol, atol=1e-7)
+        else:
+            near += 1
+            s = sig_o[t, idx_g[t, :m_g]]
+            np.testing.assert_allclose(w_g[t, :m_g], s / s.sum(), rtol=w_rtol, atol=1e-7)
+    return near

@@ -48,7 +48,7 @@ def test_binding_covers_the_header():
 
 def test_host_helpers(libmoe):
     import quantized_moe_expert_sigmoid_amd as m
-    assert libmoe.moe_abi_version() == 1
+    assert libmoe.moe_abi_version() == 2
     n, offs = m.moe_expert_block_layout(4, 6144, 2048)
     assert n == 18_915_328 and offs[0] == 0 and offs[1] == 6_291_456 and offs[5] == 18_915_328 - 4 * 6144
     assert m.moe_expert_block_layout(2, 6144, 2048)[0] == 9_478_144

@@ -212,3 +212,43 @@ def test_glm_graph_replay_multi_token(glm):
         L.forward(xs[rep % 2], zs[rep % 2])
         torch.cuda.synchronize()
     ctx.check()
+
+
+def test_glm_decode_t1_topp(glm, orc, oexp):
+    """The fused single-token path with top-p 0.7 at the GLM shape: kept ids
+    and weights as the oracle's truncation, kept slots bit-exact, dropped slots
+    zero, the combined output within 1e-3."""
+    from synth import workloads as wl
+    from tests.gpu_util import compare_topp
+    moe, ctx, L = glm
+    w = oexp.w
+    wr, bias = wl.router_fp32(w)
+    p = 0.7
+    L.top_p = p
+    try:
+        for batch in range(3):
+            x = wl.hidden_fp32(wl.DECODE1, 1, batch=batch)
+            res = L.forward(torch.from_numpy(x).cuda())
+            ctx.check()
+            got = {k: v.cpu().numpy() for k, v in res.items()}
+            idx_o, _, keys, sig = orc.router(x, wr, bias, w.k, want_keys=True)
+            assert compare_topp(got["idx"], got["w"], idx_o, keys, sig, p, orc) == 0
+            xq_o, sx_o = orc.quantize_act(x)
+            ys, ws = [], []
+            for j in range(w.k):
+                e = int(got["idx"][0, j])
+                if e < 0:
+                    assert (got["y"][0, j] == 0).all()
+                    continue
+                y = orc.expert_token(oexp.get(e), xq_o[0], float(sx_o[0]))["y"]
+                assert np.array_equal(got["y"][0, j].view(np.uint32), y.view(np.uint32)), (batch, j, e)
+                ys.append(y)
+                ws.append(got["w"][0, j])
+            m = len(ys)
+            log(f"top-p {p}: token {batch} keeps {m} of {w.k}")
+            ysh = orc.expert_token(oexp.shared, xq_o[0], float(sx_o[0]))["y"]
+            assert np.array_equal(got["y"][0, w.k], ysh)
+            ref = orc.combine(np.stack(ys + [ysh])[None], np.array([ws], np.float32), True)
+            assert rel_row_err(got["out"], ref).max() < 1e-3
+    finally:
+        L.top_p = 0.0
