@@ -196,12 +196,21 @@ def stack_pool_bench(args) -> None:
     out = torch.empty((1, H), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
+    def predicted(t, layer):
+        """The next layer's experts of the previous token (its routing there)."""
+        nl, nt = (layer + 1, t - 1) if layer + 1 < Lr else (0, t)
+        return nl, (traces[nl][nt] if nt >= 0 else None)
+
     def run(t0_, t1_):
         for t in range(t0_, t1_):
             for layer in range(Lr):
                 idx = trace_dev[layer][t:t + 1]
                 moe.moe_quantize_act_i8(ctx, xs[(t + layer) % 16], xq, sx)
                 pool.prepare(layer, traces[layer][t:t + 1], tables[layer], widths[layer])
+                if args.stack_prefetch:
+                    nl, ids = predicted(t, layer)
+                    if ids is not None:
+                        pool.prefetch(nl, ids)
                 moe.moe_expert_ffn_q4(ctx, tables[layer], shared.struct(layer), widths[layer], xq, sx, idx, H, I, E, y)
                 moe.moe_expert_ffn_q2(ctx, tables[layer], None, widths[layer], xq, sx, idx, H, I, E, y)
                 moe.moe_combine(ctx, y, wts, True, out)
@@ -210,14 +219,32 @@ def stack_pool_bench(args) -> None:
     run(0, args.stack_warmup)
     torch.cuda.synchronize()
     cold_s = time.perf_counter() - tc
+    n_pinned = 0
+    if args.stack_pin_gb > 0:
+        n_pinned = pool.pin_hot(int(args.stack_pin_gb * 1e9))
+        torch.cuda.synchronize()
     st0 = pool.stats()
+    pf0 = pool.prefetch_stats()
     tm = time.perf_counter()
     run(args.stack_warmup, ntok)
     torch.cuda.synchronize()
     dt = time.perf_counter() - tm
     ctx.check()
     st1 = pool.stats()
+    pf1 = pool.prefetch_stats()
     n = args.stack_tokens
+    # accuracy of the read-ahead predictor over the measured tokens: the share
+    # of each layer's experts that the previous token used there
+    acc_num = acc_den = 0
+    for t in range(args.stack_warmup, ntok):
+        for layer in range(Lr):
+            nl, ids = predicted(t, layer)
+            nt = t if nl > 0 else t + 1
+            if ids is None or nt >= ntok:
+                continue
+            actual = set(traces[nl][nt].tolist())
+            acc_num += len(actual & set(ids.tolist()))
+            acc_den += len(actual)
     hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
     h2d = st1["bytes_h2d"] - st0["bytes_h2d"]
     # H2D probe: one pinned 1 GB host-to-device copy
@@ -242,9 +269,14 @@ def stack_pool_bench(args) -> None:
         "misses_per_token": round(misses / n, 3),
         "h2d_GBps": round(h2d / dt / 1e9, 2),
         "h2d_probe_GBps": round(probe, 2),
+        "prefetch": {"enabled": bool(args.stack_prefetch), "issued": pf1["issued"] - pf0["issued"],
+                     "used": pf1["used"] - pf0["used"],
+                     "predictor_accuracy": round(acc_num / max(1, acc_den), 4)},
+        "pinned": {"budget_bytes": int(args.stack_pin_gb * 1e9), "experts": n_pinned},
     }
     log(f"[stack] {n} tokens in {dt:.2f}s: {n / dt:.1f} tokens/s, hit rate {res['hit_rate']}, "
-        f"{res['misses_per_token']} misses/token, H2D {res['h2d_GBps']} GB/s (probe {res['h2d_probe_GBps']} GB/s)")
+        f"{res['misses_per_token']} misses/token, H2D {res['h2d_GBps']} GB/s (probe {res['h2d_probe_GBps']} GB/s), "
+        f"prefetch {res['prefetch']}, pinned {n_pinned}")
     print(json.dumps(res), flush=True)
     pool.close()
     ctx.close()
@@ -331,6 +363,10 @@ def main():
     ap.add_argument("--stack-hot", type=int, default=192)
     ap.add_argument("--stack-tokens", type=int, default=1000)
     ap.add_argument("--stack-warmup", type=int, default=300)
+    ap.add_argument("--stack-prefetch", action="store_true",
+                    help="read-ahead: before each layer's FFN, prefetch the next layer's experts of the previous token")
+    ap.add_argument("--stack-pin-gb", type=float, default=0.0,
+                    help="after the warm-up, pin this many GB of the most requested experts (usage counts)")
     ap.add_argument("--pmc-summary", nargs=5, default=None,
                     metavar=("BENCH_FETCH", "BENCH_WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"))
     args = ap.parse_args()

@@ -300,6 +300,34 @@ moe_status moe_pool_register(moe_pool *pool, int layer, int expert, int bits, co
  * table_dev = bits_dev = NULL. */
 moe_status moe_pool_prepare(moe_pool *pool, int layer, const int32_t *topk_idx_host, int T, int k,
                             moe_expert_w *table_dev, uint8_t *bits_dev, int *n_miss_host);
+/* Read-ahead ([P-load]; remio.ai, "Colibri shows how to run GLM-5.2 on a
+ * low-spec PC", section "The RAM wall became a storage problem": the engine
+ * predicts the next layer's routing and fetches those experts early). Starts
+ * the refill of the experts ids_host[0..n) (HOST int32; -1 entries skipped)
+ * of `layer` that are not resident, on the copy stream, so that a later
+ * moe_pool_prepare of that layer finds them (it then waits for their copies
+ * as for its own). Best effort: it never evicts an expert that the latest
+ * moe_pool_prepare made resident (its kernels may not be enqueued yet) and
+ * stops at the first expert it cannot place. n_issued_host (nullable): the
+ * refills started. The prefetched experts count as recently used. MOE_EINVAL
+ * for an id that is not a registered expert of the layer. */
+moe_status moe_pool_prefetch(moe_pool *pool, int layer, const int32_t *ids_host, int n, int *n_issued_host);
+/* Usage-learned pinning ([P-load]: the engine records the experts' routing in
+ * a usage file and pins the hottest at start-up). moe_pool_usage writes, for
+ * every (layer, expert) in layer-major order (HOST uint64 [n_layers][E]), the
+ * number of moe_pool_prepare calls that requested it. moe_pool_pin_hot pins
+ * registered experts in descending order of counts_host (same layout; NULL =
+ * this pool's own counts; ties: lower layer, then lower id; zero counts never)
+ * while their blocks fit in budget_bytes (at most the capacity), making each
+ * resident now when room can be found without evicting the latest call's
+ * experts (else on its first use); pinned experts are never evicted. Leave
+ * room for a call's unpinned experts, or moe_pool_prepare may fail with
+ * MOE_EPOOL. n_pinned_host (nullable): the experts pinned by this call. */
+moe_status moe_pool_usage(const moe_pool *pool, uint64_t *counts_host);
+moe_status moe_pool_pin_hot(moe_pool *pool, const uint64_t *counts_host, size_t budget_bytes, int *n_pinned_host);
+/* Prefetch outcome: refills started by moe_pool_prefetch, and how many of
+ * those experts a later moe_pool_prepare requested while still resident. */
+moe_status moe_pool_prefetch_stats(const moe_pool *pool, uint64_t *issued, uint64_t *used);
 /* Cumulative expert hits, misses and bytes copied host-to-device. */
 moe_status moe_pool_stats(const moe_pool *pool, uint64_t *hits, uint64_t *misses, uint64_t *bytes_h2d);
 /* 1 if (layer, expert) is resident, 0 if not, -1 for invalid arguments. */

@@ -85,6 +85,10 @@ _SIGS = {
     "moe_pool_stats": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64),
                               ctypes.POINTER(ctypes.c_uint64)]),
     "moe_pool_resident": (_i32, [_vp, _i32, _i32]),
+    "moe_pool_prefetch": (_i32, [_vp, _i32, _vp, _i32, ctypes.POINTER(ctypes.c_int)]),
+    "moe_pool_usage": (_i32, [_vp, _vp]),
+    "moe_pool_pin_hot": (_i32, [_vp, _vp, _sz, ctypes.POINTER(ctypes.c_int)]),
+    "moe_pool_prefetch_stats": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]),
 }
 
 
@@ -438,6 +442,50 @@ class MoePool:
         h, m, b = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
         _ck(lib().moe_pool_stats(self.handle, ctypes.byref(h), ctypes.byref(m), ctypes.byref(b)))
         return {"hits": h.value, "misses": m.value, "bytes_h2d": b.value}
+
+    def prefetch(self, layer: int, ids_host) -> int:
+        """Start refills of the given experts of `layer` (best effort); returns
+        how many were started."""
+        import numpy as np
+        ids = np.ascontiguousarray(ids_host, dtype=np.int32).ravel()
+        n = ctypes.c_int(0)
+        _ck(lib().moe_pool_prefetch(self.handle, layer, ids.ctypes.data if ids.size else None, ids.size,
+                                    ctypes.byref(n)))
+        return n.value
+
+    def usage(self):
+        """Requests per (layer, expert): uint64 numpy array [n_layers][E]."""
+        import numpy as np
+        c = np.zeros((self.n_layers, self.n_experts), dtype=np.uint64)
+        _ck(lib().moe_pool_usage(self.handle, c.ctypes.data))
+        return c
+
+    def pin_hot(self, budget_bytes: int, counts=None) -> int:
+        """Pin the most requested experts within budget_bytes (counts: the
+        usage array of an earlier run, or None for this pool's own)."""
+        import numpy as np
+        c = None if counts is None else np.ascontiguousarray(counts, dtype=np.uint64)
+        if c is not None and c.shape != (self.n_layers, self.n_experts):
+            raise ValueError("counts must be [n_layers][n_experts]")
+        n = ctypes.c_int(0)
+        _ck(lib().moe_pool_pin_hot(self.handle, c.ctypes.data if c is not None else None, int(budget_bytes),
+                                   ctypes.byref(n)))
+        return n.value
+
+    def save_usage(self, path: str):
+        """Write the usage counts (the engine's usage file): numpy .npy."""
+        import numpy as np
+        np.save(path, self.usage(), allow_pickle=False)
+
+    @staticmethod
+    def load_usage(path: str):
+        import numpy as np
+        return np.load(path, allow_pickle=False)
+
+    def prefetch_stats(self):
+        i, u = ctypes.c_uint64(), ctypes.c_uint64()
+        _ck(lib().moe_pool_prefetch_stats(self.handle, ctypes.byref(i), ctypes.byref(u)))
+        return {"issued": i.value, "used": u.value}
 
     def resident(self, layer: int, expert: int) -> bool:
         r = lib().moe_pool_resident(self.handle, layer, expert)

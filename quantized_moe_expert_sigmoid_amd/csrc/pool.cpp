@@ -2,6 +2,15 @@
 // stack of layers, refilled from caller-owned pinned host memory on a copy
 // stream.
 //
+// Usage-learned pinning and prefetch: agentlenshq.com, "Colibri: running
+// GLM-5.2 744B MoE on consumer hardware", section "Loading mechanism" (the
+// engine records the experts' routing in a usage file and pins the hottest
+// ones at start-up); tech.takumi3488.com, "Trying colibri", section on the
+// learning cache (143 hot experts pinned, 289 s -> 254 s); remio.ai, "Colibri
+// shows how to run GLM-5.2 on a low-spec PC", section "The RAM wall became a
+// storage problem" (read-ahead predicts the next layer's routing, 71.6% of the
+// time by the project's count, and fetches those experts early).
+//
 // Pages: agentlenshq.com, "Colibri: running GLM-5.2 744B MoE on consumer
 // hardware", section "Loading mechanism" (experts stay resident under an LRU;
 // the next block is read while the current one is computed) and section
@@ -25,9 +34,16 @@
 //    makes the copy stream wait for the event of epoch n+1 first.
 //  - The context stream waits for this call's refills, then receives the
 //    layer's expert table (and widths) from a pinned staging buffer.
+//  - Every requested (layer, expert) is counted; moe_pool_pin_hot pins the
+//    most requested within a byte budget (refilling them now), and the
+//    counts can be saved and given back in a later process.
+//  - moe_pool_prefetch refills predicted experts ahead of their prepare call,
+//    best effort: it never evicts an expert of the latest prepare call (whose
+//    kernels may not be enqueued yet), so it waits for no reader of its own.
 //  - Without a context the pool only keeps the books (no memory, no copies):
 //    hit rates of a capacity can be planned, and the policy tested, on a
 //    host without a GPU.
+#include <algorithm>
 #include <list>
 #include <map>
 #include <vector>
@@ -48,6 +64,8 @@ struct Entry {
   bool resident = false;
   size_t off = 0;
   uint64_t last_use = 0;           // epoch of the last call that needed it
+  uint64_t uses = 0;               // prepare calls that requested it
+  bool prefetched = false;         // refilled by a prefetch, not yet requested
   std::list<int>::iterator lru;    // valid while resident and unpinned
   hipEvent_t ready = nullptr;      // refill completion (copy stream)
 };
@@ -70,6 +88,7 @@ struct moe_pool {
   bool staging_used[kStaging] = {};
   int staging_next = 0;
   uint64_t hits = 0, misses = 0, bytes_h2d = 0;
+  uint64_t prefetches = 0, prefetch_used = 0;
 };
 
 namespace {
@@ -104,6 +123,43 @@ void slab_free(moe_pool *p, size_t off, size_t len) {
 }
 
 size_t block_bytes(const moe_pool *p, int bits) { return moe_expert_block_layout(bits, p->H, p->I, nullptr); }
+
+// Makes entry en resident with last use `ep`: slab space, evicting from the
+// cold end entries whose last use is before `protect`, and the copy from its
+// host block on the copy stream after the context stream has passed every
+// call that could read the evicted bytes. MOE_EPOOL (nothing changed for en)
+// when the space cannot be found.
+moe_status refill(moe_pool *p, Entry &en, uint64_t ep, uint64_t protect) {
+  size_t off = 0;
+  uint64_t wait_ep = 0;  // the epoch whose start event the refill waits for
+  while (!slab_alloc(p, en.bytes, &off)) {
+    if (p->lru.empty() || p->entries[p->lru.front()].last_use >= protect) return MOE_EPOOL;
+    const int vi = p->lru.front();
+    Entry &v = p->entries[vi];
+    p->lru.pop_front();
+    v.resident = false;
+    v.prefetched = false;
+    slab_free(p, v.off, v.bytes);
+    if (v.last_use + 1 > wait_ep) wait_ep = v.last_use + 1;
+  }
+  en.off = off;
+  en.resident = true;
+  en.last_use = ep;
+  if (!en.pin) en.lru = p->lru.insert(p->lru.end(), (int)(&en - p->entries.data()));
+  p->bytes_h2d += en.bytes;
+  if (p->ctx) {
+    if (wait_ep) {
+      // events before the ring's oldest are gone; a later one is a safe wait
+      const uint64_t last = p->epoch;
+      const uint64_t w = wait_ep + kEpochEvents <= last ? last - kEpochEvents + 1 : wait_ep;
+      MOE_HIP(hipStreamWaitEvent(p->copy_stream, p->epoch_ev[w % kEpochEvents], 0));
+    }
+    MOE_HIP(hipMemcpyAsync(p->slab + off, en.host, en.bytes, hipMemcpyHostToDevice, p->copy_stream));
+    if (!en.ready) MOE_HIP(hipEventCreateWithFlags(&en.ready, hipEventDisableTiming));
+    MOE_HIP(hipEventRecord(en.ready, p->copy_stream));
+  }
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -227,50 +283,30 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   if (p->ctx) MOE_HIP(hipEventRecord(p->epoch_ev[ep % kEpochEvents], p->ctx->stream));
   // hits first: they move to the hot end and cannot be evicted below
   for (int e = 0; e < E; ++e) {
-    if (!want[e] || !row[e].resident) continue;
+    if (!want[e]) continue;
+    ++row[e].uses;
+    if (!row[e].resident) continue;
     Entry &en = row[e];
     en.last_use = ep;
     if (!en.pin) p->lru.splice(p->lru.end(), p->lru, en.lru);
     ++p->hits;
+    if (en.prefetched) {
+      ++p->prefetch_used;
+      en.prefetched = false;
+    }
   }
   int n_miss = 0;
   for (int e = 0; e < E; ++e) {
     if (!want[e] || row[e].resident) continue;
-    Entry &en = row[e];
-    size_t off = 0;
-    uint64_t wait_ep = 0;  // the epoch whose start event the refill waits for
-    while (!slab_alloc(p, en.bytes, &off)) {
-      if (p->lru.empty() || p->entries[p->lru.front()].last_use == ep) {
-        // the books stay consistent: refills already issued stay resident
-        return moe_fail(MOE_EPOOL,
-                        "moe_pool_prepare: layer %d: the pool (%zu bytes) cannot hold this call's experts "
-                        "beside its pinned and in-use blocks",
-                        layer, p->capacity);
-      }
-      const int vi = p->lru.front();
-      Entry &v = p->entries[vi];
-      p->lru.pop_front();
-      v.resident = false;
-      slab_free(p, v.off, v.bytes);
-      if (v.last_use + 1 > wait_ep) wait_ep = v.last_use + 1;
-    }
-    en.off = off;
-    en.resident = true;
-    en.last_use = ep;
-    if (!en.pin) en.lru = p->lru.insert(p->lru.end(), (int)(&en - p->entries.data()));
+    moe_status st = refill(p, row[e], ep, ep);
+    if (st == MOE_EPOOL)  // the books stay consistent: refills already issued stay resident
+      return moe_fail(MOE_EPOOL,
+                      "moe_pool_prepare: layer %d: the pool (%zu bytes) cannot hold this call's experts "
+                      "beside its pinned and in-use blocks",
+                      layer, p->capacity);
+    if (st) return st;
     ++p->misses;
-    p->bytes_h2d += en.bytes;
     ++n_miss;
-    if (p->ctx) {
-      if (wait_ep) {
-        // events before the ring's oldest are gone; a later one is a safe wait
-        const uint64_t w = wait_ep + kEpochEvents <= ep ? ep - kEpochEvents + 1 : wait_ep;
-        MOE_HIP(hipStreamWaitEvent(p->copy_stream, p->epoch_ev[w % kEpochEvents], 0));
-      }
-      MOE_HIP(hipMemcpyAsync(p->slab + off, en.host, en.bytes, hipMemcpyHostToDevice, p->copy_stream));
-      if (!en.ready) MOE_HIP(hipEventCreateWithFlags(&en.ready, hipEventDisableTiming));
-      MOE_HIP(hipEventRecord(en.ready, p->copy_stream));
-    }
   }
   if (n_miss_host) *n_miss_host = n_miss;
   if (!p->ctx) return MOE_OK;
@@ -314,6 +350,84 @@ extern "C" moe_status moe_pool_stats(const moe_pool *p, uint64_t *hits, uint64_t
   if (hits) *hits = p->hits;
   if (misses) *misses = p->misses;
   if (bytes_h2d) *bytes_h2d = p->bytes_h2d;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_prefetch(moe_pool *p, int layer, const int32_t *ids_host, int n, int *n_issued_host) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_prefetch: pool is NULL");
+  if (layer < 0 || layer >= p->n_layers) return moe_fail(MOE_EINVAL, "moe_pool_prefetch: layer %d", layer);
+  if (n < 0 || (n > 0 && !ids_host)) return moe_fail(MOE_EINVAL, "moe_pool_prefetch: n %d ids %p", n, (const void *)ids_host);
+  const int E = p->n_experts;
+  Entry *row = &p->entries[(size_t)layer * E];
+  for (int i = 0; i < n; ++i) {
+    const int e = ids_host[i];
+    if (e == -1) continue;
+    if (e < 0 || e >= E || !row[e].registered)
+      return moe_fail(MOE_EINVAL, "moe_pool_prefetch: (layer %d, expert %d) is not a registered expert", layer, e);
+  }
+  if (p->ctx) MOE_HIP(hipSetDevice(p->ctx->device));
+  int issued = 0;
+  for (int i = 0; i < n; ++i) {
+    const int e = ids_host[i];
+    if (e == -1 || row[e].resident) continue;
+    // protected: everything the latest prepare call (and earlier prefetches
+    // after it) made resident
+    const moe_status st = refill(p, row[e], p->epoch, p->epoch);
+    if (st == MOE_EPOOL) break;  // best effort: no room without evicting protected experts
+    if (st) return st;
+    row[e].prefetched = true;
+    ++p->prefetches;
+    ++issued;
+  }
+  if (n_issued_host) *n_issued_host = issued;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_usage(const moe_pool *p, uint64_t *counts_host) {
+  if (!p || !counts_host) return moe_fail(MOE_EINVAL, "moe_pool_usage: NULL argument");
+  for (size_t i = 0; i < p->entries.size(); ++i) counts_host[i] = p->entries[i].uses;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_pin_hot(moe_pool *p, const uint64_t *counts_host, size_t budget_bytes,
+                                       int *n_pinned_host) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_pin_hot: pool is NULL");
+  if (budget_bytes > p->capacity)
+    return moe_fail(MOE_EINVAL, "moe_pool_pin_hot: budget %zu exceeds the capacity %zu", budget_bytes, p->capacity);
+  std::vector<std::pair<uint64_t, int>> order;  // (count, entry), most requested first, then lower index
+  for (size_t i = 0; i < p->entries.size(); ++i) {
+    const uint64_t c = counts_host ? counts_host[i] : p->entries[i].uses;
+    if (p->entries[i].registered && !p->entries[i].pin && c > 0) order.push_back({c, (int)i});
+  }
+  std::sort(order.begin(), order.end(), [](const std::pair<uint64_t, int> &a, const std::pair<uint64_t, int> &b) {
+    return a.first != b.first ? a.first > b.first : a.second < b.second;
+  });
+  if (p->ctx) MOE_HIP(hipSetDevice(p->ctx->device));
+  size_t used = 0;
+  int pinned = 0;
+  for (auto &o : order) {
+    Entry &en = p->entries[o.second];
+    if (used + en.bytes > budget_bytes) continue;
+    if (en.resident) {
+      p->lru.erase(en.lru);
+      en.pin = true;
+    } else {
+      en.pin = true;
+      const moe_status st = refill(p, en, p->epoch, p->epoch);
+      if (st && st != MOE_EPOOL) return st;  // no room now: it stays pinned and arrives on first use
+    }
+    en.prefetched = false;
+    used += en.bytes;
+    ++pinned;
+  }
+  if (n_pinned_host) *n_pinned_host = pinned;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_prefetch_stats(const moe_pool *p, uint64_t *issued, uint64_t *used) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_prefetch_stats: pool is NULL");
+  if (issued) *issued = p->prefetches;
+  if (used) *used = p->prefetch_used;
   return MOE_OK;
 }
 

@@ -208,3 +208,94 @@ def test_capacity_planning_monotone(moe):
         pool.close()
     assert all(a <= b_ for a, b_ in zip(hits, hits[1:])), hits
     assert hits[-1] >= 1200 * k - layers * E  # everything fits: only first touches miss
+
+
+# --------------------------------------------------------------------------
+# read-ahead, usage counts and usage-learned pinning
+# --------------------------------------------------------------------------
+
+def make_pool(moe, slots, layers=1, E=16):
+    b = block(moe, 4)
+    pool = moe.MoePool(None, slots * b, layers, E, H, I)
+    for L in range(layers):
+        for e in range(E):
+            pool.register(L, e, 4, None)
+    return pool
+
+
+def test_prefetch_then_prepare_hits(moe):
+    pool = make_pool(moe, 8)
+    assert pool.prepare(0, np.array([[0, 1]], np.int32)) == 2
+    assert pool.prefetch(0, [2, 3, -1, 1]) == 2  # 1 is already resident, -1 names no expert
+    assert pool.resident(0, 2) and pool.resident(0, 3)
+    assert pool.prepare(0, np.array([[2, 3]], np.int32)) == 0
+    assert pool.prefetch_stats() == {"issued": 2, "used": 2}
+    st = pool.stats()
+    assert (st["hits"], st["misses"]) == (2, 2)
+    pool.close()
+
+
+def test_prefetch_never_evicts_the_latest_call(moe):
+    pool = make_pool(moe, 4)
+    pool.prepare(0, np.array([[0, 1, 2, 3]], np.int32))  # fills the slab
+    assert pool.prefetch(0, [4, 5]) == 0  # every resident expert belongs to the latest call
+    assert all(pool.resident(0, e) for e in range(4)) and not pool.resident(0, 4)
+    pool.prepare(0, np.array([[2, 3]], np.int32))  # 0 and 1 now belong to an older call
+    assert pool.prefetch(0, [4, 5, 6]) == 2  # evicts 0 and 1, then stops
+    assert not pool.resident(0, 0) and not pool.resident(0, 1)
+    assert pool.resident(0, 2) and pool.resident(0, 3) and pool.resident(0, 4) and pool.resident(0, 5)
+    assert not pool.resident(0, 6)
+    pool.close()
+
+
+def test_prefetched_experts_count_as_recent(moe):
+    pool = make_pool(moe, 4)
+    pool.prepare(0, np.array([[0, 1]], np.int32))
+    pool.prefetch(0, [2, 3])
+    pool.prepare(0, np.array([[4]], np.int32))  # evicts the least recent: 0, not the prefetched ones
+    assert not pool.resident(0, 0) and pool.resident(0, 2) and pool.resident(0, 3)
+    pool.close()
+
+
+def test_usage_counts(moe):
+    E, layers = 16, 3
+    pool = make_pool(moe, 40, layers, E)
+    rng = np.random.default_rng(4)
+    ref = np.zeros((layers, E), np.uint64)
+    for step in range(200):
+        L = int(rng.integers(layers))
+        ids = rng.integers(0, E, size=(2, 3)).astype(np.int32)
+        ids[ids == 7] = -1  # dropped slots are not requests
+        for e in set(ids.ravel().tolist()) - {-1}:
+            ref[L, e] += 1
+        pool.prepare(L, ids)
+    assert np.array_equal(pool.usage(), ref)
+    pool.close()
+
+
+def test_pin_hot_keeps_the_most_requested(moe, tmp_path):
+    E, layers = 16, 2
+    rng = np.random.default_rng(8)
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    p /= p.sum()
+    trace = [(t % layers, rng.choice(E, size=(1, 3), replace=False, p=p).astype(np.int32)) for t in range(300)]
+    first = make_pool(moe, 10, layers, E)
+    for L, ids in trace:
+        first.prepare(L, ids)
+    counts = first.usage()
+    first.save_usage(str(tmp_path / "usage.npy"))
+    first.close()
+    loaded = moe.MoePool.load_usage(str(tmp_path / "usage.npy"))
+    assert np.array_equal(loaded, counts)
+    # a new process: pin the 4 most requested, then run a trace that evicts heavily
+    pool = make_pool(moe, 7, layers, E)
+    assert pool.pin_hot(4 * block(moe, 4), counts=loaded) == 4
+    order = sorted(((int(c), L * E + e) for (L, e), c in np.ndenumerate(loaded) if c > 0), key=lambda v: (-v[0], v[1]))
+    hot = [(i // E, i % E) for _, i in order[:4]]
+    assert all(pool.resident(L, e) for L, e in hot)
+    for L, ids in trace[::-1]:
+        pool.prepare(L, ids)
+        assert all(pool.resident(L2, e2) for L2, e2 in hot)
+    with pytest.raises(moe.MoeError):
+        pool.pin_hot(100 * block(moe, 4))  # beyond the capacity
+    pool.close()

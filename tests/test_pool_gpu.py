@@ -201,3 +201,38 @@ def test_pool_capacity_refusal_and_reuse(moe, ctx, syn):
     tab = table.cpu().numpy()
     assert torch.equal(dev_bytes(int(tab[2, 0]), blocks.block_bytes), host[2])
     pool.close()
+
+
+def test_pool_prefetch_bit_equal(moe, ctx, syn):
+    """Each call prefetches the next call's experts before its own FFN is
+    enqueued (the prefetch may not evict what this call reads); outputs equal
+    those from an all-resident table, and prefetched experts are hits."""
+    E, T, k, slots = 10, 2, 2, 6
+    blocks, host = make_blocks(moe, ctx, syn, 4, E, seed=37)
+    pool = moe.MoePool(ctx, slots * blocks.block_bytes, 1, E, H, I)
+    for e in range(E):
+        pool.register(0, e, 4, host[e])
+    table = torch.zeros((E, 6), dtype=torch.int64, device="cuda")
+    bits = torch.zeros((E,), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(21)
+    ids_all = [np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32) for _ in range(41)]
+    calls = []
+    for c in range(40):
+        xq, sx = token_inputs(moe, ctx, syn, T, seed=300 + c)
+        idx = torch.from_numpy(ids_all[c]).cuda()
+        y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
+        pool.prepare(0, ids_all[c], table, bits)
+        pool.prefetch(0, ids_all[c + 1].ravel())
+        moe.moe_expert_ffn_q4(ctx, table, None, bits, xq, sx, idx, H, I, E, y)
+        calls.append((xq, sx, idx, y))
+    torch.cuda.synchronize()
+    ctx.check()
+    for c, (xq, sx, idx, y) in enumerate(calls):
+        ref = torch.zeros_like(y)
+        moe.moe_expert_ffn_q4(ctx, blocks.table, None, None, xq, sx, idx, H, I, E, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), c
+    ps = pool.prefetch_stats()
+    log(f"prefetch: {ps}, {pool.stats()}")
+    assert ps["issued"] > 20 and ps["used"] > 10
+    pool.close()
