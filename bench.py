@@ -526,6 +526,10 @@ def main():
                        "algorithmic_bytes": round(avg_bytes), "avg_us": round(ffn_ms * 1e3, 2),
                        "achieved_GBps": round(ffn_gbps, 1), "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4)},
         "router_bytes": router_bytes,
+        # one call reads each distinct expert once, however many of its tokens
+        # (and draft positions of a verify batch) routed to it
+        "expert_reads": {"without_dedup_per_call": T * w.k + (T if w.has_shared else 0),
+                         "with_dedup_per_call": round(n_avg, 2), "per_token": round(n_avg / T, 3)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
