@@ -127,13 +127,15 @@ def pmc_summary(bench_fetch, bench_write, copy_fetch, copy_write, out_md) -> Non
 
 def stack_pool_bench(args) -> None:
     """Decode through the HBM expert pool: a stack of GLM-shaped MoE layers
-    whose routed experts live in pinned host memory (hot experts, the layer's
-    top Zipf ranks, at int4; the rest at int2), with a slab smaller than their
+    whose routed experts live in pinned host memory in precision tiers (the
+    layer's top Zipf ranks at int8 when asked, the next at int4, the rest at
+    int2; with demotion, each int8 / int4 expert also has its next narrower
+    block, loaded on misses under pressure), with a slab smaller than their
     total, refilled over PCIe on misses. One token per step; each layer's
     routing comes from a correlated Zipf trace (a slot keeps the previous
     token's expert with probability 0.6). Per layer: quantise the token,
-    prepare the pool (misses refill on the copy stream), the int4 and int2
-    FFN calls, the combine. Prints one JSON line."""
+    prepare the pool (misses refill on the copy stream), one FFN call per
+    width, the combine. Prints one JSON line."""
     import torch
     import quantized_moe_expert_sigmoid_amd as moe
     from synth import workloads as wl
@@ -141,14 +143,18 @@ def stack_pool_bench(args) -> None:
     Lr, E, k, H, I = args.stack_layers, 256, 8, 6144, 2048
     w = wl.Workload("glm_stack_pool", H=H, I=I, E=E, k=k, T=1, seed=6)
     ctx = moe.MoeCtx(0)
-    b4, _ = moe.moe_expert_block_layout(4, H, I)
-    b2, _ = moe.moe_expert_block_layout(2, H, I)
-    hot = args.stack_hot
+    hot, hot8 = args.stack_hot, min(args.stack_hot8, args.stack_hot)
+    bsz = {b: moe.moe_expert_block_layout(b, H, I)[0] for b in (8, 4, 2)}
+    narrower = {8: 4, 4: 2}
+
+    def width_of(rank):  # the layer's most popular ranks widest
+        return 8 if rank <= hot8 else 4 if rank <= hot else 2
+
     # a few distinct packed blocks per width, packed on the GPU from seeded
     # fp32 weights, tiled over the stack's host memory (pinned)
     nsrc = 4
     src = {}
-    for bits in (4, 2):
+    for bits in ((8, 4, 2) if hot8 else (4, 2)):
         blk = moe.ExpertBlocks(nsrc, bits, H, I)
         for e in range(nsrc):
             g, u, d = wl.expert_fp32(w, e)
@@ -157,28 +163,39 @@ def stack_pool_bench(args) -> None:
         src[bits] = blk.data.cpu()
         del blk
     t0 = time.time()
-    host = []  # per layer: (int4 blocks [hot], int2 blocks [E - hot]) pinned
+    ranks = [wl.zipf_rank(w.seed, layer, E) for layer in range(Lr)]
+    host = []  # per layer: {width: pinned [n, block bytes]} for the full-width and the narrower blocks
+    host_bytes = 0
     for layer in range(Lr):
-        h4 = torch.empty((hot, b4), dtype=torch.uint8, pin_memory=True)
-        h2 = torch.empty((E - hot, b2), dtype=torch.uint8, pin_memory=True)
-        for i in range(hot):
-            h4[i].copy_(src[4][(layer + i) % nsrc])
-        for i in range(E - hot):
-            h2[i].copy_(src[2][(layer + i) % nsrc])
-        host.append((h4, h2))
-    host_bytes = Lr * (hot * b4 + (E - hot) * b2)
+        need = {}
+        for e in range(E):
+            b = width_of(ranks[layer][e])
+            need[b] = need.get(b, 0) + 1
+            if args.stack_demote and b in narrower:
+                need[narrower[b]] = need.get(narrower[b], 0) + 1
+        hl = {}
+        for b, n in need.items():
+            t = torch.empty((n, bsz[b]), dtype=torch.uint8, pin_memory=True)
+            for i in range(n):
+                t[i].copy_(src[b][(layer + i) % nsrc])
+            hl[b] = t
+            host_bytes += n * bsz[b]
+        host.append(hl)
     log(f"[stack] {Lr} layers, {host_bytes / 1e9:.1f} GB of pinned expert blocks ready in {time.time() - t0:.1f}s")
     pool = moe.MoePool(ctx, int(args.stack_pool_gb * 1e9), Lr, E, H, I)
     for layer in range(Lr):
-        rank_of = wl.zipf_rank(w.seed, layer, E)
-        n4 = n2 = 0
+        used = {b: 0 for b in host[layer]}
+
+        def take(b):
+            used[b] += 1
+            return host[layer][b][used[b] - 1]
+
         for e in range(E):
-            if rank_of[e] <= hot:
-                pool.register(layer, e, 4, host[layer][0][n4])
-                n4 += 1
-            else:
-                pool.register(layer, e, 2, host[layer][1][n2])
-                n2 += 1
+            b = width_of(ranks[layer][e])
+            pool.register(layer, e, b, take(b))
+            if args.stack_demote and b in narrower:
+                pool.register_alt(layer, e, narrower[b], take(narrower[b]))
+    pool.set_demotion(args.stack_demote)
     shared = moe.ExpertBlocks(Lr, 4, H, I)
     for layer in range(Lr):
         g, u, d = wl.shared_fp32(w, layer)
@@ -211,6 +228,8 @@ def stack_pool_bench(args) -> None:
                     nl, ids = predicted(t, layer)
                     if ids is not None:
                         pool.prefetch(nl, ids)
+                if hot8:
+                    moe.moe_expert_ffn_q8(ctx, tables[layer], None, widths[layer], xq, sx, idx, H, I, E, y)
                 moe.moe_expert_ffn_q4(ctx, tables[layer], shared.struct(layer), widths[layer], xq, sx, idx, H, I, E, y)
                 moe.moe_expert_ffn_q2(ctx, tables[layer], None, widths[layer], xq, sx, idx, H, I, E, y)
                 moe.moe_combine(ctx, y, wts, True, out)
@@ -225,6 +244,7 @@ def stack_pool_bench(args) -> None:
         torch.cuda.synchronize()
     st0 = pool.stats()
     pf0 = pool.prefetch_stats()
+    ts0 = pool.tier_stats()
     tm = time.perf_counter()
     run(args.stack_warmup, ntok)
     torch.cuda.synchronize()
@@ -232,6 +252,7 @@ def stack_pool_bench(args) -> None:
     ctx.check()
     st1 = pool.stats()
     pf1 = pool.prefetch_stats()
+    ts1 = pool.tier_stats()
     n = args.stack_tokens
     # accuracy of the read-ahead predictor over the measured tokens: the share
     # of each layer's experts that the previous token used there
@@ -258,11 +279,12 @@ def stack_pool_bench(args) -> None:
     torch.cuda.synchronize()
     probe = 4 * (1 << 30) / (time.perf_counter() - tp) / 1e9
     res = {
-        "metric": "MoE stack decode tokens/s through the expert pool (int4 hot / int2 cold, 1 GPU)",
+        "metric": "MoE stack decode tokens/s through the expert pool (precision tiers, 1 GPU)",
         "value": round(n / dt, 2), "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": args.stack_warmup,
         "ms_per_step": round(dt / n * 1e3, 4), "higher_is_better": True, "data": "synthetic",
         "config": {"workload": "glm_stack_pool", "layers": Lr, "hidden": H, "intermediate": I, "routed_experts": E,
-                   "top_k": k, "hot_experts_int4": hot, "pool_bytes": int(args.stack_pool_gb * 1e9),
+                   "top_k": k, "hot_experts_int8": hot8, "hot_experts_int4": hot - hot8,
+                   "pool_bytes": int(args.stack_pool_gb * 1e9),
                    "host_expert_bytes": host_bytes, "routing": "correlated Zipf trace (reuse 0.6, s 1.1)"},
         "cold_start_tokens_per_s": round(args.stack_warmup / cold_s, 2),
         "hit_rate": round(hits / max(1, hits + misses), 5),
@@ -273,10 +295,16 @@ def stack_pool_bench(args) -> None:
                      "used": pf1["used"] - pf0["used"],
                      "predictor_accuracy": round(acc_num / max(1, acc_den), 4)},
         "pinned": {"budget_bytes": int(args.stack_pin_gb * 1e9), "experts": n_pinned},
+        # demotion: misses under pressure load the narrower block (int8 -> int4, int4 -> int2)
+        "tiers": {"demotion": bool(args.stack_demote),
+                  "demoted_loads": ts1["demoted_loads"] - ts0["demoted_loads"],
+                  "demoted_share_of_requests": round((ts1["demoted_uses"] - ts0["demoted_uses"])
+                                                     / max(1, hits + misses), 5),
+                  "h2d_bytes_saved": ts1["bytes_saved"] - ts0["bytes_saved"]},
     }
     log(f"[stack] {n} tokens in {dt:.2f}s: {n / dt:.1f} tokens/s, hit rate {res['hit_rate']}, "
         f"{res['misses_per_token']} misses/token, H2D {res['h2d_GBps']} GB/s (probe {res['h2d_probe_GBps']} GB/s), "
-        f"prefetch {res['prefetch']}, pinned {n_pinned}")
+        f"prefetch {res['prefetch']}, pinned {n_pinned}, tiers {res['tiers']}")
     print(json.dumps(res), flush=True)
     pool.close()
     ctx.close()
@@ -361,6 +389,10 @@ def main():
     ap.add_argument("--stack-layers", type=int, default=10)
     ap.add_argument("--stack-pool-gb", type=float, default=40.0)
     ap.add_argument("--stack-hot", type=int, default=192)
+    ap.add_argument("--stack-hot8", type=int, default=0,
+                    help="the layer's N most popular experts at int8 (within --stack-hot)")
+    ap.add_argument("--stack-demote", action="store_true",
+                    help="give every int8 / int4 expert a narrower block and load it on misses under pressure")
     ap.add_argument("--stack-tokens", type=int, default=1000)
     ap.add_argument("--stack-warmup", type=int, default=300)
     ap.add_argument("--stack-prefetch", action="store_true",

@@ -328,6 +328,30 @@ moe_status moe_pool_pin_hot(moe_pool *pool, const uint64_t *counts_host, size_t 
 /* Prefetch outcome: refills started by moe_pool_prefetch, and how many of
  * those experts a later moe_pool_prepare requested while still resident. */
 moe_status moe_pool_prefetch_stats(const moe_pool *pool, uint64_t *issued, uint64_t *used);
+/* Precision tiers ([P-feat]: int8, int4 and int2 kernels with per-row
+ * scales). moe_pool_register_alt gives a registered expert a second, narrower
+ * block (bits 4 under an int8 block, or 2 under an int4 one; same ownership
+ * rules as moe_pool_register; bytes must equal moe_expert_block_layout(bits,
+ * H, I); one per expert; MOE_EINVAL otherwise). With demotion on
+ * (moe_pool_set_demotion(pool, 1); off at creation), a refill of an unpinned
+ * expert with a narrower block loads that block instead when no free extent
+ * of the slab holds the full-width one (the pool is under pressure),
+ * evicting for the narrower size only. The expert keeps the width it was
+ * loaded at until evicted; the width reaches the FFN calls through bits_dev,
+ * so a layer's experts of each width go to that width's entry point. A
+ * pinned expert always loads at full width: moe_pool_pin_hot re-loads a
+ * demoted one now (or, if the latest call uses it, at its next request).
+ * moe_pool_tier_stats: loads at the narrower width, requests served by a
+ * narrower copy (hits and misses), and host-to-device bytes saved against
+ * full-width loads. */
+moe_status moe_pool_register_alt(moe_pool *pool, int layer, int expert, int bits, const void *block_host,
+                                 size_t bytes);
+moe_status moe_pool_set_demotion(moe_pool *pool, int enable);
+moe_status moe_pool_tier_stats(const moe_pool *pool, uint64_t *demoted_loads, uint64_t *demoted_uses,
+                               uint64_t *bytes_saved);
+/* Width of the resident copy of (layer, expert): 8, 4 or 2; 0 if not
+ * resident; -1 for invalid arguments. */
+int moe_pool_resident_bits(const moe_pool *pool, int layer, int expert);
 /* Cumulative expert hits, misses and bytes copied host-to-device. */
 moe_status moe_pool_stats(const moe_pool *pool, uint64_t *hits, uint64_t *misses, uint64_t *bytes_h2d);
 /* 1 if (layer, expert) is resident, 0 if not, -1 for invalid arguments. */

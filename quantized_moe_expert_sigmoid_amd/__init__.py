@@ -89,6 +89,10 @@ _SIGS = {
     "moe_pool_usage": (_i32, [_vp, _vp]),
     "moe_pool_pin_hot": (_i32, [_vp, _vp, _sz, ctypes.POINTER(ctypes.c_int)]),
     "moe_pool_prefetch_stats": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]),
+    "moe_pool_register_alt": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz]),
+    "moe_pool_set_demotion": (_i32, [_vp, _i32]),
+    "moe_pool_tier_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 3),
+    "moe_pool_resident_bits": (_i32, [_vp, _i32, _i32]),
 }
 
 
@@ -486,6 +490,38 @@ class MoePool:
         i, u = ctypes.c_uint64(), ctypes.c_uint64()
         _ck(lib().moe_pool_prefetch_stats(self.handle, ctypes.byref(i), ctypes.byref(u)))
         return {"issued": i.value, "used": u.value}
+
+    def register_alt(self, layer: int, expert: int, bits: int, block_host: torch.Tensor | None,
+                     nbytes: int | None = None):
+        """A narrower block of an already registered expert (int4 under int8,
+        int2 under int4), loaded instead of the full one under pressure when
+        demotion is on."""
+        if block_host is not None:
+            if block_host.is_cuda or block_host.dtype != torch.uint8 or not block_host.is_contiguous():
+                raise TypeError("block_host must be a contiguous CPU uint8 tensor")
+            nbytes = block_host.numel()
+            ptr = block_host.data_ptr()
+        else:
+            nbytes = moe_expert_block_layout(bits, self.H, self.I)[0] if nbytes is None else nbytes
+            ptr = None
+        _ck(lib().moe_pool_register_alt(self.handle, layer, expert, bits, ptr, nbytes))
+        if block_host is not None:
+            self._blocks[(layer, expert, "alt")] = block_host
+
+    def set_demotion(self, enable: bool):
+        _ck(lib().moe_pool_set_demotion(self.handle, 1 if enable else 0))
+
+    def tier_stats(self):
+        v = [ctypes.c_uint64() for _ in range(3)]
+        _ck(lib().moe_pool_tier_stats(self.handle, *(ctypes.byref(x) for x in v)))
+        return {"demoted_loads": v[0].value, "demoted_uses": v[1].value, "bytes_saved": v[2].value}
+
+    def resident_bits(self, layer: int, expert: int) -> int:
+        """Width of the resident copy (8, 4, 2), 0 when not resident."""
+        r = lib().moe_pool_resident_bits(self.handle, layer, expert)
+        if r < 0:
+            raise MoeError(MOE_EINVAL, "moe_pool_resident_bits: invalid arguments")
+        return r
 
     def resident(self, layer: int, expert: int) -> bool:
         r = lib().moe_pool_resident(self.handle, layer, expert)

@@ -40,6 +40,12 @@
 //  - moe_pool_prefetch refills predicted experts ahead of their prepare call,
 //    best effort: it never evicts an expert of the latest prepare call (whose
 //    kernels may not be enqueued yet), so it waits for no reader of its own.
+//  - Precision tiers: an expert may also register a narrower block (int4 ->
+//    int2, int8 -> int4). With demotion on, a refill whose full-width block
+//    finds no free extent large enough (the pool is under pressure) brings
+//    the narrower block instead, evicting for that size; the expert keeps
+//    the width it was loaded at until it is evicted. Pinned experts always
+//    load at full width, and pinning re-loads a demoted one at full width.
 //  - Without a context the pool only keeps the books (no memory, no copies):
 //    hit rates of a capacity can be planned, and the policy tested, on a
 //    host without a GPU.
@@ -57,11 +63,16 @@ constexpr int kStaging = 8;       // ring of pinned table staging buffers
 
 struct Entry {
   bool registered = false;
-  int bits = 0;
+  int bits = 0;                    // full-width block
   const void *host = nullptr;
   size_t bytes = 0;
+  int alt_bits = 0;                // narrower block, 0 if none
+  const void *alt_host = nullptr;
+  size_t alt_bytes = 0;
   bool pin = false;
   bool resident = false;
+  int rbits = 0;                   // width of the resident copy
+  size_t rbytes = 0;
   size_t off = 0;
   uint64_t last_use = 0;           // epoch of the last call that needed it
   uint64_t uses = 0;               // prepare calls that requested it
@@ -89,6 +100,8 @@ struct moe_pool {
   int staging_next = 0;
   uint64_t hits = 0, misses = 0, bytes_h2d = 0;
   uint64_t prefetches = 0, prefetch_used = 0;
+  bool demote = false;
+  uint64_t demoted_loads = 0, demoted_uses = 0, bytes_saved = 0;
 };
 
 namespace {
@@ -124,29 +137,47 @@ void slab_free(moe_pool *p, size_t off, size_t len) {
 
 size_t block_bytes(const moe_pool *p, int bits) { return moe_expert_block_layout(bits, p->H, p->I, nullptr); }
 
+bool fits_free(const moe_pool *p, size_t len) {
+  for (const auto &f : p->free_list)
+    if (f.second >= len) return true;
+  return false;
+}
+
+// Drops resident entry v from the slab; raises *wait_ep to the epoch whose
+// start event a refill into its bytes must wait for.
+void evict(moe_pool *p, Entry &v, uint64_t *wait_ep) {
+  if (!v.pin) p->lru.erase(v.lru);
+  v.resident = false;
+  v.prefetched = false;
+  slab_free(p, v.off, v.rbytes);
+  if (v.last_use + 1 > *wait_ep) *wait_ep = v.last_use + 1;
+}
+
 // Makes entry en resident with last use `ep`: slab space, evicting from the
 // cold end entries whose last use is before `protect`, and the copy from its
 // host block on the copy stream after the context stream has passed every
-// call that could read the evicted bytes. MOE_EPOOL (nothing changed for en)
-// when the space cannot be found.
-moe_status refill(moe_pool *p, Entry &en, uint64_t ep, uint64_t protect) {
+// call that could read the evicted bytes (and epoch wait_ep, when a caller
+// evicted en itself first). The narrower block when demotion applies.
+// MOE_EPOOL (nothing changed for en) when the space cannot be found.
+moe_status refill(moe_pool *p, Entry &en, uint64_t ep, uint64_t protect, uint64_t wait_ep = 0) {
+  const bool narrow = p->demote && en.alt_bits && !en.pin && !fits_free(p, en.bytes);
+  const size_t len = narrow ? en.alt_bytes : en.bytes;
   size_t off = 0;
-  uint64_t wait_ep = 0;  // the epoch whose start event the refill waits for
-  while (!slab_alloc(p, en.bytes, &off)) {
+  while (!slab_alloc(p, len, &off)) {
     if (p->lru.empty() || p->entries[p->lru.front()].last_use >= protect) return MOE_EPOOL;
-    const int vi = p->lru.front();
-    Entry &v = p->entries[vi];
-    p->lru.pop_front();
-    v.resident = false;
-    v.prefetched = false;
-    slab_free(p, v.off, v.bytes);
-    if (v.last_use + 1 > wait_ep) wait_ep = v.last_use + 1;
+    evict(p, p->entries[p->lru.front()], &wait_ep);
   }
   en.off = off;
   en.resident = true;
+  en.rbits = narrow ? en.alt_bits : en.bits;
+  en.rbytes = len;
   en.last_use = ep;
   if (!en.pin) en.lru = p->lru.insert(p->lru.end(), (int)(&en - p->entries.data()));
-  p->bytes_h2d += en.bytes;
+  p->bytes_h2d += len;
+  if (narrow) {
+    ++p->demoted_loads;
+    p->bytes_saved += en.bytes - len;
+  }
   if (p->ctx) {
     if (wait_ep) {
       // events before the ring's oldest are gone; a later one is a safe wait
@@ -154,7 +185,8 @@ moe_status refill(moe_pool *p, Entry &en, uint64_t ep, uint64_t protect) {
       const uint64_t w = wait_ep + kEpochEvents <= last ? last - kEpochEvents + 1 : wait_ep;
       MOE_HIP(hipStreamWaitEvent(p->copy_stream, p->epoch_ev[w % kEpochEvents], 0));
     }
-    MOE_HIP(hipMemcpyAsync(p->slab + off, en.host, en.bytes, hipMemcpyHostToDevice, p->copy_stream));
+    MOE_HIP(hipMemcpyAsync(p->slab + off, narrow ? en.alt_host : en.host, len, hipMemcpyHostToDevice,
+                           p->copy_stream));
     if (!en.ready) MOE_HIP(hipEventCreateWithFlags(&en.ready, hipEventDisableTiming));
     MOE_HIP(hipEventRecord(en.ready, p->copy_stream));
   }
@@ -282,14 +314,20 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   const uint64_t ep = ++p->epoch;
   if (p->ctx) MOE_HIP(hipEventRecord(p->epoch_ev[ep % kEpochEvents], p->ctx->stream));
   // hits first: they move to the hot end and cannot be evicted below
+  std::vector<uint64_t> wait(E, 0);
   for (int e = 0; e < E; ++e) {
     if (!want[e]) continue;
     ++row[e].uses;
     if (!row[e].resident) continue;
     Entry &en = row[e];
+    if (en.pin && en.rbits != en.bits) {  // pinned after a demoted load: re-loaded at full width below
+      evict(p, en, &wait[e]);
+      continue;
+    }
     en.last_use = ep;
     if (!en.pin) p->lru.splice(p->lru.end(), p->lru, en.lru);
     ++p->hits;
+    if (en.rbits != en.bits) ++p->demoted_uses;
     if (en.prefetched) {
       ++p->prefetch_used;
       en.prefetched = false;
@@ -298,7 +336,7 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   int n_miss = 0;
   for (int e = 0; e < E; ++e) {
     if (!want[e] || row[e].resident) continue;
-    moe_status st = refill(p, row[e], ep, ep);
+    moe_status st = refill(p, row[e], ep, ep, wait[e]);
     if (st == MOE_EPOOL)  // the books stay consistent: refills already issued stay resident
       return moe_fail(MOE_EPOOL,
                       "moe_pool_prepare: layer %d: the pool (%zu bytes) cannot hold this call's experts "
@@ -307,6 +345,7 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
     if (st) return st;
     ++p->misses;
     ++n_miss;
+    if (row[e].rbits != row[e].bits) ++p->demoted_uses;
   }
   if (n_miss_host) *n_miss_host = n_miss;
   if (!p->ctx) return MOE_OK;
@@ -324,7 +363,7 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
     const Entry &en = row[e];
     if (en.resident) {
       size_t o[6];
-      moe_expert_block_layout(en.bits, p->H, p->I, o);
+      moe_expert_block_layout(en.rbits, p->H, p->I, o);
       const char *b = p->slab + en.off;
       tab[e].gate = reinterpret_cast<const uint8_t *>(b + o[0]);
       tab[e].up = reinterpret_cast<const uint8_t *>(b + o[1]);
@@ -332,7 +371,7 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
       tab[e].s_gate = reinterpret_cast<const float *>(b + o[3]);
       tab[e].s_up = reinterpret_cast<const float *>(b + o[4]);
       tab[e].s_down = reinterpret_cast<const float *>(b + o[5]);
-      bits[e] = (uint8_t)en.bits;
+      bits[e] = (uint8_t)en.rbits;
     } else {
       tab[e] = moe_expert_w{};
       bits[e] = 0;
@@ -408,12 +447,16 @@ extern "C" moe_status moe_pool_pin_hot(moe_pool *p, const uint64_t *counts_host,
   for (auto &o : order) {
     Entry &en = p->entries[o.second];
     if (used + en.bytes > budget_bytes) continue;
+    uint64_t wait_ep = 0;
+    // demoted: re-load at full width now, unless the latest call (whose
+    // kernels may not be enqueued yet) uses it; then its next request does
+    if (en.resident && en.rbits != en.bits && en.last_use < p->epoch) evict(p, en, &wait_ep);
     if (en.resident) {
       p->lru.erase(en.lru);
       en.pin = true;
     } else {
       en.pin = true;
-      const moe_status st = refill(p, en, p->epoch, p->epoch);
+      const moe_status st = refill(p, en, p->epoch, p->epoch, wait_ep);
       if (st && st != MOE_EPOOL) return st;  // no room now: it stays pinned and arrives on first use
     }
     en.prefetched = false;
@@ -429,6 +472,48 @@ extern "C" moe_status moe_pool_prefetch_stats(const moe_pool *p, uint64_t *issue
   if (issued) *issued = p->prefetches;
   if (used) *used = p->prefetch_used;
   return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_register_alt(moe_pool *p, int layer, int expert, int bits, const void *block_host,
+                                            size_t bytes) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_register_alt: pool is NULL");
+  if (layer < 0 || layer >= p->n_layers || expert < 0 || expert >= p->n_experts)
+    return moe_fail(MOE_EINVAL, "moe_pool_register_alt: (layer %d, expert %d) out of range", layer, expert);
+  Entry &en = p->entries[(size_t)layer * p->n_experts + expert];
+  if (!en.registered)
+    return moe_fail(MOE_EINVAL, "moe_pool_register_alt: (layer %d, expert %d) has no full-width block", layer, expert);
+  if (en.alt_bits) return moe_fail(MOE_EINVAL, "moe_pool_register_alt: (layer %d, expert %d) already has one", layer, expert);
+  if (!(bits == 4 || bits == 2) || bits >= en.bits)
+    return moe_fail(MOE_EINVAL, "moe_pool_register_alt: bits %d is not narrower than the registered int%d", bits, en.bits);
+  const size_t need = block_bytes(p, bits);
+  if (bytes != need)
+    return moe_fail(MOE_EINVAL, "moe_pool_register_alt: block of %zu bytes, the int%d layout needs %zu", bytes, bits, need);
+  if (p->ctx && !block_host) return moe_fail(MOE_EINVAL, "moe_pool_register_alt: block_host is NULL");
+  en.alt_bits = bits;
+  en.alt_host = block_host;
+  en.alt_bytes = bytes;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_set_demotion(moe_pool *p, int enable) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_set_demotion: pool is NULL");
+  p->demote = enable != 0;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_tier_stats(const moe_pool *p, uint64_t *demoted_loads, uint64_t *demoted_uses,
+                                          uint64_t *bytes_saved) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_tier_stats: pool is NULL");
+  if (demoted_loads) *demoted_loads = p->demoted_loads;
+  if (demoted_uses) *demoted_uses = p->demoted_uses;
+  if (bytes_saved) *bytes_saved = p->bytes_saved;
+  return MOE_OK;
+}
+
+extern "C" int moe_pool_resident_bits(const moe_pool *p, int layer, int expert) {
+  if (!p || layer < 0 || layer >= p->n_layers || expert < 0 || expert >= p->n_experts) return -1;
+  const Entry &en = p->entries[(size_t)layer * p->n_experts + expert];
+  return en.resident ? en.rbits : 0;
 }
 
 extern "C" int moe_pool_resident(const moe_pool *p, int layer, int expert) {

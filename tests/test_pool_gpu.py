@@ -236,3 +236,66 @@ def test_pool_prefetch_bit_equal(moe, ctx, syn):
     log(f"prefetch: {ps}, {pool.stats()}")
     assert ps["issued"] > 20 and ps["used"] > 10
     pool.close()
+
+
+def test_pool_tiers_bit_equal(moe, ctx, syn):
+    """Precision tiers: three experts int8 with an int4 block, the others int4
+    with an int2 block, demotion on, a slab under pressure; midway the hot
+    experts are pinned (demoted copies re-loaded at full width). Every call's
+    outputs equal those of an all-resident table at the widths the pool
+    reported for that call, one FFN call per width."""
+    E, T, k = 10, 2, 2
+    b8, h8 = make_blocks(moe, ctx, syn, 8, E, seed=38)
+    b4, h4 = make_blocks(moe, ctx, syn, 4, E, seed=38)
+    b2, h2 = make_blocks(moe, ctx, syn, 2, E, seed=38)
+    full = {e: (8 if e < 3 else 4) for e in range(E)}
+    pool = moe.MoePool(ctx, 6 * b4.block_bytes, 1, E, H, I)
+    for e in range(E):
+        if full[e] == 8:
+            pool.register(0, e, 8, h8[e])
+            pool.register_alt(0, e, 4, h4[e])
+        else:
+            pool.register(0, e, 4, h4[e])
+            pool.register_alt(0, e, 2, h2[e])
+    pool.set_demotion(True)
+    per_width = {8: b8, 4: b4, 2: b2}
+    table = torch.zeros((E, 6), dtype=torch.int64, device="cuda")
+    bits = torch.zeros((E,), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(23)
+    calls = []
+    for c in range(48):
+        if c == 24:
+            counts = np.zeros((1, E), np.uint64)
+            counts[0, 0] = 9  # pin expert 0 (int8)
+            assert pool.pin_hot(b8.block_bytes, counts) == 1
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        xq, sx = token_inputs(moe, ctx, syn, T, seed=400 + c)
+        idx = torch.from_numpy(ids).cuda()
+        y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
+        try:
+            pool.prepare(0, ids, table, bits)
+        except moe.MoeError as ex:  # first-fit fragmentation can refuse a call
+            assert ex.status == moe.MOE_EPOOL
+            continue
+        widths = {int(e): pool.resident_bits(0, int(e)) for e in set(ids.ravel())}
+        for b in (8, 4, 2):
+            getattr(moe, f"moe_expert_ffn_q{b}")(ctx, table, None, bits, xq, sx, idx, H, I, E, y)
+        calls.append((c, xq, sx, idx, y, widths))
+    torch.cuda.synchronize()
+    ctx.check()
+    ts = pool.tier_stats()
+    log(f"tiers: {ts}, {pool.stats()}")
+    assert len(calls) >= 40 and ts["demoted_loads"] > 5
+    assert any(w < full[e] for *_, ws in calls for e, w in ws.items())
+    for c, xq, sx, idx, y, widths in calls:
+        wv = [widths.get(e, 0) for e in range(E)]
+        ref_table = torch.stack([per_width[w].table[e] if w else b4.table[e] for e, w in enumerate(wv)]).contiguous()
+        ref_bits = torch.tensor(wv, dtype=torch.uint8, device="cuda")
+        ref = torch.zeros_like(y)
+        for b in (8, 4, 2):
+            getattr(moe, f"moe_expert_ffn_q{b}")(ctx, ref_table, None, ref_bits, xq, sx, idx, H, I, E, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), (c, widths)
+        if c >= 24 and 0 in widths:  # pinned before call 24: full width from then on
+            assert widths[0] == 8, (c, widths)
+    pool.close()
