@@ -386,6 +386,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--cpu-repeats", type=int, default=8)
     ap.add_argument("--copy-probe", type=float, default=0.0, help="only run a device copy of this many MB")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--stack-layers", type=int, default=10)
     ap.add_argument("--stack-pool-gb", type=float, default=40.0)
     ap.add_argument("--stack-hot", type=int, default=192)
@@ -526,6 +527,28 @@ def main():
     # shared expert's, 2 I rows of H each (multiply and add counted as 2 ops)
     gu_ops = 2.0 * T * (w.k + (1 if w.has_shared else 0)) * 2 * I * H
 
+    # the measured read ceiling: a plain streaming-read kernel reading, in one
+    # launch, as many cold bytes as the gate/up launch and as the down launch
+    # (and 1 GiB), best of a few grid sizes
+    probe = None
+    if not args.no_probe:
+        pbuf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+        sizes = {"gateup": int(n_avg * gu_bytes) // 16 * 16, "down": int(n_avg * dn_bytes) // 16 * 16,
+                 "1GiB": 1 << 30}
+        probe = {"kernel": "stream_read_kernel (moe_probe_stream_read)", "cold_buffer_bytes": pbuf.numel()}
+        for name, nb in sizes.items():
+            best = None
+            for wpc in (1, 2, 4, 8):
+                moe.moe_probe_stream_read(ctx, pbuf, nb, wpc, 4)  # warm-up launches
+                _, us = moe.moe_probe_stream_read(ctx, pbuf, nb, wpc, 20)
+                if best is None or us < best[1]:
+                    best = (wpc, us)
+            probe[name] = {"bytes": nb, "avg_us": round(best[1], 2), "GBps": round(nb / best[1] / 1e3, 1),
+                           "wg_per_cu": best[0]}
+        del pbuf
+        log(f"[bench] stream-read probe: " + ", ".join(f"{k_} {v['GBps']} GB/s" for k_, v in probe.items()
+                                                       if isinstance(v, dict)))
+
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -550,6 +573,7 @@ def main():
                      "int8_ops_per_launch": gu_ops, "int8_TOPS": round(gu_ops / (gu_ms / 1e3) / 1e12, 1),
                      "int8_peak_TOPS": INT8_PEAK_TOPS,
                      "mfma_frac": round(gu_ops / (gu_ms / 1e3) / 1e12 / INT8_PEAK_TOPS, 4) if T > 1 else None,
+                     "frac_of_probe": round(gu_gbps / probe["gateup"]["GBps"], 4) if probe else None,
                      "launch_time": "one launch" if T == 1 else
                      "sum of the 64-token and one-block launches, which overlap on two streams (a lower bound on "
                      "the rate)"},
@@ -557,6 +581,7 @@ def main():
         "expert_ffn": {"kernels": kernel_names["gateup"] + " + " + kernel_names["down"],
                        "algorithmic_bytes": round(avg_bytes), "avg_us": round(ffn_ms * 1e3, 2),
                        "achieved_GBps": round(ffn_gbps, 1), "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4)},
+        "stream_read_probe": probe,
         "router_bytes": router_bytes,
         # one call reads each distinct expert once, however many of its tokens
         # (and draft positions of a verify batch) routed to it

@@ -382,6 +382,22 @@ moe_status moe_ctx_enable_timing(moe_ctx *ctx, int enable);
  * (n_host[MOE_N_STAGES]); then forget the records. Either pointer may be NULL. */
 moe_status moe_ctx_read_timing(moe_ctx *ctx, double *ms_host, int *n_host);
 
+/* Streaming-read probe: the measured HBM read ceiling for a launch of a
+ * given size, against which the weight-streaming kernels are judged beside
+ * the data-sheet peak. Launches `reps` times a plain read kernel
+ * (ctx->n_cu * wg_per_cu workgroups of 256 threads, 16-byte loads four deep,
+ * grid-stride) on the context stream; launch r reads bytes_per_launch bytes
+ * of buf (DEVICE, 16-byte aligned) at window r mod (buf_bytes /
+ * bytes_per_launch), so a buffer larger than the last-level cache keeps every
+ * launch cold. Synchronises the context stream. xor_host (nullable): the XOR
+ * of every 32-bit word of the last launch's window; us_host (nullable): the
+ * average launch duration in microseconds (hipEvents around each launch).
+ * MOE_EINVAL for a misaligned buffer, bytes_per_launch not a positive
+ * multiple of 16 or above buf_bytes, wg_per_cu outside [1, 64] or reps
+ * outside [1, 100000]. */
+moe_status moe_probe_stream_read(moe_ctx *ctx, const void *buf, size_t buf_bytes, size_t bytes_per_launch,
+                                 int wg_per_cu, int reps, uint32_t *xor_host, double *us_host);
+
 /* ---------------------------------------------------------------------- */
 /* Test visibility                                                        */
 /* ---------------------------------------------------------------------- */

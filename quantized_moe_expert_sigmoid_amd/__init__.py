@@ -89,6 +89,8 @@ _SIGS = {
     "moe_pool_usage": (_i32, [_vp, _vp]),
     "moe_pool_pin_hot": (_i32, [_vp, _vp, _sz, ctypes.POINTER(ctypes.c_int)]),
     "moe_pool_prefetch_stats": (_i32, [_vp, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]),
+    "moe_probe_stream_read": (_i32, [_vp, _vp, _sz, _sz, _i32, _i32, ctypes.POINTER(ctypes.c_uint32),
+                                     ctypes.POINTER(ctypes.c_double)]),
     "moe_pool_register_alt": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz]),
     "moe_pool_set_demotion": (_i32, [_vp, _i32]),
     "moe_pool_tier_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 3),
@@ -305,6 +307,17 @@ def moe_combine(ctx: MoeCtx, y_slots: torch.Tensor, topk_w: torch.Tensor, has_sh
     _ck(lib().moe_combine(ctx.handle, y_slots.data_ptr(), topk_w.data_ptr(), T, k, H, 1 if has_shared else 0,
                           out.data_ptr()))
     return out
+
+
+def moe_probe_stream_read(ctx: MoeCtx, buf: torch.Tensor, bytes_per_launch: int, wg_per_cu: int = 4,
+                          reps: int = 20):
+    """Streaming-read probe over a device uint8 buffer (see include/moe.h).
+    Returns (xor of the last window's 32-bit words, average launch us)."""
+    _dev(buf, torch.uint8, "buf")
+    x, us = ctypes.c_uint32(), ctypes.c_double()
+    _ck(lib().moe_probe_stream_read(ctx.handle, buf.data_ptr(), buf.numel(), int(bytes_per_launch), int(wg_per_cu),
+                                    int(reps), ctypes.byref(x), ctypes.byref(us)))
+    return x.value, us.value
 
 
 def moe_layer_forward(ctx: MoeCtx, bits: int, x: torch.Tensor, table: torch.Tensor, shared: ExpertW | None,
