@@ -224,8 +224,8 @@ __device__ __forceinline__ void gu_load(const WaveSlots &ws, int qb, int qlast, 
     for (int j = 0; j < JG; ++j) {
       int c = lane + j * MOE_WAVE;
       c = c < cpr ? c : cpr - 1;
-      bt.g[b][j] = ldg16(gate, c);
-      bt.u[b][j] = ldg16(up, c);
+      bt.g[b][j] = ldg16_nt(gate, c);
+      bt.u[b][j] = ldg16_nt(up, c);
     }
   }
 }
@@ -243,8 +243,8 @@ __device__ __forceinline__ void gu_load_shared(const uint8_t *gate, const uint8_
       for (int j = 0; j < JG; ++j) {
         int c = lane + j * MOE_WAVE;
         c = c < cpr ? c : cpr - 1;
-        bt.g[b][j] = ldg16(gate + o, c);
-        bt.u[b][j] = ldg16(up + o, c);
+        bt.g[b][j] = ldg16_nt(gate + o, c);
+        bt.u[b][j] = ldg16_nt(up + o, c);
       }
     }
   }
@@ -751,7 +751,7 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
         for (int j = 0; j < JD; ++j) {
           int c = lane + j * MOE_WAVE;
           c = c < cpr ? c : cpr - 1;
-          bt.w[b][s][j] = ldg16(dp[s] + (int64_t)r * rowbytes, c);
+          bt.w[b][s][j] = ldg16_nt(dp[s] + (int64_t)r * rowbytes, c);
         }
       }
       bt.sd[b] = gptr(sdown_l)[r];
