@@ -149,6 +149,23 @@ def test_glm_prefill_t2048(glm, orc, oexp, packed_seen):
     run_and_check(glm, orc, oexp, x, None, [0, 2047], packed_seen)
 
 
+def test_glm_prefill_t2048_zipf(glm, orc, oexp, packed_seen):
+    """Zipf prefill: the most popular expert takes most of the 2048 tokens
+    (many 64-token tiles of one expert), the tail experts a few each."""
+    from synth import workloads as wl
+    log("prefill T=2048 zipf")
+    x = wl.hidden_fp32(wl.PREFILL2048_ZIPF, 2048)
+    z = wl.logits_fp32(wl.PREFILL2048_ZIPF, 2048)
+    L = glm[2]
+    keep, L.bias = L.bias, None  # Zipf logits route without a selection bias
+    try:
+        got = run_and_check(glm, orc, oexp, x, z, [1, 1024, 2046], packed_seen)
+    finally:
+        L.bias = keep
+    counts = np.bincount(got["idx"].ravel(), minlength=256)
+    assert counts.max() > 1000 and (counts < 16).sum() > 20  # a heavy head and a long tail
+
+
 def test_glm_graph_replay_matches_eager(glm):
     """The benchmark replays the hot path as a HIP graph: every replay, with
     eager work and synchronisations in between, equals the eager result."""
