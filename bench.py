@@ -387,6 +387,8 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=8)
     ap.add_argument("--copy-probe", type=float, default=0.0, help="only run a device copy of this many MB")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold variant (shared expert and router rotated over 16 copies)")
     ap.add_argument("--stack-layers", type=int, default=10)
     ap.add_argument("--stack-pool-gb", type=float, default=40.0)
     ap.add_argument("--stack-hot", type=int, default=192)
@@ -493,6 +495,57 @@ def main():
     gpu_ms = t0.elapsed_time(t1)
     ms_per_step = gpu_ms / steps
 
+    # "cold": the same steps with the shared expert and the router weights
+    # rotated over 16 copies (16 x 25.2 MB, more than the 256 MB memory-side
+    # cache), so that they too stream from HBM every step as the routed
+    # experts do; the line above is the layer as deployed, where those two
+    # are read every step and may stay cached
+    cold = None
+    if not args.no_cold and w.has_shared:
+        ncopy = 16
+        sh_c = moe.ExpertBlocks(ncopy, bits, w.H, w.I)
+        for c in range(ncopy):
+            sh_c.data[c].copy_(L.shared.data[0])
+        wr_c = L.w_router.unsqueeze(0).repeat(ncopy, 1, 1).contiguous()
+        b_c = L.bias.unsqueeze(0).repeat(ncopy, 1).contiguous() if L.bias is not None else None
+        bb = L.buffers(T)
+        torch.cuda.synchronize()
+
+        def step_cold(i):
+            c = i % ncopy
+            moe.moe_layer_forward(ctx, bits, xs[i % npool], L.experts.table, sh_c.struct(c), w.k, w.I, bb["out"],
+                                  w_router=None if zs[i % npool] is not None else wr_c[c],
+                                  bias=None if b_c is None else b_c[c], logits=zs[i % npool],
+                                  routed_scale=L.routed_scale, top_p=L.top_p, topk_idx=bb["idx"], topk_w=bb["w"],
+                                  xq=bb["xq"], sx=bb["sx"], y_slots=bb["y"])
+
+        ncold = max(npool, ncopy)
+        for i in range(ncold):
+            step_cold(i)
+        torch.cuda.synchronize()
+        ctx.check()
+        ctx.set_stream(cap)
+        graph_c = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_c, stream=cap):
+            for i in range(ncold):
+                step_cold(i)
+        ctx.set_stream(torch.cuda.current_stream())
+        creps = max(1, steps // ncold)
+        for _ in range(warm_reps):
+            graph_c.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(creps):
+            graph_c.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ctx.check()
+        cms = t0.elapsed_time(t1) / (creps * ncold)
+        cold = {"copies": ncopy, "ms_per_step": round(cms, 5), "tokens_per_s": round(T / (cms / 1e3), 2),
+                "effective_weight_GBps": round(avg_bytes / (cms / 1e3) / 1e9, 1)}
+        log(f"[bench] cold (16 rotated copies of the shared expert and router): {cms * 1e3:.1f} us/step")
+        del graph_c, sh_c, wr_c
+
     # per-kernel durations: hipEvents the library records around each of its
     # kernels on the context stream (eager calls over the same pool)
     ctx.enable_timing(True)
@@ -581,6 +634,7 @@ def main():
         "expert_ffn": {"kernels": kernel_names["gateup"] + " + " + kernel_names["down"],
                        "algorithmic_bytes": round(avg_bytes), "avg_us": round(ffn_ms * 1e3, 2),
                        "achieved_GBps": round(ffn_gbps, 1), "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4)},
+        "cold": cold,
         "stream_read_probe": probe,
         "router_bytes": router_bytes,
         # one call reads each distinct expert once, however many of its tokens
