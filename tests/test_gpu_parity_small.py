@@ -235,13 +235,15 @@ def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, kern, bits, T, H, I, E, 
 def test_ffn_mfma_tile_boundaries(moe, ctx, orc, syn, bits):
     """Per-expert token counts on both sides of every tile boundary of the
     matrix-core kernels (tiles of 64 tokens, one-block tiles for remainders of
-    up to 16): 16, 17, 64, 65, 80, 81, 1 and 0 tokens; the shared expert takes
-    all 324 (5 full tiles and a remainder of 4)."""
-    counts = [16, 17, 64, 65, 80, 81, 1, 0]
+    up to 16): 16, 17, 64, 65, 80, 81, 128, 129, 144, 145, 1 and 0 tokens (145
+    = two full tiles and a third of 17); the shared expert takes all 870 (13
+    full tiles and a remainder of 38, itself a full-size tile)."""
+    counts = [16, 17, 64, 65, 80, 81, 128, 129, 144, 145, 1, 0]
     ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
     rng = np.random.default_rng(7)
     idx = rng.permutation(ids).reshape(-1, 1).astype(np.int32)
-    check_ffn_intermediates(moe, ctx, orc, syn, "mfma", bits, idx.shape[0], 128, 64, 8, 1, idx, seed=45 + bits)
+    check_ffn_intermediates(moe, ctx, orc, syn, "mfma", bits, idx.shape[0], 128, 64, len(counts), 1, idx,
+                            seed=45 + bits)
 
 
 def test_ffn_kernel_selector_rejects_unknown_values(moe, ctx):
