@@ -204,7 +204,6 @@ __global__ __launch_bounds__(kThreads) void act_field_kernel(const int8_t *xq, i
 // token's row, so the 16 tokens a read instruction spans hit distinct banks.
 // The weight pieces stream through registers D steps ahead.
 // ---------------------------------------------------------------------------
-constexpr int kSlice = 512;  // bytes of codes per token and slice
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ void lds_st16(lds_u8 *p, uint4 v) {
   *reinterpret_cast<__attribute__((address_space(3))) moe_u32x4 *>(p) = moe_u32x4{v.x, v.y, v.z, v.w};
@@ -214,32 +213,35 @@ __device__ __forceinline__ uint4 lds_ld16(const lds_u8 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int BITS, int MB, int NM, int NB, int D0>
+template <int BITS, int MB, int NM, int NB, int D0, int SL>
 __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB], const int8_t *abase, int astride,
                                              const int *ids, int rowbytes, lds_u8 *lds, v4i (&acc)[MB][NM][NB]) {
   constexpr int EPC = QFmt<BITS>::kEpc, NS = EPC / 16;
-  constexpr int SC = kSlice / (4 * EPC);  // steps per slice
+  constexpr int SC = SL / (4 * EPC);      // steps per slice
   constexpr int D = D0 < SC ? D0 : SC;    // weight steps in flight (a divisor of SC)
-  constexpr int NI = MB * 2;              // staged units per thread and slice
-  constexpr int BUF = MB * 16 * kSlice;   // bytes per slice buffer
+  constexpr int UPT = SL / 16;            // 16-byte units per token and slice
+  constexpr int TPI = kThreads / UPT;     // tokens one staging round covers
+  constexpr int NI = MB * 16 / TPI;       // staged units per thread and slice
+  constexpr int BUF = MB * 16 * SL;       // bytes per slice buffer
+  static_assert(NI >= 1 && NI * TPI == MB * 16, "whole tokens per staging round");
   static_assert(SC % D == 0, "the weight buffers rotate within a slice");
   const int tid = threadIdx.x, grp = (tid & (MOE_WAVE - 1)) >> 4, r16 = tid & 15;
   const int nq = rowbytes / 16;
   const int nch = (nq + 3) / 4;
   const int nsl = (nch + SC - 1) / SC;
-  // staging: this thread moves unit su of tokens (tid >> 5) + 8 i
-  const int su = tid & 31;
+  // staging: this thread moves unit su of tokens tid / UPT + TPI i
+  const int su = tid % UPT;
   const int8_t *srow[NI];
   int sdst[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int t = (tid >> 5) + 8 * i;
+    const int t = tid / UPT + TPI * i;
     srow[i] = abase + (int64_t)ids[t] * astride;
-    sdst[i] = t * kSlice + ((su ^ (t & 7)) << 4);
+    sdst[i] = t * SL + ((su ^ (t & 7)) << 4);
   }
   uint4 st[NI];
   auto aload = [&](int sl) {
-    const int o = min(sl * kSlice + su * 16, astride - 16);  // past the row: a re-read, never used
+    const int o = min(sl * SL + su * 16, astride - 16);  // past the row: a re-read, never used
 #pragma unroll
     for (int i = 0; i < NI; ++i) st[i] = ldg16(srow[i] + o, 0);
   };
@@ -274,7 +276,7 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int t = mb * 16 + r16, u = cc * NS * 4 + s * 4 + grp;
-          x[mb] = as_v4i(lds_ld16(cur + t * kSlice + ((u ^ (t & 7)) << 4)), kv);
+          x[mb] = as_v4i(lds_ld16(cur + t * SL + ((u ^ (t & 7)) << 4)), kv);
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m)
@@ -314,6 +316,17 @@ __device__ __forceinline__ int stage_tokens(const MArgs &a, const Ex &ex, int m0
   return nt;
 }
 
+// MB = 4: the tiles of more than 16 tokens; MB = 1: the one-block tiles
+// (SL: bytes of codes per token and staged slice)
+template <int MB>
+struct GuShape {
+  static constexpr int NB = MB == 4 ? 2 : 1, D = 2, SL = 512;
+};
+template <int MB>
+struct DnShape {
+  static constexpr int NB = 2, D = 2, SL = 512;
+};
+
 // ---------------------------------------------------------------------------
 // gate + up: a workgroup takes 64 NB rows of each, a wave 16 NB
 // ---------------------------------------------------------------------------
@@ -346,7 +359,7 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = acc[mb][1][nb] = v4i{0, 0, 0, 0};
-  tile_mma_lds<BITS, MB, 2, NB, D>(wrow, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
+  tile_mma_lds<BITS, MB, 2, NB, D, GuShape<MB>::SL>(wrow, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
   // lane holds tokens 4*grp + r of each block, row row[nb]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -378,16 +391,6 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8
     }
 }
 
-// MB = 4: the tiles of more than 16 tokens; MB = 1: the one-block tiles
-template <int MB>
-struct GuShape {
-  static constexpr int NB = MB == 4 ? 2 : 1, D = MB == 4 ? 2 : 4;
-};
-template <int MB>
-struct DnShape {
-  static constexpr int NB = 2, D = MB == 4 ? 2 : 4;
-};
-
 // Workgroup -> (tile, row tile). Workgroups go to the 8 XCDs in turn (id mod
 // 8), each XCD with its own L2; the mapping gives every XCD a contiguous range
 // of the (tile, row tile) order, row tiles fastest, so the workgroups that
@@ -407,7 +410,7 @@ __device__ __forceinline__ bool xcd_work(int n_units, int ntiles, int &unit, int
 template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
-  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * kSlice];
+  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * GuShape<MB>::SL];
   lds_u8 *abuf = (lds_u8 *)abuf_s;
   int u, nt;
   if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
@@ -532,7 +535,7 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = v4i{0, 0, 0, 0};
-  tile_mma_lds<BITS, MB, 1, NB, D>(wrow, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
+  tile_mma_lds<BITS, MB, 1, NB, D, DnShape<MB>::SL>(wrow, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -555,7 +558,7 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
 template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads) void dn_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
-  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * kSlice];
+  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * DnShape<MB>::SL];
   lds_u8 *abuf = (lds_u8 *)abuf_s;
   int u, nt;
   if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
