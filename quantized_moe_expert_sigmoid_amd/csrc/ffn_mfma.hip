@@ -407,6 +407,27 @@ __device__ __forceinline__ bool xcd_work(int n_units, int ntiles, int &unit, int
   return true;
 }
 
+// Full-size tiles: within one expert's block of (tile, row tile) work, the
+// tiles vary fastest, so the workgroups that multiply the same weight rows
+// against the expert's different token tiles are dispatched one after another
+// on one XCD and read those rows from its L2 at about the same time. An
+// expert's tiles are consecutive in the tile list; unit u of the plain order
+// finds its expert's first tile (u minus its own index j) and the expert's
+// tile count (from its token count, as the bucketing formed them).
+__device__ __forceinline__ void expert_major(const MArgs &a, int ntiles, int &u, int &nt) {
+  const int L = u * ntiles + nt;
+  const int2 un = a.units[u];
+  const int j = un.y / kUnitM;
+  const int u0 = u - j;
+  const int na = *a.n_active;
+  const int c = un.x < na ? a.counts[a.active[un.x]] : a.T;  // past the active list: the shared expert
+  const int rem = c % kUnitM;
+  const int n = c / kUnitM + (rem > kUnitSmall ? 1 : 0);
+  const int local = L - u0 * ntiles;
+  nt = local / n;
+  u = u0 + (local - nt * n);
+}
+
 template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
@@ -414,6 +435,7 @@ __global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a, int ntiles) 
   lds_u8 *abuf = (lds_u8 *)abuf_s;
   int u, nt;
   if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
+  if constexpr (MB == 4) expert_major(a, ntiles, u, nt);
   const int2 un = a.units[MB == 4 ? u : a.ubig_max + u];
   gu_tile<BITS, MB, GuShape<MB>::NB, GuShape<MB>::D>(a, tt_s, abuf, un.x, un.y, nt);
 }
@@ -562,6 +584,7 @@ __global__ __launch_bounds__(kThreads) void dn_mfma_kernel(MArgs a, int ntiles) 
   lds_u8 *abuf = (lds_u8 *)abuf_s;
   int u, nt;
   if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
+  if constexpr (MB == 4) expert_major(a, ntiles, u, nt);
   const int2 un = a.units[MB == 4 ? u : a.ubig_max + u];
   dn_tile<BITS, MB, DnShape<MB>::NB, DnShape<MB>::D>(a, tt_s, abuf, un.x, un.y, nt);
 }
