@@ -498,7 +498,7 @@ moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts
   a.dbg_on = ctx->dbg_on ? 1 : 0;
   st = launch_bucket(ctx, topk_idx, T, k, E, const_cast<int32_t *>(a.counts), const_cast<int32_t *>(a.offsets),
                      const_cast<int32_t *>(a.perm), expert_bits, bits, const_cast<int32_t *>(a.active),
-                     const_cast<int32_t *>(a.n_active), nullptr, nullptr, 0, 0);
+                     const_cast<int32_t *>(a.n_active), nullptr, nullptr, 0, 0, kUnitSmall);
   if (st) return st;
   const int dmax = (int)std::min<int64_t>(E, (int64_t)T * k) + a.has_shared;
   switch (bits) {

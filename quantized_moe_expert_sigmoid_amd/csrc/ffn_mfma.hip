@@ -61,6 +61,7 @@ struct MArgs {
   const int2 *units;      // tiles: [ubig_max] of up to 64 tokens, then the one-block tiles
   const int32_t *n_units;  // [2] tiles of each kind
   int ubig_max;
+  int small_max;           // remainders of up to this many tokens are one-block tiles
   float *A;      // [P][I] SwiGLU intermediate, P = T (k + 1)
   int8_t *aq;    // [P][astride] its codes, field order
   int32_t *aqs;  // [P] code sums
@@ -422,7 +423,7 @@ __device__ __forceinline__ void expert_major(const MArgs &a, int ntiles, int &u,
   const int na = *a.n_active;
   const int c = un.x < na ? a.counts[a.active[un.x]] : a.T;  // past the active list: the shared expert
   const int rem = c % kUnitM;
-  const int n = c / kUnitM + (rem > kUnitSmall ? 1 : 0);
+  const int n = c / kUnitM + (rem > a.small_max ? 1 : 0);
   const int local = L - u0 * ntiles;
   nt = local / n;
   u = u0 + (local - nt * n);
@@ -688,8 +689,12 @@ moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *ex
   a.y = y_slots;
   a.dbg = ctx->dbg;
   a.dbg_on = ctx->dbg_on ? 1 : 0;
+  // when experts average many tokens (k T / E >= 32), a remainder becomes a
+  // full-size tile too: it then runs beside the expert's other tiles and
+  // shares their weight rows through L2 instead of streaming them again
+  a.small_max = (int64_t)T * k >= 32 * (int64_t)E ? 0 : kUnitSmall;
   st = launch_bucket(ctx, topk_idx, T, k, E, counts, offsets, perm, expert_bits, bits, active, nact, units, nunits,
-                     ubig, has_shared);
+                     ubig, has_shared, a.small_max);
   if (st) return st;
   if (T == 0) return MOE_OK;
   switch (bits) {

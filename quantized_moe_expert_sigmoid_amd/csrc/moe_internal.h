@@ -119,12 +119,14 @@ moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts
                              const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
                              int T, int H, int I, int E, int k, float *y_slots);
 // Token tiles of the matrix-core expert FFN: up to kUnitM tokens of one
-// expert per tile; a remainder of at most kUnitSmall tokens is a one-block tile.
+// expert per tile; a remainder of at most kUnitSmall tokens is a one-block tile
+// (when experts average few tokens; otherwise every tile is full-size).
 constexpr int kUnitM = 64;
 constexpr int kUnitSmall = 16;
 moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
                          int32_t *perm, const uint8_t *expert_bits, int want_bits, int32_t *active,
-                         int32_t *n_active, int2 *units, int32_t *n_units, int ubig_max, int has_shared);
+                         int32_t *n_active, int2 *units, int32_t *n_units, int ubig_max, int has_shared,
+                         int small_max);
 bool expert_ffn_mfma_supported(int bits, int H, int I);
 moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                                   const uint8_t *expert_bits, const int8_t *xq, const float *sx,

@@ -169,11 +169,12 @@ struct BucketArgs {
   // nullable: token tiles of the active experts (and of the shared expert,
   // active position n_active, when has_shared) for the matrix-core FFN:
   // units[0 .. n_units[0]) are (active position, first token) of tiles of up
-  // to kUnitM tokens holding more than kUnitSmall of them; units[ubig_max +
-  // 0 .. n_units[1]) the remainders of 1..kUnitSmall tokens
+  // to kUnitM tokens holding more than small_max of them; units[ubig_max +
+  // 0 .. n_units[1]) the remainders of 1..small_max tokens (small_max 0: none)
   int2 *units;
   int32_t *n_units;
   int ubig_max, has_shared;
+  int small_max;
 };
 
 // Exclusive prefix sum over the workgroup's threads (in thread order): an
@@ -265,8 +266,8 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
   __syncthreads();
   if (a.units) {
     const int rem = c % kUnitM;
-    const int nb = act ? c / kUnitM + (rem > kUnitSmall ? 1 : 0) : 0;
-    const int ns = (act && rem > 0 && rem <= kUnitSmall) ? 1 : 0;
+    const int nb = act ? c / kUnitM + (rem > a.small_max ? 1 : 0) : 0;
+    const int ns = (act && rem > 0 && rem <= a.small_max) ? 1 : 0;
     const int bb = block_exclusive_scan(nb, tmp);
     const int sb = block_exclusive_scan(ns, tmp);
     for (int j = 0; j < nb; ++j) a.units[bb + j] = make_int2(apos, j * kUnitM);
@@ -281,11 +282,11 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
     int nbig = tot[0], nsmall = tot[1];
     if (a.has_shared) {  // the shared expert takes every token
       const int sr = T % kUnitM;
-      const int snb = T / kUnitM + (sr > kUnitSmall ? 1 : 0);
+      const int snb = T / kUnitM + (sr > a.small_max ? 1 : 0);
       for (int j = tid; j < snb; j += kBThreads) a.units[nbig + j] = make_int2(tot[2], j * kUnitM);
-      if (tid == 0 && sr > 0 && sr <= kUnitSmall) a.units[a.ubig_max + nsmall] = make_int2(tot[2], (T / kUnitM) * kUnitM);
+      if (tid == 0 && sr > 0 && sr <= a.small_max) a.units[a.ubig_max + nsmall] = make_int2(tot[2], (T / kUnitM) * kUnitM);
       nbig += snb;
-      nsmall += (sr > 0 && sr <= kUnitSmall) ? 1 : 0;
+      nsmall += (sr > 0 && sr <= a.small_max) ? 1 : 0;
     }
     if (tid == 0) {
       a.n_units[0] = nbig;
@@ -340,10 +341,11 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
 
 moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
                          int32_t *perm, const uint8_t *expert_bits, int want_bits, int32_t *active,
-                         int32_t *n_active, int2 *units, int32_t *n_units, int ubig_max, int has_shared) {
+                         int32_t *n_active, int2 *units, int32_t *n_units, int ubig_max, int has_shared,
+                         int small_max) {
   BucketArgs a{idx,    T,        k,         E,         counts,     offsets,   perm,
                expert_bits, want_bits, active, n_active, ctx->dev_small, units, n_units,
-               ubig_max, has_shared};
+               ubig_max, has_shared, small_max};
   {
     MoeTimer tm_(ctx, MOE_STAGE_BUCKET);
     hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBThreads), 0, ctx->stream, a);
@@ -355,7 +357,7 @@ moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, 
 moe_status launch_bucket_public(moe_ctx *ctx, const int32_t *topk_idx, int T, int k, int E, int32_t *counts,
                                 int32_t *offsets, int32_t *perm) {
   return launch_bucket(ctx, topk_idx, T, k, E, counts, offsets, perm, nullptr, 0, nullptr, nullptr, nullptr, nullptr,
-                       0, 0);
+                       0, 0, kUnitSmall);
 }
 
 moe_status launch_router(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x, const float *w_router,

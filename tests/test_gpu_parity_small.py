@@ -231,18 +231,21 @@ def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, kern, bits, T, H, I, E, 
     check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, seed=40 + bits)
 
 
+@pytest.mark.parametrize("E", [64, 12])
 @pytest.mark.parametrize("bits", [4, 8, 2])
-def test_ffn_mfma_tile_boundaries(moe, ctx, orc, syn, bits):
+def test_ffn_mfma_tile_boundaries(moe, ctx, orc, syn, bits, E):
     """Per-expert token counts on both sides of every tile boundary of the
-    matrix-core kernels (tiles of 64 tokens, one-block tiles for remainders of
-    up to 16): 16, 17, 64, 65, 80, 81, 128, 129, 144, 145, 1 and 0 tokens (145
-    = two full tiles and a third of 17); the shared expert takes all 870 (13
-    full tiles and a remainder of 38, itself a full-size tile)."""
+    matrix-core kernels (tiles of 64 tokens): 16, 17, 64, 65, 80, 81, 128, 129,
+    144, 145, 1 and 0 tokens (145 = two full tiles and a third of 17); the
+    shared expert takes all 870 (13 full tiles and a remainder of 38). With 64
+    experts (52 of them unused: few tokens per expert on average) a remainder
+    of up to 16 tokens is a one-block tile; with 12 (many per expert) every
+    remainder is a full-size tile beside the expert's other tiles."""
     counts = [16, 17, 64, 65, 80, 81, 128, 129, 144, 145, 1, 0]
     ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
     rng = np.random.default_rng(7)
     idx = rng.permutation(ids).reshape(-1, 1).astype(np.int32)
-    check_ffn_intermediates(moe, ctx, orc, syn, "mfma", bits, idx.shape[0], 128, 64, len(counts), 1, idx,
+    check_ffn_intermediates(moe, ctx, orc, syn, "mfma", bits, idx.shape[0], 128, 64, E, 1, idx,
                             seed=45 + bits)
 
 
