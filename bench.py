@@ -110,8 +110,8 @@ def pmc_summary(bench_fetch, bench_write, copy_fetch, copy_write, out_md) -> Non
     with open(out_md, "w") as fh:
         fh.write("# HBM traffic per launch: single-token kernels, GLM decode (T=1, int4)\n\n")
         fh.write("Commands (from the repository root, each counter in a run of its own):\n\n")
-        fh.write("    rocprofv3 --pmc FETCH_SIZE -d <dir> --output-format csv -- python3 bench.py --steps 64 --warmup 64 --no-cpu-baseline --no-probe\n")
-        fh.write("    rocprofv3 --pmc WRITE_SIZE -d <dir> --output-format csv -- python3 bench.py --steps 64 --warmup 64 --no-cpu-baseline --no-probe\n")
+        fh.write("    rocprofv3 --pmc FETCH_SIZE -d <dir> --output-format csv -- python3 bench.py --steps 64 --warmup 64 --no-cpu-baseline --no-probe --no-cold\n")
+        fh.write("    rocprofv3 --pmc WRITE_SIZE -d <dir> --output-format csv -- python3 bench.py --steps 64 --warmup 64 --no-cpu-baseline --no-probe --no-cold\n")
         fh.write(f"    rocprofv3 --pmc FETCH_SIZE -d <dir> --output-format csv -- python3 bench.py --copy-probe {COPY_PROBE_MB}\n")
         fh.write(f"    rocprofv3 --pmc WRITE_SIZE -d <dir> --output-format csv -- python3 bench.py --copy-probe {COPY_PROBE_MB}\n")
         fh.write("    python3 bench.py --pmc-summary <4 dirs> profiles/traffic_glm_decode_t1_int4.md\n\n")
