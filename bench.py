@@ -218,21 +218,43 @@ def stack_pool_bench(args) -> None:
         nl, nt = (layer + 1, t - 1) if layer + 1 < Lr else (0, t)
         return nl, (traces[nl][nt] if nt >= 0 else None)
 
+    # The per-token loop issues the library calls with arguments marshalled
+    # once (as a serving loop would): the same calls the checked wrappers
+    # make, without their per-call validation in Python.
+    import ctypes
+    lib_, ck = moe.lib(), moe._ck
+    ctx_h, pool_h = ctx.handle, pool.handle
+    tr_host = [np.ascontiguousarray(tr, dtype=np.int32) for tr in traces]
+    tr_host_p = [a.ctypes.data for a in tr_host]
+    tr_dev_p = [a.data_ptr() for a in trace_dev]
+    tab_p = [a.data_ptr() for a in tables]
+    wid_p = [a.data_ptr() for a in widths]
+    sh_w = [shared.struct(layer) for layer in range(Lr)]
+    sh_ref = [ctypes.byref(x_) for x_ in sh_w]
+    xs_p = [a.data_ptr() for a in xs]
+    xq_p, sx_p, y_p, out_p, wts_p = xq.data_ptr(), sx.data_ptr(), y.data_ptr(), out.data_ptr(), wts.data_ptr()
+    nmiss = ctypes.c_int(0)
+    rowb = 4 * k
+
     def run(t0_, t1_):
         for t in range(t0_, t1_):
             for layer in range(Lr):
-                idx = trace_dev[layer][t:t + 1]
-                moe.moe_quantize_act_i8(ctx, xs[(t + layer) % 16], xq, sx)
-                pool.prepare(layer, traces[layer][t:t + 1], tables[layer], widths[layer])
+                idx_p = tr_dev_p[layer] + t * rowb
+                ck(lib_.moe_quantize_act_i8(ctx_h, xs_p[(t + layer) % 16], 1, H, xq_p, sx_p))
+                ck(lib_.moe_pool_prepare(pool_h, layer, tr_host_p[layer] + t * rowb, 1, k, tab_p[layer],
+                                         wid_p[layer], ctypes.byref(nmiss)))
                 if args.stack_prefetch:
                     nl, ids = predicted(t, layer)
                     if ids is not None:
                         pool.prefetch(nl, ids)
                 if hot8:
-                    moe.moe_expert_ffn_q8(ctx, tables[layer], None, widths[layer], xq, sx, idx, H, I, E, y)
-                moe.moe_expert_ffn_q4(ctx, tables[layer], shared.struct(layer), widths[layer], xq, sx, idx, H, I, E, y)
-                moe.moe_expert_ffn_q2(ctx, tables[layer], None, widths[layer], xq, sx, idx, H, I, E, y)
-                moe.moe_combine(ctx, y, wts, True, out)
+                    ck(lib_.moe_expert_ffn_q8(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H, I,
+                                              E, k, y_p))
+                ck(lib_.moe_expert_ffn_q4(ctx_h, tab_p[layer], sh_ref[layer], wid_p[layer], xq_p, sx_p, idx_p, 1, H,
+                                          I, E, k, y_p))
+                ck(lib_.moe_expert_ffn_q2(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H, I, E, k,
+                                          y_p))
+                ck(lib_.moe_combine(ctx_h, y_p, wts_p, 1, k, H, 1, out_p))
 
     tc = time.perf_counter()
     run(0, args.stack_warmup)
@@ -268,6 +290,16 @@ def stack_pool_bench(args) -> None:
             acc_den += len(actual)
     hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
     h2d = st1["bytes_h2d"] - st0["bytes_h2d"]
+    # expert bytes the FFN read from HBM over the measured tokens: every
+    # requested expert at its full width (demoted copies counted at the
+    # narrower width, from the tier counters) plus the shared expert per layer
+    full_bytes = 0
+    for t in range(args.stack_warmup, ntok):
+        for layer in range(Lr):
+            for e in set(traces[layer][t].tolist()):
+                full_bytes += bsz[width_of(ranks[layer][e])]
+    demoted_uses = ts1["demoted_uses"] - ts0["demoted_uses"]
+    served = full_bytes - demoted_uses * (bsz[4] - bsz[2]) + n * Lr * bsz[4]
     # H2D probe: one pinned 1 GB host-to-device copy
     hp = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
     dp = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -290,6 +322,10 @@ def stack_pool_bench(args) -> None:
         "hit_rate": round(hits / max(1, hits + misses), 5),
         "misses_per_token": round(misses / n, 3),
         "h2d_GBps": round(h2d / dt / 1e9, 2),
+        # expert bytes served from HBM per second (routed at their resident
+        # width, plus the shared expert), next to the refill rate above;
+        # demoted requests are counted as int4 -> int2
+        "hbm_expert_GBps": round(served / dt / 1e9, 1),
         "h2d_probe_GBps": round(probe, 2),
         "prefetch": {"enabled": bool(args.stack_prefetch), "issued": pf1["issued"] - pf0["issued"],
                      "used": pf1["used"] - pf0["used"],

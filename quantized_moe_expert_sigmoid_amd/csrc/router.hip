@@ -298,8 +298,9 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
   // stable placement, tokens in chunks of 32 W (one bit per token and expert
   // in LDS): an entry's rank in its expert's list is the expert's count from
   // earlier chunks, plus its set bits in earlier words, plus those below it
-  int W = kBitmapWords / E;  // words per expert
+  int W = kBitmapWords / E;  // words per expert: as many as the LDS holds, at most 64,
   if (W > 64) W = 64;
+  if (W > (T + 31) / 32) W = (T + 31) / 32;  // and no more than the tokens need
   const int TC = 32 * W;
   for (int c0 = 0; c0 < T; c0 += TC) {
     const int nt = min(TC, T - c0);
