@@ -205,8 +205,11 @@ def stack_pool_bench(args) -> None:
     trace_dev = [torch.from_numpy(tr).cuda() for tr in traces]
     wts = torch.full((1, k), 1.0 / k, dtype=torch.float32, device="cuda")
     xs = [torch.from_numpy(wl.hidden_fp32(w, 1, batch=i)).cuda() for i in range(16)]
-    tables = [torch.zeros((E, 6), dtype=torch.int64, device="cuda") for _ in range(Lr)]
-    widths = [torch.zeros((E,), dtype=torch.uint8, device="cuda") for _ in range(Lr)]
+    # per layer: the expert table and, right after it, the widths (one
+    # host-to-device copy per prepare carries both)
+    tw = [torch.zeros((E * 48 + E,), dtype=torch.uint8, device="cuda") for _ in range(Lr)]
+    tables = [b_[:E * 48].view(torch.int64).view(E, 6) for b_ in tw]
+    widths = [b_[E * 48:] for b_ in tw]
     xq = torch.empty((1, H), dtype=torch.int8, device="cuda")
     sx = torch.empty((1,), dtype=torch.float32, device="cuda")
     y = torch.zeros((1, k + 1, H), dtype=torch.float32, device="cuda")

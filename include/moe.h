@@ -292,7 +292,8 @@ moe_status moe_pool_register(moe_pool *pool, int layer, int expert, int bits, co
  * in order, the layer's table: table_dev DEVICE moe_expert_w [E] (resident
  * experts point into the slab, the others are zero) and bits_dev DEVICE
  * uint8 [E] (the experts' widths, 0 when absent; nullable) -- ready for
- * moe_expert_ffn_q* with expert_bits = bits_dev. n_miss_host (nullable): this
+ * moe_expert_ffn_q* with expert_bits = bits_dev (when bits_dev starts right
+ * after the E table entries, one copy carries both). n_miss_host (nullable): this
  * call's misses; an id of -1 (a slot dropped by top-p) is skipped.
  * MOE_EINVAL for another id outside [0, E) or an unregistered
  * expert; MOE_EPOOL when the slab cannot hold this call's experts beside the

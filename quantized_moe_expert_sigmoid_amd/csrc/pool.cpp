@@ -377,8 +377,15 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
       bits[e] = 0;
     }
   }
-  MOE_HIP(hipMemcpyAsync(table_dev, tab, (size_t)E * sizeof(moe_expert_w), hipMemcpyHostToDevice, p->ctx->stream));
-  if (bits_dev) MOE_HIP(hipMemcpyAsync(bits_dev, bits, (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
+  // the widths sit right after the table in the staging buffer: when the
+  // caller's bits_dev directly follows table_dev too, one copy carries both
+  const size_t tab_bytes = (size_t)E * sizeof(moe_expert_w);
+  if (bits_dev == reinterpret_cast<uint8_t *>(table_dev) + tab_bytes) {
+    MOE_HIP(hipMemcpyAsync(table_dev, tab, tab_bytes + (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
+  } else {
+    MOE_HIP(hipMemcpyAsync(table_dev, tab, tab_bytes, hipMemcpyHostToDevice, p->ctx->stream));
+    if (bits_dev) MOE_HIP(hipMemcpyAsync(bits_dev, bits, (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
+  }
   MOE_HIP(hipEventRecord(p->staging_ev[si], p->ctx->stream));
   p->staging_used[si] = true;
   return MOE_OK;

@@ -224,7 +224,10 @@ __device__ __forceinline__ bool token_ids(const BucketArgs &a, int64_t t, int id
   return ok;
 }
 
+constexpr int kIdsCache = 4096;  // (token, slot) ids kept in LDS after the first read
+
 __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
+  __shared__ int ids_s[kIdsCache];
   __shared__ int cnt[1024];
   __shared__ int off[1025];
   __shared__ int cursor[1024];
@@ -233,6 +236,17 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
   __shared__ int before[kBitmapWords];  // entries of the expert in earlier words of the chunk
   const int tid = threadIdx.x;
   const int E = a.E, k = a.k, T = a.T;
+  // the width filter is read now, so its latency overlaps the counting
+  const int eb = (a.expert_bits && tid < E) ? a.expert_bits[tid] : 0;
+  // small calls keep the validated ids in LDS for the later passes
+  const bool cached = (int64_t)T * k <= kIdsCache;
+  auto ids_of = [&](int t, int (&ids)[16]) {
+    if (cached) {
+      for (int j = 0; j < k; ++j) ids[j] = ids_s[t * k + j];
+    } else {
+      token_ids(a, t, ids);
+    }
+  };
 
   for (int e = tid; e < 1024; e += kBThreads) {
     cnt[e] = 0;
@@ -243,8 +257,10 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
   for (int t = tid; t < T; t += kBThreads) {
     int ids[16];
     bad |= !token_ids(a, t, ids);
-    for (int j = 0; j < k; ++j)
+    for (int j = 0; j < k; ++j) {
       if (ids[j] >= 0) atomicAdd(&cnt[ids[j]], 1);
+      if (cached) ids_s[t * k + j] = ids[j];
+    }
   }
   if (bad) atomicOr(a.err, (uint32_t)ERRF_BAD_INDEX);
   __syncthreads();
@@ -259,7 +275,7 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
     off[E] = ex + c;
     a.offsets[E] = ex + c;
   }
-  const int act = (tid < E && c > 0 && (!a.expert_bits || a.expert_bits[tid] == a.want_bits)) ? 1 : 0;
+  const int act = (tid < E && c > 0 && (!a.expert_bits || eb == a.want_bits)) ? 1 : 0;
   const int apos = block_exclusive_scan(act, tmp);
   if (a.active && act) a.active[apos] = tid;
   if (a.n_active && tid == E - 1) *a.n_active = apos + act;
@@ -308,7 +324,7 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
     __syncthreads();
     for (int tl = tid; tl < nt; tl += kBThreads) {
       int ids[16];
-      token_ids(a, c0 + tl, ids);
+      ids_of(c0 + tl, ids);
       for (int j = 0; j < k; ++j)
         if (ids[j] >= 0) atomicOr(&bitmap[ids[j] * W + (tl >> 5)], 1u << (tl & 31));
     }
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
     __syncthreads();
     for (int tl = tid; tl < nt; tl += kBThreads) {
       int ids[16];
-      token_ids(a, c0 + tl, ids);
+      ids_of(c0 + tl, ids);
       const int w = tl >> 5;
       const uint32_t below = (1u << (tl & 31)) - 1u;
       for (int j = 0; j < k; ++j) {

@@ -299,3 +299,25 @@ def test_pool_tiers_bit_equal(moe, ctx, syn):
         if c >= 24 and 0 in widths:  # pinned before call 24: full width from then on
             assert widths[0] == 8, (c, widths)
     pool.close()
+
+
+def test_pool_table_and_widths_in_one_buffer(moe, ctx, syn):
+    """When the widths start right after the table, prepare writes both with
+    one copy; the contents equal those written into separate buffers."""
+    E = 6
+    b4, h4 = make_blocks(moe, ctx, syn, 4, E, seed=39)
+    b2, h2 = make_blocks(moe, ctx, syn, 2, E, seed=39)
+    pool = moe.MoePool(ctx, 3 * b4.block_bytes, 1, E, H, I)
+    for e in range(E):
+        pool.register(0, e, 4 if e % 2 == 0 else 2, h4[e] if e % 2 == 0 else h2[e])
+    sep_t = torch.zeros((E, 6), dtype=torch.int64, device="cuda")
+    sep_b = torch.zeros((E,), dtype=torch.uint8, device="cuda")
+    one = torch.zeros((E * 48 + E,), dtype=torch.uint8, device="cuda")
+    one_t, one_b = one[:E * 48].view(torch.int64).view(E, 6), one[E * 48:]
+    for ids in ([[0, 1]], [[2, 3]], [[4, 1]]):
+        pool.prepare(0, np.array(ids, np.int32), sep_t, sep_b)
+        pool.prepare(0, np.array(ids, np.int32), one_t, one_b)  # all hits: the same residency
+        torch.cuda.synchronize()
+        assert torch.equal(sep_t, one_t) and torch.equal(sep_b, one_b)
+        assert set(np.nonzero(one_b.cpu().numpy())[0]) >= set(np.array(ids).ravel())
+    pool.close()
