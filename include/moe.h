@@ -122,11 +122,13 @@ const char *moe_last_error(void);
 int moe_abi_version(void);
 /* Which kernels compute the expert FFN of moe_expert_ffn_q* and of the
  * multi-token path of moe_layer_forward. MOE_FFN_AUTO (the default): the
- * int8 matrix-core kernels for two or more tokens, the vector dot-product
- * kernels for one. MOE_FFN_DOT4: always the vector kernels. MOE_FFN_MFMA:
- * always the matrix-core kernels. Both take every shape the FFN entry points
- * accept and compute the same exact integer sums and the same fp32 epilogue,
- * so their results are bit-identical. Any other value: MOE_EINVAL.
+ * int8 matrix-core kernels for two or more tokens; for one token the
+ * single-token kernels of the whole-layer decode path (without its router
+ * and combine) where the shape fits them, else the vector dot-product
+ * kernels. MOE_FFN_DOT4: always the vector kernels. MOE_FFN_MFMA: always the
+ * matrix-core kernels. All take every shape they are chosen for and compute
+ * the same exact integer sums and the same fp32 epilogue, so their results
+ * are bit-identical. Any other value: MOE_EINVAL.
  * Host-only setting; enqueues nothing. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_DOT4 = 1, MOE_FFN_MFMA = 2 };
 moe_status moe_ctx_set_ffn_kernels(moe_ctx *ctx, int which);
@@ -201,8 +203,10 @@ moe_status moe_bucket_tokens(moe_ctx *ctx, const int32_t *topk_idx, int T, int k
  * are left untouched), so a mixed-precision layer is one call per width.
  * xq int8 [T][H], sx fp32 [T]: from moe_quantize_act_i8. topk_idx int32
  * [T][k]; an id of -1 (a slot dropped by top-p) names no expert: its slot is
- * not computed and not written; any other id outside [0, E) is an error
- * reported by moe_ctx_check. y_slots fp32 [T][k+1][H] (slot k is the shared
+ * not computed and not written; any other id outside [0, E), or an id
+ * repeated within one token's k slots, is an error reported by
+ * moe_ctx_check (that slot, the later one of a repeated pair, is not
+ * written). y_slots fp32 [T][k+1][H] (slot k is the shared
  * expert's; it is written only when shared != NULL). */
 moe_status moe_expert_ffn_q4(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
                              const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,

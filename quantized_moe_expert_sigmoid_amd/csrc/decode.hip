@@ -40,6 +40,11 @@
 //     order as moe_combine). A CU keeps only some tens of KB of loads in
 //     flight and a wave that queues more stalls at issue, so the kernels
 //     queue about that much at a time.
+// The per-step expert FFN of one token (routing given by the caller) runs K2,
+// K3 and K4 without K1 and without the combine: K2 then builds the slot table
+// from the given ids instead of the top-k, keeping only the slots whose expert
+// has the call's width (the others, and ids of -1, are left to their own
+// call), and K4 writes y of those slots and of the shared expert only.
 // Kernel boundaries order the four steps: no atomics across workgroups, no
 // cross-workgroup waits (contended device-scope atomics serialise at the
 // memory side). Streaming loads are branch-free: a lane whose chunk index
@@ -56,8 +61,8 @@ constexpr int kMaxSlots = 9;                       // top-k <= 8 plus the shared
 constexpr int kMaxSlices = 16;                     // K slices of the router logits
 constexpr int kMaxE = 1024;
 constexpr int kMaxX4 = 8;        // float4 of x per thread in the max pass: H <= 8192
-constexpr int kMaxIDown = 4096;
-constexpr int kMaxPairsWg = kFfnThreads;  // routed row pairs per gate/up workgroup (one per thread)  // intermediate held in LDS by the down kernel
+constexpr int kMaxIDown = 4096;            // intermediate held in LDS by the down kernel
+constexpr int kMaxPairsWg = kFfnThreads;  // routed row pairs per gate/up workgroup (one per thread)
 
 // One slot of the token: the expert's weights and its routing weight.
 struct SlotEntry {
@@ -192,6 +197,12 @@ struct GateUpT1Args {
   float *A;  // [S][I]
   moe_debug_bufs dbg;
   int dbg_on;
+  // given routing (the per-step expert FFN): the slots' ids, and the width
+  // filter (experts of another width are left to that width's call)
+  const int32_t *given_idx;  // [k]
+  const uint8_t *expert_bits;
+  int want_bits;
+  uint32_t *err;  // error flags: an id out of range or repeated
 };
 
 template <int BITS, int JG, int NB>
@@ -274,7 +285,7 @@ __device__ __forceinline__ void gu_compute(int n, int lane0, int lane, const GuB
   }
 }
 
-template <int BITS, int JG, int NB>
+template <int BITS, int JG, int NB, bool GIVEN>
 __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) {
   static_assert(NB == 1, "routed pairs are taken one at a time");
   constexpr int OFF = QFmt<BITS>::kOff;
@@ -310,7 +321,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   float zs[kPer][kMaxSlices], bs[kPer];
 #pragma unroll
   for (int m = 0; m < kPer; ++m) {
-    if (m == 0 || a.E > m * kFfnThreads) {
+    if (!GIVEN && (m == 0 || a.E > m * kFfnThreads)) {
       const int e = min(tid + m * kFfnThreads, a.E - 1);
 #pragma unroll
       for (int s = 0; s < kMaxSlices / 2; ++s) zs[m][s] = gptr(zsrc)[(int64_t)min(s, nsum - 1) * a.E + e];
@@ -325,7 +336,8 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   uint4 exr[kExpPer];
 #pragma unroll
   for (int i = 0; i < kExpPer; ++i)
-    if (i < 2 || 3 * a.E > i * kFfnThreads) exr[i] = ldg16(a.experts, min(tid + i * kFfnThreads, 3 * a.E - 1));
+    if (!GIVEN && (i < 2 || 3 * a.E > i * kFfnThreads))
+      exr[i] = ldg16(a.experts, min(tid + i * kFfnThreads, 3 * a.E - 1));
   constexpr int EPC = QFmt<BITS>::kEpc;
   uint4 xraw[JG][EPC / 16];
 #pragma unroll
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
 #pragma unroll
   for (int i = 0; i < kExpPer; ++i) {
     const int idx = tid + i * kFfnThreads;
-    if (idx < 3 * a.E) reinterpret_cast<uint4 *>(exp_s)[idx] = exr[i];
+    if (!GIVEN && idx < 3 * a.E) reinterpret_cast<uint4 *>(exp_s)[idx] = exr[i];
   }
   ActChunk<BITS> xr[JG];
   int xs_lane = 0;
@@ -377,7 +389,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
 #pragma unroll
   for (int m = 0; m < kPer; ++m) {
     const int e = tid + m * kFfnThreads;
-    if (m > 0 && a.E <= m * kFfnThreads) break;
+    if (GIVEN || (m > 0 && a.E <= m * kFfnThreads)) break;
     float z = zs[m][0];  // slices in order
 #pragma unroll
     for (int s = 1; s < kMaxSlices; ++s)
@@ -392,8 +404,90 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   }
   __syncthreads();
 
+  // ---- given routing: the slot table from the ids (wave 0). The global
+  // table keeps the slots in their own order (a slot without work -- another
+  // width, or -1 -- gets expert -1 and valid pointers of a slot with work);
+  // in LDS the slots with work come first, each with its own index ----
+  if constexpr (GIVEN) {
+    if (wave == 0) {
+      const int e = lane < a.k ? a.given_idx[lane] : -1;
+      bool valid = e == -1 || (e >= 0 && e < a.E);
+      bool act = e >= 0 && e < a.E;
+      for (int j = 0; j < a.k; ++j) {  // a repeated id is an error, and computed for its first slot only
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        if (j < lane && act && ej == e) {
+          act = false;
+          valid = false;
+        }
+      }
+      const uint64_t bad = __ballot(!valid);
+      if (bad && blockIdx.x == 0 && lane == 0) atomicOr(a.err, 1u);
+      if (act && a.expert_bits) act = a.expert_bits[e] == a.want_bits;
+      const uint64_t m = __ballot(act);
+      const int na = __popcll(m);
+      const int first = na ? __ffsll((unsigned long long)m) - 1 : 0;
+      const int e_first = na ? __builtin_amdgcn_readlane(e, first) : -1;
+      auto row_of = [&](int ex, uint4 (&row)[3]) {
+        if (ex >= 0) {
+#pragma unroll
+          for (int q = 0; q < 3; ++q) row[q] = ldg16(a.experts + ex, q);
+        } else if (a.has_shared) {
+          const uint64_t pp[6] = {(uint64_t)a.shared.gate, (uint64_t)a.shared.up, (uint64_t)a.shared.down,
+                                  (uint64_t)a.shared.s_gate, (uint64_t)a.shared.s_up, (uint64_t)a.shared.s_down};
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+            row[q] = make_uint4((uint32_t)pp[2 * q], (uint32_t)(pp[2 * q] >> 32), (uint32_t)pp[2 * q + 1],
+                                (uint32_t)(pp[2 * q + 1] >> 32));
+        } else {
+#pragma unroll
+          for (int q = 0; q < 3; ++q) row[q] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      };
+      uint4 own[3], dummy[3];
+      row_of(act ? e : e_first, own);
+      row_of(e_first, dummy);
+      if (lane < a.k) {
+        const uint4 tag = make_uint4(0u, (uint32_t)(act ? e : -1), (uint32_t)lane, 0u);
+        if (blockIdx.x == 0) {
+          uint4 *gdst = reinterpret_cast<uint4 *>(a.slots + lane);
+#pragma unroll
+          for (int q = 0; q < 3; ++q) gdst[q] = own[q];
+          gdst[3] = tag;
+        }
+        if (act) {
+          uint4 *dst = reinterpret_cast<uint4 *>(slot_s + __popcll(m & ((1ull << lane) - 1ull)));
+#pragma unroll
+          for (int q = 0; q < 3; ++q) dst[q] = own[q];
+          dst[3] = tag;
+        }
+        if (lane >= na) {  // entries past the slots with work: valid pointers, never given pairs
+          uint4 *dst = reinterpret_cast<uint4 *>(slot_s + lane);
+#pragma unroll
+          for (int q = 0; q < 3; ++q) dst[q] = dummy[q];
+          dst[3] = make_uint4(0u, (uint32_t)-1, (uint32_t)lane, 0u);
+        }
+      } else if (lane == a.k && a.has_shared) {
+        row_of(-1, own);
+        const uint4 tag = make_uint4(__float_as_uint(1.0f), (uint32_t)-1, (uint32_t)a.k, 0u);
+        uint4 *dst = reinterpret_cast<uint4 *>(slot_s + lane);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) dst[q] = own[q];
+        dst[3] = tag;
+        if (blockIdx.x == 0) {
+          uint4 *gdst = reinterpret_cast<uint4 *>(a.slots + lane);
+#pragma unroll
+          for (int q = 0; q < 3; ++q) gdst[q] = own[q];
+          gdst[3] = tag;
+        }
+      }
+      if (lane == 0) nkeep_s = na;
+    }
+    __syncthreads();
+    if (nkeep_s == 0 && !a.has_shared) return;  // nothing for this width
+  }
+
   // ---- top-k and the slot table (wave 0) ----
-  if (wave == 0) {
+  if (!GIVEN && wave == 0) {
     const int my_id = (a.E <= 4 * MOE_WAVE) ? wave_topk4(key_s, a.E, a.k, lane) : wave_topk16(key_s, a.E, a.k, lane);
     const float my_sig = lane < a.k ? sig_s[my_id] : 0.0f;
     float sum = 0.0f;  // in rank order
@@ -517,7 +611,9 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
     const float g = (float)gi * sg * sxv;
     const float u = (float)ui * su * sxv;
     const float av = moe_silu_f32(g) * u;
-    const int64_t o = (int64_t)slot * a.I + i;
+    // with given routing the LDS slots with work come first: each keeps its own index
+    const int own = (GIVEN && slot < a.k) ? slot_s[slot].pad[0] : slot;
+    const int64_t o = (int64_t)own * a.I + i;
     a.A[o] = av;
     if (a.dbg_on) {
       if (a.dbg.accg) a.dbg.accg[o] = gi;
@@ -593,6 +689,7 @@ struct RequantT1Args {
   float *sa;       // [S] per-slot scale
   moe_debug_bufs dbg;
   int dbg_on;
+  int given;  // given routing: a routed slot with expert -1 has no work here
 };
 
 // Slot blockIdx.x: sa = max|a|/127 and aq = rint(a/sa) (the activation rule),
@@ -609,6 +706,7 @@ __global__ __launch_bounds__(kRqThreads) void requant_t1_kernel(RequantT1Args a)
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
   const int s = blockIdx.x;
+  if (a.given && s < a.k && a.slots[s].expert == -1) return;  // another width's slot: left alone
   const float4 *As = reinterpret_cast<const float4 *>(a.A + (int64_t)s * a.I);
   const int ng = a.I / G;
   // the thread's groups stay in registers between the two passes
@@ -703,7 +801,7 @@ struct DownT1Args {
 
 constexpr int kAq16 = (kMaxSlots * kMaxIDown / 16 + kFfnThreads - 1) / kFfnThreads;  // 16-byte code pieces per thread
 
-template <int BITS, int JD, int RB>
+template <int BITS, int JD, int RB, bool GIVEN>
 __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args a) {
   constexpr int OFF = QFmt<BITS>::kOff;
   constexpr int EPC = QFmt<BITS>::kEpc;
@@ -723,6 +821,10 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   const uint8_t *down_l = a.slots[ls].w.down;
   const float *sdown_l = a.slots[ls].w.s_down;
   const float w_l = a.slots[ls].weight;
+  // given routing: only the slots with work here are written (a slot of
+  // another width belongs to that width's call)
+  const bool act_l = GIVEN ? (lane < S && (lane == a.k ? a.has_shared != 0 : a.slots[ls].expert != -1)) : lane < S;
+  if (GIVEN && __ballot(act_l) == 0) return;
   const int aqsum_l = a.sums[ls];
   const float sa_l = a.sa[ls];
   // every slot's codes (S*I bytes), unconditional loads: pieces past the end
@@ -810,16 +912,18 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
         }
       }
       const float yv = (float)mine * bt.sd[b] * sa_l;
-      if (lane < S) {
+      if (act_l) {
         a.y[(int64_t)lane * a.H + r] = yv;
         if (a.dbg_on && a.dbg.accd) a.dbg.accd[(int64_t)lane * a.H + r] = mine;
       }
-      // combine in slot order: shared first, then j = 0..k-1
-      float acc = a.has_shared ? readlane_f(yv, a.k) : 0.0f;
+      if constexpr (!GIVEN) {
+        // combine in slot order: shared first, then j = 0..k-1
+        float acc = a.has_shared ? readlane_f(yv, a.k) : 0.0f;
 #pragma unroll
-      for (int s = 0; s < kMaxSlots - 1; ++s)
-        if (s < a.k) acc = __builtin_fmaf(readlane_f(w_l, s), readlane_f(yv, s), acc);
-      if (lane == 0) a.out[r] = acc;
+        for (int s = 0; s < kMaxSlots - 1; ++s)
+          if (s < a.k) acc = __builtin_fmaf(readlane_f(w_l, s), readlane_f(yv, s), acc);
+        if (lane == 0) a.out[r] = acc;
+      }
     }
   };
   for (int rb = r0; rb < r1; rb += 2 * RB) {
@@ -834,15 +938,15 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
-template <int BITS, int JG, int NB>
+template <int BITS, int JG, int NB, bool GIVEN = false>
 moe_status launch_gu(moe_ctx *ctx, const GateUpT1Args &g, int nwg) {
-  moe_launch(ctx, MOE_STAGE_GATEUP, gateup_t1_kernel<BITS, JG, NB>, dim3(nwg), dim3(kFfnThreads), g);
+  moe_launch(ctx, MOE_STAGE_GATEUP, gateup_t1_kernel<BITS, JG, NB, GIVEN>, dim3(nwg), dim3(kFfnThreads), g);
   MOE_CHECK_LAUNCH("gateup_t1_kernel");
   return MOE_OK;
 }
-template <int BITS, int JD, int RB>
+template <int BITS, int JD, int RB, bool GIVEN = false>
 moe_status launch_dn(moe_ctx *ctx, const DownT1Args &d, int nwg) {
-  moe_launch(ctx, MOE_STAGE_DOWN, down_combine_t1_kernel<BITS, JD, RB>, dim3(nwg), dim3(kFfnThreads), d);
+  moe_launch(ctx, MOE_STAGE_DOWN, down_combine_t1_kernel<BITS, JD, RB, GIVEN>, dim3(nwg), dim3(kFfnThreads), d);
   MOE_CHECK_LAUNCH("down_combine_t1_kernel");
   return MOE_OK;
 }
@@ -996,5 +1100,91 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
     case 4: return launch_dn<4, T1Shape<4>::JD, T1Shape<4>::RB>(ctx, d, nwg);
     case 8: return launch_dn<8, T1Shape<8>::JD, T1Shape<8>::RB>(ctx, d, nwg);
     default: return launch_dn<2, T1Shape<2>::JD, T1Shape<2>::RB>(ctx, d, nwg);
+  }
+}
+
+// The expert FFN of one token with its routing given (ids, activation codes
+// and scale from the caller): the gate/up, requantisation and down kernels
+// above without the router and the combine. Slot j's output goes to y_slots
+// row j for every valid id whose expert has this width (all of them without a
+// width filter), the shared expert's to row k; the other rows are left as
+// they were. An id outside [0, E), or one repeated within the token, raises the
+// bad-index flag and gives no output (the later copy of a repeated id).
+moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
+                         const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
+                         int H, int I, int E, int k, float *y_slots) {
+  const int S = k + (shared ? 1 : 0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = moe_round_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_slots = take(sizeof(SlotEntry) * kMaxSlots), o_A = take(sizeof(float) * S * I),
+               o_aq = take((size_t)S * I), o_sum = take(4 * S), o_sa = take(4 * S);
+  void *scr = nullptr;
+  moe_status st = moe_scratch(ctx, off, &scr);
+  if (st) return st;
+  char *base = static_cast<char *>(scr);
+  SlotEntry *slots = reinterpret_cast<SlotEntry *>(base + o_slots);
+
+  GateUpT1Args g{};
+  g.E = E; g.k = k; g.ks = 1;
+  g.experts = experts;
+  if (shared) g.shared = *shared;
+  g.has_shared = shared ? 1 : 0;
+  g.slots = slots;
+  g.xq = xq;
+  g.sx = sx;
+  g.H = H; g.I = I; g.S = S;
+  g.A = reinterpret_cast<float *>(base + o_A);
+  g.dbg = ctx->dbg;
+  g.dbg_on = ctx->dbg_on ? 1 : 0;
+  g.given_idx = topk_idx;
+  g.expert_bits = expert_bits;
+  g.want_bits = bits;
+  g.err = ctx->dev_small;
+  const int nwg = ctx->n_cu;
+  switch (bits) {
+    case 4: st = launch_gu<4, T1Shape<4>::JG, T1Shape<4>::NB, true>(ctx, g, nwg); break;
+    case 8: st = launch_gu<8, T1Shape<8>::JG, T1Shape<8>::NB, true>(ctx, g, nwg); break;
+    default: st = launch_gu<2, T1Shape<2>::JG, T1Shape<2>::NB, true>(ctx, g, nwg); break;
+  }
+  if (st) return st;
+
+  RequantT1Args q{};
+  q.A = g.A;
+  q.slots = slots;
+  q.k = k;
+  q.I = I;
+  q.S = S;
+  q.aqf = reinterpret_cast<uint32_t *>(base + o_aq);
+  q.sums = reinterpret_cast<int *>(base + o_sum);
+  q.sa = reinterpret_cast<float *>(base + o_sa);
+  q.dbg = ctx->dbg;
+  q.dbg_on = ctx->dbg_on ? 1 : 0;
+  q.given = 1;
+  switch (bits) {
+    case 4: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<4>, dim3(S), dim3(kRqThreads), q); break;
+    case 8: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<8>, dim3(S), dim3(kRqThreads), q); break;
+    default: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<2>, dim3(S), dim3(kRqThreads), q); break;
+  }
+  MOE_CHECK_LAUNCH("requant_t1_kernel");
+
+  DownT1Args d{};
+  d.slots = slots;
+  d.aqf = q.aqf;
+  d.sums = q.sums;
+  d.sa = q.sa;
+  d.H = H; d.I = I; d.S = S; d.k = k;
+  d.has_shared = shared ? 1 : 0;
+  d.y = y_slots;
+  d.out = nullptr;
+  d.dbg = ctx->dbg;
+  d.dbg_on = ctx->dbg_on ? 1 : 0;
+  switch (bits) {
+    case 4: return launch_dn<4, T1Shape<4>::JD, T1Shape<4>::RB, true>(ctx, d, nwg);
+    case 8: return launch_dn<8, T1Shape<8>::JD, T1Shape<8>::RB, true>(ctx, d, nwg);
+    default: return launch_dn<2, T1Shape<2>::JD, T1Shape<2>::RB, true>(ctx, d, nwg);
   }
 }

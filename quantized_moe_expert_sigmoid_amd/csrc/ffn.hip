@@ -457,6 +457,9 @@ moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts
                     bits);
   if (mfma_ok && (ctx->ffn_kernels == MOE_FFN_MFMA || (ctx->ffn_kernels == MOE_FFN_AUTO && T >= 2)))
     return launch_expert_ffn_mfma(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots);
+  // one token: the single-token kernels (no bucketing pass)
+  if (T == 1 && ctx->ffn_kernels == MOE_FFN_AUTO && decode_t1_supported(bits, H, I, k, shared ? 1 : 0, ctx->n_cu))
+    return launch_ffn_t1(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, H, I, E, k, y_slots);
   const int64_t P = (int64_t)T * (k + 1);
   FfnArgs a{};
   a.tiles1 = I / rows_per_wg_gu(bits);

@@ -138,6 +138,9 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
                            const float *w_router, const float *bias, const moe_expert_w *experts,
                            const moe_expert_w *shared, int H, int I, float *out, int32_t *topk_idx, float *topk_w,
                            int8_t *xq, float *sx, float *y_slots);
+moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
+                         const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
+                         int H, int I, int E, int k, float *y_slots);
 
 // ---------------------------------------------------------------------------
 // Device side

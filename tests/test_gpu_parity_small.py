@@ -184,9 +184,10 @@ def random_routing(syn, T, E, k, seed):
     return np.argsort(-z, axis=1, kind="stable")[:, :k].astype(np.int32)
 
 
-def check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, seed):
-    """Every intermediate of every (token, slot) pair bit-equal to the oracle's."""
-    log(f"ffn kernels={kern} bits={bits} T={T} H={H} I={I} E={E} k={k}")
+def check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, seed, with_shared=True):
+    """Every intermediate of every (token, slot) pair bit-equal to the oracle's
+    (slots of id -1, and the shared slot without a shared expert, untouched)."""
+    log(f"ffn kernels={kern} bits={bits} T={T} H={H} I={I} E={E} k={k} shared={with_shared}")
     blocks, shared, oexp, osh = make_experts(moe, orc, syn, bits, H, I, E, seed=seed)
     x = syn.hidden(seed + 1, T, H)
     xq_o, sx_o = orc.quantize_act(x)
@@ -197,11 +198,12 @@ def check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, 
                aq=torch.zeros((P, I), dtype=torch.int8, device="cuda"),
                sa=torch.zeros((P,), dtype=torch.float32, device="cuda"),
                accd=torch.zeros((P, H), dtype=torch.int32, device="cuda"))
-    y = torch.zeros((T, k + 1, H), dtype=torch.float32, device="cuda")
+    y = torch.full((T, k + 1, H), 7.0, dtype=torch.float32, device="cuda")
     ctx.set_debug(dbg)
     ctx.set_ffn_kernels(kern)
     try:
-        moe.FFN_BY_BITS[bits](ctx, blocks.table, shared.struct(0), None, dev(xq_o), dev(sx_o), dev(idx), H, I, E, y)
+        sh = shared.struct(0) if with_shared else None
+        moe.FFN_BY_BITS[bits](ctx, blocks.table, sh, None, dev(xq_o), dev(sx_o), dev(idx), H, I, E, y)
         ctx.check()
     finally:
         ctx.set_debug(None)
@@ -210,6 +212,9 @@ def check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, 
     yg = host(y)
     for t in range(T):
         for j in range(k + 1):
+            if (j == k and not with_shared) or (j < k and idx[t, j] == -1):
+                assert np.all(yg[t, j] == 7.0) and not got["accg"][t * (k + 1) + j].any(), (t, j)
+                continue
             ex = osh if j == k else oexp[idx[t, j]]
             r = orc.expert_token(ex, xq_o[t], float(sx_o[t]))
             p = t * (k + 1) + j
@@ -229,6 +234,62 @@ def check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, 
 def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, kern, bits, T, H, I, E, k):
     idx = random_routing(syn, T, E, k, 42)
     check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, seed=40 + bits)
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("H,I,E,k,shared", [(128, 64, 8, 2, True), (512, 192, 16, 8, True), (256, 128, 8, 3, False),
+                                            (1024, 448, 40, 6, False)])
+def test_ffn_one_token(moe, ctx, orc, syn, bits, H, I, E, k, shared):
+    """One token through the per-step expert FFN: the single-token kernels with
+    the routing given (the default for T = 1) and the vector kernels, every
+    intermediate bit-exact against the oracle; then a token with dropped slots
+    (id -1), whose slots stay untouched."""
+    idx = random_routing(syn, 1, E, k, 90 + k)
+    for kern in ("auto", "dot4"):
+        check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, 1, H, I, E, k, idx, seed=91 + bits, with_shared=shared)
+    idx[0, 1:k:2] = -1
+    check_ffn_intermediates(moe, ctx, orc, syn, "auto", bits, 1, H, I, E, k, idx, seed=91 + bits, with_shared=shared)
+
+
+def test_ffn_one_token_nothing_to_do(moe, ctx, orc, syn):
+    """A token whose slots are all -1 (or of another width) and no shared
+    expert: the call writes nothing."""
+    H, I, E, k = 256, 128, 8, 3
+    blocks, _, _, _ = make_experts(moe, orc, syn, 4, H, I, E, seed=95)
+    xq_o, sx_o = orc.quantize_act(syn.hidden(96, 1, H))
+    y = torch.full((1, k + 1, H), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn_q4(ctx, blocks.table, None, None, dev(xq_o), dev(sx_o), dev(np.full((1, k), -1, np.int32)),
+                          H, I, E, y)
+    eb = dev(np.full(E, 2, np.uint8))
+    moe.moe_expert_ffn_q4(ctx, blocks.table, None, eb, dev(xq_o), dev(sx_o), dev(np.array([[0, 3, 5]], np.int32)),
+                          H, I, E, y)
+    ctx.check()
+    assert np.all(host(y) == 7.0)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_ffn_repeated_and_bad_ids(moe, ctx, orc, syn, T):
+    """An id repeated within a token, or outside [0, E), is reported by the
+    context check; the slots with valid first ids are still computed and the
+    offending slots are left untouched."""
+    H, I, E, k = 256, 128, 8, 3
+    blocks, shared, oexp, osh = make_experts(moe, orc, syn, 4, H, I, E, seed=97)
+    xq_o, sx_o = orc.quantize_act(syn.hidden(98, T, H))
+    for bad, ok in (([2, 5, 2], [0, 1]), ([2, 9, 5], [0, 2]), ([-3, 5, 1], [1, 2]), ([4, 4, 4], [0])):
+        idx = np.repeat(np.array([bad], np.int32), T, axis=0)
+        y = torch.full((T, k + 1, H), 7.0, dtype=torch.float32, device="cuda")
+        moe.moe_expert_ffn_q4(ctx, blocks.table, shared.struct(0), None, dev(xq_o), dev(sx_o), dev(idx), H, I, E, y)
+        with pytest.raises(moe.MoeError):
+            ctx.check()
+        yg = host(y)
+        for t in range(T):
+            for j in range(k):
+                if j in ok:
+                    r = orc.expert_token(oexp[idx[t, j]], xq_o[t], float(sx_o[t]))
+                    assert np.array_equal(yg[t, j], r["y"]), (bad, t, j)
+                else:
+                    assert np.all(yg[t, j] == 7.0), (bad, t, j)
+            assert np.array_equal(yg[t, k], orc.expert_token(osh, xq_o[t], float(sx_o[t]))["y"])
 
 
 @pytest.mark.parametrize("E", [64, 12])
@@ -272,10 +333,12 @@ def test_ffn_without_shared_leaves_slot(moe, ctx, orc, syn):
         assert np.array_equal(yg[t, 0], r["y"])
 
 
-def test_ffn_mixed_precision_filter(moe, ctx, orc, syn):
+@pytest.mark.parametrize("T", [9, 1])
+def test_ffn_mixed_precision_filter(moe, ctx, orc, syn, T):
     """expert_bits selects which experts a width's entry point computes: a
-    mixed int4/int2 layer is two calls writing disjoint slots."""
-    H, I, E, k, T = 256, 128, 8, 3, 9
+    mixed int4/int2 layer is two calls writing disjoint slots (one token: the
+    single-token kernels, several: the matrix-core kernels)."""
+    H, I, E, k = 256, 128, 8, 3
     b4, sh4, o4, osh4 = make_experts(moe, orc, syn, 4, H, I, E, seed=60)
     b2, _, o2, _ = make_experts(moe, orc, syn, 2, H, I, E, seed=60)
     bits = np.array([4, 2, 4, 2, 2, 4, 4, 2], np.uint8)
