@@ -206,10 +206,15 @@ def stack_pool_bench(args) -> None:
     wts = torch.full((1, k), 1.0 / k, dtype=torch.float32, device="cuda")
     xs = [torch.from_numpy(wl.hidden_fp32(w, 1, batch=i)).cuda() for i in range(16)]
     # per layer: the expert table and, right after it, the widths (one
-    # host-to-device copy per prepare carries both)
-    tw = [torch.zeros((E * 48 + E,), dtype=torch.uint8, device="cuda") for _ in range(Lr)]
-    tables = [b_[:E * 48].view(torch.int64).view(E, 6) for b_ in tw]
-    widths = [b_[E * 48:] for b_ in tw]
+    # host-to-device copy carries both): by default the pool's own tables,
+    # copied only when a layer's table changed; --stack-caller-tables: the
+    # caller's buffers, copied on every call
+    if args.stack_caller_tables:
+        tw = [torch.zeros((E * 48 + E,), dtype=torch.uint8, device="cuda") for _ in range(Lr)]
+        tab_p = [b_.data_ptr() for b_ in tw]
+        wid_p = [b_.data_ptr() + E * 48 for b_ in tw]
+    else:
+        tab_p, wid_p = map(list, zip(*(pool.layer_table(layer) for layer in range(Lr))))
     xq = torch.empty((1, H), dtype=torch.int8, device="cuda")
     sx = torch.empty((1,), dtype=torch.float32, device="cuda")
     y = torch.zeros((1, k + 1, H), dtype=torch.float32, device="cuda")
@@ -230,8 +235,6 @@ def stack_pool_bench(args) -> None:
     tr_host = [np.ascontiguousarray(tr, dtype=np.int32) for tr in traces]
     tr_host_p = [a.ctypes.data for a in tr_host]
     tr_dev_p = [a.data_ptr() for a in trace_dev]
-    tab_p = [a.data_ptr() for a in tables]
-    wid_p = [a.data_ptr() for a in widths]
     sh_w = [shared.struct(layer) for layer in range(Lr)]
     sh_ref = [ctypes.byref(x_) for x_ in sh_w]
     xs_p = [a.data_ptr() for a in xs]
@@ -270,6 +273,7 @@ def stack_pool_bench(args) -> None:
     st0 = pool.stats()
     pf0 = pool.prefetch_stats()
     ts0 = pool.tier_stats()
+    tb0 = pool.table_stats()
     tm = time.perf_counter()
     run(args.stack_warmup, ntok)
     torch.cuda.synchronize()
@@ -278,6 +282,7 @@ def stack_pool_bench(args) -> None:
     st1 = pool.stats()
     pf1 = pool.prefetch_stats()
     ts1 = pool.tier_stats()
+    tb1 = pool.table_stats()
     n = args.stack_tokens
     # accuracy of the read-ahead predictor over the measured tokens: the share
     # of each layer's experts that the previous token used there
@@ -340,6 +345,9 @@ def stack_pool_bench(args) -> None:
                   "demoted_share_of_requests": round((ts1["demoted_uses"] - ts0["demoted_uses"])
                                                      / max(1, hits + misses), 5),
                   "h2d_bytes_saved": ts1["bytes_saved"] - ts0["bytes_saved"]},
+        # the layers' expert tables: host-to-device copies made and skipped (unchanged)
+        "table_copies": {"tables": "caller" if args.stack_caller_tables else "pool",
+                         "made": tb1["copies"] - tb0["copies"], "skipped": tb1["skipped"] - tb0["skipped"]},
     }
     log(f"[stack] {n} tokens in {dt:.2f}s: {n / dt:.1f} tokens/s, hit rate {res['hit_rate']}, "
         f"{res['misses_per_token']} misses/token, H2D {res['h2d_GBps']} GB/s (probe {res['h2d_probe_GBps']} GB/s), "
@@ -433,6 +441,9 @@ def main():
     ap.add_argument("--stack-hot", type=int, default=192)
     ap.add_argument("--stack-hot8", type=int, default=0,
                     help="the layer's N most popular experts at int8 (within --stack-hot)")
+    ap.add_argument("--stack-caller-tables", action="store_true",
+                    help="the layers' expert tables in the caller's buffers (copied on every call) rather than "
+                         "the pool's own (copied when changed)")
     ap.add_argument("--stack-demote", action="store_true",
                     help="give every int8 / int4 expert a narrower block and load it on misses under pressure")
     ap.add_argument("--stack-tokens", type=int, default=1000)

@@ -277,7 +277,8 @@ typedef struct moe_pool moe_pool;
 moe_status moe_pool_create(moe_ctx *ctx, size_t capacity_bytes, int n_layers, int n_experts, int H, int I,
                            moe_pool **out);
 /* Wait for the pool's copies and for the context stream (whose kernels may
- * read the slab), then free everything the pool owns. */
+ * read the slab), then free everything the pool owns. The pool's context
+ * must still exist: destroy pools before their context. */
 void moe_pool_destroy(moe_pool *pool);
 /* Register expert (layer, expert) at `bits` in {8,4,2}: block_host holds its
  * block (bytes must equal moe_expert_block_layout(bits, H, I)); the caller
@@ -297,7 +298,12 @@ moe_status moe_pool_register(moe_pool *pool, int layer, int expert, int bits, co
  * experts point into the slab, the others are zero) and bits_dev DEVICE
  * uint8 [E] (the experts' widths, 0 when absent; nullable) -- ready for
  * moe_expert_ffn_q* with expert_bits = bits_dev (when bits_dev starts right
- * after the E table entries, one copy carries both). n_miss_host (nullable): this
+ * after the E table entries, one copy carries both). table_dev may be the
+ * layer's own table of the pool (moe_pool_layer_table; bits_dev then NULL or
+ * that table's widths): the pool copies into it only when the layer's table
+ * bytes changed since its last copy there (an expert of the layer loaded,
+ * evicted or re-loaded), so at a high hit rate most calls copy nothing. A
+ * pointer into another layer's own table is MOE_EINVAL. n_miss_host (nullable): this
  * call's misses; an id of -1 (a slot dropped by top-p) is skipped.
  * MOE_EINVAL for another id outside [0, E) or an unregistered
  * expert; MOE_EPOOL when the slab cannot hold this call's experts beside the
@@ -305,6 +311,15 @@ moe_status moe_pool_register(moe_pool *pool, int layer, int expert, int bits, co
  * table_dev = bits_dev = NULL. */
 moe_status moe_pool_prepare(moe_pool *pool, int layer, const int32_t *topk_idx_host, int T, int k,
                             moe_expert_w *table_dev, uint8_t *bits_dev, int *n_miss_host);
+/* The pool's own device table of `layer` (a pool with a context): DEVICE
+ * moe_expert_w [E] at *table_dev, its widths uint8 [E] right after it at
+ * *bits_dev (nullable). Allocated with the pool, freed by moe_pool_destroy;
+ * written only by moe_pool_prepare of that layer (callers only read it).
+ * Host-only. */
+moe_status moe_pool_layer_table(moe_pool *pool, int layer, moe_expert_w **table_dev, uint8_t **bits_dev);
+/* Table copies of moe_pool_prepare: made, and skipped because the layer's
+ * own table already held the bytes. Host-only. */
+moe_status moe_pool_table_stats(const moe_pool *pool, uint64_t *copies, uint64_t *skipped);
 /* Read-ahead ([P-load]; remio.ai, "Colibri shows how to run GLM-5.2 on a
  * low-spec PC", section "The RAM wall became a storage problem": the engine
  * predicts the next layer's routing and fetches those experts early). Starts

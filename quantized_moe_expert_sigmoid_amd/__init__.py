@@ -14,7 +14,9 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 import threading
+import weakref
 
 import torch
 
@@ -95,6 +97,8 @@ _SIGS = {
     "moe_pool_set_demotion": (_i32, [_vp, _i32]),
     "moe_pool_tier_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 3),
     "moe_pool_resident_bits": (_i32, [_vp, _i32, _i32]),
+    "moe_pool_table_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 2),
+    "moe_pool_layer_table": (_i32, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
 }
 
 
@@ -153,13 +157,18 @@ class MoeCtx:
         _ck(lib().moe_ctx_create(device, ctypes.c_void_p(s.cuda_stream), ctypes.byref(h)))
         self.handle = h
         self._dbg_keep = None
+        self._pools = weakref.WeakSet()  # pools on this context: closed before it
 
     def close(self):
         if self.handle:
+            for p in list(self._pools):
+                p.close()
             lib().moe_ctx_destroy(self.handle)
             self.handle = None
 
     def __del__(self):
+        if sys.is_finalizing():  # the HIP runtime may already be gone
+            return
         try:
             self.close()
         except Exception:
@@ -406,6 +415,8 @@ class MoePool:
                                   H, I, ctypes.byref(h)))
         self.handle = h.value
         self._blocks = {}  # keeps the registered host blocks alive
+        if ctx is not None:
+            ctx._pools.add(self)
 
     def close(self):
         if self.handle:
@@ -414,6 +425,8 @@ class MoePool:
             self._blocks.clear()
 
     def __del__(self):
+        if sys.is_finalizing():  # the HIP runtime may already be gone
+            return
         try:
             self.close()
         except Exception:
@@ -438,21 +451,24 @@ class MoePool:
     def prepare(self, layer: int, topk_idx_host, table: torch.Tensor | None = None,
                 bits: torch.Tensor | None = None) -> int:
         """topk_idx_host: int32 [T][k] on the host (numpy array or CPU tensor).
-        table: device int64 [E][6] (moe_expert_w rows), bits: device uint8 [E].
-        Returns the number of misses."""
+        table: device int64 [E][6] (moe_expert_w rows), bits: device uint8 [E];
+        or the raw addresses from layer_table(layer). Returns the number of
+        misses."""
         import numpy as np
         idx = np.ascontiguousarray(topk_idx_host if not isinstance(topk_idx_host, torch.Tensor)
                                    else topk_idx_host.cpu().numpy(), dtype=np.int32)
         if idx.ndim != 2:
             raise ValueError("topk_idx_host must be [T][k]")
         T, k = idx.shape
-        if table is not None:
+        if table is not None and not isinstance(table, int):
             _dev(table, torch.int64, "table", (self.n_experts, 6))
-        if bits is not None:
+        if bits is not None and not isinstance(bits, int):
             _dev(bits, torch.uint8, "bits", (self.n_experts,))
+        tp = table if isinstance(table, int) else _ptr(table)
+        bp = bits if isinstance(bits, int) else _ptr(bits)
         n = ctypes.c_int(0)
         _ck(lib().moe_pool_prepare(self.handle, layer, idx.ctypes.data if idx.size else None, T, k,
-                                   _ptr(table), _ptr(bits), ctypes.byref(n)))
+                                   tp, bp, ctypes.byref(n)))
         return n.value
 
     def stats(self):
@@ -528,6 +544,19 @@ class MoePool:
         v = [ctypes.c_uint64() for _ in range(3)]
         _ck(lib().moe_pool_tier_stats(self.handle, *(ctypes.byref(x) for x in v)))
         return {"demoted_loads": v[0].value, "demoted_uses": v[1].value, "bytes_saved": v[2].value}
+
+    def table_stats(self):
+        v = [ctypes.c_uint64() for _ in range(2)]
+        _ck(lib().moe_pool_table_stats(self.handle, *(ctypes.byref(x) for x in v)))
+        return {"copies": v[0].value, "skipped": v[1].value}
+
+    def layer_table(self, layer: int):
+        """The pool's own device table of `layer`: (table address, widths
+        address), raw device pointers (the widths follow the table). Passing
+        them to prepare lets it skip copies of an unchanged table."""
+        t, b = _vp(), _vp()
+        _ck(lib().moe_pool_layer_table(self.handle, layer, ctypes.byref(t), ctypes.byref(b)))
+        return t.value, b.value
 
     def resident_bits(self, layer: int, expert: int) -> int:
         """Width of the resident copy (8, 4, 2), 0 when not resident."""

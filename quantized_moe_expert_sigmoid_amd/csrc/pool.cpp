@@ -33,7 +33,11 @@
 //    A refill into memory freed by evicting an expert last used in epoch n
 //    makes the copy stream wait for the event of epoch n+1 first.
 //  - The context stream waits for this call's refills, then receives the
-//    layer's expert table (and widths) from a pinned staging buffer.
+//    layer's expert table (and widths) from a pinned staging buffer, unless
+//    the destination already holds them: the pool remembers, per device
+//    buffer range it wrote, which layer's table of which generation went
+//    there (a layer's generation rises whenever its table's bytes change),
+//    so at a high hit rate most calls copy nothing.
 //  - Every requested (layer, expert) is counted; moe_pool_pin_hot pins the
 //    most requested within a byte budget (refilling them now), and the
 //    counts can be saved and given back in a later process.
@@ -50,6 +54,7 @@
 //    hit rates of a capacity can be planned, and the policy tested, on a
 //    host without a GPU.
 #include <algorithm>
+#include <cstring>
 #include <list>
 #include <map>
 #include <vector>
@@ -102,6 +107,17 @@ struct moe_pool {
   uint64_t prefetches = 0, prefetch_used = 0;
   bool demote = false;
   uint64_t demoted_loads = 0, demoted_uses = 0, bytes_saved = 0;
+  // the pool's own device tables, one per layer (table, then widths), and
+  // each layer's latest table as built on the host: its generation rises when
+  // the bytes change, and an own table that holds the current generation is
+  // not copied again
+  uint8_t *own_tables = nullptr;
+  size_t own_stride = 0;
+  std::vector<std::vector<uint8_t>> shadow;  // [n_layers]
+  std::vector<uint64_t> gen;                 // [n_layers]
+  std::vector<uint64_t> own_gen;             // [n_layers] generation the own table holds (0: none)
+  std::vector<uint8_t> build;
+  uint64_t table_copies = 0, table_skips = 0;
 };
 
 namespace {
@@ -136,6 +152,10 @@ void slab_free(moe_pool *p, size_t off, size_t len) {
 }
 
 size_t block_bytes(const moe_pool *p, int bits) { return moe_expert_block_layout(bits, p->H, p->I, nullptr); }
+
+moe_expert_w *own_table(const moe_pool *p, int layer) {
+  return p->own_tables ? reinterpret_cast<moe_expert_w *>(p->own_tables + p->own_stride * (size_t)layer) : nullptr;
+}
 
 bool fits_free(const moe_pool *p, size_t len) {
   for (const auto &f : p->free_list)
@@ -213,6 +233,9 @@ extern "C" moe_status moe_pool_create(moe_ctx *ctx, size_t capacity_bytes, int n
   p->H = H;
   p->I = I;
   p->entries.resize((size_t)n_layers * n_experts);
+  p->shadow.resize((size_t)n_layers);
+  p->gen.assign((size_t)n_layers, 0);
+  p->own_gen.assign((size_t)n_layers, 0);
   p->free_list[0] = p->capacity;
   if (ctx) {
     auto fail = [&](hipError_t e, const char *what) {
@@ -234,6 +257,9 @@ extern "C" moe_status moe_pool_create(moe_ctx *ctx, size_t capacity_bytes, int n
       if (e != hipSuccess) return fail(e, "hipEventCreateWithFlags");
     }
     const size_t sbytes = (size_t)n_experts * (sizeof(moe_expert_w) + 1);
+    p->own_stride = moe_round_up(sbytes, 256);
+    e = hipMalloc((void **)&p->own_tables, p->own_stride * (size_t)n_layers);
+    if (e != hipSuccess) return fail(e, "hipMalloc");
     for (int i = 0; i < kStaging; ++i) {
       e = hipHostMalloc((void **)&p->staging[i], sbytes, hipHostMallocDefault);
       if (e != hipSuccess) return fail(e, "hipHostMalloc");
@@ -261,6 +287,7 @@ extern "C" void moe_pool_destroy(moe_pool *p) {
     }
     if (p->copy_stream) (void)hipStreamDestroy(p->copy_stream);
     if (p->slab) (void)hipFree(p->slab);
+    if (p->own_tables) (void)hipFree(p->own_tables);
   }
   delete p;
 }
@@ -296,6 +323,17 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   if (!p->ctx && (table_dev || bits_dev))
     return moe_fail(MOE_EINVAL, "moe_pool_prepare: a pool without a context writes no device table");
   if (p->ctx && !table_dev) return moe_fail(MOE_EINVAL, "moe_pool_prepare: table_dev is NULL");
+  if (p->ctx) {
+    // the pool's own tables take only their own layer's table and widths
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p->own_tables), hi = lo + p->own_stride * (size_t)p->n_layers;
+    const uintptr_t t = reinterpret_cast<uintptr_t>(table_dev), b = reinterpret_cast<uintptr_t>(bits_dev);
+    const uint8_t *own_bits = reinterpret_cast<const uint8_t *>(own_table(p, layer)) +
+                              (size_t)p->n_experts * sizeof(moe_expert_w);
+    const bool in_own = (t >= lo && t < hi) || (bits_dev && b >= lo && b < hi);
+    if (in_own && (table_dev != own_table(p, layer) || (bits_dev && bits_dev != own_bits)))
+      return moe_fail(MOE_EINVAL, "moe_pool_prepare: layer %d: the pool's own tables take only that layer's table "
+                      "and widths (moe_pool_layer_table)", layer);
+  }
   const int E = p->n_experts;
   Entry *row = &p->entries[(size_t)layer * E];
   // the call's distinct experts, ascending (each expert is read once)
@@ -353,12 +391,11 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   // the context stream waits for every refill this call's experts depend on
   for (int e = 0; e < E; ++e)
     if (want[e] && row[e].ready) MOE_HIP(hipStreamWaitEvent(p->ctx->stream, row[e].ready, 0));
-  // the layer's table from a pinned staging buffer
-  const int si = p->staging_next;
-  p->staging_next = (si + 1) % kStaging;
-  if (p->staging_used[si]) MOE_HIP(hipEventSynchronize(p->staging_ev[si]));
-  moe_expert_w *tab = reinterpret_cast<moe_expert_w *>(p->staging[si]);
-  uint8_t *bits = p->staging[si] + (size_t)E * sizeof(moe_expert_w);
+  // the layer's table and widths, built on the host
+  const size_t tab_bytes = (size_t)E * sizeof(moe_expert_w);
+  p->build.assign(tab_bytes + (size_t)E, 0);
+  moe_expert_w *tab = reinterpret_cast<moe_expert_w *>(p->build.data());
+  uint8_t *bits = p->build.data() + tab_bytes;
   for (int e = 0; e < E; ++e) {
     const Entry &en = row[e];
     if (en.resident) {
@@ -372,22 +409,53 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
       tab[e].s_up = reinterpret_cast<const float *>(b + o[4]);
       tab[e].s_down = reinterpret_cast<const float *>(b + o[5]);
       bits[e] = (uint8_t)en.rbits;
-    } else {
-      tab[e] = moe_expert_w{};
-      bits[e] = 0;
     }
   }
-  // the widths sit right after the table in the staging buffer: when the
-  // caller's bits_dev directly follows table_dev too, one copy carries both
-  const size_t tab_bytes = (size_t)E * sizeof(moe_expert_w);
-  if (bits_dev == reinterpret_cast<uint8_t *>(table_dev) + tab_bytes) {
-    MOE_HIP(hipMemcpyAsync(table_dev, tab, tab_bytes + (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
+  if (p->build != p->shadow[layer]) {
+    p->shadow[layer] = p->build;
+    ++p->gen[layer];
+  }
+  // the layer's own table already holding these bytes (an earlier call's
+  // copy, in stream order) is not written again
+  const bool own = table_dev == own_table(p, layer);
+  if (own && p->own_gen[layer] == p->gen[layer]) {
+    ++p->table_skips;
+    return MOE_OK;
+  }
+  // the copy goes from a pinned staging buffer; the widths sit right after
+  // the table there: when the caller's bits_dev directly follows table_dev
+  // too, one copy carries both
+  const int si = p->staging_next;
+  p->staging_next = (si + 1) % kStaging;
+  if (p->staging_used[si]) MOE_HIP(hipEventSynchronize(p->staging_ev[si]));
+  std::memcpy(p->staging[si], p->build.data(), p->build.size());
+  if (own || bits_dev == reinterpret_cast<uint8_t *>(table_dev) + tab_bytes) {
+    MOE_HIP(hipMemcpyAsync(table_dev, p->staging[si], tab_bytes + (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
   } else {
-    MOE_HIP(hipMemcpyAsync(table_dev, tab, tab_bytes, hipMemcpyHostToDevice, p->ctx->stream));
-    if (bits_dev) MOE_HIP(hipMemcpyAsync(bits_dev, bits, (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
+    MOE_HIP(hipMemcpyAsync(table_dev, p->staging[si], tab_bytes, hipMemcpyHostToDevice, p->ctx->stream));
+    if (bits_dev)
+      MOE_HIP(hipMemcpyAsync(bits_dev, p->staging[si] + tab_bytes, (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
   }
   MOE_HIP(hipEventRecord(p->staging_ev[si], p->ctx->stream));
   p->staging_used[si] = true;
+  if (own) p->own_gen[layer] = p->gen[layer];
+  ++p->table_copies;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_table_stats(const moe_pool *p, uint64_t *copies, uint64_t *skipped) {
+  if (!p) return moe_fail(MOE_EINVAL, "moe_pool_table_stats: pool is NULL");
+  if (copies) *copies = p->table_copies;
+  if (skipped) *skipped = p->table_skips;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_layer_table(moe_pool *p, int layer, moe_expert_w **table_dev, uint8_t **bits_dev) {
+  if (!p || !p->ctx) return moe_fail(MOE_EINVAL, "moe_pool_layer_table: a pool with a context is needed");
+  if (layer < 0 || layer >= p->n_layers) return moe_fail(MOE_EINVAL, "moe_pool_layer_table: layer %d", layer);
+  if (!table_dev) return moe_fail(MOE_EINVAL, "moe_pool_layer_table: table_dev is NULL");
+  *table_dev = own_table(p, layer);
+  if (bits_dev) *bits_dev = reinterpret_cast<uint8_t *>(*table_dev) + (size_t)p->n_experts * sizeof(moe_expert_w);
   return MOE_OK;
 }
 

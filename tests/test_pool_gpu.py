@@ -321,3 +321,55 @@ def test_pool_table_and_widths_in_one_buffer(moe, ctx, syn):
         assert torch.equal(sep_t, one_t) and torch.equal(sep_b, one_b)
         assert set(np.nonzero(one_b.cpu().numpy())[0]) >= set(np.array(ids).ravel())
     pool.close()
+
+
+def test_pool_own_tables_copy_only_changes(moe, ctx, syn):
+    """The pool's own per-layer tables: prepare copies a layer's table there
+    only when its bytes changed since its last copy there. After every call
+    the own table equals the table the same residency gives in a caller's
+    buffer, and a copy is skipped exactly when the bytes equal the layer's
+    previous ones (each call is made twice in a row: the repeat always
+    skips). Pointers into another layer's own table are rejected."""
+    E, L = 6, 2
+    b4, h4 = make_blocks(moe, ctx, syn, 4, E, seed=41)
+    b2, h2 = make_blocks(moe, ctx, syn, 2, E, seed=41)
+    pool = moe.MoePool(ctx, 3 * b4.block_bytes, L, E, H, I)
+    try:
+        for layer in range(L):
+            for e in range(E):
+                pool.register(layer, e, 4 if e % 3 else 2, h4[e] if e % 3 else h2[e])
+        own = [pool.layer_table(layer) for layer in range(L)]
+        assert own[1][0] != own[0][0] and own[0][1] == own[0][0] + E * 48
+        ext = torch.zeros((E * 48 + E,), dtype=torch.uint8, device="cuda")
+        ext_t, ext_b = ext[:E * 48].view(torch.int64).view(E, 6), ext[E * 48:]
+        rng = np.random.default_rng(5)
+        last = [None] * L
+        n_skip = n_copy = 0
+        for step in range(30):
+            layer = int(rng.integers(0, L))
+            ids = rng.choice(E, size=2, replace=False).astype(np.int32)[None, :]
+            for rep in range(2):
+                c0 = pool.table_stats()
+                pool.prepare(layer, ids, own[layer][0], own[layer][1])
+                c1 = pool.table_stats()
+                pool.prepare(layer, ids, ext_t, ext_b)  # all hits: the same residency
+                torch.cuda.synchronize()
+                want = ext.cpu()
+                got = dev_bytes(own[layer][0], E * 48 + E)
+                assert torch.equal(got, want), (step, rep)
+                same = last[layer] is not None and torch.equal(want, last[layer])
+                assert same or rep == 0, (step, rep)
+                made = (c1["skipped"] - c0["skipped"], c1["copies"] - c0["copies"])
+                assert made == ((1, 0) if same else (0, 1)), (step, rep)
+                n_skip += int(same)
+                n_copy += int(not same)
+                last[layer] = want
+        assert n_skip >= 30 and n_copy > 2
+        with pytest.raises(moe.MoeError):
+            pool.prepare(0, np.array([[0]], np.int32), own[1][0], own[1][1])
+        with pytest.raises(moe.MoeError):
+            pool.prepare(0, np.array([[0]], np.int32), own[0][0], ext_b)
+        with pytest.raises(moe.MoeError):
+            pool.prepare(0, np.array([[0]], np.int32), ext_t, own[1][1])
+    finally:
+        pool.close()
