@@ -134,8 +134,9 @@ def stack_pool_bench(args) -> None:
     total, refilled over PCIe on misses. One token per step; each layer's
     routing comes from a correlated Zipf trace (a slot keeps the previous
     token's expert with probability 0.6). Per layer: quantise the token,
-    prepare the pool (misses refill on the copy stream), one FFN call per
-    width, the combine. Prints one JSON line."""
+    prepare the pool (misses refill on the copy stream), the expert FFN of
+    every width in one call (or one call per width), the combine. Prints
+    one JSON line."""
     import torch
     import quantized_moe_expert_sigmoid_amd as moe
     from synth import workloads as wl
@@ -241,6 +242,7 @@ def stack_pool_bench(args) -> None:
     xq_p, sx_p, y_p, out_p, wts_p = xq.data_ptr(), sx.data_ptr(), y.data_ptr(), out.data_ptr(), wts.data_ptr()
     nmiss = ctypes.c_int(0)
     rowb = 4 * k
+    wmask = (1 << 8 if hot8 else 0) | (1 << 4) | (1 << 2)
 
     def run(t0_, t1_):
         for t in range(t0_, t1_):
@@ -253,13 +255,17 @@ def stack_pool_bench(args) -> None:
                     nl, ids = predicted(t, layer)
                     if ids is not None:
                         pool.prefetch(nl, ids)
-                if hot8:
-                    ck(lib_.moe_expert_ffn_q8(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H, I,
-                                              E, k, y_p))
-                ck(lib_.moe_expert_ffn_q4(ctx_h, tab_p[layer], sh_ref[layer], wid_p[layer], xq_p, sx_p, idx_p, 1, H,
-                                          I, E, k, y_p))
-                ck(lib_.moe_expert_ffn_q2(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H, I, E, k,
-                                          y_p))
+                if not args.stack_per_width:
+                    ck(lib_.moe_expert_ffn_mixed(ctx_h, tab_p[layer], sh_ref[layer], 4, wid_p[layer], wmask, xq_p,
+                                                 sx_p, idx_p, 1, H, I, E, k, y_p))
+                else:
+                    if hot8:
+                        ck(lib_.moe_expert_ffn_q8(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H,
+                                                  I, E, k, y_p))
+                    ck(lib_.moe_expert_ffn_q4(ctx_h, tab_p[layer], sh_ref[layer], wid_p[layer], xq_p, sx_p, idx_p, 1,
+                                              H, I, E, k, y_p))
+                    ck(lib_.moe_expert_ffn_q2(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H, I, E,
+                                              k, y_p))
                 ck(lib_.moe_combine(ctx_h, y_p, wts_p, 1, k, H, 1, out_p))
 
     tc = time.perf_counter()
@@ -346,6 +352,7 @@ def stack_pool_bench(args) -> None:
                                                      / max(1, hits + misses), 5),
                   "h2d_bytes_saved": ts1["bytes_saved"] - ts0["bytes_saved"]},
         # the layers' expert tables: host-to-device copies made and skipped (unchanged)
+        "ffn_calls": "one per width" if args.stack_per_width else "one mixed-width call per layer",
         "table_copies": {"tables": "caller" if args.stack_caller_tables else "pool",
                          "made": tb1["copies"] - tb0["copies"], "skipped": tb1["skipped"] - tb0["skipped"]},
     }
@@ -441,6 +448,9 @@ def main():
     ap.add_argument("--stack-hot", type=int, default=192)
     ap.add_argument("--stack-hot8", type=int, default=0,
                     help="the layer's N most popular experts at int8 (within --stack-hot)")
+    ap.add_argument("--stack-per-width", action="store_true",
+                    help="one expert FFN call per width (moe_expert_ffn_q8/q4/q2) rather than one "
+                         "moe_expert_ffn_mixed call per layer")
     ap.add_argument("--stack-caller-tables", action="store_true",
                     help="the layers' expert tables in the caller's buffers (copied on every call) rather than "
                          "the pool's own (copied when changed)")

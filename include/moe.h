@@ -217,6 +217,21 @@ moe_status moe_expert_ffn_q8(moe_ctx *ctx, const moe_expert_w *experts, const mo
 moe_status moe_expert_ffn_q2(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
                              const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
                              int T, int H, int I, int E, int k, float *y_slots);
+/* A mixed-precision layer's expert FFN in one call ([P-feat]: int8, int4 and
+ * int2 experts side by side): every slot computed at its expert's width
+ * expert_bits[e] (DEVICE uint8 [E], required), bit-identical to the calls
+ * of moe_expert_ffn_q8/q4/q2 with that filter. widths_mask: bit b set (b in
+ * {8, 4, 2}) when the layer has experts of width b. The shared expert
+ * (nullable) is computed at shared_bits, which then counts as set in the
+ * mask too. A slot whose expert's width is not in the mask (0: not
+ * resident) is not computed and not written. The widths run one after
+ * the other on the context stream (with one token, each through the
+ * single-token kernels). Other arguments, errors and y_slots as for
+ * moe_expert_ffn_q4. */
+moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                                int shared_bits, const uint8_t *expert_bits, int widths_mask, const int8_t *xq,
+                                const float *sx, const int32_t *topk_idx, int T, int H, int I, int E, int k,
+                                float *y_slots);
 
 /* ---------------------------------------------------------------------- */
 /* Combine ([P-moe], [P-mem])                                             */

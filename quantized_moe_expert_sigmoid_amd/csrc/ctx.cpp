@@ -302,9 +302,10 @@ extern "C" moe_status moe_bucket_tokens(moe_ctx *ctx, const int32_t *topk_idx, i
   return launch_bucket_public(ctx, topk_idx, T, k, E, counts, offsets, perm);
 }
 
-static moe_status ffn_entry(const char *fn, int bits, moe_ctx *ctx, const moe_expert_w *experts,
-                            const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
-                            const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots) {
+// Argument checks of the expert FFN entry points (T == 0 passes: nothing to do).
+static moe_status ffn_check(const char *fn, moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                            const int8_t *xq, const float *sx, const int32_t *topk_idx, int T, int H, int I, int E,
+                            int k, float *y_slots) {
   moe_status st = bind(ctx, fn);
   if (st) return st;
   REQUIRE(T >= 0, "%s: T %d", fn, T);
@@ -320,7 +321,47 @@ static moe_status ffn_entry(const char *fn, int bits, moe_ctx *ctx, const moe_ex
     REQUIRE(moe_aligned16(shared->gate) && moe_aligned16(shared->up) && moe_aligned16(shared->down),
             "%s: shared expert weights must be 16-byte aligned", fn);
   }
+  return MOE_OK;
+}
+
+static moe_status ffn_entry(const char *fn, int bits, moe_ctx *ctx, const moe_expert_w *experts,
+                            const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                            const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots) {
+  moe_status st = ffn_check(fn, ctx, experts, shared, xq, sx, topk_idx, T, H, I, E, k, y_slots);
+  if (st || T == 0) return st;
   return launch_expert_ffn(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots);
+}
+
+extern "C" moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                                           int shared_bits, const uint8_t *expert_bits, int widths_mask,
+                                           const int8_t *xq, const float *sx, const int32_t *topk_idx, int T, int H,
+                                           int I, int E, int k, float *y_slots) {
+  const char *fn = "moe_expert_ffn_mixed";
+  moe_status st = ffn_check(fn, ctx, experts, shared, xq, sx, topk_idx, T, H, I, E, k, y_slots);
+  if (st) return st;
+  const int all = (1 << 8) | (1 << 4) | (1 << 2);
+  REQUIRE(widths_mask != 0 && (widths_mask & ~all) == 0, "%s: widths_mask 0x%x (bits 8, 4 and 2 only)", fn,
+          widths_mask);
+  REQUIRE(!shared || shared_bits == 8 || shared_bits == 4 || shared_bits == 2, "%s: shared_bits %d", fn, shared_bits);
+  REQUIRE(expert_bits, "%s: expert_bits is NULL", fn);
+  if (T == 0) return MOE_OK;
+  int widths[3], n = 0;
+  bool t1 = T == 1 && ctx->ffn_kernels == MOE_FFN_AUTO;
+  for (int b : {8, 4, 2}) {
+    const bool sh = shared && b == shared_bits;
+    if (!(widths_mask & (1 << b)) && !sh) continue;
+    widths[n++] = b;
+    t1 = t1 && decode_t1_supported(b, H, I, k, sh ? 1 : 0, ctx->n_cu);
+  }
+  if (t1)
+    return launch_ffn_t1_mixed(ctx, widths, n, shared_bits, experts, shared, expert_bits, xq, sx, topk_idx, H, I, E, k,
+                               y_slots);
+  for (int w = 0; w < n; ++w) {
+    const moe_expert_w *sh = (shared && widths[w] == shared_bits) ? shared : nullptr;
+    if ((st = launch_expert_ffn(ctx, widths[w], experts, sh, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots)))
+      return st;
+  }
+  return MOE_OK;
 }
 
 extern "C" moe_status moe_expert_ffn_q4(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,

@@ -939,14 +939,15 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
 // launch
 // ---------------------------------------------------------------------------
 template <int BITS, int JG, int NB, bool GIVEN = false>
-moe_status launch_gu(moe_ctx *ctx, const GateUpT1Args &g, int nwg) {
-  moe_launch(ctx, MOE_STAGE_GATEUP, gateup_t1_kernel<BITS, JG, NB, GIVEN>, dim3(nwg), dim3(kFfnThreads), g);
+moe_status launch_gu(moe_ctx *ctx, hipStream_t stream, const GateUpT1Args &g, int nwg) {
+  moe_launch_on(ctx, stream, MOE_STAGE_GATEUP, gateup_t1_kernel<BITS, JG, NB, GIVEN>, dim3(nwg), dim3(kFfnThreads), g);
   MOE_CHECK_LAUNCH("gateup_t1_kernel");
   return MOE_OK;
 }
 template <int BITS, int JD, int RB, bool GIVEN = false>
-moe_status launch_dn(moe_ctx *ctx, const DownT1Args &d, int nwg) {
-  moe_launch(ctx, MOE_STAGE_DOWN, down_combine_t1_kernel<BITS, JD, RB, GIVEN>, dim3(nwg), dim3(kFfnThreads), d);
+moe_status launch_dn(moe_ctx *ctx, hipStream_t stream, const DownT1Args &d, int nwg) {
+  moe_launch_on(ctx, stream, MOE_STAGE_DOWN, down_combine_t1_kernel<BITS, JD, RB, GIVEN>, dim3(nwg), dim3(kFfnThreads),
+                d);
   MOE_CHECK_LAUNCH("down_combine_t1_kernel");
   return MOE_OK;
 }
@@ -1061,9 +1062,9 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
   g.dbg_on = ctx->dbg_on ? 1 : 0;
   const int nwg = ctx->n_cu;  // one 8-wave workgroup per CU
   switch (bits) {
-    case 4: st = launch_gu<4, T1Shape<4>::JG, T1Shape<4>::NB>(ctx, g, nwg); break;
-    case 8: st = launch_gu<8, T1Shape<8>::JG, T1Shape<8>::NB>(ctx, g, nwg); break;
-    default: st = launch_gu<2, T1Shape<2>::JG, T1Shape<2>::NB>(ctx, g, nwg); break;
+    case 4: st = launch_gu<4, T1Shape<4>::JG, T1Shape<4>::NB>(ctx, ctx->stream, g, nwg); break;
+    case 8: st = launch_gu<8, T1Shape<8>::JG, T1Shape<8>::NB>(ctx, ctx->stream, g, nwg); break;
+    default: st = launch_gu<2, T1Shape<2>::JG, T1Shape<2>::NB>(ctx, ctx->stream, g, nwg); break;
   }
   if (st) return st;
 
@@ -1097,22 +1098,32 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
   d.dbg = ctx->dbg;
   d.dbg_on = ctx->dbg_on ? 1 : 0;
   switch (bits) {
-    case 4: return launch_dn<4, T1Shape<4>::JD, T1Shape<4>::RB>(ctx, d, nwg);
-    case 8: return launch_dn<8, T1Shape<8>::JD, T1Shape<8>::RB>(ctx, d, nwg);
-    default: return launch_dn<2, T1Shape<2>::JD, T1Shape<2>::RB>(ctx, d, nwg);
+    case 4: return launch_dn<4, T1Shape<4>::JD, T1Shape<4>::RB>(ctx, ctx->stream, d, nwg);
+    case 8: return launch_dn<8, T1Shape<8>::JD, T1Shape<8>::RB>(ctx, ctx->stream, d, nwg);
+    default: return launch_dn<2, T1Shape<2>::JD, T1Shape<2>::RB>(ctx, ctx->stream, d, nwg);
   }
 }
 
+namespace {
+
 // The expert FFN of one token with its routing given (ids, activation codes
 // and scale from the caller): the gate/up, requantisation and down kernels
-// above without the router and the combine. Slot j's output goes to y_slots
-// row j for every valid id whose expert has this width (all of them without a
+// above without the router and the combine, enqueued on `stream` with its
+// scratch at `base` (t1_chain_bytes). Slot j's output goes to y_slots row j
+// for every valid id whose expert has this width (all of them without a
 // width filter), the shared expert's to row k; the other rows are left as
-// they were. An id outside [0, E), or one repeated within the token, raises the
-// bad-index flag and gives no output (the later copy of a repeated id).
-moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
-                         const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
-                         int H, int I, int E, int k, float *y_slots) {
+// they were. An id outside [0, E), or one repeated within the token, raises
+// the bad-index flag and gives no output (the later copy of a repeated id).
+size_t t1_chain_bytes(int I, int S) {
+  size_t off = 0;
+  for (size_t b : {sizeof(SlotEntry) * kMaxSlots, sizeof(float) * S * I, (size_t)S * I, (size_t)4 * S, (size_t)4 * S})
+    off = moe_round_up(off + b, 256);
+  return off;
+}
+
+moe_status t1_chain(moe_ctx *ctx, hipStream_t stream, char *base, int bits, const moe_expert_w *experts,
+                    const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                    const int32_t *topk_idx, int H, int I, int E, int k, float *y_slots) {
   const int S = k + (shared ? 1 : 0);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -1122,10 +1133,6 @@ moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, co
   };
   const size_t o_slots = take(sizeof(SlotEntry) * kMaxSlots), o_A = take(sizeof(float) * S * I),
                o_aq = take((size_t)S * I), o_sum = take(4 * S), o_sa = take(4 * S);
-  void *scr = nullptr;
-  moe_status st = moe_scratch(ctx, off, &scr);
-  if (st) return st;
-  char *base = static_cast<char *>(scr);
   SlotEntry *slots = reinterpret_cast<SlotEntry *>(base + o_slots);
 
   GateUpT1Args g{};
@@ -1145,10 +1152,11 @@ moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, co
   g.want_bits = bits;
   g.err = ctx->dev_small;
   const int nwg = ctx->n_cu;
+  moe_status st;
   switch (bits) {
-    case 4: st = launch_gu<4, T1Shape<4>::JG, T1Shape<4>::NB, true>(ctx, g, nwg); break;
-    case 8: st = launch_gu<8, T1Shape<8>::JG, T1Shape<8>::NB, true>(ctx, g, nwg); break;
-    default: st = launch_gu<2, T1Shape<2>::JG, T1Shape<2>::NB, true>(ctx, g, nwg); break;
+    case 4: st = launch_gu<4, T1Shape<4>::JG, T1Shape<4>::NB, true>(ctx, stream, g, nwg); break;
+    case 8: st = launch_gu<8, T1Shape<8>::JG, T1Shape<8>::NB, true>(ctx, stream, g, nwg); break;
+    default: st = launch_gu<2, T1Shape<2>::JG, T1Shape<2>::NB, true>(ctx, stream, g, nwg); break;
   }
   if (st) return st;
 
@@ -1165,9 +1173,9 @@ moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, co
   q.dbg_on = ctx->dbg_on ? 1 : 0;
   q.given = 1;
   switch (bits) {
-    case 4: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<4>, dim3(S), dim3(kRqThreads), q); break;
-    case 8: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<8>, dim3(S), dim3(kRqThreads), q); break;
-    default: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<2>, dim3(S), dim3(kRqThreads), q); break;
+    case 4: moe_launch_on(ctx, stream, MOE_STAGE_REQUANT, requant_t1_kernel<4>, dim3(S), dim3(kRqThreads), q); break;
+    case 8: moe_launch_on(ctx, stream, MOE_STAGE_REQUANT, requant_t1_kernel<8>, dim3(S), dim3(kRqThreads), q); break;
+    default: moe_launch_on(ctx, stream, MOE_STAGE_REQUANT, requant_t1_kernel<2>, dim3(S), dim3(kRqThreads), q); break;
   }
   MOE_CHECK_LAUNCH("requant_t1_kernel");
 
@@ -1183,8 +1191,41 @@ moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, co
   d.dbg = ctx->dbg;
   d.dbg_on = ctx->dbg_on ? 1 : 0;
   switch (bits) {
-    case 4: return launch_dn<4, T1Shape<4>::JD, T1Shape<4>::RB, true>(ctx, d, nwg);
-    case 8: return launch_dn<8, T1Shape<8>::JD, T1Shape<8>::RB, true>(ctx, d, nwg);
-    default: return launch_dn<2, T1Shape<2>::JD, T1Shape<2>::RB, true>(ctx, d, nwg);
+    case 4: return launch_dn<4, T1Shape<4>::JD, T1Shape<4>::RB, true>(ctx, stream, d, nwg);
+    case 8: return launch_dn<8, T1Shape<8>::JD, T1Shape<8>::RB, true>(ctx, stream, d, nwg);
+    default: return launch_dn<2, T1Shape<2>::JD, T1Shape<2>::RB, true>(ctx, stream, d, nwg);
   }
+}
+
+}  // namespace
+
+moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
+                         const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
+                         int H, int I, int E, int k, float *y_slots) {
+  void *scr = nullptr;
+  moe_status st = moe_scratch(ctx, t1_chain_bytes(I, k + (shared ? 1 : 0)), &scr);
+  if (st) return st;
+  return t1_chain(ctx, ctx->stream, static_cast<char *>(scr), bits, experts, shared, expert_bits, xq, sx, topk_idx,
+                  H, I, E, k, y_slots);
+}
+
+// Every width of a mixed layer for one token: the widths' chains one after
+// the other on the context stream (each computes only its width's slots, so
+// the chains write disjoint rows of y_slots and can share one scratch area).
+// Running the narrower widths' chains on a second stream beside the first
+// was slower: the fork and join cost more than the overlap gained.
+moe_status launch_ffn_t1_mixed(moe_ctx *ctx, const int *widths, int n_widths, int shared_bits,
+                               const moe_expert_w *experts, const moe_expert_w *shared, const uint8_t *expert_bits,
+                               const int8_t *xq, const float *sx, const int32_t *topk_idx, int H, int I, int E, int k,
+                               float *y_slots) {
+  void *scr = nullptr;
+  moe_status st = moe_scratch(ctx, t1_chain_bytes(I, k + (shared ? 1 : 0)), &scr);
+  if (st) return st;
+  for (int w = 0; w < n_widths; ++w) {
+    const moe_expert_w *sh = (shared && widths[w] == shared_bits) ? shared : nullptr;
+    st = t1_chain(ctx, ctx->stream, static_cast<char *>(scr), widths[w], experts, sh, expert_bits, xq, sx, topk_idx,
+                  H, I, E, k, y_slots);
+    if (st) return st;
+  }
+  return MOE_OK;
 }

@@ -360,6 +360,49 @@ def test_ffn_mixed_precision_filter(moe, ctx, orc, syn, T):
         assert np.array_equal(yg[t, k], orc.expert_token(osh4, xq_o[t], float(sx_o[t]))["y"])
 
 
+@pytest.mark.parametrize("T", [1, 6])
+@pytest.mark.parametrize("shared_bits", [4, 8, None])
+def test_ffn_mixed_one_call(moe, ctx, orc, syn, T, shared_bits):
+    """moe_expert_ffn_mixed: a layer of int8, int4 and int2 experts in one
+    call, every slot bit-exact against the oracle at its expert's width (one
+    token: the widths' single-token kernels on two streams); a width left out
+    of the mask (unless it is the shared expert's), and a width-0 (absent)
+    expert, leave their slots untouched."""
+    H, I, E, k = 256, 128, 9, 4
+    made = {b: make_experts(moe, orc, syn, b, H, I, E, seed=70) for b in (8, 4, 2)}
+    bits = np.array([8, 4, 2, 4, 2, 8, 4, 0, 2], np.uint8)
+    table = made[4][0].table.clone()
+    for e in range(E):
+        if bits[e] in (8, 2):
+            table[e] = made[int(bits[e])][0].table[e]
+    x = syn.hidden(71, T, H)
+    xq_o, sx_o = orc.quantize_act(x)
+    idx = random_routing(syn, T, E, k, 72)
+    idx[0, :] = [7, 0, 1, 2]  # the first token also names the absent expert
+    for widths in ((8, 4, 2), (4, 2)):
+        log(f"mixed T={T} shared_bits={shared_bits} widths={widths}")
+        y = torch.full((T, k + 1, H), 7.0, dtype=torch.float32, device="cuda")
+        sh = made[shared_bits][1].struct(0) if shared_bits else None
+        moe.moe_expert_ffn_mixed(ctx, table, sh, shared_bits or 0, dev(bits), widths, dev(xq_o), dev(sx_o), dev(idx),
+                                 H, I, E, y)
+        ctx.check()
+        yg = host(y)
+        for t in range(T):
+            for j in range(k):
+                e = idx[t, j]
+                b = int(bits[e])
+                if b in widths or b == shared_bits:  # the shared expert's width is always computed
+                    r = orc.expert_token(made[b][2][e], xq_o[t], float(sx_o[t]))
+                    assert np.array_equal(yg[t, j].view(np.uint32), r["y"].view(np.uint32)), (widths, t, j)
+                else:
+                    assert np.all(yg[t, j] == 7.0), (widths, t, j)
+            if shared_bits:
+                r = orc.expert_token(made[shared_bits][3], xq_o[t], float(sx_o[t]))
+                assert np.array_equal(yg[t, k].view(np.uint32), r["y"].view(np.uint32)), (widths, t)
+            else:
+                assert np.all(yg[t, k] == 7.0)
+
+
 # --------------------------------------------------------------------------
 # combine and the whole layer
 # --------------------------------------------------------------------------
