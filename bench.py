@@ -243,6 +243,7 @@ def stack_pool_bench(args) -> None:
     nmiss = ctypes.c_int(0)
     rowb = 4 * k
     wmask = (1 << 8 if hot8 else 0) | (1 << 4) | (1 << 2)
+    cw = ctypes.c_int(0)
 
     def run(t0_, t1_):
         for t in range(t0_, t1_):
@@ -255,17 +256,23 @@ def stack_pool_bench(args) -> None:
                     nl, ids = predicted(t, layer)
                     if ids is not None:
                         pool.prefetch(nl, ids)
+                # the widths this token's experts have here (the shared expert's, int4, always runs)
+                m = wmask
+                if not args.stack_all_widths:
+                    ck(lib_.moe_pool_call_widths(pool_h, ctypes.byref(cw)))
+                    m = cw.value | (1 << 4)
                 if not args.stack_per_width:
-                    ck(lib_.moe_expert_ffn_mixed(ctx_h, tab_p[layer], sh_ref[layer], 4, wid_p[layer], wmask, xq_p,
+                    ck(lib_.moe_expert_ffn_mixed(ctx_h, tab_p[layer], sh_ref[layer], 4, wid_p[layer], m, xq_p,
                                                  sx_p, idx_p, 1, H, I, E, k, y_p))
                 else:
-                    if hot8:
+                    if m & (1 << 8):
                         ck(lib_.moe_expert_ffn_q8(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H,
                                                   I, E, k, y_p))
                     ck(lib_.moe_expert_ffn_q4(ctx_h, tab_p[layer], sh_ref[layer], wid_p[layer], xq_p, sx_p, idx_p, 1,
                                               H, I, E, k, y_p))
-                    ck(lib_.moe_expert_ffn_q2(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H, I, E,
-                                              k, y_p))
+                    if m & (1 << 2):
+                        ck(lib_.moe_expert_ffn_q2(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H,
+                                                  I, E, k, y_p))
                 ck(lib_.moe_combine(ctx_h, y_p, wts_p, 1, k, H, 1, out_p))
 
     tc = time.perf_counter()
@@ -352,7 +359,8 @@ def stack_pool_bench(args) -> None:
                                                      / max(1, hits + misses), 5),
                   "h2d_bytes_saved": ts1["bytes_saved"] - ts0["bytes_saved"]},
         # the layers' expert tables: host-to-device copies made and skipped (unchanged)
-        "ffn_calls": "one per width" if args.stack_per_width else "one mixed-width call per layer",
+        "ffn_calls": ("one per width" if args.stack_per_width else "one mixed-width call per layer")
+        + ("" if args.stack_all_widths else ", widths of the token's experts only"),
         "table_copies": {"tables": "caller" if args.stack_caller_tables else "pool",
                          "made": tb1["copies"] - tb0["copies"], "skipped": tb1["skipped"] - tb0["skipped"]},
     }
@@ -448,6 +456,9 @@ def main():
     ap.add_argument("--stack-hot", type=int, default=192)
     ap.add_argument("--stack-hot8", type=int, default=0,
                     help="the layer's N most popular experts at int8 (within --stack-hot)")
+    ap.add_argument("--stack-all-widths", action="store_true",
+                    help="run every width of the layer on every token, not only those its experts have "
+                         "(moe_pool_call_widths)")
     ap.add_argument("--stack-per-width", action="store_true",
                     help="one expert FFN call per width (moe_expert_ffn_q8/q4/q2) rather than one "
                          "moe_expert_ffn_mixed call per layer")

@@ -332,6 +332,12 @@ moe_status moe_pool_prepare(moe_pool *pool, int layer, const int32_t *topk_idx_h
  * written only by moe_pool_prepare of that layer (callers only read it).
  * Host-only. */
 moe_status moe_pool_layer_table(moe_pool *pool, int layer, moe_expert_w **table_dev, uint8_t **bits_dev);
+/* The widths the latest moe_pool_prepare call's experts are resident at:
+ * bit b set (b in {8, 4, 2}) when one of them is at width b (0 after a
+ * call with no expert). A mixed layer's caller can pass it as widths_mask
+ * to moe_expert_ffn_mixed, so that a width none of the token's experts has
+ * costs no launches. Host-only. */
+moe_status moe_pool_call_widths(const moe_pool *pool, int *mask_host);
 /* Table copies of moe_pool_prepare: made, and skipped because the layer's
  * own table already held the bytes. Host-only. */
 moe_status moe_pool_table_stats(const moe_pool *pool, uint64_t *copies, uint64_t *skipped);

@@ -99,6 +99,7 @@ _SIGS = {
     "moe_pool_resident_bits": (_i32, [_vp, _i32, _i32]),
     "moe_expert_ffn_mixed": (_i32, [_vp, _vp, ctypes.POINTER(ExpertW), _i32, _vp, _i32, _vp, _vp, _vp] + [_i32] * 5
                              + [_vp]),
+    "moe_pool_call_widths": (_i32, [_vp, ctypes.POINTER(_i32)]),
     "moe_pool_table_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 2),
     "moe_pool_layer_table": (_i32, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
 }
@@ -571,6 +572,12 @@ class MoePool:
         v = [ctypes.c_uint64() for _ in range(2)]
         _ck(lib().moe_pool_table_stats(self.handle, *(ctypes.byref(x) for x in v)))
         return {"copies": v[0].value, "skipped": v[1].value}
+
+    def call_widths(self) -> int:
+        """Bit b set when an expert of the latest prepare call is resident at width b."""
+        m = ctypes.c_int()
+        _ck(lib().moe_pool_call_widths(self.handle, ctypes.byref(m)))
+        return m.value
 
     def layer_table(self, layer: int):
         """The pool's own device table of `layer`: (table address, widths

@@ -118,6 +118,7 @@ struct moe_pool {
   std::vector<uint64_t> own_gen;             // [n_layers] generation the own table holds (0: none)
   std::vector<uint8_t> build;
   uint64_t table_copies = 0, table_skips = 0;
+  int call_widths = 0;  // widths of the latest prepare call's experts (bit b: width b)
 };
 
 namespace {
@@ -386,6 +387,9 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
     if (row[e].rbits != row[e].bits) ++p->demoted_uses;
   }
   if (n_miss_host) *n_miss_host = n_miss;
+  p->call_widths = 0;
+  for (int e = 0; e < E; ++e)
+    if (want[e]) p->call_widths |= 1 << row[e].rbits;
   if (!p->ctx) return MOE_OK;
 
   // the context stream waits for every refill this call's experts depend on
@@ -447,6 +451,12 @@ extern "C" moe_status moe_pool_table_stats(const moe_pool *p, uint64_t *copies, 
   if (!p) return moe_fail(MOE_EINVAL, "moe_pool_table_stats: pool is NULL");
   if (copies) *copies = p->table_copies;
   if (skipped) *skipped = p->table_skips;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_pool_call_widths(const moe_pool *p, int *mask_host) {
+  if (!p || !mask_host) return moe_fail(MOE_EINVAL, "moe_pool_call_widths: NULL argument");
+  *mask_host = p->call_widths;
   return MOE_OK;
 }
 

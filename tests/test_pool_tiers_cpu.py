@@ -167,6 +167,7 @@ def test_tiers_match_reference(moe, demote, cap_blocks, E, k, layers, seed):
                 pool.prepare(L, ids[None, :])
             break
         pool.prepare(L, ids[None, :])
+        assert pool.call_widths() == sum({1 << ref.width((L, int(e))) for e in ids}), step
         for LL in range(layers):
             for e in range(E):
                 w = pool.resident_bits(LL, e)
