@@ -262,8 +262,10 @@ def stack_pool_bench(args) -> None:
                     ck(lib_.moe_pool_call_widths(pool_h, ctypes.byref(cw)))
                     m = cw.value | (1 << 4)
                 if not args.stack_per_width:
+                    # with the combine in the same call
                     ck(lib_.moe_expert_ffn_mixed(ctx_h, tab_p[layer], sh_ref[layer], 4, wid_p[layer], m, xq_p,
-                                                 sx_p, idx_p, 1, H, I, E, k, y_p))
+                                                 sx_p, idx_p, wts_p, 1, H, I, E, k, y_p, out_p))
+                    continue
                 else:
                     if m & (1 << 8):
                         ck(lib_.moe_expert_ffn_q8(ctx_h, tab_p[layer], None, wid_p[layer], xq_p, sx_p, idx_p, 1, H,

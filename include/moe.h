@@ -224,14 +224,18 @@ moe_status moe_expert_ffn_q2(moe_ctx *ctx, const moe_expert_w *experts, const mo
  * {8, 4, 2}) when the layer has experts of width b. The shared expert
  * (nullable) is computed at shared_bits, which then counts as set in the
  * mask too. A slot whose expert's width is not in the mask (0: not
- * resident) is not computed and not written. The widths run one after
- * the other on the context stream (with one token, each through the
- * single-token kernels). Other arguments, errors and y_slots as for
+ * resident) is not computed and not written. out (DEVICE fp32 [T][H],
+ * nullable; needs topk_w, DEVICE fp32 [T][k]): also the combine of the
+ * y_slots this call leaves, exactly as moe_combine computes it (with the
+ * shared slot when shared != NULL). The widths run one after the other on
+ * the context stream; with one token each goes through the single-token
+ * kernels, the shared expert's width last, whose down kernel then also does
+ * the combine. Other arguments, errors and y_slots as for
  * moe_expert_ffn_q4. */
 moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
                                 int shared_bits, const uint8_t *expert_bits, int widths_mask, const int8_t *xq,
-                                const float *sx, const int32_t *topk_idx, int T, int H, int I, int E, int k,
-                                float *y_slots);
+                                const float *sx, const int32_t *topk_idx, const float *topk_w, int T, int H, int I,
+                                int E, int k, float *y_slots, float *out);
 
 /* ---------------------------------------------------------------------- */
 /* Combine ([P-moe], [P-mem])                                             */

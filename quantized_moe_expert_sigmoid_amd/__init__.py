@@ -97,8 +97,8 @@ _SIGS = {
     "moe_pool_set_demotion": (_i32, [_vp, _i32]),
     "moe_pool_tier_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 3),
     "moe_pool_resident_bits": (_i32, [_vp, _i32, _i32]),
-    "moe_expert_ffn_mixed": (_i32, [_vp, _vp, ctypes.POINTER(ExpertW), _i32, _vp, _i32, _vp, _vp, _vp] + [_i32] * 5
-                             + [_vp]),
+    "moe_expert_ffn_mixed": (_i32, [_vp, _vp, ctypes.POINTER(ExpertW), _i32, _vp, _i32, _vp, _vp, _vp, _vp]
+                             + [_i32] * 5 + [_vp, _vp]),
     "moe_pool_call_widths": (_i32, [_vp, ctypes.POINTER(_i32)]),
     "moe_pool_table_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 2),
     "moe_pool_layer_table": (_i32, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
@@ -308,9 +308,11 @@ def moe_expert_ffn_q2(ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E
 FFN_BY_BITS = {4: moe_expert_ffn_q4, 8: moe_expert_ffn_q8, 2: moe_expert_ffn_q2}
 
 
-def moe_expert_ffn_mixed(ctx, table, shared, shared_bits, expert_bits, widths, xq, sx, topk_idx, H, I, E, y_slots):
+def moe_expert_ffn_mixed(ctx, table, shared, shared_bits, expert_bits, widths, xq, sx, topk_idx, H, I, E, y_slots,
+                         topk_w=None, out=None):
     """Every slot at its expert's width (expert_bits, device uint8 [E]);
-    widths: the widths the layer has (iterable of 8, 4, 2)."""
+    widths: the widths the layer has (iterable of 8, 4, 2). With out (and
+    topk_w): also the combine of the slots."""
     T, k = topk_idx.shape
     _dev(table, torch.int64, "experts table", (E, 6))
     _dev(xq, torch.int8, "xq", (T, H))
@@ -318,13 +320,16 @@ def moe_expert_ffn_mixed(ctx, table, shared, shared_bits, expert_bits, widths, x
     _dev(topk_idx, torch.int32, "topk_idx")
     _dev(y_slots, torch.float32, "y_slots", (T, k + 1, H))
     _dev(expert_bits, torch.uint8, "expert_bits", (E,))
+    if out is not None:
+        _dev(out, torch.float32, "out", (T, H))
+        _dev(topk_w, torch.float32, "topk_w", (T, k))
     mask = 0
     for b in widths:
         mask |= 1 << int(b)
     sh = ctypes.byref(shared) if shared is not None else None
     _ck(lib().moe_expert_ffn_mixed(ctx.handle, table.data_ptr(), sh, int(shared_bits), expert_bits.data_ptr(), mask,
-                                   xq.data_ptr(), sx.data_ptr(), topk_idx.data_ptr(), T, H, I, E, k,
-                                   y_slots.data_ptr()))
+                                   xq.data_ptr(), sx.data_ptr(), topk_idx.data_ptr(), _ptr(topk_w), T, H, I, E, k,
+                                   y_slots.data_ptr(), _ptr(out)))
     return y_slots
 
 

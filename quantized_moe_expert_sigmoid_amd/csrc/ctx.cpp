@@ -334,8 +334,9 @@ static moe_status ffn_entry(const char *fn, int bits, moe_ctx *ctx, const moe_ex
 
 extern "C" moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
                                            int shared_bits, const uint8_t *expert_bits, int widths_mask,
-                                           const int8_t *xq, const float *sx, const int32_t *topk_idx, int T, int H,
-                                           int I, int E, int k, float *y_slots) {
+                                           const int8_t *xq, const float *sx, const int32_t *topk_idx,
+                                           const float *topk_w, int T, int H, int I, int E, int k, float *y_slots,
+                                           float *out) {
   const char *fn = "moe_expert_ffn_mixed";
   moe_status st = ffn_check(fn, ctx, experts, shared, xq, sx, topk_idx, T, H, I, E, k, y_slots);
   if (st) return st;
@@ -345,6 +346,8 @@ extern "C" moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *exp
   REQUIRE(!shared || shared_bits == 8 || shared_bits == 4 || shared_bits == 2, "%s: shared_bits %d", fn, shared_bits);
   REQUIRE(expert_bits, "%s: expert_bits is NULL", fn);
   if (T == 0) return MOE_OK;
+  REQUIRE(!out || topk_w, "%s: out needs topk_w", fn);
+  REQUIRE(!out || moe_aligned16(out), "%s: out must be 16-byte aligned", fn);
   int widths[3], n = 0;
   bool t1 = T == 1 && ctx->ffn_kernels == MOE_FFN_AUTO;
   for (int b : {8, 4, 2}) {
@@ -354,14 +357,14 @@ extern "C" moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *exp
     t1 = t1 && decode_t1_supported(b, H, I, k, sh ? 1 : 0, ctx->n_cu);
   }
   if (t1)
-    return launch_ffn_t1_mixed(ctx, widths, n, shared_bits, experts, shared, expert_bits, xq, sx, topk_idx, H, I, E, k,
-                               y_slots);
+    return launch_ffn_t1_mixed(ctx, widths, n, shared_bits, experts, shared, expert_bits, xq, sx, topk_idx, topk_w, H,
+                               I, E, k, y_slots, out);
   for (int w = 0; w < n; ++w) {
     const moe_expert_w *sh = (shared && widths[w] == shared_bits) ? shared : nullptr;
     if ((st = launch_expert_ffn(ctx, widths[w], experts, sh, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots)))
       return st;
   }
-  return MOE_OK;
+  return out ? launch_combine(ctx, y_slots, topk_w, T, k, H, shared ? 1 : 0, out) : MOE_OK;
 }
 
 extern "C" moe_status moe_expert_ffn_q4(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,

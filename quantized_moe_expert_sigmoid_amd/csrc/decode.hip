@@ -794,9 +794,12 @@ struct DownT1Args {
   const float *sa;      // [S]
   int H, I, S, k, has_shared;
   float *y;    // [S][H] (the token's y_slots; slot stride H)
-  float *out;  // [H]
+  float *out;  // [H]; given routing: nullable (no combine)
   moe_debug_bufs dbg;
   int dbg_on;
+  // given routing with the combine: the slots' routing weights [k]; the
+  // slots another width's call computed are read back from y
+  const float *w_given;
 };
 
 constexpr int kAq16 = (kMaxSlots * kMaxIDown / 16 + kFfnThreads - 1) / kFfnThreads;  // 16-byte code pieces per thread
@@ -824,7 +827,9 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   // given routing: only the slots with work here are written (a slot of
   // another width belongs to that width's call)
   const bool act_l = GIVEN ? (lane < S && (lane == a.k ? a.has_shared != 0 : a.slots[ls].expert != -1)) : lane < S;
-  if (GIVEN && __ballot(act_l) == 0) return;
+  const bool comb = GIVEN && a.out != nullptr;
+  const float wg_l = (comb && lane < a.k) ? a.w_given[lane] : 0.0f;
+  if (GIVEN && !comb && __ballot(act_l) == 0) return;
   const int aqsum_l = a.sums[ls];
   const float sa_l = a.sa[ls];
   // every slot's codes (S*I bytes), unconditional loads: pieces past the end
@@ -922,6 +927,19 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
 #pragma unroll
         for (int s = 0; s < kMaxSlots - 1; ++s)
           if (s < a.k) acc = __builtin_fmaf(readlane_f(w_l, s), readlane_f(yv, s), acc);
+        if (lane == 0) a.out[r] = acc;
+      } else if (comb) {
+        // the combine over the whole of y_slots as the combine entry point
+        // computes it: shared first, then the slots of nonzero weight in
+        // order (a slot without work here holds what its own call wrote)
+        float yall = yv;
+        if (!act_l && lane < a.k && wg_l != 0.0f) yall = a.y[(int64_t)lane * a.H + r];
+        float acc = a.has_shared ? readlane_f(yall, a.k) : 0.0f;
+#pragma unroll
+        for (int s = 0; s < kMaxSlots - 1; ++s) {
+          const float ws = readlane_f(wg_l, s);
+          if (s < a.k && ws != 0.0f) acc = __builtin_fmaf(ws, readlane_f(yall, s), acc);
+        }
         if (lane == 0) a.out[r] = acc;
       }
     }
@@ -1123,7 +1141,8 @@ size_t t1_chain_bytes(int I, int S) {
 
 moe_status t1_chain(moe_ctx *ctx, hipStream_t stream, char *base, int bits, const moe_expert_w *experts,
                     const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
-                    const int32_t *topk_idx, int H, int I, int E, int k, float *y_slots) {
+                    const int32_t *topk_idx, int H, int I, int E, int k, float *y_slots, const float *topk_w = nullptr,
+                    float *out = nullptr) {
   const int S = k + (shared ? 1 : 0);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -1187,7 +1206,8 @@ moe_status t1_chain(moe_ctx *ctx, hipStream_t stream, char *base, int bits, cons
   d.H = H; d.I = I; d.S = S; d.k = k;
   d.has_shared = shared ? 1 : 0;
   d.y = y_slots;
-  d.out = nullptr;
+  d.out = out;
+  d.w_given = topk_w;
   d.dbg = ctx->dbg;
   d.dbg_on = ctx->dbg_on ? 1 : 0;
   switch (bits) {
@@ -1211,20 +1231,27 @@ moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, co
 
 // Every width of a mixed layer for one token: the widths' chains one after
 // the other on the context stream (each computes only its width's slots, so
-// the chains write disjoint rows of y_slots and can share one scratch area).
-// Running the narrower widths' chains on a second stream beside the first
-// was slower: the fork and join cost more than the overlap gained.
+// the chains write disjoint rows of y_slots and can share one scratch area),
+// the shared expert's width last; with out, that last down kernel also does
+// the combine, reading the earlier chains' slots back from y_slots. Running
+// the narrower widths' chains on a second stream beside the first was
+// slower: the fork and join cost more than the overlap gained.
 moe_status launch_ffn_t1_mixed(moe_ctx *ctx, const int *widths, int n_widths, int shared_bits,
                                const moe_expert_w *experts, const moe_expert_w *shared, const uint8_t *expert_bits,
-                               const int8_t *xq, const float *sx, const int32_t *topk_idx, int H, int I, int E, int k,
-                               float *y_slots) {
+                               const int8_t *xq, const float *sx, const int32_t *topk_idx, const float *topk_w, int H,
+                               int I, int E, int k, float *y_slots, float *out) {
   void *scr = nullptr;
   moe_status st = moe_scratch(ctx, t1_chain_bytes(I, k + (shared ? 1 : 0)), &scr);
   if (st) return st;
-  for (int w = 0; w < n_widths; ++w) {
-    const moe_expert_w *sh = (shared && widths[w] == shared_bits) ? shared : nullptr;
-    st = t1_chain(ctx, ctx->stream, static_cast<char *>(scr), widths[w], experts, sh, expert_bits, xq, sx, topk_idx,
-                  H, I, E, k, y_slots);
+  const int last_bits = shared ? shared_bits : widths[n_widths - 1];
+  int order[3], n = 0;
+  for (int w = 0; w < n_widths; ++w)
+    if (widths[w] != last_bits) order[n++] = widths[w];
+  order[n++] = last_bits;
+  for (int w = 0; w < n; ++w) {
+    const bool last = w == n - 1;
+    st = t1_chain(ctx, ctx->stream, static_cast<char *>(scr), order[w], experts, last ? shared : nullptr,
+                  expert_bits, xq, sx, topk_idx, H, I, E, k, y_slots, last ? topk_w : nullptr, last ? out : nullptr);
     if (st) return st;
   }
   return MOE_OK;

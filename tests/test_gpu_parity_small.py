@@ -367,7 +367,9 @@ def test_ffn_mixed_one_call(moe, ctx, orc, syn, T, shared_bits):
     call, every slot bit-exact against the oracle at its expert's width (one
     token: the widths' single-token kernels on two streams); a width left out
     of the mask (unless it is the shared expert's), and a width-0 (absent)
-    expert, leave their slots untouched."""
+    expert, leave their slots untouched. The combine done in the same call
+    is bit-identical to moe_combine over the y_slots the call leaves (slots
+    of other calls read back, zero weights skipped)."""
     H, I, E, k = 256, 128, 9, 4
     made = {b: make_experts(moe, orc, syn, b, H, I, E, seed=70) for b in (8, 4, 2)}
     bits = np.array([8, 4, 2, 4, 2, 8, 4, 0, 2], np.uint8)
@@ -379,13 +381,19 @@ def test_ffn_mixed_one_call(moe, ctx, orc, syn, T, shared_bits):
     xq_o, sx_o = orc.quantize_act(x)
     idx = random_routing(syn, T, E, k, 72)
     idx[0, :] = [7, 0, 1, 2]  # the first token also names the absent expert
+    wts = np.abs(syn.normal(73, syn.stream_id(syn.K_MISC, 73), (T, k))).astype(np.float32)
+    wts[0, 2] = 0.0  # a zero weight: that slot is skipped
     for widths in ((8, 4, 2), (4, 2)):
         log(f"mixed T={T} shared_bits={shared_bits} widths={widths}")
         y = torch.full((T, k + 1, H), 7.0, dtype=torch.float32, device="cuda")
+        out = torch.empty((T, H), dtype=torch.float32, device="cuda")
         sh = made[shared_bits][1].struct(0) if shared_bits else None
         moe.moe_expert_ffn_mixed(ctx, table, sh, shared_bits or 0, dev(bits), widths, dev(xq_o), dev(sx_o), dev(idx),
-                                 H, I, E, y)
+                                 H, I, E, y, topk_w=dev(wts), out=out)
         ctx.check()
+        ref = torch.empty_like(out)
+        moe.moe_combine(ctx, y, dev(wts), shared_bits is not None, ref)
+        assert np.array_equal(host(out).view(np.uint32), host(ref).view(np.uint32)), widths
         yg = host(y)
         for t in range(T):
             for j in range(k):
