@@ -67,7 +67,7 @@ def test_quantize_rows_half_ties(moe, ctx, orc):
         assert np.array_equal(host(p), ref_p) and np.array_equal(host(s), ref_s)
 
 
-@pytest.mark.parametrize("T,H", [(1, 6144), (33, 128), (64, 6144)])
+@pytest.mark.parametrize("T,H", [(1, 6144), (33, 128), (64, 6144), (3, 8192), (5, 64), (4, 1088)])
 def test_quantize_act_bitexact(moe, ctx, orc, syn, T, H):
     log(f"quantize_act T={T} H={H}")
     x = syn.hidden(21, T, H)
