@@ -829,7 +829,23 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   const bool act_l = GIVEN ? (lane < S && (lane == a.k ? a.has_shared != 0 : a.slots[ls].expert != -1)) : lane < S;
   const bool comb = GIVEN && a.out != nullptr;
   const float wg_l = (comb && lane < a.k) ? a.w_given[lane] : 0.0f;
-  if (GIVEN && !comb && __ballot(act_l) == 0) return;
+  if (GIVEN && __ballot(act_l) == 0) {
+    if (!comb) return;
+    // no slot has work here (and so no shared expert): the combine alone,
+    // every slot read back; no weight row is read, as the slots' pointers
+    // may be null in this case
+    for (int r = r0; r < r1; ++r) {
+      const float yall = (lane < a.k && wg_l != 0.0f) ? a.y[(int64_t)lane * a.H + r] : 0.0f;
+      float acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < kMaxSlots - 1; ++s) {
+        const float ws = readlane_f(wg_l, s);
+        if (s < a.k && ws != 0.0f) acc = __builtin_fmaf(ws, readlane_f(yall, s), acc);
+      }
+      if (lane == 0) a.out[r] = acc;
+    }
+    return;
+  }
   const int aqsum_l = a.sums[ls];
   const float sa_l = a.sa[ls];
   // every slot's codes (S*I bytes), unconditional loads: pieces past the end

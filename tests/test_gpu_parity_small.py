@@ -411,6 +411,31 @@ def test_ffn_mixed_one_call(moe, ctx, orc, syn, T, shared_bits):
                 assert np.all(yg[t, k] == 7.0)
 
 
+def test_ffn_mixed_last_width_without_work(moe, ctx, orc, syn):
+    """One token, no shared expert, a combine: the width that runs last (int2)
+    has none of the token's experts, so its down kernel only combines the
+    slots the int4 kernels wrote (no weight row is read)."""
+    H, I, E, k = 256, 128, 6, 3
+    b4, _, o4, _ = make_experts(moe, orc, syn, 4, H, I, E, seed=75)
+    bits = np.array([4, 4, 2, 4, 2, 4], np.uint8)
+    xq_o, sx_o = orc.quantize_act(syn.hidden(76, 1, H))
+    idx = np.array([[3, 0, 5]], np.int32)
+    wts = np.array([[0.5, 0.0, 0.25]], np.float32)
+    y = torch.full((1, k + 1, H), 7.0, dtype=torch.float32, device="cuda")
+    out = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn_mixed(ctx, b4.table, None, 0, dev(bits), (4, 2), dev(xq_o), dev(sx_o), dev(idx), H, I, E, y,
+                             topk_w=dev(wts), out=out)
+    ctx.check()
+    yg = host(y)
+    for j in range(k):
+        r = orc.expert_token(o4[idx[0, j]], xq_o[0], float(sx_o[0]))
+        assert np.array_equal(yg[0, j].view(np.uint32), r["y"].view(np.uint32)), j
+    assert np.all(yg[0, k] == 7.0)
+    ref = torch.empty_like(out)
+    moe.moe_combine(ctx, y, dev(wts), False, ref)
+    assert np.array_equal(host(out).view(np.uint32), host(ref).view(np.uint32))
+
+
 # --------------------------------------------------------------------------
 # combine and the whole layer
 # --------------------------------------------------------------------------
