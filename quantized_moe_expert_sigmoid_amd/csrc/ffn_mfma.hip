@@ -31,10 +31,12 @@
 //     32 rows; y = acc * s_down * sa into the slot buffer.
 // A tile holds up to 64 tokens of one expert, run as 4 blocks of 16 through
 // the matrix core (rows past the expert's last token repeat it and are not
-// stored); an expert's remainder of 1..16 tokens is a one-block tile. Each
-// kind has its own launch (the one-block kernel needs fewer registers and
-// keeps four steps of loads in flight instead of two). Weight rows stream
-// from HBM once per tile; the activation rows are re-read from L2.
+// stored); an expert's remainder of 1..16 tokens is a one-block tile (when
+// experts average 32 or more tokens, a remainder is a full-size tile too).
+// Each kind has its own launch: the one-block kernel needs fewer registers
+// and runs more workgroups per CU, both keeping two weight steps in flight.
+// Weight rows stream from HBM once per tile; the activation rows are re-read
+// from L2.
 #include <algorithm>
 
 #include "gemv_common.h"

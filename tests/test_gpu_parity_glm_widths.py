@@ -77,3 +77,58 @@ def test_glm_shape_other_widths(moe, orc, bits):
                 assert err.max() < 1e-3, err
     finally:
         ctx.close()
+
+
+def test_glm_shape_mixed_one_token(moe, orc):
+    """The pool stack's per-layer call at the GLM expert shape: one token,
+    int4 and int2 experts in one moe_expert_ffn_mixed call with the int4
+    shared expert and the combine (the single-token kernels with the routing
+    given). Every slot bit-exact against the oracle at its expert's width;
+    the combined output bit-identical to moe_combine over the same slots and
+    within 1e-3 of the row max of the oracle's combine."""
+    from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
+    from synth import workloads as wl
+    w = wl.Workload("glm_shape_e16", H=6144, I=2048, E=16, k=8, T=1, seed=9)
+    ctx = moe.MoeCtx(0)
+    try:
+        L4 = MoeLayer(ctx, w.H, w.I, w.E, w.k, bits=4)
+        L2 = MoeLayer(ctx, w.H, w.I, w.E, w.k, bits=2)
+        for e, g, u, d in wl.iter_experts(w, range(w.E)):
+            (L4 if e % 3 else L2).set_expert_fp32(e, g, u, d)
+        L4.set_shared_fp32(*wl.shared_fp32(w))
+        torch.cuda.synchronize()
+        bits = np.array([4 if e % 3 else 2 for e in range(w.E)], np.uint8)
+        table = torch.where(torch.from_numpy(bits == 4).cuda()[:, None], L4.experts.table, L2.experts.table).contiguous()
+        osh = orc.pack_expert(4, *wl.shared_fp32(w))
+        x = wl.hidden_fp32(w, 1)
+        xq_o, sx_o = orc.quantize_act(x)
+        rng = np.random.default_rng(11)
+        for rep in range(2):
+            idx = rng.choice(w.E, size=w.k, replace=False).astype(np.int32)[None, :]
+            wts = rng.random((1, w.k)).astype(np.float32)
+            log(f"mixed GLM shape, ids {idx[0].tolist()}")
+            y = torch.full((1, w.k + 1, w.H), 7.0, dtype=torch.float32, device="cuda")
+            out = torch.empty((1, w.H), dtype=torch.float32, device="cuda")
+            moe.moe_expert_ffn_mixed(ctx, table, L4.shared.struct(0), 4, torch.from_numpy(bits).cuda(), (4, 2),
+                                     torch.from_numpy(xq_o).cuda(), torch.from_numpy(sx_o).cuda(),
+                                     torch.from_numpy(idx).cuda(), w.H, w.I, w.E, y,
+                                     topk_w=torch.from_numpy(wts).cuda(), out=out)
+            ctx.check()
+            ref = torch.empty_like(out)
+            moe.moe_combine(ctx, y, torch.from_numpy(wts).cuda(), True, ref)
+            torch.cuda.synchronize()
+            yg, og = y.cpu().numpy(), out.cpu().numpy()
+            assert np.array_equal(og.view(np.uint32), ref.cpu().numpy().view(np.uint32))
+            ys = []
+            for j in range(w.k):
+                e = int(idx[0, j])
+                ex = orc.pack_expert(int(bits[e]), *wl.expert_fp32(w, e))
+                r = orc.expert_token(ex, xq_o[0], float(sx_o[0]))["y"]
+                assert np.array_equal(yg[0, j].view(np.uint32), r.view(np.uint32)), (rep, j, e)
+                ys.append(r)
+            ysh = orc.expert_token(osh, xq_o[0], float(sx_o[0]))["y"]
+            assert np.array_equal(yg[0, w.k].view(np.uint32), ysh.view(np.uint32)), rep
+            oref = orc.combine(np.stack(ys + [ysh])[None], wts, True)
+            assert rel_row_err(og, oref).max() < 1e-3
+    finally:
+        ctx.close()
