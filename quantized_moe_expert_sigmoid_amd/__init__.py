@@ -311,23 +311,32 @@ FFN_BY_BITS = {4: moe_expert_ffn_q4, 8: moe_expert_ffn_q8, 2: moe_expert_ffn_q2}
 def moe_expert_ffn_mixed(ctx, table, shared, shared_bits, expert_bits, widths, xq, sx, topk_idx, H, I, E, y_slots,
                          topk_w=None, out=None):
     """Every slot at its expert's width (expert_bits, device uint8 [E]);
-    widths: the widths the layer has (iterable of 8, 4, 2). With out (and
-    topk_w): also the combine of the slots."""
+    widths: the widths the layer has (iterable of 8, 4, 2), or the mask
+    itself (an int, as moe_pool_call_widths gives it). With out (and
+    topk_w): also the combine of the slots. table and expert_bits may be raw
+    device addresses (a pool's own table, MoePool.layer_table)."""
     T, k = topk_idx.shape
-    _dev(table, torch.int64, "experts table", (E, 6))
+    if not isinstance(table, int):
+        _dev(table, torch.int64, "experts table", (E, 6))
     _dev(xq, torch.int8, "xq", (T, H))
     _dev(sx, torch.float32, "sx", (T,))
     _dev(topk_idx, torch.int32, "topk_idx")
     _dev(y_slots, torch.float32, "y_slots", (T, k + 1, H))
-    _dev(expert_bits, torch.uint8, "expert_bits", (E,))
+    if not isinstance(expert_bits, int):
+        _dev(expert_bits, torch.uint8, "expert_bits", (E,))
     if out is not None:
         _dev(out, torch.float32, "out", (T, H))
         _dev(topk_w, torch.float32, "topk_w", (T, k))
-    mask = 0
-    for b in widths:
-        mask |= 1 << int(b)
+    if isinstance(widths, int):
+        mask = widths
+    else:
+        mask = 0
+        for b in widths:
+            mask |= 1 << int(b)
     sh = ctypes.byref(shared) if shared is not None else None
-    _ck(lib().moe_expert_ffn_mixed(ctx.handle, table.data_ptr(), sh, int(shared_bits), expert_bits.data_ptr(), mask,
+    tp = table if isinstance(table, int) else table.data_ptr()
+    bp = expert_bits if isinstance(expert_bits, int) else expert_bits.data_ptr()
+    _ck(lib().moe_expert_ffn_mixed(ctx.handle, tp, sh, int(shared_bits), bp, mask,
                                    xq.data_ptr(), sx.data_ptr(), topk_idx.data_ptr(), _ptr(topk_w), T, H, I, E, k,
                                    y_slots.data_ptr(), _ptr(out)))
     return y_slots

@@ -373,3 +373,60 @@ def test_pool_own_tables_copy_only_changes(moe, ctx, syn):
             pool.prepare(0, np.array([[0]], np.int32), ext_t, own[1][1])
     finally:
         pool.close()
+
+
+@pytest.mark.parametrize("slots", [8, 10])
+def test_pool_one_token_mixed_loop(moe, ctx, syn, slots):
+    """The decode loop through the pool, one token per call, as the stack
+    benchmark runs it: prepare into the layer's own table, the call's widths,
+    one mixed-width FFN call with the combine. 40 calls over two layers are
+    enqueued back to back while the pool keeps evicting (the two layers'
+    blocks take about 13 int4-block sizes; 8 slots always leave room for a
+    call's three experts whatever the first-fit placement left behind, as
+    2 hits split at most 6 free slots into 3 extents); every call's slots
+    and output equal those of the same mixed call on an all-resident table,
+    and the output equals moe_combine over its slots."""
+    E, k, L = 8, 3, 2
+    b4, h4 = make_blocks(moe, ctx, syn, 4, E, seed=37)
+    b2, h2 = make_blocks(moe, ctx, syn, 2, E, seed=37)
+    shared_blocks, _ = make_blocks(moe, ctx, syn, 4, 1, seed=38)
+    shared = shared_blocks.struct(0)
+    wbits = np.array([4, 2, 4, 4, 2, 4, 2, 4], np.uint8)
+    full = torch.where(torch.from_numpy(wbits == 4).cuda()[:, None], b4.table, b2.table).contiguous()
+    full_bits = torch.from_numpy(wbits).cuda()
+    pool = moe.MoePool(ctx, slots * b4.block_bytes, L, E, H, I)
+    try:
+        for layer in range(L):
+            for e in range(E):
+                pool.register(layer, e, int(wbits[e]), h4[e] if wbits[e] == 4 else h2[e])
+        own = [pool.layer_table(layer) for layer in range(L)]
+        rng = np.random.default_rng(slots)
+        calls = []
+        for c in range(40):
+            layer = c % L
+            ids = rng.choice(E, size=k, replace=False).astype(np.int32)[None, :]
+            wts = torch.from_numpy(rng.random((1, k)).astype(np.float32)).cuda()
+            xq, sx = token_inputs(moe, ctx, syn, 1, seed=200 + c)
+            idx = torch.from_numpy(ids).cuda()
+            y = torch.zeros((1, k + 1, H), dtype=torch.float32, device="cuda")
+            out = torch.empty((1, H), dtype=torch.float32, device="cuda")
+            pool.prepare(layer, ids, own[layer][0], own[layer][1])
+            mask = pool.call_widths() | (1 << 4)
+            assert mask == sum({1 << int(wbits[e]) for e in ids[0]} | {1 << 4})
+            moe.moe_expert_ffn_mixed(ctx, own[layer][0], shared, 4, own[layer][1], mask, xq, sx, idx, H, I, E, y,
+                                     topk_w=wts, out=out)
+            calls.append((xq, sx, idx, wts, mask, y, out))
+        torch.cuda.synchronize()
+        ctx.check()
+        assert pool.table_stats()["skipped"] > 0
+        for c, (xq, sx, idx, wts, mask, y, out) in enumerate(calls):
+            ry = torch.zeros_like(y)
+            ro = torch.empty_like(out)
+            moe.moe_expert_ffn_mixed(ctx, full, shared, 4, full_bits, mask, xq, sx, idx, H, I, E, ry, topk_w=wts,
+                                     out=ro)
+            rc = torch.empty_like(out)
+            moe.moe_combine(ctx, y, wts, True, rc)
+            torch.cuda.synchronize()
+            assert torch.equal(y, ry) and torch.equal(out, ro) and torch.equal(out, rc), c
+    finally:
+        pool.close()
