@@ -238,12 +238,14 @@ def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, kern, bits, T, H, I, E, 
 
 @pytest.mark.parametrize("bits", [4, 8, 2])
 @pytest.mark.parametrize("H,I,E,k,shared", [(128, 64, 8, 2, True), (512, 192, 16, 8, True), (256, 128, 8, 3, False),
-                                            (1024, 448, 40, 6, False)])
+                                            (1024, 448, 40, 6, False), (64, 64, 2, 1, True), (128, 64, 4, 4, False),
+                                            (8192, 128, 8, 2, True)])
 def test_ffn_one_token(moe, ctx, orc, syn, bits, H, I, E, k, shared):
     """One token through the per-step expert FFN: the single-token kernels with
-    the routing given (the default for T = 1) and the vector kernels, every
-    intermediate bit-exact against the oracle; then a token with dropped slots
-    (id -1), whose slots stay untouched."""
+    the routing given (the default for T = 1; hidden 8192 is past their limit
+    and takes the vector kernels) and the vector kernels, every intermediate
+    bit-exact against the oracle; then a token with dropped slots (id -1),
+    whose slots stay untouched."""
     idx = random_routing(syn, 1, E, k, 90 + k)
     for kern in ("auto", "dot4"):
         check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, 1, H, I, E, k, idx, seed=91 + bits, with_shared=shared)
