@@ -322,11 +322,15 @@ moe_status moe_pool_register(moe_pool *pool, int layer, int expert, int bits, co
  * that table's widths): the pool copies into it only when the layer's table
  * bytes changed since its last copy there (an expert of the layer loaded,
  * evicted or re-loaded), so at a high hit rate most calls copy nothing. A
- * pointer into another layer's own table is MOE_EINVAL. n_miss_host (nullable): this
+ * pointer into another layer's own table is MOE_EINVAL. n_miss_host
+ * (nullable): this
  * call's misses; an id of -1 (a slot dropped by top-p) is skipped.
  * MOE_EINVAL for another id outside [0, E) or an unregistered
  * expert; MOE_EPOOL when the slab cannot hold this call's experts beside the
- * pinned ones (the pool stays consistent). A bookkeeping-only pool takes
+ * pinned ones, even after evicting every other unpinned expert (placement is
+ * first-fit without moving resident blocks, so the free space left between
+ * this call's resident experts can refuse a call whose total would fit; the
+ * pool stays consistent). A bookkeeping-only pool takes
  * table_dev = bits_dev = NULL. */
 moe_status moe_pool_prepare(moe_pool *pool, int layer, const int32_t *topk_idx_host, int T, int k,
                             moe_expert_w *table_dev, uint8_t *bits_dev, int *n_miss_host);
