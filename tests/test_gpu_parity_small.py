@@ -438,6 +438,59 @@ def test_ffn_mixed_last_width_without_work(moe, ctx, orc, syn):
     assert np.array_equal(host(out).view(np.uint32), host(ref).view(np.uint32))
 
 
+def test_ffn_mixed_one_token_graph_replay(moe, ctx, orc, syn):
+    """The one-token mixed call (single-token kernels of each width, the
+    combine in the last down kernel) captured in a HIP graph for four tokens:
+    every replay, with eager work and synchronisations in between, equals the
+    eager results, slot by slot and combined."""
+    H, I, E, k = 256, 128, 8, 3
+    b4, sh4, _, _ = make_experts(moe, orc, syn, 4, H, I, E, seed=78)
+    b2, _, _, _ = make_experts(moe, orc, syn, 2, H, I, E, seed=78)
+    bits = np.array([4, 2, 4, 2, 4, 4, 2, 4], np.uint8)
+    table = torch.where(torch.from_numpy(bits == 4).cuda()[:, None], b4.table, b2.table).contiguous()
+    eb = dev(bits)
+    toks = []
+    for t in range(4):
+        xq_o, sx_o = orc.quantize_act(syn.hidden(79 + t, 1, H))
+        idx = random_routing(syn, 1, E, k, 80 + t)
+        wts = np.abs(syn.normal(81, syn.stream_id(syn.K_MISC, 81, t), (1, k))).astype(np.float32)
+        toks.append((dev(xq_o), dev(sx_o), dev(idx), dev(wts)))
+    def run(i, y, out):
+        xq, sx, idx, wts = toks[i]
+        moe.moe_expert_ffn_mixed(ctx, table, sh4.struct(0), 4, eb, (4, 2), xq, sx, idx, H, I, E, y, topk_w=wts,
+                                 out=out)
+    eager = []
+    for i in range(4):
+        y = torch.zeros((1, k + 1, H), dtype=torch.float32, device="cuda")
+        out = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        run(i, y, out)
+        torch.cuda.synchronize()
+        eager.append((y, out))
+    ys = [torch.zeros((1, k + 1, H), dtype=torch.float32, device="cuda") for _ in range(4)]
+    outs = [torch.empty((1, H), dtype=torch.float32, device="cuda") for _ in range(4)]
+    cap = torch.cuda.Stream()
+    old = ctx.stream
+    ctx.set_stream(cap)
+    g = torch.cuda.CUDAGraph()
+    try:
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(4):
+                run(i, ys[i], outs[i])
+    finally:
+        ctx.set_stream(old)
+    for rep in range(3):
+        for y in ys:
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(4):
+            assert torch.equal(ys[i], eager[i][0]) and torch.equal(outs[i], eager[i][1]), (rep, i)
+        run(rep, torch.zeros((1, k + 1, H), dtype=torch.float32, device="cuda"),
+            torch.empty((1, H), dtype=torch.float32, device="cuda"))  # eager work between replays
+        torch.cuda.synchronize()
+    ctx.check()
+
+
 # --------------------------------------------------------------------------
 # combine and the whole layer
 # --------------------------------------------------------------------------
