@@ -200,7 +200,8 @@ moe_status moe_bucket_tokens(moe_ctx *ctx, const int32_t *topk_idx, int T, int k
  * pointers). shared: HOST pointer to one moe_expert_w, or NULL.
  * expert_bits: DEVICE uint8 [E] or NULL. When given, only experts whose
  * entry equals this entry point's width are computed (slots of the others
- * are left untouched), so a mixed-precision layer is one call per width.
+ * are left untouched), so a mixed-precision layer is one call per width (or
+ * one moe_expert_ffn_mixed call).
  * xq int8 [T][H], sx fp32 [T]: from moe_quantize_act_i8. topk_idx int32
  * [T][k]; an id of -1 (a slot dropped by top-p) names no expert: its slot is
  * not computed and not written; any other id outside [0, E), or an id
