@@ -293,7 +293,10 @@ typedef struct moe_pool moe_pool;
  * n_layers x n_experts experts of hidden H and intermediate I (multiples of
  * 64). ctx == NULL creates a bookkeeping-only pool: no memory and no copies,
  * the same residency decisions and statistics (capacity planning, tests on a
- * host without a GPU). MOE_ENOMEM if the slab cannot be allocated. */
+ * host without a GPU). MOE_ENOMEM if the slab cannot be allocated. With a
+ * context the pool also allocates the layers' own device tables
+ * (moe_pool_layer_table): n_layers x (n_experts x 49 bytes, rounded up to
+ * 256), and eight pinned host staging buffers of n_experts x 49 bytes. */
 moe_status moe_pool_create(moe_ctx *ctx, size_t capacity_bytes, int n_layers, int n_experts, int H, int I,
                            moe_pool **out);
 /* Wait for the pool's copies and for the context stream (whose kernels may
