@@ -299,3 +299,22 @@ def test_pin_hot_keeps_the_most_requested(moe, tmp_path):
     with pytest.raises(moe.MoeError):
         pool.pin_hot(100 * block(moe, 4))  # beyond the capacity
     pool.close()
+
+
+def test_bookkeeping_pool_has_no_device_tables(moe):
+    """A pool without a context keeps no device tables: asking for a layer's
+    own table is an error, and prepare takes no table pointers; the widths of
+    the latest call are still reported."""
+    pool = moe.MoePool(None, 4 * moe.moe_expert_block_layout(4, 256, 128)[0], 2, 4, 256, 128)
+    for e in range(4):
+        pool.register(0, e, 4 if e % 2 else 2, None)
+    with pytest.raises(moe.MoeError):
+        pool.layer_table(0)
+    pool.prepare(0, np.array([[1, 3]], np.int32))
+    assert pool.call_widths() == 1 << 4
+    pool.prepare(0, np.array([[0, 1]], np.int32))
+    assert pool.call_widths() == (1 << 4) | (1 << 2)
+    pool.prepare(0, np.array([[-1, -1]], np.int32))
+    assert pool.call_widths() == 0
+    assert pool.table_stats() == {"copies": 0, "skipped": 0}
+    pool.close()
