@@ -436,7 +436,7 @@ moe_status moe_ctx_enable_timing(moe_ctx *ctx, int enable);
 moe_status moe_ctx_read_timing(moe_ctx *ctx, double *ms_host, int *n_host);
 
 /* Streaming-read probe: the measured HBM read ceiling for a launch of a
- * given size, against which the weight-streaming kernels are judged beside
+ * given size, with which the weight-streaming kernels are compared beside
  * the data-sheet peak. Launches `reps` times a plain read kernel
  * (ctx->n_cu * wg_per_cu workgroups of 256 threads, 16-byte loads four deep,
  * grid-stride) on the context stream; launch r reads bytes_per_launch bytes
