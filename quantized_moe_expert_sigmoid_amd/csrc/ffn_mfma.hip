@@ -320,7 +320,10 @@ __device__ __forceinline__ int stage_tokens(const MArgs &a, const Ex &ex, int m0
 }
 
 // MB = 4: the tiles of more than 16 tokens; MB = 1: the one-block tiles
-// (SL: bytes of codes per token and staged slice)
+// (SL: bytes of codes per token and staged slice). When experts average 32
+// or more tokens (every remainder a full-size tile), the 64-token tiles stage
+// 256-byte slices: half the LDS, so more workgroups per CU (T = 2048: 1.80
+// against 1.86 ms per call); with fewer tokens 512-byte slices do better.
 template <int MB>
 struct GuShape {
   static constexpr int NB = MB == 4 ? 2 : 1, D = 2, SL = 512;
@@ -329,11 +332,12 @@ template <int MB>
 struct DnShape {
   static constexpr int NB = 2, D = 2, SL = 512;
 };
+constexpr int kSlWide = 256;  // the 64-token tiles' slice when experts average 32 or more tokens
 
 // ---------------------------------------------------------------------------
 // gate + up: a workgroup takes 64 NB rows of each, a wave 16 NB
 // ---------------------------------------------------------------------------
-template <int BITS, int MB, int NB, int D>
+template <int BITS, int MB, int NB, int D, int SL>
 __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8 *lds, int d, int m0, int ntile) {
   constexpr int OFF = QFmt<BITS>::kOff;
   Ex ex;
@@ -362,7 +366,7 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = acc[mb][1][nb] = v4i{0, 0, 0, 0};
-  tile_mma_lds<BITS, MB, 2, NB, D, GuShape<MB>::SL>(wrow, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
+  tile_mma_lds<BITS, MB, 2, NB, D, SL>(wrow, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
   // lane holds tokens 4*grp + r of each block, row row[nb]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -431,16 +435,16 @@ __device__ __forceinline__ void expert_major(const MArgs &a, int ntiles, int &u,
   u = u0 + (local - nt * n);
 }
 
-template <int BITS, int MB>
+template <int BITS, int MB, int SL = GuShape<MB>::SL>
 __global__ __launch_bounds__(kThreads) void gu_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
-  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * GuShape<MB>::SL];
+  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * SL];
   lds_u8 *abuf = (lds_u8 *)abuf_s;
   int u, nt;
   if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
   if constexpr (MB == 4) expert_major(a, ntiles, u, nt);
   const int2 un = a.units[MB == 4 ? u : a.ubig_max + u];
-  gu_tile<BITS, MB, GuShape<MB>::NB, GuShape<MB>::D>(a, tt_s, abuf, un.x, un.y, nt);
+  gu_tile<BITS, MB, GuShape<MB>::NB, GuShape<MB>::D, SL>(a, tt_s, abuf, un.x, un.y, nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -535,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void requant_mfma_kernel(MArgs a) {
 // ---------------------------------------------------------------------------
 // down: a workgroup takes 64 NB rows, a wave 16 NB
 // ---------------------------------------------------------------------------
-template <int BITS, int MB, int NB, int D>
+template <int BITS, int MB, int NB, int D, int SL>
 __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8 *lds, int d, int m0, int ntile) {
   constexpr int OFF = QFmt<BITS>::kOff;
   Ex ex;
@@ -560,7 +564,7 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = v4i{0, 0, 0, 0};
-  tile_mma_lds<BITS, MB, 1, NB, D, DnShape<MB>::SL>(wrow, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
+  tile_mma_lds<BITS, MB, 1, NB, D, SL>(wrow, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -580,16 +584,16 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
     }
 }
 
-template <int BITS, int MB>
+template <int BITS, int MB, int SL = DnShape<MB>::SL>
 __global__ __launch_bounds__(kThreads) void dn_mfma_kernel(MArgs a, int ntiles) {
   __shared__ TileTokens tt_s;
-  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * DnShape<MB>::SL];
+  __shared__ __align__(16) uint8_t abuf_s[2 * MB * 16 * SL];
   lds_u8 *abuf = (lds_u8 *)abuf_s;
   int u, nt;
   if (!xcd_work(a.n_units[MB == 4 ? 0 : 1], ntiles, u, nt)) return;
   if constexpr (MB == 4) expert_major(a, ntiles, u, nt);
   const int2 un = a.units[MB == 4 ? u : a.ubig_max + u];
-  dn_tile<BITS, MB, DnShape<MB>::NB, DnShape<MB>::D>(a, tt_s, abuf, un.x, un.y, nt);
+  dn_tile<BITS, MB, DnShape<MB>::NB, DnShape<MB>::D, SL>(a, tt_s, abuf, un.x, un.y, nt);
 }
 
 template <int BITS>
@@ -606,9 +610,14 @@ moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *x
   // workgroups return at once. The two tile kinds write disjoint rows: the
   // 64-token tiles run on the side stream, overlapping the one-block tiles.
   moe_status st;
+  const bool wide = a.small_max == 0;  // experts average 32 or more tokens
   if ((st = moe_side_fork(ctx))) return st;
-  moe_launch_on(ctx, ctx->side, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max * g4), dim3(kThreads), a,
-                g4);
+  if (wide)
+    moe_launch_on(ctx, ctx->side, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4, kSlWide>, dim3(a.ubig_max * g4),
+                  dim3(kThreads), a, g4);
+  else
+    moe_launch_on(ctx, ctx->side, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max * g4), dim3(kThreads),
+                  a, g4);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
   moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 1>, dim3(usmall * g1), dim3(kThreads), a, g1);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
@@ -616,8 +625,12 @@ moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *x
   moe_launch(ctx, MOE_STAGE_REQUANT, requant_mfma_kernel<BITS>, dim3(a.T * (a.k + 1)), dim3(kThreads), a);
   MOE_CHECK_LAUNCH("requant_mfma_kernel");
   if ((st = moe_side_fork(ctx))) return st;
-  moe_launch_on(ctx, ctx->side, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max * d4), dim3(kThreads), a,
-                d4);
+  if (wide)
+    moe_launch_on(ctx, ctx->side, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4, kSlWide>, dim3(a.ubig_max * d4),
+                  dim3(kThreads), a, d4);
+  else
+    moe_launch_on(ctx, ctx->side, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max * d4), dim3(kThreads), a,
+                  d4);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
   moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 1>, dim3(usmall * d1), dim3(kThreads), a, d1);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
