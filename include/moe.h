@@ -44,7 +44,13 @@
  *    enqueued.
  *  - Ownership: the caller owns every tensor it passes; the library never
  *    frees caller memory. The library owns only the context's scratch memory
- *    (grown on demand with hipMalloc, freed by moe_ctx_destroy) and pools.
+ *    and pools. Scratch grows on demand with hipMalloc when a call needs more
+ *    than the context holds; a buffer it outgrows is kept, not freed, until
+ *    moe_ctx_destroy, so work already enqueued and HIP graphs captured from
+ *    earlier calls keep valid addresses (an eager call at a larger size
+ *    between two replays of a graph is safe). A call made during graph
+ *    capture that needs to grow the scratch fails (hipMalloc cannot be
+ *    captured): run one call at the largest size before capturing.
  *  - A context is bound to one device and one stream and is not thread-safe;
  *    calls on one context must not overlap.
  *  - Errors: every call returns a moe_status; on failure moe_last_error()

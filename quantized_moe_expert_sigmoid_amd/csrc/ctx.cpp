@@ -26,16 +26,17 @@ moe_status moe_hip_fail(hipError_t e, const char *what) {
 extern "C" const char *moe_last_error(void) { return g_err; }
 extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+// Scratch grows by allocating a larger buffer; the one it replaces is kept
+// until moe_ctx_destroy, never freed earlier: a HIP graph captured from
+// earlier calls holds its address, and so may work still queued on the
+// stream, so freeing it would turn a later replay into a use of freed memory.
 static moe_status grow(moe_ctx *ctx, void **buf, size_t *have, size_t bytes, void **out) {
   if (bytes > *have) {
-    if (*buf) {
-      MOE_HIP(hipStreamSynchronize(ctx->stream));
-      MOE_HIP(hipFree(*buf));
-      *buf = nullptr;
-      *have = 0;
-    }
-    size_t want = moe_round_up(bytes + bytes / 4, 1 << 20);
-    MOE_HIP(hipMalloc(buf, want));
+    const size_t want = moe_round_up(bytes + bytes / 4, 1 << 20);
+    void *p = nullptr;
+    MOE_HIP(hipMalloc(&p, want));
+    if (*buf) ctx->retired.push_back(*buf);
+    *buf = p;
     *have = want;
   }
   *out = *buf;
@@ -188,6 +189,7 @@ extern "C" void moe_ctx_destroy(moe_ctx *ctx) {
   for (auto e : ctx->event_pool) (void)hipEventDestroy(e);
   if (ctx->scratch) (void)hipFree(ctx->scratch);
   if (ctx->io) (void)hipFree(ctx->io);
+  for (void *p : ctx->retired) (void)hipFree(p);
   if (ctx->dev_small) (void)hipFree(ctx->dev_small);
   delete ctx;
 }

@@ -31,6 +31,9 @@ struct moe_ctx {
   // which the per-step entry points reuse)
   void *io = nullptr;
   size_t io_bytes = 0;
+  // buffers that scratch or io outgrew: freed only by moe_ctx_destroy, as
+  // captured graphs and queued work may still address them
+  std::vector<void *> retired;
   // small persistent device block: error flags and counters
   uint32_t *dev_small = nullptr;  // [0] error flags, [1..] counters
   int ffn_kernels = MOE_FFN_AUTO;

@@ -142,11 +142,28 @@ def test_glm_mtp_verify_t96(glm, orc, oexp, packed_seen):
     run_and_check(glm, orc, oexp, x, None, [5, 95], packed_seen)
 
 
+def check_expert_tiles(orc, oexp, got, x, e):
+    """Every (token, slot) pair of expert e's first 64-token tile and of its
+    last tile (the bucket's stable order: ascending token, then slot), each
+    slot output bit-exact against the oracle."""
+    xq_o, sx_o = orc.quantize_act(x)
+    pairs = np.argwhere(got["idx"] == e)  # row-major: ascending (token, slot)
+    n = len(pairs)
+    last = n - (n % 64 or 64)
+    chosen = list(pairs[:64]) + list(pairs[max(last, 64):])
+    for t, j in chosen:
+        y = orc.expert_token(oexp.get(int(e)), xq_o[t], float(sx_o[t]))["y"]
+        assert np.array_equal(got["y"][t, j].view(np.uint32), y.view(np.uint32)), (e, t, j)
+    log(f"expert {e}: {n} tokens, {len(chosen)} of them (first and last tile) bit-exact")
+
+
 def test_glm_prefill_t2048(glm, orc, oexp, packed_seen):
     from synth import workloads as wl
     log("prefill T=2048")
     x = wl.hidden_fp32(wl.PREFILL2048, 2048)
-    run_and_check(glm, orc, oexp, x, None, [0, 2047], packed_seen)
+    got = run_and_check(glm, orc, oexp, x, None, [0, 2047], packed_seen)
+    counts = np.bincount(got["idx"].ravel(), minlength=256)
+    check_expert_tiles(orc, oexp, got, x, int(np.argmax(counts)))
 
 
 def test_glm_prefill_t2048_zipf(glm, orc, oexp, packed_seen):
@@ -269,3 +286,48 @@ def test_glm_decode_t1_topp(glm, orc, oexp):
             assert rel_row_err(got["out"], ref).max() < 1e-3
     finally:
         L.top_p = 0.0
+
+
+def test_glm_graph_replay_after_scratch_growth(glm):
+    """A graph captured on a fresh context from one-token calls keeps working
+    after an eager 64-token call has grown the context's scratch: the buffer
+    the graph addresses is kept (not freed) until the context is destroyed,
+    so every replay still equals the eager one-token results."""
+    from synth import workloads as wl
+    moe, ctx0, L = glm
+    fresh = moe.MoeCtx(0)
+    L.ctx = fresh
+    try:
+        xs = [torch.from_numpy(wl.hidden_fp32(wl.DECODE1, 1, batch=b)).cuda() for b in range(3)]
+        eager = []
+        for x in xs:
+            r = L.forward(x)
+            torch.cuda.synchronize()
+            eager.append((r["y"].clone(), r["out"].clone()))
+        cap = torch.cuda.Stream()
+        fresh.set_stream(cap)
+        g = torch.cuda.CUDAGraph()
+        outs = []
+        with torch.cuda.graph(g, stream=cap):
+            for x in xs:
+                r = L.forward(x)
+                outs.append((r["y"].clone(), r["out"].clone()))
+        fresh.set_stream(torch.cuda.current_stream())
+        x64 = torch.from_numpy(wl.hidden_fp32(wl.DECODE64, 64)).cuda()
+        z64 = torch.from_numpy(wl.logits_fp32(wl.DECODE64, 64)).cuda()
+        keep, L.bias = L.bias, None
+        try:
+            for rep in range(3):
+                L.forward(x64, z64)  # grows the scratch on the first pass
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                for i in range(len(xs)):
+                    assert torch.equal(outs[i][0], eager[i][0]), (rep, i)
+                    assert torch.equal(outs[i][1], eager[i][1]), (rep, i)
+        finally:
+            L.bias = keep
+        fresh.check()
+    finally:
+        L.ctx = ctx0
+        fresh.close()
