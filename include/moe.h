@@ -280,6 +280,30 @@ moe_status moe_layer_forward(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, 
                              const moe_expert_w *shared, int T, int H, int I, float *out, int32_t *topk_idx,
                              float *topk_w, int8_t *xq, float *sx, float *y_slots);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer call as moe_layer_forward -- same arguments, kernels, arithmetic and
+ * results -- whose scratch is the library's static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU (resident from the library's first
+ * context on that GPU until the process ends) instead of the context's
+ * growable scratch. The call allocates nothing: no hipMalloc, no hipFree, no
+ * stream or event creation. The caller still provides every input and the
+ * outputs it names. Scratch needed: one token at most a few hundred KB; more
+ * tokens at the GLM shape (H 6144, I 2048, E 256, k 8) about 330 KB per
+ * token, so up to about 140 tokens fit. A call needing more than the array
+ * holds is MOE_EINVAL before anything is enqueued, as is a call with
+ * per-kernel timing on (moe_ctx_enable_timing records events). Every call of
+ * this entry point on one GPU shares that GPU's array, which keeps the last
+ * call's contents (no part of it needs clearing: each call writes every word
+ * it reads): calls that overlap on one GPU -- from two contexts, or on two
+ * streams without ordering between them -- race. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+moe_status moe_layer_forward_noalloc(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x,
+                                     const float *logits, const float *w_router, const float *bias,
+                                     const moe_expert_w *experts, const moe_expert_w *shared, int T, int H, int I,
+                                     float *out, int32_t *topk_idx, float *topk_w, int8_t *xq, float *sx,
+                                     float *y_slots);
+
 /* ---------------------------------------------------------------------- */
 /* Expert pool ([P-load], [P-mem], [P-dedup])                             */
 /* ---------------------------------------------------------------------- */

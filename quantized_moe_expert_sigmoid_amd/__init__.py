@@ -102,6 +102,8 @@ _SIGS = {
     "moe_pool_call_widths": (_i32, [_vp, ctypes.POINTER(_i32)]),
     "moe_pool_table_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 2),
     "moe_pool_layer_table": (_i32, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
+    "moe_layer_forward_noalloc": (_i32, [_vp, _i32, ctypes.POINTER(RouterCfg), _vp, _vp, _vp, _vp, _vp,
+                                         ctypes.POINTER(ExpertW), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -372,6 +374,23 @@ def moe_layer_forward(ctx: MoeCtx, bits: int, x: torch.Tensor, table: torch.Tens
                       routed_scale: float = 1.0, topk_idx=None, topk_w=None, xq=None, sx=None, y_slots=None,
                       top_p: float = 0.0):
     """Whole layer in one call (see include/moe.h). Optional outputs may be None."""
+    return _layer("moe_layer_forward", ctx, bits, x, table, shared, k, I, out, w_router, bias, logits, routed_scale,
+                  topk_idx, topk_w, xq, sx, y_slots, top_p)
+
+
+def moe_layer_forward_noalloc(ctx: MoeCtx, bits: int, x: torch.Tensor, table: torch.Tensor, shared: ExpertW | None,
+                              k: int, I: int, out: torch.Tensor, w_router: torch.Tensor | None = None,
+                              bias: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                              routed_scale: float = 1.0, topk_idx=None, topk_w=None, xq=None, sx=None,
+                              y_slots=None, top_p: float = 0.0):
+    """moe_layer_forward with the library's static scratch: allocates nothing
+    (see include/moe.h for its size limit and sharing rule)."""
+    return _layer("moe_layer_forward_noalloc", ctx, bits, x, table, shared, k, I, out, w_router, bias, logits,
+                  routed_scale, topk_idx, topk_w, xq, sx, y_slots, top_p)
+
+
+def _layer(name, ctx, bits, x, table, shared, k, I, out, w_router, bias, logits, routed_scale, topk_idx, topk_w, xq,
+           sx, y_slots, top_p):
     T, H = x.shape
     E = table.shape[0]
     _dev(x, torch.float32, "x")
@@ -390,10 +409,10 @@ def moe_layer_forward(ctx: MoeCtx, bits: int, x: torch.Tensor, table: torch.Tens
             _dev(t, dt, nm, shp)
     cfg = RouterCfg(E, k, float(routed_scale), 1 if logits is not None else 0, float(top_p))
     sh = ctypes.byref(shared) if shared is not None else None
-    _ck(lib().moe_layer_forward(ctx.handle, bits, ctypes.byref(cfg), x.data_ptr(), _ptr(logits),
-                                None if logits is not None else w_router.data_ptr(), _ptr(bias), table.data_ptr(), sh,
-                                T, H, I, out.data_ptr(), _ptr(topk_idx), _ptr(topk_w), _ptr(xq), _ptr(sx),
-                                _ptr(y_slots)))
+    _ck(getattr(lib(), name)(ctx.handle, bits, ctypes.byref(cfg), x.data_ptr(), _ptr(logits),
+                             None if logits is not None else w_router.data_ptr(), _ptr(bias), table.data_ptr(), sh,
+                             T, H, I, out.data_ptr(), _ptr(topk_idx), _ptr(topk_w), _ptr(xq), _ptr(sx),
+                             _ptr(y_slots)))
     return out
 
 

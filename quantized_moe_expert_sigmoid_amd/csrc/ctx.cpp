@@ -1,6 +1,8 @@
 // Context, error reporting, argument validation and the exported C ABI.
 // Kernels live in the .hip files; every entry point here validates its
 // arguments completely before anything is enqueued.
+#include <algorithm>
+#include <mutex>
 #include <new>
 #include <stdarg.h>
 #include <stdio.h>
@@ -44,11 +46,57 @@ static moe_status grow(moe_ctx *ctx, void **buf, size_t *have, size_t bytes, voi
 }
 
 moe_status moe_scratch(moe_ctx *ctx, size_t bytes, void **out) {
+  if (ctx->fixed_scr) {  // an allocation-free call: its region of the static array
+    if (bytes > ctx->fixed_scr_bytes)
+      return moe_fail(MOE_EINVAL, "allocation-free call: %zu scratch bytes needed, %zu reserved", bytes,
+                      ctx->fixed_scr_bytes);
+    *out = ctx->fixed_scr;
+    return MOE_OK;
+  }
   return grow(ctx, &ctx->scratch, &ctx->scratch_bytes, bytes, out);
 }
 
 moe_status moe_io_scratch(moe_ctx *ctx, size_t bytes, void **out) {
+  if (ctx->fixed_io) {
+    if (bytes > ctx->fixed_io_bytes)
+      return moe_fail(MOE_EINVAL, "allocation-free call: %zu io bytes needed, %zu reserved", bytes,
+                      ctx->fixed_io_bytes);
+    *out = ctx->fixed_io;
+    return MOE_OK;
+  }
   return grow(ctx, &ctx->io, &ctx->io_bytes, bytes, out);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: one static device array per
+// GPU (the code object's own global, resident until the process ends). Host
+// code never uses the array's name as an address: moe_ctx_create takes the
+// device address of each GPU's copy once, with that device current, and the
+// allocation-free call hands that address to the launchers.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char noalloc_scratch[kNoAllocBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_noalloc_mu;
+static void *g_noalloc_ptr[kMaxDevices];
+
+// With `device` current: record the device address of its copy of the array.
+static moe_status noalloc_bind(int device) {
+  if (device < 0 || device >= kMaxDevices)
+    return moe_fail(MOE_EUNSUPPORTED, "moe_ctx_create: device %d beyond the %d the library tracks", device,
+                    kMaxDevices);
+  std::lock_guard<std::mutex> g(g_noalloc_mu);
+  if (g_noalloc_ptr[device]) return MOE_OK;
+  void *p = nullptr;
+  MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)));
+  if (!p) return moe_fail(MOE_EHIP, "hipGetSymbolAddress(noalloc_scratch) returned NULL");
+  g_noalloc_ptr[device] = p;
+  return MOE_OK;
+}
+
+static void *noalloc_ptr(int device) {
+  std::lock_guard<std::mutex> g(g_noalloc_mu);
+  return (device >= 0 && device < kMaxDevices) ? g_noalloc_ptr[device] : nullptr;
 }
 
 extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out) {
@@ -63,6 +111,8 @@ extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return moe_fail(MOE_EUNSUPPORTED, "moe_ctx_create: device %d is %s, this library is built for gfx950", device,
                     prop.gcnArchName);
+  moe_status st = noalloc_bind(device);
+  if (st) return st;
   moe_ctx *c = new (std::nothrow) moe_ctx();
   if (!c) return moe_fail(MOE_ENOMEM, "moe_ctx_create: host allocation");
   c->device = device;
@@ -75,21 +125,23 @@ extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out
   }
   e = hipMemset(c->dev_small, 0, 4096);
   if (e == hipSuccess) e = hipDeviceSynchronize();
+  // the side stream and its events exist from the start, so no later call
+  // (the allocation-free one included) creates them
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
   if (e != hipSuccess) {
+    if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+    if (c->side) (void)hipStreamDestroy(c->side);
     (void)hipFree(c->dev_small);
     delete c;
-    return moe_hip_fail(e, "hipMemset(ctx counters)");
+    return moe_hip_fail(e, "moe_ctx_create: counters, side stream and events");
   }
   *out = c;
   return MOE_OK;
 }
 
 moe_status moe_side_fork(moe_ctx *ctx) {
-  if (!ctx->side) {
-    MOE_HIP(hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
-    MOE_HIP(hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming));
-    MOE_HIP(hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming));
-  }
   MOE_HIP(hipEventRecord(ctx->ev_fork, ctx->stream));
   MOE_HIP(hipStreamWaitEvent(ctx->side, ctx->ev_fork, 0));
   return MOE_OK;
@@ -412,55 +464,129 @@ extern "C" size_t moe_expert_block_layout(int bits, int H, int I, size_t *offset
   return off;
 }
 
-extern "C" moe_status moe_layer_forward(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x,
-                                        const float *logits, const float *w_router, const float *bias,
-                                        const moe_expert_w *experts, const moe_expert_w *shared, int T, int H, int I,
-                                        float *out, int32_t *topk_idx, float *topk_w, int8_t *xq, float *sx,
-                                        float *y_slots) {
-  moe_status st = bind(ctx, "moe_layer_forward");
+// Argument checks of the whole-layer entry points (T == 0 passes).
+static moe_status layer_check(const char *fn, moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x,
+                              const float *logits, const float *w_router, const moe_expert_w *experts,
+                              const moe_expert_w *shared, int T, int H, int I, float *out, int8_t *xq,
+                              float *y_slots) {
+  moe_status st = bind(ctx, fn);
   if (st) return st;
-  REQUIRE(bits == 8 || bits == 4 || bits == 2, "moe_layer_forward: bits %d not in {8,4,2}", bits);
-  REQUIRE(cfg, "moe_layer_forward: cfg is NULL");
-  REQUIRE(cfg->top_p == cfg->top_p, "moe_layer_forward: top_p is NaN");
+  REQUIRE(bits == 8 || bits == 4 || bits == 2, "%s: bits %d not in {8,4,2}", fn, bits);
+  REQUIRE(cfg, "%s: cfg is NULL", fn);
+  REQUIRE(cfg->top_p == cfg->top_p, "%s: top_p is NaN", fn);
   const int E = cfg->n_experts, k = cfg->top_k;
-  REQUIRE(E >= 1 && E <= 1024 && k >= 1 && k <= 16 && k <= E, "moe_layer_forward: E %d k %d", E, k);
-  REQUIRE(T >= 0 && (int64_t)T * (k + 1) <= (1 << 22), "moe_layer_forward: T %d", T);
-  REQUIRE(dim_ok(H) && dim_ok(I), "moe_layer_forward: H %d and I %d must be positive multiples of 64, <= 8192", H, I);
+  REQUIRE(E >= 1 && E <= 1024 && k >= 1 && k <= 16 && k <= E, "%s: E %d k %d", fn, E, k);
+  REQUIRE(T >= 0 && (int64_t)T * (k + 1) <= (1 << 22), "%s: T %d", fn, T);
+  REQUIRE(dim_ok(H) && dim_ok(I), "%s: H %d and I %d must be positive multiples of 64, <= 8192", fn, H, I);
   if (T == 0) return MOE_OK;
-  REQUIRE(x && experts && out, "moe_layer_forward: NULL pointer");
+  REQUIRE(x && experts && out, "%s: NULL pointer", fn);
   REQUIRE(cfg->logits_in ? (logits != nullptr) : (w_router != nullptr),
-          "moe_layer_forward: logits_in needs logits, otherwise w_router is required");
+          "%s: logits_in needs logits, otherwise w_router is required", fn);
   REQUIRE(moe_aligned16(x) && moe_aligned16(out) && (!xq || moe_aligned16(xq)) && (!y_slots || moe_aligned16(y_slots)),
-          "moe_layer_forward: pointers must be 16-byte aligned");
-  REQUIRE(cfg->logits_in || moe_aligned16(w_router), "moe_layer_forward: w_router must be 16-byte aligned");
+          "%s: pointers must be 16-byte aligned", fn);
+  REQUIRE(cfg->logits_in || moe_aligned16(w_router), "%s: w_router must be 16-byte aligned", fn);
   if (shared)
     REQUIRE(shared->gate && shared->up && shared->down && shared->s_gate && shared->s_up && shared->s_down,
-            "moe_layer_forward: shared expert has a NULL member");
+            "%s: shared expert has a NULL member", fn);
+  return MOE_OK;
+}
+
+static bool layer_is_t1(const moe_ctx *ctx, int bits, const moe_router_cfg *cfg, int T, int H, int I, int has_shared) {
+  return T == 1 && decode_t1_supported(bits, H, I, cfg->top_k, has_shared, ctx->n_cu);
+}
+
+// io area of the composed path: the intermediates the caller did not ask for
+struct LayerIo {
+  size_t o_idx, o_w, o_xq, o_sx, o_y, size;
+};
+static LayerIo layer_io_layout(int T, int H, int k) {
+  LayerIo l;
+  MoeLayout m;
+  l.o_idx = m.take(4 * (size_t)T * k);
+  l.o_w = m.take(4 * (size_t)T * k);
+  l.o_xq = m.take((size_t)T * H);
+  l.o_sx = m.take(4 * (size_t)T);
+  l.o_y = m.take(4 * (size_t)T * (k + 1) * H);
+  l.size = m.size;
+  return l;
+}
+
+// The layer's steps on the context stream (arguments already checked).
+static moe_status layer_body(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x, const float *logits,
+                             const float *w_router, const float *bias, const moe_expert_w *experts,
+                             const moe_expert_w *shared, int T, int H, int I, float *out, int32_t *topk_idx,
+                             float *topk_w, int8_t *xq, float *sx, float *y_slots) {
+  const int E = cfg->n_experts, k = cfg->top_k;
   const float *lg = cfg->logits_in ? logits : nullptr;
-  if (T == 1 && decode_t1_supported(bits, H, I, k, shared ? 1 : 0, ctx->n_cu))
+  if (layer_is_t1(ctx, bits, cfg, T, H, I, shared ? 1 : 0))
     return launch_layer_t1(ctx, bits, cfg, x, lg, w_router, bias, experts, shared, H, I, out, topk_idx, topk_w, xq, sx,
                            y_slots);
-  // composed path: intermediates the caller did not ask for live in io scratch
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off = moe_round_up(off + bytes, 256);
-    return o;
-  };
-  const size_t o_idx = take(4 * (size_t)T * k), o_w = take(4 * (size_t)T * k), o_xq = take((size_t)T * H),
-               o_sx = take(4 * (size_t)T), o_y = take(4 * (size_t)T * (k + 1) * H);
+  const LayerIo l = layer_io_layout(T, H, k);
   void *io = nullptr;
-  st = moe_io_scratch(ctx, off, &io);
+  moe_status st = moe_io_scratch(ctx, l.size, &io);
   if (st) return st;
   char *b = static_cast<char *>(io);
-  if (!topk_idx) topk_idx = reinterpret_cast<int32_t *>(b + o_idx);
-  if (!topk_w) topk_w = reinterpret_cast<float *>(b + o_w);
-  if (!xq) xq = reinterpret_cast<int8_t *>(b + o_xq);
-  if (!sx) sx = reinterpret_cast<float *>(b + o_sx);
-  if (!y_slots) y_slots = reinterpret_cast<float *>(b + o_y);
+  if (!topk_idx) topk_idx = reinterpret_cast<int32_t *>(b + l.o_idx);
+  if (!topk_w) topk_w = reinterpret_cast<float *>(b + l.o_w);
+  if (!xq) xq = reinterpret_cast<int8_t *>(b + l.o_xq);
+  if (!sx) sx = reinterpret_cast<float *>(b + l.o_sx);
+  if (!y_slots) y_slots = reinterpret_cast<float *>(b + l.o_y);
   if ((st = launch_quantize_act(ctx, x, T, H, xq, sx))) return st;
   if ((st = launch_router(ctx, cfg, lg ? lg : x, w_router, bias, T, H, topk_idx, topk_w))) return st;
   if ((st = launch_expert_ffn(ctx, bits, experts, shared, nullptr, xq, sx, topk_idx, T, H, I, E, k, y_slots)))
     return st;
   return launch_combine(ctx, y_slots, topk_w, T, k, H, shared ? 1 : 0, out);
+}
+
+extern "C" moe_status moe_layer_forward(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x,
+                                        const float *logits, const float *w_router, const float *bias,
+                                        const moe_expert_w *experts, const moe_expert_w *shared, int T, int H, int I,
+                                        float *out, int32_t *topk_idx, float *topk_w, int8_t *xq, float *sx,
+                                        float *y_slots) {
+  moe_status st = layer_check("moe_layer_forward", ctx, bits, cfg, x, logits, w_router, experts, shared, T, H, I, out,
+                              xq, y_slots);
+  if (st || T == 0) return st;
+  return layer_body(ctx, bits, cfg, x, logits, w_router, bias, experts, shared, T, H, I, out, topk_idx, topk_w, xq,
+                    sx, y_slots);
+}
+
+// Clears a context's fixed scratch regions when the allocation-free call returns.
+struct FixedScratchScope {
+  moe_ctx *c;
+  ~FixedScratchScope() {
+    c->fixed_io = c->fixed_scr = nullptr;
+    c->fixed_io_bytes = c->fixed_scr_bytes = 0;
+  }
+};
+
+extern "C" moe_status moe_layer_forward_noalloc(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x,
+                                                const float *logits, const float *w_router, const float *bias,
+                                                const moe_expert_w *experts, const moe_expert_w *shared, int T,
+                                                int H, int I, float *out, int32_t *topk_idx, float *topk_w,
+                                                int8_t *xq, float *sx, float *y_slots) {
+  const char *fn = "moe_layer_forward_noalloc";
+  moe_status st = layer_check(fn, ctx, bits, cfg, x, logits, w_router, experts, shared, T, H, I, out, xq, y_slots);
+  if (st || T == 0) return st;
+  REQUIRE(!ctx->timing, "%s: per-kernel timing records events, which allocates; switch timing off", fn);
+  const int has_shared = shared ? 1 : 0;
+  size_t io = 0, scr = 0;
+  if (layer_is_t1(ctx, bits, cfg, T, H, I, has_shared)) {
+    scr = layer_t1_scratch_bytes(ctx, cfg, has_shared, H, I);
+  } else {
+    io = layer_io_layout(T, H, cfg->top_k).size;
+    scr = std::max(router_scratch_bytes(ctx, cfg, T, H),
+                   expert_ffn_scratch_bytes(ctx, bits, has_shared, T, H, I, cfg->n_experts, cfg->top_k));
+  }
+  REQUIRE(io + scr <= kNoAllocBytes,
+          "%s: T %d, H %d, I %d, E %d, k %d needs %zu bytes of scratch; the static area holds %zu", fn, T, H, I,
+          cfg->n_experts, cfg->top_k, io + scr, kNoAllocBytes);
+  char *base = static_cast<char *>(noalloc_ptr(ctx->device));
+  if (!base) return moe_fail(MOE_EHIP, "%s: no static scratch address for device %d", fn, ctx->device);
+  FixedScratchScope scope{ctx};
+  ctx->fixed_io = base;
+  ctx->fixed_io_bytes = io;
+  ctx->fixed_scr = base + io;
+  ctx->fixed_scr_bytes = kNoAllocBytes - io;
+  return layer_body(ctx, bits, cfg, x, logits, w_router, bias, experts, shared, T, H, I, out, topk_idx, topk_w, xq,
+                    sx, y_slots);
 }

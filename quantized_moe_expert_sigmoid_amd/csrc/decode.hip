@@ -1025,34 +1025,58 @@ bool decode_t1_supported(int bits, int H, int I, int k, int has_shared, int n_cu
   }
 }
 
+namespace {
+// Scratch layout of the single-token layer: router K slices (the same slicing
+// as moe_router_topk, so both paths add the same partial sums in the same
+// order), the slot table, the intermediate and its codes, and the outputs a
+// caller did not ask for.
+struct T1LayerLayout {
+  int ks;
+  size_t o_part, o_slots, o_A, o_aq, o_sum, o_sa, o_idx, o_w, o_xq, o_sx, o_y, size;
+};
+T1LayerLayout t1_layer_layout(const moe_ctx *ctx, int E, int k, int S, bool logits_in, int H, int I) {
+  T1LayerLayout l;
+  l.ks = 1;
+  if (!logits_in) {
+    const int groups = (E + 3) / 4;
+    while (groups * l.ks < 2 * ctx->n_cu && H % (l.ks * 2 * 256) == 0 && l.ks < kMaxSlices) l.ks *= 2;
+  } else {
+    while (H % (l.ks * 2 * 256) == 0 && l.ks < 8) l.ks *= 2;
+  }
+  MoeLayout m;
+  l.o_part = m.take(sizeof(float) * l.ks * E);
+  l.o_slots = m.take(sizeof(SlotEntry) * kMaxSlots);
+  l.o_A = m.take(sizeof(float) * S * I);
+  l.o_aq = m.take((size_t)S * I);
+  l.o_sum = m.take(4 * S);
+  l.o_sa = m.take(4 * S);
+  l.o_idx = m.take(4 * k);
+  l.o_w = m.take(4 * k);
+  l.o_xq = m.take(H);
+  l.o_sx = m.take(4);
+  l.o_y = m.take(sizeof(float) * (k + 1) * H);
+  l.size = m.size;
+  return l;
+}
+}  // namespace
+
+size_t layer_t1_scratch_bytes(const moe_ctx *ctx, const moe_router_cfg *cfg, int has_shared, int H, int I) {
+  return t1_layer_layout(ctx, cfg->n_experts, cfg->top_k, cfg->top_k + has_shared, cfg->logits_in != 0, H, I).size;
+}
+
 moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, const float *x, const float *logits,
                            const float *w_router, const float *bias, const moe_expert_w *experts,
                            const moe_expert_w *shared, int H, int I, float *out, int32_t *topk_idx, float *topk_w,
                            int8_t *xq, float *sx, float *y_slots) {
   const int E = cfg->n_experts, k = cfg->top_k;
   const int S = k + (shared ? 1 : 0);
-  // router K slices (the same slicing as moe_router_topk, so both paths add
-  // the same partial sums in the same order)
-  int ks = 1;
-  if (!logits) {
-    const int groups = (E + 3) / 4;
-    while (groups * ks < 2 * ctx->n_cu && H % (ks * 2 * 256) == 0 && ks < kMaxSlices) ks *= 2;
-  } else {
-    while (H % (ks * 2 * 256) == 0 && ks < 8) ks *= 2;
-  }
+  const T1LayerLayout l = t1_layer_layout(ctx, E, k, S, logits != nullptr, H, I);
+  const int ks = l.ks;
   const int kl = H / ks;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off = moe_round_up(off + bytes, 256);
-    return o;
-  };
-  const size_t o_part = take(sizeof(float) * ks * E), o_slots = take(sizeof(SlotEntry) * kMaxSlots),
-               o_A = take(sizeof(float) * S * I), o_aq = take((size_t)S * I), o_sum = take(4 * S),
-               o_sa = take(4 * S), o_idx = take(4 * k), o_w = take(4 * k), o_xq = take(H), o_sx = take(4),
-               o_y = take(sizeof(float) * (k + 1) * H);
+  const size_t o_part = l.o_part, o_slots = l.o_slots, o_A = l.o_A, o_aq = l.o_aq, o_sum = l.o_sum, o_sa = l.o_sa,
+               o_idx = l.o_idx, o_w = l.o_w, o_xq = l.o_xq, o_sx = l.o_sx, o_y = l.o_y;
   void *scr = nullptr;
-  moe_status st = moe_scratch(ctx, off, &scr);
+  moe_status st = moe_scratch(ctx, l.size, &scr);
   if (st) return st;
   char *base = static_cast<char *>(scr);
   if (!topk_idx) topk_idx = reinterpret_cast<int32_t *>(base + o_idx);
@@ -1234,6 +1258,8 @@ moe_status t1_chain(moe_ctx *ctx, hipStream_t stream, char *base, int bits, cons
 }
 
 }  // namespace
+
+size_t ffn_t1_scratch_bytes(int I, int S) { return t1_chain_bytes(I, S); }
 
 moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                          const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,

@@ -446,36 +446,77 @@ moe_status launch_ffn_bits(moe_ctx *ctx, FfnArgs &a, int dmax) {
 int rows_per_wg_gu(int bits) { return kWaves * (bits == 8 ? Shape<8>::kRwGU : bits == 4 ? Shape<4>::kRwGU : Shape<2>::kRwGU); }
 int rows_per_wg_d(int bits) { return kWaves * (bits == 8 ? Shape<8>::kRwD : bits == 4 ? Shape<4>::kRwD : Shape<2>::kRwD); }
 
+
+// Which kernel family computes a call's expert FFN.
+enum FfnRoute { kRouteMfma, kRouteT1, kRouteDot4, kRouteUnsupported };
+FfnRoute ffn_route(const moe_ctx *ctx, int bits, int has_shared, int T, int H, int I, int k) {
+  const bool mfma_ok = expert_ffn_mfma_supported(bits, H, I);
+  if (ctx->ffn_kernels == MOE_FFN_MFMA && !mfma_ok) return kRouteUnsupported;
+  if (mfma_ok && (ctx->ffn_kernels == MOE_FFN_MFMA || (ctx->ffn_kernels == MOE_FFN_AUTO && T >= 2))) return kRouteMfma;
+  // one token: the single-token kernels (no bucketing pass)
+  if (T == 1 && ctx->ffn_kernels == MOE_FFN_AUTO && decode_t1_supported(bits, H, I, k, has_shared, ctx->n_cu))
+    return kRouteT1;
+  return kRouteDot4;
+}
+
+// Scratch layout of the vector FFN.
+struct Dot4Layout {
+  int tiles1, tiles2;
+  size_t o_counts, o_offsets, o_perm, o_active, o_nact, o_tmax, o_A, o_aq, o_sa, size;
+};
+Dot4Layout dot4_layout(int bits, int T, int H, int I, int E, int k) {
+  Dot4Layout l;
+  const int64_t P = (int64_t)T * (k + 1);
+  l.tiles1 = I / rows_per_wg_gu(bits);
+  l.tiles2 = H / rows_per_wg_d(bits);
+  MoeLayout m;
+  l.o_counts = m.take(4 * (size_t)E);
+  l.o_offsets = m.take(4 * (size_t)(E + 1));
+  l.o_perm = m.take(4 * (size_t)T * k);
+  l.o_active = m.take(4 * (size_t)E);
+  l.o_nact = m.take(4);
+  l.o_tmax = m.take(4 * (size_t)P * l.tiles1);
+  l.o_A = m.take(4 * (size_t)P * I);
+  l.o_aq = m.take((size_t)P * I);
+  l.o_sa = m.take(4 * (size_t)P);
+  l.size = m.size;
+  return l;
+}
+
 }  // namespace
+
+size_t expert_ffn_scratch_bytes(const moe_ctx *ctx, int bits, int has_shared, int T, int H, int I, int E, int k) {
+  switch (ffn_route(ctx, bits, has_shared, T, H, I, k)) {
+    case kRouteMfma: return expert_ffn_mfma_scratch_bytes(bits, has_shared, T, H, I, E, k);
+    case kRouteT1: return ffn_t1_scratch_bytes(I, k + has_shared);
+    case kRouteDot4: return dot4_layout(bits, T, H, I, E, k).size;
+    default: return 0;
+  }
+}
 
 moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                              const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
                              int T, int H, int I, int E, int k, float *y_slots) {
-  const bool mfma_ok = expert_ffn_mfma_supported(bits, H, I);
-  if (ctx->ffn_kernels == MOE_FFN_MFMA && !mfma_ok)
-    return moe_fail(MOE_EUNSUPPORTED, "expert FFN: the matrix-core kernels do not take H %d, I %d at %d bits", H, I,
-                    bits);
-  if (mfma_ok && (ctx->ffn_kernels == MOE_FFN_MFMA || (ctx->ffn_kernels == MOE_FFN_AUTO && T >= 2)))
-    return launch_expert_ffn_mfma(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots);
-  // one token: the single-token kernels (no bucketing pass)
-  if (T == 1 && ctx->ffn_kernels == MOE_FFN_AUTO && decode_t1_supported(bits, H, I, k, shared ? 1 : 0, ctx->n_cu))
-    return launch_ffn_t1(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, H, I, E, k, y_slots);
-  const int64_t P = (int64_t)T * (k + 1);
+  switch (ffn_route(ctx, bits, shared ? 1 : 0, T, H, I, k)) {
+    case kRouteUnsupported:
+      return moe_fail(MOE_EUNSUPPORTED, "expert FFN: the matrix-core kernels do not take H %d, I %d at %d bits", H, I,
+                      bits);
+    case kRouteMfma:
+      return launch_expert_ffn_mfma(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k,
+                                    y_slots);
+    case kRouteT1:
+      return launch_ffn_t1(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, H, I, E, k, y_slots);
+    default:
+      break;
+  }
+  const Dot4Layout l = dot4_layout(bits, T, H, I, E, k);
   FfnArgs a{};
-  a.tiles1 = I / rows_per_wg_gu(bits);
-  a.tiles2 = H / rows_per_wg_d(bits);
-  // scratch layout
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off = moe_round_up(off + bytes, 256);
-    return o;
-  };
-  const size_t o_counts = take(4 * (size_t)E), o_offsets = take(4 * (size_t)(E + 1)), o_perm = take(4 * (size_t)T * k),
-               o_active = take(4 * (size_t)E), o_nact = take(4), o_tmax = take(4 * (size_t)P * a.tiles1),
-               o_A = take(4 * (size_t)P * I), o_aq = take((size_t)P * I), o_sa = take(4 * (size_t)P);
+  a.tiles1 = l.tiles1;
+  a.tiles2 = l.tiles2;
+  const size_t o_counts = l.o_counts, o_offsets = l.o_offsets, o_perm = l.o_perm, o_active = l.o_active,
+               o_nact = l.o_nact, o_tmax = l.o_tmax, o_A = l.o_A, o_aq = l.o_aq, o_sa = l.o_sa;
   void *scr = nullptr;
-  moe_status st = moe_scratch(ctx, off, &scr);
+  moe_status st = moe_scratch(ctx, l.size, &scr);
   if (st) return st;
   char *base = static_cast<char *>(scr);
   a.experts = experts;

@@ -643,64 +643,88 @@ bool expert_ffn_mfma_supported(int bits, int H, int I) {
   return H % 16 == 0 && I % 16 == 0 && I <= kMaxI && (H * bits / 8) % 16 == 0 && (I * bits / 8) % 16 == 0;
 }
 
+namespace {
+// Scratch layout of one matrix-core FFN call.
+struct MfmaLayout {
+  int dact, ubig, usmall, xstride, astride;
+  size_t o_counts, o_offsets, o_perm, o_active, o_nact, o_units, o_nunits, o_xa, o_xsum, o_A, o_aq, o_aqs, o_sa;
+  size_t size;
+};
+
+MfmaLayout mfma_layout(int bits, int has_shared, int T, int H, int I, int E, int k) {
+  MfmaLayout l;
+  const int64_t P = (int64_t)T * (k + 1);
+  l.dact = (int)std::min<int64_t>(E, (int64_t)T * k);
+  // sum over experts of ceil(n_e / 64) <= T k / 64 + (active experts), plus the shared expert's tiles
+  l.ubig = (int)(((int64_t)T * k) / kUnitM + l.dact + 1 + (has_shared ? (T + kUnitM - 1) / kUnitM : 0));
+  l.usmall = l.dact + 1;
+  // rows of field-ordered codes hold whole groups of four lane pieces
+  const int grp_bytes = 4 * (128 / bits);
+  l.xstride = bits == 8 ? H : (int)moe_round_up(H, grp_bytes);
+  l.astride = (int)moe_round_up(I, grp_bytes);
+  MoeLayout m;
+  l.o_counts = m.take(4 * (size_t)E);
+  l.o_offsets = m.take(4 * (size_t)(E + 1));
+  l.o_perm = m.take(4 * (size_t)T * k);
+  l.o_active = m.take(4 * (size_t)E);
+  l.o_nact = m.take(4);
+  l.o_units = m.take(8 * (size_t)(l.ubig + l.usmall));
+  l.o_nunits = m.take(8);
+  l.o_xa = m.take(bits == 8 ? 0 : (size_t)T * l.xstride);
+  l.o_xsum = m.take(4 * (size_t)T);
+  l.o_A = m.take(4 * (size_t)P * I);
+  l.o_aq = m.take((size_t)P * l.astride);
+  l.o_aqs = m.take(4 * (size_t)P);
+  l.o_sa = m.take(4 * (size_t)P);
+  l.size = m.size;
+  return l;
+}
+}  // namespace
+
+size_t expert_ffn_mfma_scratch_bytes(int bits, int has_shared, int T, int H, int I, int E, int k) {
+  return mfma_layout(bits, has_shared, T, H, I, E, k).size;
+}
+
 moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                                   const uint8_t *expert_bits, const int8_t *xq, const float *sx,
                                   const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots) {
-  const int64_t P = (int64_t)T * (k + 1);
   const int has_shared = shared ? 1 : 0;
-  const int dact = (int)std::min<int64_t>(E, (int64_t)T * k);
-  // sum over experts of ceil(n_e / 64) <= T k / 64 + (active experts), plus the shared expert's tiles
-  const int ubig = (int)(((int64_t)T * k) / kUnitM + dact + 1 + (has_shared ? (T + kUnitM - 1) / kUnitM : 0));
-  const int usmall = dact + 1;
-  // rows of field-ordered codes hold whole groups of four lane pieces
-  const int grp_bytes = 4 * (128 / bits);
-  const int xstride = bits == 8 ? H : (int)moe_round_up(H, grp_bytes);
-  const int astride = (int)moe_round_up(I, grp_bytes);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off = moe_round_up(off + bytes, 256);
-    return o;
-  };
-  const size_t o_counts = take(4 * (size_t)E), o_offsets = take(4 * (size_t)(E + 1)), o_perm = take(4 * (size_t)T * k),
-               o_active = take(4 * (size_t)E), o_nact = take(4), o_units = take(8 * (size_t)(ubig + usmall)),
-               o_nunits = take(8), o_xa = take(bits == 8 ? 0 : (size_t)T * xstride), o_xsum = take(4 * (size_t)T),
-               o_A = take(4 * (size_t)P * I), o_aq = take((size_t)P * astride), o_aqs = take(4 * (size_t)P),
-               o_sa = take(4 * (size_t)P);
+  const MfmaLayout l = mfma_layout(bits, has_shared, T, H, I, E, k);
+  const int ubig = l.ubig, usmall = l.usmall;
   void *scr = nullptr;
-  moe_status st = moe_scratch(ctx, off, &scr);
+  moe_status st = moe_scratch(ctx, l.size, &scr);
   if (st) return st;
   char *base = static_cast<char *>(scr);
   MArgs a{};
   a.experts = experts;
   a.has_shared = has_shared;
   if (shared) a.shared = *shared;
-  int8_t *xa = bits == 8 ? const_cast<int8_t *>(xq) : reinterpret_cast<int8_t *>(base + o_xa);
-  int32_t *xsum = reinterpret_cast<int32_t *>(base + o_xsum);
+  int8_t *xa = bits == 8 ? const_cast<int8_t *>(xq) : reinterpret_cast<int8_t *>(base + l.o_xa);
+  int32_t *xsum = reinterpret_cast<int32_t *>(base + l.o_xsum);
   a.xa = xa;
-  a.xstride = xstride;
-  a.astride = astride;
+  a.xstride = l.xstride;
+  a.astride = l.astride;
   a.xsum = xsum;
   a.sx = sx;
   a.topk_idx = topk_idx;
   a.expert_bits = expert_bits;
   a.bits = bits;
   a.T = T; a.H = H; a.I = I; a.E = E; a.k = k;
-  int32_t *counts = reinterpret_cast<int32_t *>(base + o_counts);
-  int32_t *offsets = reinterpret_cast<int32_t *>(base + o_offsets);
-  int32_t *perm = reinterpret_cast<int32_t *>(base + o_perm);
-  int32_t *active = reinterpret_cast<int32_t *>(base + o_active);
-  int32_t *nact = reinterpret_cast<int32_t *>(base + o_nact);
-  int2 *units = reinterpret_cast<int2 *>(base + o_units);
-  int32_t *nunits = reinterpret_cast<int32_t *>(base + o_nunits);
+  int32_t *counts = reinterpret_cast<int32_t *>(base + l.o_counts);
+  int32_t *offsets = reinterpret_cast<int32_t *>(base + l.o_offsets);
+  int32_t *perm = reinterpret_cast<int32_t *>(base + l.o_perm);
+  int32_t *active = reinterpret_cast<int32_t *>(base + l.o_active);
+  int32_t *nact = reinterpret_cast<int32_t *>(base + l.o_nact);
+  int2 *units = reinterpret_cast<int2 *>(base + l.o_units);
+  int32_t *nunits = reinterpret_cast<int32_t *>(base + l.o_nunits);
   a.counts = counts; a.offsets = offsets; a.perm = perm; a.active = active; a.n_active = nact;
   a.units = units;
   a.n_units = nunits;
   a.ubig_max = ubig;
-  a.A = reinterpret_cast<float *>(base + o_A);
-  a.aq = reinterpret_cast<int8_t *>(base + o_aq);
-  a.aqs = reinterpret_cast<int32_t *>(base + o_aqs);
-  a.sa = reinterpret_cast<float *>(base + o_sa);
+  a.A = reinterpret_cast<float *>(base + l.o_A);
+  a.aq = reinterpret_cast<int8_t *>(base + l.o_aq);
+  a.aqs = reinterpret_cast<int32_t *>(base + l.o_aqs);
+  a.sa = reinterpret_cast<float *>(base + l.o_sa);
   a.y = y_slots;
   a.dbg = ctx->dbg;
   a.dbg_on = ctx->dbg_on ? 1 : 0;

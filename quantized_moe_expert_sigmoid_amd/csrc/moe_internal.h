@@ -34,6 +34,11 @@ struct moe_ctx {
   // buffers that scratch or io outgrew: freed only by moe_ctx_destroy, as
   // captured graphs and queued work may still address them
   std::vector<void *> retired;
+  // while an allocation-free call runs: its io and scratch regions in the
+  // library's static device array (moe_scratch / moe_io_scratch hand these
+  // out instead of growing the context's buffers)
+  char *fixed_io = nullptr, *fixed_scr = nullptr;
+  size_t fixed_io_bytes = 0, fixed_scr_bytes = 0;
   // small persistent device block: error flags and counters
   uint32_t *dev_small = nullptr;  // [0] error flags, [1..] counters
   int ffn_kernels = MOE_FFN_AUTO;
@@ -110,6 +115,17 @@ moe_status moe_io_scratch(moe_ctx *ctx, size_t bytes, void **out);
 static inline bool moe_aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 static inline size_t moe_round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Parts of a scratch area laid out one after another, each on a 256-byte
+// boundary; `size` is the area's total.
+struct MoeLayout {
+  size_t size = 0;
+  size_t take(size_t bytes) {
+    const size_t o = size;
+    size = moe_round_up(size + bytes, 256);
+    return o;
+  }
+};
+
 // Launchers implemented in the .hip files
 moe_status launch_quantize_rows(moe_ctx *ctx, int bits, const float *w, int64_t rows, int cols, uint8_t *packed,
                                 float *scales);
@@ -131,6 +147,13 @@ moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, 
                          int32_t *n_active, int2 *units, int32_t *n_units, int ubig_max, int has_shared,
                          int small_max);
 bool expert_ffn_mfma_supported(int bits, int H, int I);
+// Scratch bytes (moe_scratch) a launcher takes for these arguments: the same
+// layouts the launchers use, so a caller can size a fixed area beforehand.
+size_t router_scratch_bytes(const moe_ctx *ctx, const moe_router_cfg *cfg, int T, int H);
+size_t expert_ffn_scratch_bytes(const moe_ctx *ctx, int bits, int has_shared, int T, int H, int I, int E, int k);
+size_t expert_ffn_mfma_scratch_bytes(int bits, int has_shared, int T, int H, int I, int E, int k);
+size_t layer_t1_scratch_bytes(const moe_ctx *ctx, const moe_router_cfg *cfg, int has_shared, int H, int I);
+size_t ffn_t1_scratch_bytes(int I, int S);
 moe_status launch_expert_ffn_mfma(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                                   const uint8_t *expert_bits, const int8_t *xq, const float *sx,
                                   const int32_t *topk_idx, int T, int H, int I, int E, int k, float *y_slots);

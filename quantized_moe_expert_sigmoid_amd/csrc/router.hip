@@ -377,23 +377,36 @@ moe_status launch_bucket_public(moe_ctx *ctx, const int32_t *topk_idx, int T, in
                        0, 0, kUnitSmall);
 }
 
+namespace {
+// K slices of the router logits (1 when the caller passes logits)
+int router_slices(const moe_ctx *ctx, const moe_router_cfg *cfg, int T, int H) {
+  if (cfg->logits_in) return 1;
+  const int E = cfg->n_experts;
+  int ks = 1;
+  if (T <= kSmallT) {
+    // enough waves to stream w_router with the whole chip: ~4 waves per CU
+    const int groups = (E + 3) / 4;
+    while (groups * ks < 2 * ctx->n_cu && H % (ks * 2 * 256) == 0 && ks < 16) ks *= 2;
+  } else {
+    const int tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
+    while (tiles * ks < 2 * ctx->n_cu && H % (ks * 2 * kTileK) == 0 && H / (ks * 2) >= 256 && ks < 16) ks *= 2;
+  }
+  return ks;
+}
+}  // namespace
+
+size_t router_scratch_bytes(const moe_ctx *ctx, const moe_router_cfg *cfg, int T, int H) {
+  if (cfg->logits_in) return 0;
+  return sizeof(float) * (size_t)router_slices(ctx, cfg, T, H) * T * cfg->n_experts;
+}
+
 moe_status launch_router(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x, const float *w_router,
                          const float *bias, int T, int H, int32_t *topk_idx, float *topk_w) {
   const int E = cfg->n_experts, k = cfg->top_k;
   const float *partial = x;
   int nslices = 1;
   if (!cfg->logits_in) {
-    int ks;
-    if (T <= kSmallT) {
-      // enough waves to stream w_router with the whole chip: ~4 waves per CU
-      const int groups = (E + 3) / 4;
-      ks = 1;
-      while (groups * ks < 2 * ctx->n_cu && H % (ks * 2 * 256) == 0 && ks < 16) ks *= 2;
-    } else {
-      const int tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
-      ks = 1;
-      while (tiles * ks < 2 * ctx->n_cu && H % (ks * 2 * kTileK) == 0 && H / (ks * 2) >= 256 && ks < 16) ks *= 2;
-    }
+    const int ks = router_slices(ctx, cfg, T, H);
     const int kl = H / ks;
     void *scr = nullptr;
     moe_status st = moe_scratch(ctx, sizeof(float) * (size_t)ks * T * E, &scr);
