@@ -392,6 +392,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def graph_upload(g) -> None:
+    """Upload an instantiated graph to the device ahead of its first replay
+    (hipGraphUpload), so that a timed replay does not include the upload."""
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipGraphUpload.restype = ctypes.c_int
+    rc = hip.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()),
+                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"hipGraphUpload failed ({rc})")
+    torch.cuda.synchronize()
+
+
 def build_gpu_layer(ctx, w, bits):
     import torch
     from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
@@ -410,12 +425,26 @@ def build_gpu_layer(ctx, w, bits):
     return L
 
 
-def cpu_baseline(w, bits, n_tokens, repeats, top_p=0.0):
-    """Time the oracle's full layer on n_tokens distinct tokens x repeats."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, bits, n_tokens, repeats, top_p=0.0, all_tokens=16, all_repeats=2):
+    """Time the oracle's full layer on the host: one thread on n_tokens
+    distinct tokens x repeats, then every host thread the box gives this
+    process (its (token, slot) pairs spread by OpenMP) on all_tokens tokens x
+    all_repeats. The experts the tokens route to are packed beforehand, untimed."""
     import oracle as orc
     from synth import workloads as wl
     orc.build()
-    T = n_tokens
+    T = max(n_tokens, all_tokens)
     x = wl.hidden_fp32(w, T, batch=0)
     logits = wl.logits_fp32(w, T) if w.routing == "zipf" else None
     wr, b = wl.router_fp32(w)
@@ -427,13 +456,28 @@ def cpu_baseline(w, bits, n_tokens, repeats, top_p=0.0):
         exps[e] = orc.pack_expert(bits, g, u, d)
     sh = orc.pack_expert(bits, *wl.shared_fp32(w)) if w.has_shared else None
     table = orc.ExpertTable(exps)
-    t0 = time.perf_counter()
-    for _ in range(repeats):
-        orc.layer(x, table, sh, w.k, wr=wr, bias=b, logits=logits, top_p=top_p)
-    dt = time.perf_counter() - t0
-    return {"value": round(T * repeats / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{T} distinct tokens x {repeats} repeats of the full layer ({len(need)} routed experts "
-                      f"packed beforehand, untimed); {dt:.1f} s single-threaded scalar C"}
+
+    def rate(nt, reps):
+        xs = np.ascontiguousarray(x[:nt])
+        lg = None if logits is None else np.ascontiguousarray(logits[:nt])
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            orc.layer(xs, table, sh, w.k, wr=wr, bias=b, logits=lg, top_p=top_p)
+        return nt * reps / (time.perf_counter() - t0)
+
+    threads_all = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    orc.set_threads(1)
+    r1 = rate(n_tokens, repeats)
+    used = orc.set_threads(threads_all)
+    ra = rate(all_tokens, all_repeats)
+    orc.set_threads(1)
+    return {"value": round(ra, 4), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": round(r1, 4), "cores": 1,
+                              "sample": f"{n_tokens} distinct tokens x {repeats} repeats"},
+            "sample": f"{all_tokens} distinct tokens x {all_repeats} repeats of the full layer on {used} threads "
+                      f"(OpenMP over the (token, slot) pairs, scalar C inner loops, gcc -O2); "
+                      f"{len(need)} routed experts packed beforehand, untimed"}
 
 
 def main():
@@ -542,25 +586,40 @@ def main():
     # tokens/s: one HIP graph holds npool consecutive layer calls (one per pool
     # entry); the timed region replays it back to back.
     cap = torch.cuda.Stream()
-    ctx.set_stream(cap)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
-        for i in range(npool):
-            step(i)
-    ctx.set_stream(torch.cuda.current_stream())
-    reps = max(1, args.steps // npool)
-    warm_reps = max(1, args.warmup // npool)
-    steps = reps * npool
-    for _ in range(warm_reps):
-        graph.replay()
+
+    def capture(n):
+        ctx.set_stream(cap)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(n):
+                step(i)
+        ctx.set_stream(torch.cuda.current_stream())
+        graph_upload(g)
+        return g
+
+    # exactly `steps` calls: whole replays of the npool-call graph, then one
+    # replay of a graph of the remaining calls
+    graph = capture(npool)
+    steps = max(1, args.steps)
+    reps, rem = divmod(steps, npool)
+    graph_rem = capture(rem) if rem else None
+    warm_reps, warm_rem = divmod(max(0, args.warmup), npool)
+    graph_wrem = capture(warm_rem) if warm_rem else None
+
+    def run(nrep, g_rem):
+        for _ in range(nrep):
+            graph.replay()
+        if g_rem is not None:
+            g_rem.replay()
+
+    run(warm_reps, graph_wrem)
     torch.cuda.synchronize()
     ctx.check()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
-    for _ in range(reps):
-        graph.replay()
+    run(reps, graph_rem)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -604,7 +663,7 @@ def main():
                 step_cold(i)
         ctx.set_stream(torch.cuda.current_stream())
         creps = max(1, steps // ncold)
-        for _ in range(warm_reps):
+        for _ in range(max(1, warm_reps)):
             graph_c.replay()
         torch.cuda.synchronize()
         t0.record()
@@ -640,7 +699,7 @@ def main():
         f"{avg_bytes / 1e6:.1f} MB/step, layer {eff_gbps:.0f} GB/s; kernels per call: " +
         ", ".join(f"{k_} {v[0] * 1e3:.1f} us" for k_, v in per_call.items()) +
         f"; gate/up {gu_gbps:.0f} GB/s, FFN {ffn_gbps:.0f} GB/s")
-    args.steps, args.warmup = steps, warm_reps * npool
+    args.steps, args.warmup = steps, max(0, args.warmup)
     traffic_gu = None
     tr = load_traffic() if (T == 1 and bits == 4 and w.name == "glm_decode_t1") else None
     if tr:

@@ -22,22 +22,30 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_LIB: another build of the same source (the sanitizer build)
+_SO = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "libmoe_oracle.so")
+SANITIZED_SO = os.path.join(_HERE, "libmoe_oracle_asan.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _HDR = os.path.join(_HERE, "moe_oracle.h")
-CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11"]
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
 _lock = threading.Lock()
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile libmoe_oracle.so with gcc (no fast-math, no FP contraction)."""
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile libmoe_oracle.so with gcc (no fast-math, no FP contraction);
+    sanitize: the AddressSanitizer + UndefinedBehaviorSanitizer build
+    (libmoe_oracle_asan.so, loaded through MOE_ORACLE_LIB with libasan
+    preloaded)."""
+    sanitize = sanitize or os.path.abspath(_SO) == SANITIZED_SO
+    so = SANITIZED_SO if sanitize else _SO
     newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
-    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < newest:
-        tmp = _SO + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _SO)
-    return _SO
+    if force or not os.path.exists(so) or os.path.getmtime(so) < newest:
+        tmp = so + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, *(SANITIZE_FLAGS if sanitize else []), _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, so)
+    return so
 
 
 class _Expert(ctypes.Structure):
@@ -71,6 +79,8 @@ def _load():
                                       i32, i32, i32, i32, i32, dbl, vp, vp, vp, vp, vp, vp]
             lib.orc_topp.argtypes = [i32, i32, i32, vp, dbl, dbl, vp, vp, vp]
             lib.orc_swiglu_f64.argtypes = [vp, vp, vp, vp, i32, i32, vp]
+            lib.orc_set_threads.argtypes = [i32]
+            lib.orc_set_threads.restype = i32
             _lib = lib
     return _lib
 
@@ -292,6 +302,12 @@ def layer(x: np.ndarray, table: ExpertTable, shared: Expert | None, k: int, wr: 
                              _p(res["xq"]), _p(res["sx"]), _p(res["idx"]), _p(res["w"]), _p(res["y_slots"]),
                              _p(res["out"])), "layer")
     return res
+
+
+def set_threads(n: int) -> int:
+    """Threads the layer's (token, slot) loop uses (n <= 0: unchanged); returns
+    the count now in use."""
+    return int(_load().orc_set_threads(int(n)))
 
 
 def swiglu_f64(wg, wu, wd, x):

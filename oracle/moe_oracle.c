@@ -5,9 +5,11 @@
  * benchmark's CPU-baseline leg use it. It is independent of the GPU library:
  * no shared code, headers, tables or constants.
  *
- * Build: gcc -O2 -ffp-contract=off -fno-fast-math (every floating-point
- * operation below is a single correctly rounded IEEE operation, and fused
- * multiply-adds appear only where fmaf() is written out).
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp (every
+ * floating-point operation below is a single correctly rounded IEEE
+ * operation, and fused multiply-adds appear only where fmaf() is written
+ * out). OpenMP only spreads the layer's independent (token, slot) pairs over
+ * threads; it changes no arithmetic.
  *
  * Function-to-page map (full citations in moe_oracle.h):
  *  O1 quantise/pack rows ...... agentlenshq "Key features": packed int4 /
@@ -372,22 +374,30 @@ int orc_layer(const float *x, const float *logits, const float *wr, const float 
     rc = orc_router(0, x, wr, bias, T, H, E, k, routed_scale, idx_, w_, NULL, sig);
   if (rc) goto done;
   if (top_p > 0.0 && (rc = orc_topp(T, E, k, sig, routed_scale, top_p, idx_, w_, NULL)) != 0) goto done;
-  for (int t = 0; t < T; ++t) {
-    for (int j = 0; j < k; ++j) {
-      int e = idx_[(int64_t)t * k + j];
-      if (e < 0) { /* dropped by top-p: no expert, a zero slot */
-        memset(ys_ + ((int64_t)t * S + j) * H, 0, sizeof(float) * (size_t)H);
-        continue;
+  /* every (token, slot) pair is one expert applied to one token, independent
+     of the others: with OpenMP they are spread over the threads (each pair
+     still computed by one thread in the scalar order above) */
+  {
+    int prc = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : prc)
+    for (int64_t p = 0; p < (int64_t)T * S; ++p) {
+      const int64_t t = p / S;
+      const int j = (int)(p - t * S);
+      float *yp = ys_ + ((int64_t)t * S + j) * H;
+      int r = 0;
+      if (j < k) {
+        const int e = idx_[t * k + j];
+        if (e < 0) /* dropped by top-p: no expert, a zero slot */
+          memset(yp, 0, sizeof(float) * (size_t)H);
+        else
+          r = orc_expert_token(bits[e], &experts[e], xq_ + t * H, sx_[t], H, I, NULL, NULL, NULL, NULL, NULL, NULL,
+                               yp);
+      } else {
+        r = orc_expert_token(shared_bits, shared, xq_ + t * H, sx_[t], H, I, NULL, NULL, NULL, NULL, NULL, NULL, yp);
       }
-      rc = orc_expert_token(bits[e], &experts[e], xq_ + (int64_t)t * H, sx_[t], H, I, NULL, NULL, NULL, NULL, NULL,
-                            NULL, ys_ + ((int64_t)t * S + j) * H);
-      if (rc) goto done;
+      if (r < prc) prc = r;
     }
-    if (shared) {
-      rc = orc_expert_token(shared_bits, shared, xq_ + (int64_t)t * H, sx_[t], H, I, NULL, NULL, NULL, NULL, NULL,
-                            NULL, ys_ + ((int64_t)t * S + k) * H);
-      if (rc) goto done;
-    }
+    if ((rc = prc) != 0) goto done;
   }
   rc = orc_combine(ys_, w_, T, k, H, shared ? 1 : 0, out);
 done:
@@ -398,6 +408,20 @@ done:
   if (!w) free(w_);
   if (!y_slots) free(ys_);
   return rc;
+}
+
+/* Threads of the layer's (token, slot) loop (OpenMP builds; 1 otherwise). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
 }
 
 /* ------------------------------------------------------------------------ */

@@ -112,6 +112,10 @@ int orc_layer(const float *x, const float *logits, const float *wr, const float 
  * figure only): y = Wd (silu(Wg x) * (Wu x)). wg, wu [I][H]; wd [H][I]. */
 int orc_swiglu_f64(const float *wg, const float *wu, const float *wd, const float *x, int H, int I, double *y);
 
+/* Threads the layer spreads its (token, slot) pairs over (OpenMP builds):
+ * n > 0 sets them; returns the number now in use (1 without OpenMP). */
+int orc_set_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

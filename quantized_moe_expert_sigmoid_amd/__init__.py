@@ -21,7 +21,9 @@ import weakref
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIBRARY: another build of the same sources (the sanitizer build of the
+# host code); by default the in-tree libmoe.so
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 _lock = threading.Lock()
 _lib = None
 

@@ -22,6 +22,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+# host code under AddressSanitizer + UndefinedBehaviorSanitizer (device code
+# unchanged): the pool's bookkeeping and the argument checks, run on a host
+# without a GPU with the clang ASan runtime preloaded
+SANITIZED_LIB = os.path.join(PKG, "libmoe_asan.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 ARCH = "gfx950"
@@ -44,35 +50,39 @@ def headers():
     return hs + [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + (".asan.o" if sanitize else ".o"))
+    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(force: bool = True, jobs: int | None = None) -> str:
-    """Compile every HIP source and link libmoe.so. Always recompiles when force."""
+def build(force: bool = True, jobs: int | None = None, sanitize: bool = False) -> str:
+    """Compile every HIP source and link libmoe.so (sanitize: libmoe_asan.so,
+    host code under ASan + UBSan). Always recompiles when force."""
+    lib = SANITIZED_LIB if sanitize else LIB
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    if not force and os.path.exists(LIB):
+    if not force and os.path.exists(lib):
         newest = max(os.path.getmtime(p) for p in srcs + headers())
-        if os.path.getmtime(LIB) >= newest:
-            return LIB
+        if os.path.getmtime(lib) >= newest:
+            return lib
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError("hipcc not found: cannot build the HIP library")
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda src: _compile(src, sanitize), srcs))
+    tmp = lib + ".tmp%d" % os.getpid()
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"] \
+        if sanitize else []
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

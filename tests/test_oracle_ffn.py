@@ -126,9 +126,12 @@ def test_combine_and_identical_experts(orc, syn):
         assert np.allclose(res["out"][t], yy.astype(np.float64) + ys, rtol=1e-5, atol=1e-6)
 
 
-def test_tiny_layer_composes_stages(orc, syn):
+@pytest.mark.parametrize("threads", [1, 4])
+def test_tiny_layer_composes_stages(orc, syn, threads):
     """The layer equals its stages run one by one (tiny shape: hidden 128,
-    8 experts + 1 shared, top-2, intermediate 64, seed 0)."""
+    8 experts + 1 shared, top-2, intermediate 64, seed 0), on one thread and
+    with its (token, slot) pairs spread over four."""
+    assert orc.set_threads(threads) == threads
     T, H, E, k, I = 32, 128, 8, 2, 64
     x = syn.hidden(0, T, H)
     wr = syn.router_weights(0, 0, E, H)

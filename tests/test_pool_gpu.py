@@ -3,7 +3,9 @@ host blocks, and expert FFN outputs computed from pool tables are bit-equal
 to those from an all-resident table, over many calls enqueued without
 synchronisation while the pool keeps evicting (so every refill into memory
 an earlier call still reads must wait for it), for one width and for a
-mixed int4/int2 layer.
+mixed int4/int2 layer. Every slot a pool-backed call computes is also
+compared directly with the oracle (its own packing of the same fp32 weights
+and its own quantisation of the same hidden states), bit for bit.
 """
 import numpy as np
 import pytest
@@ -62,6 +64,43 @@ def make_blocks(moe, ctx, syn, bits, E, seed):
     return blocks, host
 
 
+class OracleBlocks:
+    """The oracle's own packing of the fp32 weights make_blocks packs on the
+    GPU (same seeds), built lazily per (width, expert)."""
+
+    def __init__(self, orc, syn, seed):
+        self.orc, self.syn, self.seed, self.cache = orc, syn, seed, {}
+
+    def get(self, bits, e):
+        if (bits, e) not in self.cache:
+            self.cache[(bits, e)] = self.orc.pack_expert(bits, *self.syn.expert_weights(self.seed, 0, e, H, I))
+        return self.cache[(bits, e)]
+
+
+def check_slots_vs_oracle(orc, syn, seed, y, ids, expert_of, shared_ex=None):
+    """Every slot (t, j) of y against the oracle: expert_of(e) gives the
+    oracle-packed expert (None: the slot was not computed here); slot k
+    against shared_ex when given. Tokens are syn.hidden(seed, T, H),
+    quantised by the oracle."""
+    T, k = ids.shape
+    xq, sx = orc.quantize_act(syn.hidden(seed, T, H))
+    yh = y.cpu().numpy()
+    n = 0
+    for t in range(T):
+        for j in range(k):
+            ex = expert_of(int(ids[t, j]))
+            if ex is None:
+                continue
+            r = orc.expert_token(ex, xq[t], float(sx[t]))["y"]
+            assert np.array_equal(yh[t, j].view(np.uint32), r.view(np.uint32)), (t, j)
+            n += 1
+        if shared_ex is not None:
+            r = orc.expert_token(shared_ex, xq[t], float(sx[t]))["y"]
+            assert np.array_equal(yh[t, k].view(np.uint32), r.view(np.uint32)), t
+            n += 1
+    return n
+
+
 def token_inputs(moe, ctx, syn, T, seed):
     x = torch.from_numpy(syn.hidden(seed, T, H)).cuda()
     xq = torch.empty((T, H), dtype=torch.int8, device="cuda")
@@ -98,7 +137,7 @@ def test_refilled_slots_equal_host_blocks(moe, ctx, syn):
 
 
 @pytest.mark.parametrize("slots", [4, 8])
-def test_pool_ffn_bit_equal_under_eviction(moe, ctx, syn, slots):
+def test_pool_ffn_bit_equal_under_eviction(moe, ctx, orc, syn, slots):
     """40 calls, two tokens of top-2 each, enqueued back to back; the pool
     holds `slots` blocks (4 = one call's worst case, so calls keep evicting
     what the previous call read)."""
@@ -123,11 +162,13 @@ def test_pool_ffn_bit_equal_under_eviction(moe, ctx, syn, slots):
         calls.append((xq, sx, idx, y))
     torch.cuda.synchronize()
     ctx.check()
+    oe, osh = OracleBlocks(orc, syn, 32), OracleBlocks(orc, syn, 33).get(4, 0)
     for c, (xq, sx, idx, y) in enumerate(calls):
         ref = torch.zeros_like(y)
         moe.moe_expert_ffn_q4(ctx, blocks.table, shared, None, xq, sx, idx, H, I, E, ref)
         torch.cuda.synchronize()
         assert torch.equal(y, ref), c
+        check_slots_vs_oracle(orc, syn, 100 + c, y, idx.cpu().numpy(), lambda e: oe.get(4, e), osh)
     st = pool.stats()
     log(f"pool slots={slots}: {st}")
     assert st["hits"] + st["misses"] == sum(len(set(i.cpu().numpy().ravel())) for _, _, i, _ in calls)
@@ -136,7 +177,7 @@ def test_pool_ffn_bit_equal_under_eviction(moe, ctx, syn, slots):
     pool.close()
 
 
-def test_pool_mixed_widths(moe, ctx, syn):
+def test_pool_mixed_widths(moe, ctx, orc, syn):
     """Even experts int4, odd experts int2, two layers sharing one slab; one
     FFN call per width with the pool's width table."""
     E, T, k, L = 8, 3, 2, 2
@@ -171,16 +212,19 @@ def test_pool_mixed_widths(moe, ctx, syn):
             continue
         moe.moe_expert_ffn_q4(ctx, table, None, bits, xq, sx, idx, H, I, E, y)
         moe.moe_expert_ffn_q2(ctx, table, None, bits, xq, sx, idx, H, I, E, y)
-        outs.append((xq, sx, idx, y))
+        outs.append((c, xq, sx, idx, y))
     torch.cuda.synchronize()
     ctx.check()
     assert len(outs) >= 8
-    for xq, sx, idx, y in outs:
+    o4, o2 = OracleBlocks(orc, syn, 34), OracleBlocks(orc, syn, 35)
+    for c, xq, sx, idx, y in outs:
         ref = torch.zeros_like(y)
         moe.moe_expert_ffn_q4(ctx, ref_table, None, ref_bits, xq, sx, idx, H, I, E, ref)
         moe.moe_expert_ffn_q2(ctx, ref_table, None, ref_bits, xq, sx, idx, H, I, E, ref)
         torch.cuda.synchronize()
         assert torch.equal(y, ref)
+        check_slots_vs_oracle(orc, syn, 200 + c, y, idx.cpu().numpy(),
+                              lambda e: o4.get(4, e) if e % 2 == 0 else o2.get(2, e))
     pool.close()
 
 
@@ -203,7 +247,7 @@ def test_pool_capacity_refusal_and_reuse(moe, ctx, syn):
     pool.close()
 
 
-def test_pool_prefetch_bit_equal(moe, ctx, syn):
+def test_pool_prefetch_bit_equal(moe, ctx, orc, syn):
     """Each call prefetches the next call's experts before its own FFN is
     enqueued (the prefetch may not evict what this call reads); outputs equal
     those from an all-resident table, and prefetched experts are hits."""
@@ -227,18 +271,20 @@ def test_pool_prefetch_bit_equal(moe, ctx, syn):
         calls.append((xq, sx, idx, y))
     torch.cuda.synchronize()
     ctx.check()
+    oe = OracleBlocks(orc, syn, 37)
     for c, (xq, sx, idx, y) in enumerate(calls):
         ref = torch.zeros_like(y)
         moe.moe_expert_ffn_q4(ctx, blocks.table, None, None, xq, sx, idx, H, I, E, ref)
         torch.cuda.synchronize()
         assert torch.equal(y, ref), c
+        check_slots_vs_oracle(orc, syn, 300 + c, y, idx.cpu().numpy(), lambda e: oe.get(4, e))
     ps = pool.prefetch_stats()
     log(f"prefetch: {ps}, {pool.stats()}")
     assert ps["issued"] > 20 and ps["used"] > 10
     pool.close()
 
 
-def test_pool_tiers_bit_equal(moe, ctx, syn):
+def test_pool_tiers_bit_equal(moe, ctx, orc, syn):
     """Precision tiers: three experts int8 with an int4 block, the others int4
     with an int2 block, demotion on, a slab under pressure; midway the hot
     experts are pinned (demoted copies re-loaded at full width). Every call's
@@ -287,6 +333,7 @@ def test_pool_tiers_bit_equal(moe, ctx, syn):
     log(f"tiers: {ts}, {pool.stats()}")
     assert len(calls) >= 40 and ts["demoted_loads"] > 5
     assert any(w < full[e] for *_, ws in calls for e, w in ws.items())
+    ot = OracleBlocks(orc, syn, 38)
     for c, xq, sx, idx, y, widths in calls:
         wv = [widths.get(e, 0) for e in range(E)]
         ref_table = torch.stack([per_width[w].table[e] if w else b4.table[e] for e, w in enumerate(wv)]).contiguous()
@@ -296,6 +343,7 @@ def test_pool_tiers_bit_equal(moe, ctx, syn):
             getattr(moe, f"moe_expert_ffn_q{b}")(ctx, ref_table, None, ref_bits, xq, sx, idx, H, I, E, ref)
         torch.cuda.synchronize()
         assert torch.equal(y, ref), (c, widths)
+        check_slots_vs_oracle(orc, syn, 400 + c, y, idx.cpu().numpy(), lambda e: ot.get(widths[e], e))
         if c >= 24 and 0 in widths:  # pinned before call 24: full width from then on
             assert widths[0] == 8, (c, widths)
     pool.close()
@@ -376,7 +424,7 @@ def test_pool_own_tables_copy_only_changes(moe, ctx, syn):
 
 
 @pytest.mark.parametrize("slots", [8, 10])
-def test_pool_one_token_mixed_loop(moe, ctx, syn, slots):
+def test_pool_one_token_mixed_loop(moe, ctx, orc, syn, slots):
     """The decode loop through the pool, one token per call, as the stack
     benchmark runs it: prepare into the layer's own table, the call's widths,
     one mixed-width FFN call with the combine. 40 calls over two layers are
@@ -419,7 +467,9 @@ def test_pool_one_token_mixed_loop(moe, ctx, syn, slots):
         torch.cuda.synchronize()
         ctx.check()
         assert pool.table_stats()["skipped"] > 0
+        oe, osh = OracleBlocks(orc, syn, 37), OracleBlocks(orc, syn, 38).get(4, 0)
         for c, (xq, sx, idx, wts, mask, y, out) in enumerate(calls):
+            check_slots_vs_oracle(orc, syn, 200 + c, y, idx.cpu().numpy(), lambda e: oe.get(int(wbits[e]), e), osh)
             ry = torch.zeros_like(y)
             ro = torch.empty_like(out)
             moe.moe_expert_ffn_mixed(ctx, full, shared, 4, full_bits, mask, xq, sx, idx, H, I, E, ry, topk_w=wts,
