@@ -407,6 +407,90 @@ def graph_upload(g) -> None:
     torch.cuda.synchronize()
 
 
+def crossover_bench(args) -> None:
+    """Expert FFN time at the GLM shape against the tokens per call, for each
+    kernel family: the vector dot-product kernels, the int8 matrix-core
+    kernels, the single-token kernels run once per token (one
+    moe_expert_ffn_q4 call per token), and the library's own choice
+    (MOE_FFN_AUTO, one call). Routing from hidden states (the router
+    with its bias) and from Zipf logits. Each point: a HIP graph of 8 calls
+    over 8 distinct batches, replayed; the median of 5 timed replays."""
+    import torch
+    import quantized_moe_expert_sigmoid_amd as moe
+    from synth import workloads as wl
+    moe.lib()
+    ctx = moe.MoeCtx(0)
+    w = wl.DECODE1
+    L = build_gpu_layer(ctx, w, args.bits)
+    ffn = moe.FFN_BY_BITS[args.bits]
+    sh = L.shared.struct(0)
+    rows = []
+    nb = 8
+    for routing in ("hidden", "zipf"):
+        for T in [int(v) for v in args.crossover.split(",")]:
+            batches = []
+            for b in range(nb):
+                x = torch.from_numpy(wl.hidden_fp32(w, T, batch=100 + b)).cuda()
+                xq = torch.empty((T, w.H), dtype=torch.int8, device="cuda")
+                sx = torch.empty((T,), dtype=torch.float32, device="cuda")
+                moe.moe_quantize_act_i8(ctx, x, xq, sx)
+                idx = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
+                wt = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
+                if routing == "zipf":
+                    z = torch.from_numpy(wl.logits_fp32(wl.DECODE64, T, batch=100 + b)).cuda()
+                    moe.moe_router_topk(ctx, z, None, None, w.k, idx, wt, logits_in=True)
+                else:
+                    moe.moe_router_topk(ctx, x, L.w_router, L.bias, w.k, idx, wt)
+                y = torch.zeros((T, w.k + 1, w.H), dtype=torch.float32, device="cuda")
+                batches.append((xq, sx, idx, y))
+            torch.cuda.synchronize()
+            distinct = float(np.mean([len(np.unique(b[2].cpu().numpy())) for b in batches])) + 1
+            row = {"routing": routing, "T": T, "distinct_experts": round(distinct, 1)}
+            for fam in ("dot4", "mfma", "t1_per_token", "auto"):
+                ctx.set_ffn_kernels("auto" if fam in ("t1_per_token", "auto") else fam)
+
+                def call(b):
+                    xq, sx, idx, y = batches[b]
+                    if fam == "t1_per_token":
+                        for t in range(T):
+                            ffn(ctx, L.experts.table, sh, None, xq[t:t + 1], sx[t:t + 1], idx[t:t + 1], w.H, w.I,
+                                w.E, y[t:t + 1])
+                    else:
+                        ffn(ctx, L.experts.table, sh, None, xq, sx, idx, w.H, w.I, w.E, y)
+                for b in range(nb):
+                    call(b)
+                torch.cuda.synchronize()
+                ctx.check()
+                cap = torch.cuda.Stream()
+                ctx.set_stream(cap)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for b in range(nb):
+                        call(b)
+                ctx.set_stream(torch.cuda.current_stream())
+                graph_upload(g)
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ts = []
+                for _ in range(5):
+                    e0.record()
+                    g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3 / nb)
+                row[fam + "_us"] = round(float(np.median(ts)), 1)
+                del g
+            ctx.set_ffn_kernels("auto")
+            per = L.experts.block_bytes
+            row["best"] = min(("dot4", "mfma", "t1_per_token"), key=lambda f: row[f + "_us"])
+            row["best_GBps"] = round(distinct * per / (row[row["best"] + "_us"] * 1e-6) / 1e9, 1)
+            rows.append(row)
+            log("[crossover] " + json.dumps(row))
+    print(json.dumps({"crossover": rows}), flush=True)
+    ctx.close()
+
+
 def build_gpu_layer(ctx, w, bits):
     import torch
     from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
@@ -519,6 +603,8 @@ def main():
                     help="read-ahead: before each layer's FFN, prefetch the next layer's experts of the previous token")
     ap.add_argument("--stack-pin-gb", type=float, default=0.0,
                     help="after the warm-up, pin this many GB of the most requested experts (usage counts)")
+    ap.add_argument("--crossover", default="",
+                    help="comma-separated token counts: time the expert FFN's kernel families at each (GLM shape)")
     ap.add_argument("--pmc-summary", nargs=5, default=None,
                     metavar=("BENCH_FETCH", "BENCH_WRITE", "COPY_FETCH", "COPY_WRITE", "OUT"))
     args = ap.parse_args()
@@ -543,6 +629,9 @@ def main():
         return
     if args.workload == "glm_stack_pool":
         stack_pool_bench(args)
+        return
+    if args.crossover:
+        crossover_bench(args)
         return
     moe.lib()
     w = wl.ALL[args.workload]

@@ -127,11 +127,13 @@ moe_status moe_ctx_set_stream(moe_ctx *ctx, void *hip_stream);
 const char *moe_last_error(void);
 int moe_abi_version(void);
 /* Which kernels compute the expert FFN of moe_expert_ffn_q* and of the
- * multi-token path of moe_layer_forward. MOE_FFN_AUTO (the default): the
- * int8 matrix-core kernels for two or more tokens; for one token the
- * single-token kernels of the whole-layer decode path (without its router
- * and combine) where the shape fits them, else the vector dot-product
- * kernels. MOE_FFN_DOT4: always the vector kernels. MOE_FFN_MFMA: always the
+ * multi-token path of moe_layer_forward. MOE_FFN_AUTO (the default), from
+ * the measured crossover at the GLM shape: up to 4 tokens the single-token
+ * kernels of the whole-layer decode path (without its router and combine)
+ * run once per token, where the shape fits them; from 5 tokens on the int8
+ * matrix-core kernels, whose tiles read each expert once for all its
+ * tokens; the vector dot-product kernels where neither takes the shape.
+ * MOE_FFN_DOT4: always the vector kernels. MOE_FFN_MFMA: always the
  * matrix-core kernels. All take every shape they are chosen for and compute
  * the same exact integer sums and the same fp32 epilogue, so their results
  * are bit-identical. Any other value: MOE_EINVAL.

@@ -447,15 +447,22 @@ int rows_per_wg_gu(int bits) { return kWaves * (bits == 8 ? Shape<8>::kRwGU : bi
 int rows_per_wg_d(int bits) { return kWaves * (bits == 8 ? Shape<8>::kRwD : bits == 4 ? Shape<4>::kRwD : Shape<2>::kRwD); }
 
 
-// Which kernel family computes a call's expert FFN.
+// Which kernel family computes a call's expert FFN. MOE_FFN_AUTO follows
+// the measured crossover at the GLM shape (int4, hidden 6144, intermediate
+// 2048, top-8 + shared): up to kT1MaxTokens tokens the single-token kernels
+// run once per token (2 tokens: 77 us against 101 for the vector kernels
+// and 117 for the matrix cores; 4 tokens: 156 against 163 and 167); from 8
+// tokens on the matrix cores win (8: 237 against 279 and 311), their
+// per-expert tiles reading each expert once for all its tokens.
+constexpr int kT1MaxTokens = 4;
 enum FfnRoute { kRouteMfma, kRouteT1, kRouteDot4, kRouteUnsupported };
 FfnRoute ffn_route(const moe_ctx *ctx, int bits, int has_shared, int T, int H, int I, int k) {
   const bool mfma_ok = expert_ffn_mfma_supported(bits, H, I);
   if (ctx->ffn_kernels == MOE_FFN_MFMA && !mfma_ok) return kRouteUnsupported;
-  if (mfma_ok && (ctx->ffn_kernels == MOE_FFN_MFMA || (ctx->ffn_kernels == MOE_FFN_AUTO && T >= 2))) return kRouteMfma;
-  // one token: the single-token kernels (no bucketing pass)
-  if (T == 1 && ctx->ffn_kernels == MOE_FFN_AUTO && decode_t1_supported(bits, H, I, k, has_shared, ctx->n_cu))
+  if (ctx->ffn_kernels == MOE_FFN_AUTO && T <= kT1MaxTokens &&
+      decode_t1_supported(bits, H, I, k, has_shared, ctx->n_cu))
     return kRouteT1;
+  if (mfma_ok && (ctx->ffn_kernels == MOE_FFN_MFMA || (ctx->ffn_kernels == MOE_FFN_AUTO && T >= 2))) return kRouteMfma;
   return kRouteDot4;
 }
 
@@ -504,8 +511,28 @@ moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts
     case kRouteMfma:
       return launch_expert_ffn_mfma(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k,
                                     y_slots);
-    case kRouteT1:
-      return launch_ffn_t1(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, H, I, E, k, y_slots);
+    case kRouteT1: {
+      // one single-token chain per token, in token order on the stream (the
+      // chains share the scratch; each starts after the previous has ended).
+      // Captured intermediates go to each token's rows.
+      const moe_debug_bufs dbg = ctx->dbg;
+      moe_status st = MOE_OK;
+      for (int t = 0; t < T && st == MOE_OK; ++t) {
+        if (ctx->dbg_on) {
+          const int64_t p0 = (int64_t)t * (k + 1);
+          ctx->dbg.accg = dbg.accg ? dbg.accg + p0 * I : nullptr;
+          ctx->dbg.accu = dbg.accu ? dbg.accu + p0 * I : nullptr;
+          ctx->dbg.a = dbg.a ? dbg.a + p0 * I : nullptr;
+          ctx->dbg.aq = dbg.aq ? dbg.aq + p0 * I : nullptr;
+          ctx->dbg.sa = dbg.sa ? dbg.sa + p0 : nullptr;
+          ctx->dbg.accd = dbg.accd ? dbg.accd + p0 * H : nullptr;
+        }
+        st = launch_ffn_t1(ctx, bits, experts, shared, expert_bits, xq + (int64_t)t * H, sx + t,
+                           topk_idx + (int64_t)t * k, H, I, E, k, y_slots + (int64_t)t * (k + 1) * H);
+      }
+      ctx->dbg = dbg;
+      return st;
+    }
     default:
       break;
   }

@@ -227,11 +227,14 @@ def check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, 
             assert np.array_equal(yg[t, j].view(np.uint32), r["y"].view(np.uint32)), (t, j)
 
 
-@pytest.mark.parametrize("kern", ["dot4", "mfma"])
+@pytest.mark.parametrize("kern", ["dot4", "mfma", "auto"])
 @pytest.mark.parametrize("bits", [4, 8, 2])
 @pytest.mark.parametrize("T,H,I,E,k", [(32, 128, 64, 8, 2), (37, 256, 192, 8, 2), (3, 512, 128, 16, 4),
-                                       (150, 256, 128, 4, 2)])
+                                       (150, 256, 128, 4, 2), (2, 256, 128, 8, 3), (4, 128, 64, 6, 2)])
 def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, kern, bits, T, H, I, E, k):
+    """Every intermediate of every (token, slot) pair bit-exact, for each
+    kernel family ("auto": up to 4 tokens the single-token kernels once per
+    token, more the matrix cores)."""
     idx = random_routing(syn, T, E, k, 42)
     check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, seed=40 + bits)
 
