@@ -291,6 +291,7 @@ def stack_pool_bench(args) -> None:
     tb0 = pool.table_stats()
     tm = time.perf_counter()
     run(args.stack_warmup, ntok)
+    issue_s = time.perf_counter() - tm  # the host's time to issue the calls (the GPU may still be running)
     torch.cuda.synchronize()
     dt = time.perf_counter() - tm
     ctx.check()
@@ -342,6 +343,9 @@ def stack_pool_bench(args) -> None:
                    "pool_bytes": int(args.stack_pool_gb * 1e9),
                    "host_expert_bytes": host_bytes, "routing": "correlated Zipf trace (reuse 0.6, s 1.1)"},
         "cold_start_tokens_per_s": round(args.stack_warmup / cold_s, 2),
+        # host time to issue one token's calls through every layer: near
+        # ms_per_step when the loop is bound by the host, not the GPU
+        "host_issue_ms_per_token": round(issue_s / n * 1e3, 4),
         "hit_rate": round(hits / max(1, hits + misses), 5),
         "misses_per_token": round(misses / n, 3),
         "h2d_GBps": round(h2d / dt / 1e9, 2),

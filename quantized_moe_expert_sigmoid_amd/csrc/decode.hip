@@ -63,6 +63,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxX4 = 8;        // float4 of x per thread in the max pass: H <= 8192
 constexpr int kMaxIDown = 4096;            // intermediate held in LDS by the down kernel
 constexpr int kMaxPairsWg = kFfnThreads;  // routed row pairs per gate/up workgroup (one per thread)
+constexpr int MOE_WAVE_HOST = 64;          // lanes per wave, for host-side shape choices
 
 // One slot of the token: the expert's weights and its routing weight.
 struct SlotEntry {
@@ -216,6 +217,25 @@ struct WaveSlots {
   const uint8_t *gate0, *up0, *gate1, *up1;
 };
 
+// Per-width kernel shapes: 16-byte chunks per lane of a gate/up row (JG) and
+// of a down row (JD) the kernels are compiled for, row pairs per gate/up
+// batch (NB) and down rows per batch (RB), two batches in flight each. A CU
+// keeps some tens of KB of loads in flight; deeper queues only stall issue.
+template <int BITS>
+struct T1Shape;
+template <>
+struct T1Shape<4> {
+  static constexpr int JG = 3, JD = 1, NB = 1, RB = 1;
+};
+template <>
+struct T1Shape<8> {
+  static constexpr int JG = 6, JD = 2, NB = 1, RB = 1;
+};
+template <>
+struct T1Shape<2> {
+  static constexpr int JG = 2, JD = 1, NB = 1, RB = 1;
+};
+
 // Load NB routed row pairs starting at routed pair qb; pairs past qlast (the
 // wave's last pair, or pair 0 for a wave without routed pairs) re-read it
 // (their results are dropped). The loads are unconditional, so the compiler
@@ -285,8 +305,13 @@ __device__ __forceinline__ void gu_compute(int n, int lane0, int lane, const GuB
   }
 }
 
+// The gate/up work of workgroup vb of vn: the whole grid, or in the
+// mixed-width kernel this width's part of it. has_sh: this part computes the
+// shared expert; want_bits: the width whose slots it computes (given
+// routing); write_table: it writes the global slot table and the error flag.
 template <int BITS, int JG, int NB, bool GIVEN>
-__global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) {
+__device__ __forceinline__ void gateup_t1_body(const GateUpT1Args &a, int vb, int vn, int has_sh, int want_bits,
+                                               bool write_table) {
   static_assert(NB == 1, "routed pairs are taken one at a time");
   constexpr int OFF = QFmt<BITS>::kOff;
   __shared__ float key_s[kMaxE], sig_s[kMaxE];
@@ -297,13 +322,13 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   const int tid = threadIdx.x;
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
-  const int nw = gridDim.x * kFfnWaves;
-  const int gw = blockIdx.x * kFfnWaves + wave;
+  const int nw = vn * kFfnWaves;
+  const int gw = vb * kFfnWaves + wave;
   const int rowbytes = a.H * BITS / 8;
   const int cpr = rowbytes / 16;
   // this wave's shared pairs [sh0, sh0 + ns); lanes [0, ns) keep their sums
-  const int sh0 = a.has_shared ? uniform((int)((int64_t)gw * a.I / nw)) : 0;
-  const int ns = a.has_shared ? uniform((int)((int64_t)(gw + 1) * a.I / nw)) - sh0 : 0;
+  const int sh0 = has_sh ? uniform((int)((int64_t)gw * a.I / nw)) : 0;
+  const int ns = has_sh ? uniform((int)((int64_t)(gw + 1) * a.I / nw)) - sh0 : 0;
   __shared__ int nkeep_s;  // routed slots kept (k, or fewer under top-p)
   if (tid == 0) next_s = 0;
 
@@ -354,13 +379,13 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   // expert a dummy in-bounds row of xq is read and dropped) ----
   GuBatch<BITS, JG, NB> b0, b1;
   {
-    const uint8_t *sg_p = a.has_shared ? a.shared.gate : reinterpret_cast<const uint8_t *>(a.xq);
-    const uint8_t *su_p = a.has_shared ? a.shared.up : reinterpret_cast<const uint8_t *>(a.xq);
-    gu_load_shared<BITS, JG, NB>(sg_p, su_p, a.has_shared ? sh0 : 0, ns, lane, rowbytes, cpr, b0);
+    const uint8_t *sg_p = has_sh ? a.shared.gate : reinterpret_cast<const uint8_t *>(a.xq);
+    const uint8_t *su_p = has_sh ? a.shared.up : reinterpret_cast<const uint8_t *>(a.xq);
+    gu_load_shared<BITS, JG, NB>(sg_p, su_p, has_sh ? sh0 : 0, ns, lane, rowbytes, cpr, b0);
   }
   float sg_sh, su_sh;
   {
-    const bool use = a.has_shared != 0;
+    const bool use = has_sh != 0;
     const int li = use ? sh0 + min(lane, max(ns - 1, 0)) : 0;
     sg_sh = gptr(use ? a.shared.s_gate : a.sx)[li];
     su_sh = gptr(use ? a.shared.s_up : a.sx)[li];
@@ -421,8 +446,8 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
         }
       }
       const uint64_t bad = __ballot(!valid);
-      if (bad && blockIdx.x == 0 && lane == 0) atomicOr(a.err, 1u);
-      if (act && a.expert_bits) act = a.expert_bits[e] == a.want_bits;
+      if (bad && write_table && lane == 0) atomicOr(a.err, 1u);
+      if (act && a.expert_bits) act = a.expert_bits[e] == want_bits;
       const uint64_t m = __ballot(act);
       const int na = __popcll(m);
       const int first = na ? __ffsll((unsigned long long)m) - 1 : 0;
@@ -431,7 +456,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
         if (ex >= 0) {
 #pragma unroll
           for (int q = 0; q < 3; ++q) row[q] = ldg16(a.experts + ex, q);
-        } else if (a.has_shared) {
+        } else if (has_sh) {
           const uint64_t pp[6] = {(uint64_t)a.shared.gate, (uint64_t)a.shared.up, (uint64_t)a.shared.down,
                                   (uint64_t)a.shared.s_gate, (uint64_t)a.shared.s_up, (uint64_t)a.shared.s_down};
 #pragma unroll
@@ -448,7 +473,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
       row_of(e_first, dummy);
       if (lane < a.k) {
         const uint4 tag = make_uint4(0u, (uint32_t)(act ? e : -1), (uint32_t)lane, 0u);
-        if (blockIdx.x == 0) {
+        if (write_table) {
           uint4 *gdst = reinterpret_cast<uint4 *>(a.slots + lane);
 #pragma unroll
           for (int q = 0; q < 3; ++q) gdst[q] = own[q];
@@ -466,14 +491,14 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
           for (int q = 0; q < 3; ++q) dst[q] = dummy[q];
           dst[3] = make_uint4(0u, (uint32_t)-1, (uint32_t)lane, 0u);
         }
-      } else if (lane == a.k && a.has_shared) {
+      } else if (lane == a.k && has_sh) {
         row_of(-1, own);
         const uint4 tag = make_uint4(__float_as_uint(1.0f), (uint32_t)-1, (uint32_t)a.k, 0u);
         uint4 *dst = reinterpret_cast<uint4 *>(slot_s + lane);
 #pragma unroll
         for (int q = 0; q < 3; ++q) dst[q] = own[q];
         dst[3] = tag;
-        if (blockIdx.x == 0) {
+        if (write_table) {
           uint4 *gdst = reinterpret_cast<uint4 *>(a.slots + lane);
 #pragma unroll
           for (int q = 0; q < 3; ++q) gdst[q] = own[q];
@@ -483,7 +508,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
       if (lane == 0) nkeep_s = na;
     }
     __syncthreads();
-    if (nkeep_s == 0 && !a.has_shared) return;  // nothing for this width
+    if (nkeep_s == 0 && !has_sh) return;  // nothing for this width
   }
 
   // ---- top-k and the slot table (wave 0) ----
@@ -509,11 +534,11 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
       row[2] = src[2];
       row[3] = make_uint4(__float_as_uint(wgt), (uint32_t)(kp ? my_id : -1), 0u, 0u);
       have = true;
-      if (blockIdx.x == 0) {
+      if (write_table) {
         a.topk_idx[lane] = kp ? my_id : -1;
         a.topk_w[lane] = wgt;
       }
-    } else if (lane == a.k && a.has_shared) {
+    } else if (lane == a.k && has_sh) {
       const uint64_t p[6] = {(uint64_t)a.shared.gate, (uint64_t)a.shared.up, (uint64_t)a.shared.down,
                              (uint64_t)a.shared.s_gate, (uint64_t)a.shared.s_up, (uint64_t)a.shared.s_down};
 #pragma unroll
@@ -527,7 +552,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
       uint4 *dst = reinterpret_cast<uint4 *>(slot_s + lane);
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = row[q];
-      if (blockIdx.x == 0) {
+      if (write_table) {
         uint4 *gdst = reinterpret_cast<uint4 *>(a.slots + lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) gdst[q] = row[q];
@@ -540,8 +565,8 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   // taken one at a time by its waves from an LDS counter: a wave whose loads
   // are served late takes fewer
   const int R = uniform(nkeep_s) * a.I;
-  const int Q0 = uniform((int)((int64_t)blockIdx.x * R / gridDim.x));
-  const int np = uniform((int)((int64_t)(blockIdx.x + 1) * R / gridDim.x)) - Q0;
+  const int Q0 = uniform((int)((int64_t)vb * R / vn));
+  const int np = uniform((int)((int64_t)(vb + 1) * R / vn)) - Q0;
 
   // ---- the workgroup's routed slots (a contiguous range spans at most two) ----
   WaveSlots ws;
@@ -579,9 +604,15 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   }
   const int xsum = wave_sum_all(xs_lane);
 
-  // the wave's shared pairs (lanes [0, ns) keep their sums)
+  // the wave's shared pairs (lanes [0, ns) keep their sums): the first batch
+  // was issued before routing; more than one batch only when a width's part
+  // of the mixed-width kernel has fewer waves than the shared expert has rows
   int res_g = 0, res_u = 0;
-  if (ns > 0) gu_compute<BITS, JG, NB>(ns, 0, lane, b0, xr, res_g, res_u);
+  if (ns > 0) gu_compute<BITS, JG, NB>(ns < NB ? ns : NB, 0, lane, b0, xr, res_g, res_u);
+  for (int p = NB; p < ns; p += NB) {
+    gu_load_shared<BITS, JG, NB>(a.shared.gate, a.shared.up, sh0 + p, ns - p, lane, rowbytes, cpr, b0);
+    gu_compute<BITS, JG, NB>(ns - p < NB ? ns - p : NB, p, lane, b0, xr, res_g, res_u);
+  }
   int pb = grab();
   gu_load<BITS, JG, NB>(ws, pair_at(pb), qlast, lane, rowbytes, cpr, b0);
   // routed pairs, two in flight (pairs past np re-read the last one; pa < pb)
@@ -626,6 +657,119 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
   if (rt_mine) {
     const int2 r = res_s[tid];
     epilogue(r.x, r.y, rt_sg, rt_su, rt_slot, rt_i);
+  }
+}
+
+template <int BITS, int JG, int NB, bool GIVEN>
+__global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) {
+  gateup_t1_body<BITS, JG, NB, GIVEN>(a, blockIdx.x, gridDim.x, a.has_shared, a.want_bits, blockIdx.x == 0);
+}
+
+// One token, every width of a mixed layer in one launch (routing given).
+// Every workgroup reads the ids and the experts' widths and computes the same
+// split of the grid between the widths present (8, 4, 2 in that order), in
+// proportion to the bytes of their row pairs (the shared expert counted at
+// its width); each part runs that width's gate/up over its share of the
+// workgroups. Workgroup 0 writes the global slot table: each slot's expert
+// with its width in pad[1], or expert -1 (no expert, a width outside the
+// call's mask, a repeated id) with valid pointers for the down kernel's
+// unconditional loads; it also raises the error flag for bad ids.
+__global__ __launch_bounds__(kFfnThreads) void gateup_mixed_t1_kernel(GateUpT1Args a, int mask, int shared_bits) {
+  const int lane = threadIdx.x & (MOE_WAVE - 1);
+  const int wave = threadIdx.x >> 6;
+  const int e = lane < a.k ? a.given_idx[lane] : -1;
+  bool valid = e == -1 || (e >= 0 && e < a.E);
+  bool act = e >= 0 && e < a.E;
+  for (int j = 0; j < a.k; ++j) {  // a repeated id is an error, and computed for its first slot only
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    if (j < lane && act && ej == e) {
+      act = false;
+      valid = false;
+    }
+  }
+  const int sbits = a.has_shared ? shared_bits : 0;
+  const int emask = mask | (sbits ? 1 << sbits : 0);  // the shared expert's width always runs
+  int b = act ? (int)a.expert_bits[e] : 0;
+  if (!((b == 8 || b == 4 || b == 2) && ((emask >> b) & 1))) b = 0;
+  const int wb[3] = {8, 4, 2};
+  int64_t bytes[3], tot = 0;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const int n = __popcll(__ballot(b == wb[w])) + (sbits == wb[w] ? 1 : 0);
+    bytes[w] = (int64_t)n * wb[w];
+    tot += bytes[w];
+  }
+  if (blockIdx.x == 0 && wave == 0) {
+    if (__ballot(!valid) && lane == 0) atomicOr(a.err, 1u);
+    const uint64_t m = __ballot(b != 0);
+    const int first = m ? __ffsll((unsigned long long)m) - 1 : 0;
+    const int e_first = m ? __builtin_amdgcn_readlane(e, first) : -1;
+    auto row_of = [&](int ex, uint4 (&row)[3]) {
+      if (ex >= 0) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) row[q] = ldg16(a.experts + ex, q);
+      } else if (a.has_shared) {
+        const uint64_t pp[6] = {(uint64_t)a.shared.gate, (uint64_t)a.shared.up, (uint64_t)a.shared.down,
+                                (uint64_t)a.shared.s_gate, (uint64_t)a.shared.s_up, (uint64_t)a.shared.s_down};
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          row[q] = make_uint4((uint32_t)pp[2 * q], (uint32_t)(pp[2 * q] >> 32), (uint32_t)pp[2 * q + 1],
+                              (uint32_t)(pp[2 * q + 1] >> 32));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) row[q] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    };
+    uint4 row[3];
+    if (lane < a.k) {
+      row_of(b ? e : e_first, row);
+      const uint4 tag = make_uint4(0u, (uint32_t)(b ? e : -1), (uint32_t)lane, (uint32_t)b);
+      uint4 *gdst = reinterpret_cast<uint4 *>(a.slots + lane);
+#pragma unroll
+      for (int q = 0; q < 3; ++q) gdst[q] = row[q];
+      gdst[3] = tag;
+    } else if (lane == a.k && a.has_shared) {
+      row_of(-1, row);
+      const uint4 tag = make_uint4(__float_as_uint(1.0f), (uint32_t)-1, (uint32_t)a.k, (uint32_t)sbits);
+      uint4 *gdst = reinterpret_cast<uint4 *>(a.slots + lane);
+#pragma unroll
+      for (int q = 0; q < 3; ++q) gdst[q] = row[q];
+      gdst[3] = tag;
+    }
+  }
+  if (tot == 0) return;
+  // workgroups per width: first each width's minimum (enough that no
+  // workgroup takes more than kMaxPairsWg routed pairs and no wave more than
+  // one lane's worth of shared pairs; the launcher checks that the minimums
+  // fit the grid), then the rest of the grid in proportion to the bytes of
+  // the row pairs, its rounding remainder to the largest part
+  const int nwg = gridDim.x;
+  int cnt[3], big = 0, used = 0;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const int routed = __popcll(__ballot(b == wb[w]));
+    int mn = bytes[w] ? max(1, (routed * a.I + kMaxPairsWg - 1) / kMaxPairsWg) : 0;
+    if (sbits == wb[w]) mn = max(mn, (a.I + kFfnWaves * MOE_WAVE - 1) / (kFfnWaves * MOE_WAVE));
+    cnt[w] = mn;
+    used += mn;
+    if (bytes[w] > bytes[big]) big = w;
+  }
+  const int rest = max(nwg - used, 0);
+  int given_out = 0;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const int add = (int)(rest * bytes[w] / tot);
+    cnt[w] += add;
+    given_out += add;
+  }
+  cnt[big] += rest - given_out;
+  const int vb0 = blockIdx.x;
+  if (vb0 < cnt[0]) {
+    gateup_t1_body<8, T1Shape<8>::JG, 1, true>(a, vb0, cnt[0], sbits == 8, 8, false);
+  } else if (vb0 < cnt[0] + cnt[1]) {
+    gateup_t1_body<4, T1Shape<4>::JG, 1, true>(a, vb0 - cnt[0], cnt[1], sbits == 4, 4, false);
+  } else if (vb0 < cnt[0] + cnt[1] + cnt[2]) {
+    gateup_t1_body<2, T1Shape<2>::JG, 1, true>(a, vb0 - cnt[0] - cnt[1], cnt[2], sbits == 2, 2, false);
   }
 }
 
@@ -697,7 +841,7 @@ struct RequantT1Args {
 // holds whole field groups (int8: 4 elements, int4: 8, int2: 16), so the
 // reordering stays in registers.
 template <int BITS>
-__global__ __launch_bounds__(kRqThreads) void requant_t1_kernel(RequantT1Args a) {
+__device__ __forceinline__ void requant_t1_body(const RequantT1Args &a, int s) {
   constexpr int G = (BITS == 8) ? 4 : (BITS == 4 ? 8 : 16);
   constexpr int GD = G / 4;  // dwords (float4 of a) per group
   __shared__ float red_m[kRqThreads / MOE_WAVE];
@@ -705,8 +849,6 @@ __global__ __launch_bounds__(kRqThreads) void requant_t1_kernel(RequantT1Args a)
   const int tid = threadIdx.x;
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
-  const int s = blockIdx.x;
-  if (a.given && s < a.k && a.slots[s].expert == -1) return;  // another width's slot: left alone
   const float4 *As = reinterpret_cast<const float4 *>(a.A + (int64_t)s * a.I);
   const int ng = a.I / G;
   // the thread's groups stay in registers between the two passes
@@ -781,6 +923,27 @@ __global__ __launch_bounds__(kRqThreads) void requant_t1_kernel(RequantT1Args a)
     a.sums[s] = red_c[0] + red_c[1] + red_c[2] + red_c[3];
     a.sa[s] = sc;
     if (a.dbg_on && a.dbg.sa) a.dbg.sa[s] = sc;
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kRqThreads) void requant_t1_kernel(RequantT1Args a) {
+  const int s = blockIdx.x;
+  if (a.given && s < a.k && a.slots[s].expert == -1) return;  // another width's slot: left alone
+  requant_t1_body<BITS>(a, s);
+}
+
+// The mixed-width chain: slot blockIdx.x at its own width (pad[1] of its
+// entry, written by the mixed gate/up kernel); a slot without work is left
+// alone.
+__global__ __launch_bounds__(kRqThreads) void requant_mixed_t1_kernel(RequantT1Args a) {
+  const int s = blockIdx.x;
+  if (s < a.k && a.slots[s].expert == -1) return;
+  switch (a.slots[s].pad[1]) {
+    case 8: requant_t1_body<8>(a, s); break;
+    case 4: requant_t1_body<4>(a, s); break;
+    case 2: requant_t1_body<2>(a, s); break;
+    default: break;
   }
 }
 
@@ -970,6 +1133,205 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
 }
 
 // ---------------------------------------------------------------------------
+// K4 of the mixed-width chain (routing given): the down projection of every
+// slot at its own width (pad[1] of its entry), then the combine. Lane l owns
+// the 32-element units l, l + 64, ... of each slot's rows: a unit is 32 bytes
+// of int8 codes, 16 of int4 and 8 of int2, and meets 32 codes of a in the
+// field order of the slot's width (the requantisation kernel's layout: field
+// groups at their natural positions), so a slot of any width keeps every lane
+// busy. The loads are the same for every width -- one 16-byte piece per unit
+// (two when the call has int8 slots) at a per-slot offset, an int2 unit's 8
+// bytes being one half of its piece -- and only the dot product branches on
+// the slot's width.
+// ---------------------------------------------------------------------------
+// 32 int2 fields (8 bytes) against 32 codes in int2 field order
+__device__ __forceinline__ int dot_q2_half(uint32_t w0, uint32_t w1, const uint32_t *c, int acc) {
+  constexpr uint32_t M = 0x03030303u;
+  acc = sdot4((int)(w0 & M), (int)c[0], acc);
+  acc = sdot4((int)((w0 >> 2) & M), (int)c[1], acc);
+  acc = sdot4((int)((w0 >> 4) & M), (int)c[2], acc);
+  acc = sdot4((int)((w0 >> 6) & M), (int)c[3], acc);
+  acc = sdot4((int)(w1 & M), (int)c[4], acc);
+  acc = sdot4((int)((w1 >> 2) & M), (int)c[5], acc);
+  acc = sdot4((int)((w1 >> 4) & M), (int)c[6], acc);
+  return sdot4((int)((w1 >> 6) & M), (int)c[7], acc);
+}
+
+template <int MAXB, int JU>
+__global__ __launch_bounds__(kFfnThreads) void down_mixed_t1_kernel(DownT1Args a) {
+  constexpr int NP = MAXB == 8 ? 2 : 1;  // 16-byte pieces loaded per unit
+  __shared__ __align__(16) int8_t aq_s[kMaxSlots * kMaxIDown];
+  const int tid = threadIdx.x;
+  const int lane = tid & (MOE_WAVE - 1);
+  const int wave = tid >> 6;
+  const int nw = gridDim.x * kFfnWaves;
+  const int gw = blockIdx.x * kFfnWaves + wave;
+  const int r0 = uniform((int)((int64_t)gw * a.H / nw)), r1 = uniform((int)((int64_t)(gw + 1) * a.H / nw));
+  const int S = a.S;
+  const int nu = a.I / 32;  // units per row
+
+  // ---- slot fields (lane s < S holds slot s's), then the codes ----
+  const int ls = lane < S ? lane : S - 1;
+  const uint8_t *down_l = a.slots[ls].w.down;
+  const float *sdown_l = a.slots[ls].w.s_down;
+  const int bits_l = a.slots[ls].pad[1];
+  const bool act_l = lane < S && (lane == a.k ? a.has_shared != 0 : a.slots[ls].expert != -1);
+  const bool comb = a.out != nullptr;
+  const float wg_l = (comb && lane < a.k) ? a.w_given[lane] : 0.0f;
+  if (__ballot(act_l) == 0) {
+    if (!comb) return;
+    // no slot has work: the combine alone, every slot read back
+    for (int r = r0; r < r1; ++r) {
+      const float yall = (lane < a.k && wg_l != 0.0f) ? a.y[(int64_t)lane * a.H + r] : 0.0f;
+      float acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < kMaxSlots - 1; ++s) {
+        const float ws = readlane_f(wg_l, s);
+        if (s < a.k && ws != 0.0f) acc = __builtin_fmaf(ws, readlane_f(yall, s), acc);
+      }
+      if (lane == 0) a.out[r] = acc;
+    }
+    return;
+  }
+  const int aqsum_l = a.sums[ls];
+  const float sa_l = a.sa[ls];
+  const int n16 = S * a.I / 16;
+  uint4 aqv[kAq16];
+#pragma unroll
+  for (int j = 0; j < kAq16; ++j) aqv[j] = ldg16(a.aqf, min(tid + j * kFfnThreads, n16 - 1));
+  const uint8_t *dp[kMaxSlots];
+  int bits[kMaxSlots], rowb[kMaxSlots];
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s) {
+    const int sl = s < S ? s : S - 1;
+    dp[s] = readlane_p(down_l, sl);
+    // a slot without work reads (valid) rows as if int4 and drops them
+    const int b = __builtin_amdgcn_readlane(bits_l, sl);
+    bits[s] = (b == 8 || b == 2) ? b : 4;
+    rowb[s] = a.I * bits[s] / 8;
+  }
+  // byte offset of this lane's unit u in a row of slot s: 16-byte aligned;
+  // an int2 unit is 8 bytes, read as one half of the piece holding it
+  auto unit_off = [&](int s, int u) {
+    const int off = u * 4 * bits[s];
+    return bits[s] == 2 ? min(off & ~15, rowb[s] - 16) : off;
+  };
+
+  struct RowBatch {
+    uint4 w[kMaxSlots][JU][NP];
+    float sd;
+  };
+  auto load_rows = [&](int r, RowBatch &bt) {
+    r = max(min(r, r1 - 1), 0);
+#pragma unroll
+    for (int s = 0; s < kMaxSlots; ++s) {
+      const uint8_t *row = dp[s] + (int64_t)r * rowb[s];
+#pragma unroll
+      for (int j = 0; j < JU; ++j) {
+        const int u = min(lane + j * MOE_WAVE, nu - 1);
+        const int o = unit_off(s, u);
+        bt.w[s][j][0] = ldg16_nt(row + o, 0);
+        if constexpr (NP == 2) bt.w[s][j][1] = ldg16_nt(row + (bits[s] == 8 ? o + 16 : o), 0);
+      }
+    }
+    bt.sd = gptr(sdown_l)[r];
+  };
+  RowBatch b0, b1;
+  load_rows(r0, b0);  // the first down rows of every slot go out right behind the codes
+
+  // ---- the codes into LDS ----
+#pragma unroll
+  for (int j = 0; j < kAq16; ++j) {
+    const int i = tid + j * kFfnThreads;
+    if (i < n16) reinterpret_cast<uint4 *>(aq_s)[i] = aqv[j];
+  }
+  __syncthreads();
+  if (r0 >= r1) return;
+  load_rows(r0 + 1, b1);
+
+  // every slot's 32 codes per unit, in registers
+  uint32_t aqr[kMaxSlots][JU][8];
+  int aqsum[kMaxSlots];
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s) {
+    aqsum[s] = __builtin_amdgcn_readlane(aqsum_l, s < S ? s : S - 1);
+#pragma unroll
+    for (int j = 0; j < JU; ++j) {
+      const int u = lane + j * MOE_WAVE;
+      if (s < S && u < nu) {
+        const uint4 v0 = reinterpret_cast<const uint4 *>(aq_s + s * a.I + u * 32)[0];
+        const uint4 v1 = reinterpret_cast<const uint4 *>(aq_s + s * a.I + u * 32)[1];
+        aqr[s][j][0] = v0.x; aqr[s][j][1] = v0.y; aqr[s][j][2] = v0.z; aqr[s][j][3] = v0.w;
+        aqr[s][j][4] = v1.x; aqr[s][j][5] = v1.y; aqr[s][j][6] = v1.z; aqr[s][j][7] = v1.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) aqr[s][j][q] = 0u;
+      }
+    }
+  }
+  auto compute_row = [&](int r, const RowBatch &bt) {
+    int mine = 0;  // lane s keeps slot s's accumulator
+#pragma unroll
+    for (int s = 0; s < kMaxSlots; ++s) {
+      if (s < S) {
+        int acc = 0;
+#pragma unroll
+        for (int j = 0; j < JU; ++j) {
+          const uint4 w = bt.w[s][j][0];
+          if (bits[s] == 8) {
+            const uint4 w1 = bt.w[s][j][NP - 1];
+            const uint32_t wd[8] = {w.x, w.y, w.z, w.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc = sdot4((int)wd[q], (int)aqr[s][j][q], acc);
+          } else if (bits[s] == 4) {
+            constexpr uint32_t M = 0x0f0f0f0fu;
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              acc = sdot4((int)(wd[m] & M), (int)aqr[s][j][2 * m], acc);
+              acc = sdot4((int)((wd[m] >> 4) & M), (int)aqr[s][j][2 * m + 1], acc);
+            }
+          } else {
+            const int u = lane + j * MOE_WAVE;
+            const bool hi = (u * 8) - unit_off(s, min(u, nu - 1)) == 8;
+            acc = dot_q2_half(hi ? w.z : w.x, hi ? w.w : w.y, aqr[s][j], acc);
+          }
+        }
+        const int off = bits[s] == 8 ? 0 : (bits[s] == 4 ? 8 : 2);
+        acc = wave_sum_all(acc) - off * aqsum[s];
+        if (lane == s) mine = acc;
+      }
+    }
+    const float yv = (float)mine * bt.sd * sa_l;
+    if (act_l) {
+      a.y[(int64_t)lane * a.H + r] = yv;
+      if (a.dbg_on && a.dbg.accd) a.dbg.accd[(int64_t)lane * a.H + r] = mine;
+    }
+    if (comb) {
+      // the combine as the combine entry point computes it: shared first, then
+      // the slots of nonzero weight in order (a slot without work here holds
+      // what another call wrote)
+      float yall = yv;
+      if (!act_l && lane < a.k && wg_l != 0.0f) yall = a.y[(int64_t)lane * a.H + r];
+      float acc = a.has_shared ? readlane_f(yall, a.k) : 0.0f;
+#pragma unroll
+      for (int s = 0; s < kMaxSlots - 1; ++s) {
+        const float ws = readlane_f(wg_l, s);
+        if (s < a.k && ws != 0.0f) acc = __builtin_fmaf(ws, readlane_f(yall, s), acc);
+      }
+      if (lane == 0) a.out[r] = acc;
+    }
+  };
+  for (int r = r0; r < r1; r += 2) {
+    compute_row(r, b0);
+    if (r + 1 >= r1) break;
+    if (r + 2 < r1) load_rows(r + 2, b0);
+    compute_row(r + 1, b1);
+    if (r + 3 < r1) load_rows(r + 3, b1);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
 template <int BITS, int JG, int NB, bool GIVEN = false>
@@ -985,25 +1347,6 @@ moe_status launch_dn(moe_ctx *ctx, hipStream_t stream, const DownT1Args &d, int 
   MOE_CHECK_LAUNCH("down_combine_t1_kernel");
   return MOE_OK;
 }
-
-// Per-width kernel shapes: 16-byte chunks per lane of a gate/up row (JG) and
-// of a down row (JD) the kernels are compiled for, row pairs per gate/up
-// batch (NB) and down rows per batch (RB), two batches in flight each. A CU
-// keeps some tens of KB of loads in flight; deeper queues only stall issue.
-template <int BITS>
-struct T1Shape;
-template <>
-struct T1Shape<4> {
-  static constexpr int JG = 3, JD = 1, NB = 1, RB = 1;
-};
-template <>
-struct T1Shape<8> {
-  static constexpr int JG = 6, JD = 2, NB = 1, RB = 1;
-};
-template <>
-struct T1Shape<2> {
-  static constexpr int JG = 2, JD = 1, NB = 1, RB = 1;
-};
 
 }  // namespace
 
@@ -1278,6 +1621,84 @@ moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, co
 // the combine, reading the earlier chains' slots back from y_slots. Running
 // the narrower widths' chains on a second stream beside the first was
 // slower: the fork and join cost more than the overlap gained.
+namespace {
+// Every width of a one-token mixed layer in one chain of three kernels: the
+// width-split gate/up, the requantisation of every slot at its width, the
+// down projection of every slot at its width with the combine (when out).
+moe_status t1_mixed_chain(moe_ctx *ctx, char *base, int mask, int shared_bits, const moe_expert_w *experts,
+                          const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
+                          const int32_t *topk_idx, const float *topk_w, int H, int I, int E, int k, float *y_slots,
+                          float *out) {
+  const int S = k + (shared ? 1 : 0);
+  MoeLayout m;
+  const size_t o_slots = m.take(sizeof(SlotEntry) * kMaxSlots), o_A = m.take(sizeof(float) * S * I),
+               o_aq = m.take((size_t)S * I), o_sum = m.take(4 * (size_t)S), o_sa = m.take(4 * (size_t)S);
+  SlotEntry *slots = reinterpret_cast<SlotEntry *>(base + o_slots);
+  GateUpT1Args g{};
+  g.E = E; g.k = k; g.ks = 1;
+  g.experts = experts;
+  if (shared) g.shared = *shared;
+  g.has_shared = shared ? 1 : 0;
+  g.slots = slots;
+  g.xq = xq;
+  g.sx = sx;
+  g.H = H; g.I = I; g.S = S;
+  g.A = reinterpret_cast<float *>(base + o_A);
+  g.dbg = ctx->dbg;
+  g.dbg_on = ctx->dbg_on ? 1 : 0;
+  g.given_idx = topk_idx;
+  g.expert_bits = expert_bits;
+  g.err = ctx->dev_small;
+  const int nwg = ctx->n_cu;
+  moe_launch(ctx, MOE_STAGE_GATEUP, gateup_mixed_t1_kernel, dim3(nwg), dim3(kFfnThreads), g, mask, shared_bits);
+  MOE_CHECK_LAUNCH("gateup_mixed_t1_kernel");
+  RequantT1Args q{};
+  q.A = g.A;
+  q.slots = slots;
+  q.k = k;
+  q.I = I;
+  q.S = S;
+  q.aqf = reinterpret_cast<uint32_t *>(base + o_aq);
+  q.sums = reinterpret_cast<int *>(base + o_sum);
+  q.sa = reinterpret_cast<float *>(base + o_sa);
+  q.dbg = ctx->dbg;
+  q.dbg_on = ctx->dbg_on ? 1 : 0;
+  q.given = 1;
+  moe_launch(ctx, MOE_STAGE_REQUANT, requant_mixed_t1_kernel, dim3(S), dim3(kRqThreads), q);
+  MOE_CHECK_LAUNCH("requant_mixed_t1_kernel");
+  DownT1Args d{};
+  d.slots = slots;
+  d.aqf = q.aqf;
+  d.sums = q.sums;
+  d.sa = q.sa;
+  d.H = H; d.I = I; d.S = S; d.k = k;
+  d.has_shared = shared ? 1 : 0;
+  d.y = y_slots;
+  d.out = out;
+  d.w_given = topk_w;
+  d.dbg = ctx->dbg;
+  d.dbg_on = ctx->dbg_on ? 1 : 0;
+  moe_launch(ctx, MOE_STAGE_DOWN, down_mixed_t1_kernel<4, 1>, dim3(nwg), dim3(kFfnThreads), d);
+  MOE_CHECK_LAUNCH("down_mixed_t1_kernel");
+  return MOE_OK;
+}
+}  // namespace
+
+// Whether the one-chain mixed path takes a call: int4 and int2 experts (the
+// shared one included) and at most 64 units of 32 intermediate elements per
+// lane (with int8 slots, or a longer intermediate, its down kernel would hold
+// twice the registers per slot and spill); other mixes run one chain per width.
+static bool t1_mixed_chain_ok(const moe_ctx *ctx, int mask, int shared_bits, bool has_shared, int I, int k) {
+  const int m = mask | (has_shared ? 1 << shared_bits : 0);
+  if ((m & ~((1 << 4) | (1 << 2))) != 0 || I / 32 > MOE_WAVE_HOST) return false;
+  // the gate/up kernel's per-width minimum workgroup counts, at their largest
+  // (two widths, the routed slots split between them, the shared expert on
+  // one of them), must fit its grid of one workgroup per CU
+  const int64_t worst = ((int64_t)k * I + kMaxPairsWg - 1) / kMaxPairsWg + 2 +
+                        (has_shared ? (I + kFfnWaves * MOE_WAVE_HOST - 1) / (kFfnWaves * MOE_WAVE_HOST) : 0);
+  return worst <= ctx->n_cu;
+}
+
 moe_status launch_ffn_t1_mixed(moe_ctx *ctx, const int *widths, int n_widths, int shared_bits,
                                const moe_expert_w *experts, const moe_expert_w *shared, const uint8_t *expert_bits,
                                const int8_t *xq, const float *sx, const int32_t *topk_idx, const float *topk_w, int H,
@@ -1285,6 +1706,11 @@ moe_status launch_ffn_t1_mixed(moe_ctx *ctx, const int *widths, int n_widths, in
   void *scr = nullptr;
   moe_status st = moe_scratch(ctx, t1_chain_bytes(I, k + (shared ? 1 : 0)), &scr);
   if (st) return st;
+  int mask = 0;
+  for (int w = 0; w < n_widths; ++w) mask |= 1 << widths[w];
+  if (n_widths > 1 && t1_mixed_chain_ok(ctx, mask, shared_bits, shared != nullptr, I, k))
+    return t1_mixed_chain(ctx, static_cast<char *>(scr), mask, shared_bits, experts, shared, expert_bits, xq, sx,
+                          topk_idx, topk_w, H, I, E, k, y_slots, out);
   const int last_bits = shared ? shared_bits : widths[n_widths - 1];
   int order[3], n = 0;
   for (int w = 0; w < n_widths; ++w)

@@ -416,6 +416,72 @@ def test_ffn_mixed_one_call(moe, ctx, orc, syn, T, shared_bits):
                 assert np.all(yg[t, k] == 7.0)
 
 
+@pytest.mark.parametrize("H,I", [(512, 192), (256, 64), (6144, 2048)])
+@pytest.mark.parametrize("shared_bits", [4, 2, None])
+def test_ffn_mixed_one_chain_intermediates(moe, ctx, orc, syn, H, I, shared_bits):
+    """One token, int4 and int2 experts in one moe_expert_ffn_mixed call: the
+    single chain whose kernels take each slot at its own width (the gate/up
+    workgroups split between the widths; the down kernel's lanes each own 32
+    elements of every slot, whatever its width). Every captured intermediate
+    of every slot bit-exact against the oracle at its expert's width; a slot
+    of id -1 and one whose width is absent (0) are left untouched; the combine
+    bit-identical to moe_combine."""
+    E, k = 8, 6
+    log(f"mixed one chain H={H} I={I} shared_bits={shared_bits}")
+    made = {b: make_experts(moe, orc, syn, b, H, I, E, seed=140) for b in (4, 2)}
+    bits = np.array([4, 2, 2, 4, 0, 2, 4, 4], np.uint8)
+    table = made[4][0].table.clone()
+    for e in range(E):
+        if bits[e] == 2:
+            table[e] = made[2][0].table[e]
+    xq_o, sx_o = orc.quantize_act(syn.hidden(141, 1, H))
+    for rep, ids in enumerate(([[1, 0, 2, 3, 5, 6]], [[6, -1, 4, 1, 3, 2]], [[0, 3, 6, 7, -1, 4]])):
+        idx = np.array(ids, np.int32)
+        wts = np.abs(syn.normal(142, syn.stream_id(syn.K_MISC, 142, rep), (1, k))).astype(np.float32)
+        P = k + 1
+        dbg = dict(accg=torch.zeros((P, I), dtype=torch.int32, device="cuda"),
+                   accu=torch.zeros((P, I), dtype=torch.int32, device="cuda"),
+                   a=torch.zeros((P, I), dtype=torch.float32, device="cuda"),
+                   aq=torch.zeros((P, I), dtype=torch.int8, device="cuda"),
+                   sa=torch.zeros((P,), dtype=torch.float32, device="cuda"),
+                   accd=torch.zeros((P, H), dtype=torch.int32, device="cuda"))
+        y = torch.full((1, k + 1, H), 7.0, dtype=torch.float32, device="cuda")
+        out = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        sh = made[shared_bits][1].struct(0) if shared_bits else None
+        ctx.set_debug(dbg)
+        try:
+            moe.moe_expert_ffn_mixed(ctx, table, sh, shared_bits or 0, dev(bits), (4, 2), dev(xq_o), dev(sx_o),
+                                     dev(idx), H, I, E, y, topk_w=dev(wts), out=out)
+            ctx.check()
+        finally:
+            ctx.set_debug(None)
+        got = {n: host(t) for n, t in dbg.items()}
+        yg = host(y)
+        for j in range(k + 1):
+            if j == k:
+                if not shared_bits:
+                    assert np.all(yg[0, k] == 7.0)
+                    continue
+                ex = made[shared_bits][3]
+            else:
+                e = int(idx[0, j])
+                if e < 0 or bits[e] == 0:
+                    assert np.all(yg[0, j] == 7.0), (rep, j)
+                    continue
+                ex = made[int(bits[e])][2][e]
+            r = orc.expert_token(ex, xq_o[0], float(sx_o[0]))
+            assert np.array_equal(got["accg"][j], r["accg"]), (rep, j)
+            assert np.array_equal(got["accu"][j], r["accu"]), (rep, j)
+            assert np.array_equal(got["a"][j].view(np.uint32), r["a"].view(np.uint32)), (rep, j)
+            assert np.array_equal(got["aq"][j], r["aq"]), (rep, j)
+            assert got["sa"][j] == np.float32(r["sa"]), (rep, j)
+            assert np.array_equal(got["accd"][j], r["accd"]), (rep, j)
+            assert np.array_equal(yg[0, j].view(np.uint32), r["y"].view(np.uint32)), (rep, j)
+        ref = torch.empty_like(out)
+        moe.moe_combine(ctx, y, dev(wts), shared_bits is not None, ref)
+        assert np.array_equal(host(out).view(np.uint32), host(ref).view(np.uint32)), rep
+
+
 def test_ffn_mixed_last_width_without_work(moe, ctx, orc, syn):
     """One token, no shared expert, a combine: the width that runs last (int2)
     has none of the token's experts, so its down kernel only combines the
