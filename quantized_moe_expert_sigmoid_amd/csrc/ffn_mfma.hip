@@ -126,10 +126,6 @@ __device__ __forceinline__ v4i wfield(uint4 w) {
   }
 }
 
-__device__ __forceinline__ v4i as_v4i(uint4 v, bool keep) {
-  return keep ? v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w} : v4i{0, 0, 0, 0};
-}
-
 __device__ __forceinline__ v4i mfma(v4i x, v4i w, v4i acc) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(x, w, acc, 0, 0, 0);
 }
@@ -203,8 +199,9 @@ __global__ __launch_bounds__(kThreads) void act_field_kernel(const int8_t *xq, i
 // abase + ids[t] * astride) are staged in LDS once per workgroup: slices of
 // 512 bytes per token, double-buffered, loaded one slice ahead into registers
 // and written to LDS after the current slice is consumed, one barrier per
-// slice. In LDS the 16-byte unit u of token t sits at unit u ^ (t & 7) of the
-// token's row, so the 16 tokens a read instruction spans hit distinct banks.
+// slice. In LDS the 16-byte unit u of token t sits at unit u ^ (t & 15) of the
+// token's row (t & (units - 1) for rows of fewer than 16 units), so the 16
+// tokens a read instruction spans hit distinct banks.
 // The weight pieces stream through registers D steps ahead.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -216,9 +213,19 @@ __device__ __forceinline__ uint4 lds_ld16(const lds_u8 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// a wave-uniform pointer, held in scalar registers
+template <typename P>
+__device__ __forceinline__ P sgpr_p(P p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (P)(((uint64_t)hi << 32) | lo);
+}
+
 template <int BITS, int MB, int NM, int NB, int D0, int SL>
-__device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB], const int8_t *abase, int astride,
-                                             const int *ids, int rowbytes, lds_u8 *lds, v4i (&acc)[MB][NM][NB]) {
+__device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wbase)[NM], const uint32_t (&woff)[NB],
+                                             const int8_t *abase, int astride, const int *ids, int rowbytes,
+                                             lds_u8 *lds, v4i (&acc)[MB][NM][NB]) {
   constexpr int EPC = QFmt<BITS>::kEpc, NS = EPC / 16;
   constexpr int SC = SL / (4 * EPC);      // steps per slice
   constexpr int D = D0 < SC ? D0 : SC;    // weight steps in flight (a divisor of SC)
@@ -228,6 +235,7 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB
   constexpr int BUF = MB * 16 * SL;       // bytes per slice buffer
   static_assert(NI >= 1 && NI * TPI == MB * 16, "whole tokens per staging round");
   static_assert(SC % D == 0, "the weight buffers rotate within a slice");
+  constexpr int SW = UPT < 16 ? UPT - 1 : 15;  // the LDS swizzle: unit u of token t at u ^ (t & SW)
   const int tid = threadIdx.x, grp = (tid & (MOE_WAVE - 1)) >> 4, r16 = tid & 15;
   const int nq = rowbytes / 16;
   const int nch = (nq + 3) / 4;
@@ -240,25 +248,39 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB
   for (int i = 0; i < NI; ++i) {
     const int t = tid / UPT + TPI * i;
     srow[i] = abase + (int64_t)ids[t] * astride;
-    sdst[i] = t * SL + ((su ^ (t & 7)) << 4);
+    sdst[i] = t * SL + ((su ^ (t & SW)) << 4);
   }
+  // A staged unit whose piece lies past the row end (the last chunk's, or any
+  // past the last chunk) is stored as zeros, so the weight pieces loaded for it
+  // (clamped re-reads of the row's last piece) add nothing.
   uint4 st[NI];
+  bool sv = true;      // the unit this thread stages in the slice in flight lies in the row
+  bool sfull = true;   // every unit of that slice does (uniform)
+  const int fullb = (nq / 4) * 4 * EPC;  // bytes of the row's complete chunks
   auto aload = [&](int sl) {
-    const int o = min(sl * SL + su * 16, astride - 16);  // past the row: a re-read, never used
+    const int o = sl * SL + su * 16;
+    sv = (o / (4 * EPC)) * 4 + ((o >> 4) & 3) < nq;
+    sfull = (sl + 1) * SL <= fullb;
+    const int oc = min(o, astride - 16);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) st[i] = ldg16(srow[i] + o, 0);
+    for (int i = 0; i < NI; ++i) st[i] = ldg16(srow[i] + oc, 0);
   };
   auto astore = [&](int b) {
+    if (sfull) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) lds_st16(lds + b * BUF + sdst[i], st[i]);
+      for (int i = 0; i < NI; ++i) lds_st16(lds + b * BUF + sdst[i], st[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) lds_st16(lds + b * BUF + sdst[i], sv ? st[i] : make_uint4(0u, 0u, 0u, 0u));
+    }
   };
   uint4 wv[D][NM][NB];
   auto bload = [&](int c, int b) {
-    const int qc = min(c * 4 + grp, nq - 1);
+    const uint32_t qo = (uint32_t)min(c * 4 + grp, nq - 1) << 4;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) wv[b][m][nb] = ldg16(wrow[m][nb] + qc * 16, 0);
+      for (int nb = 0; nb < NB; ++nb) wv[b][m][nb] = ldg16(wbase[m] + (woff[nb] + qo), 0);
     __builtin_amdgcn_sched_barrier(0);  // issue here, D steps ahead of the use
   };
 #pragma unroll
@@ -272,14 +294,14 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wrow)[NM][NB
 #pragma unroll
     for (int cc = 0; cc < SC; ++cc) {
       const int c = sl * SC + cc, b = cc % D;
-      const bool kv = c * 4 + grp < nq;  // pieces past the row end multiply zeros
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         v4i x[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int t = mb * 16 + r16, u = cc * NS * 4 + s * 4 + grp;
-          x[mb] = as_v4i(lds_ld16(cur + t * SL + ((u ^ (t & 7)) << 4)), kv);
+          const uint4 v = lds_ld16(cur + t * SL + ((u ^ (t & SW)) << 4));
+          x[mb] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m)
@@ -347,14 +369,14 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   const int nt = stage_tokens<MB>(a, ex, m0, false, OFF, tt_s);
   const int rowbytes = a.H * BITS / 8;
   int row[NB];
-  const uint8_t *wrow[2][NB];
+  const uint8_t *const wbase[2] = {sgpr_p(ex.w.gate), sgpr_p(ex.w.up)};
+  uint32_t woff[NB];
   float sg[NB], su[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     row[nb] = ntile * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
     const int rc = min(row[nb], a.I - 1);  // rows past I: re-read, not stored
-    wrow[0][nb] = ex.w.gate + (int64_t)rc * rowbytes;
-    wrow[1][nb] = ex.w.up + (int64_t)rc * rowbytes;
+    woff[nb] = (uint32_t)rc * (uint32_t)rowbytes;
     // global-space loads: a pending flat load would make every wait in the
     // K loop below a wait for all loads
     sg[nb] = gptr(ex.w.s_gate)[rc];
@@ -366,7 +388,7 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = acc[mb][1][nb] = v4i{0, 0, 0, 0};
-  tile_mma_lds<BITS, MB, 2, NB, D, SL>(wrow, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
+  tile_mma_lds<BITS, MB, 2, NB, D, SL>(wbase, woff, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
   // lane holds tokens 4*grp + r of each block, row row[nb]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -549,13 +571,14 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   const int nt = stage_tokens<MB>(a, ex, m0, true, OFF, tt_s);
   const int rowbytes = a.I * BITS / 8;
   int row[NB];
-  const uint8_t *wrow[1][NB];
+  const uint8_t *const wbase[1] = {sgpr_p(ex.w.down)};
+  uint32_t woff[NB];
   float sd[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     row[nb] = ntile * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
     const int rc = min(row[nb], a.H - 1);
-    wrow[0][nb] = ex.w.down + (int64_t)rc * rowbytes;
+    woff[nb] = (uint32_t)rc * (uint32_t)rowbytes;
     sd[nb] = gptr(ex.w.s_down)[rc];
   }
   __syncthreads();
@@ -564,7 +587,7 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = v4i{0, 0, 0, 0};
-  tile_mma_lds<BITS, MB, 1, NB, D, SL>(wrow, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
+  tile_mma_lds<BITS, MB, 1, NB, D, SL>(wbase, woff, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
