@@ -133,10 +133,11 @@ def stack_pool_bench(args) -> None:
     block, loaded on misses under pressure), with a slab smaller than their
     total, refilled over PCIe on misses. One token per step; each layer's
     routing comes from a correlated Zipf trace (a slot keeps the previous
-    token's expert with probability 0.6). Per layer: quantise the token,
-    prepare the pool (misses refill on the copy stream), the expert FFN of
-    every width in one call (or one call per width), the combine. Prints
-    one JSON line."""
+    token's expert with probability 0.6). Per layer: prepare the pool
+    (misses refill on the copy stream), then one call that quantises the
+    token, runs the expert FFN of every width and the combine (or, with
+    --stack-per-width, the quantisation, one call per width and the
+    combine). Prints one JSON line."""
     import torch
     import quantized_moe_expert_sigmoid_amd as moe
     from synth import workloads as wl
@@ -249,7 +250,9 @@ def stack_pool_bench(args) -> None:
         for t in range(t0_, t1_):
             for layer in range(Lr):
                 idx_p = tr_dev_p[layer] + t * rowb
-                ck(lib_.moe_quantize_act_i8(ctx_h, xs_p[(t + layer) % 16], 1, H, xq_p, sx_p))
+                x_p = xs_p[(t + layer) % 16]
+                if args.stack_per_width:
+                    ck(lib_.moe_quantize_act_i8(ctx_h, x_p, 1, H, xq_p, sx_p))
                 ck(lib_.moe_pool_prepare(pool_h, layer, tr_host_p[layer] + t * rowb, 1, k, tab_p[layer],
                                          wid_p[layer], ctypes.byref(nmiss)))
                 if args.stack_prefetch:
@@ -262,9 +265,9 @@ def stack_pool_bench(args) -> None:
                     ck(lib_.moe_pool_call_widths(pool_h, ctypes.byref(cw)))
                     m = cw.value | (1 << 4)
                 if not args.stack_per_width:
-                    # with the combine in the same call
-                    ck(lib_.moe_expert_ffn_mixed(ctx_h, tab_p[layer], sh_ref[layer], 4, wid_p[layer], m, xq_p,
-                                                 sx_p, idx_p, wts_p, 1, H, I, E, k, y_p, out_p))
+                    # the token's hidden state in, quantised inside the FFN call, the combine in it too
+                    ck(lib_.moe_expert_ffn_mixed_x(ctx_h, tab_p[layer], sh_ref[layer], 4, wid_p[layer], m, x_p,
+                                                   idx_p, wts_p, 1, H, I, E, k, y_p, out_p))
                     continue
                 else:
                     if m & (1 << 8):
@@ -365,7 +368,8 @@ def stack_pool_bench(args) -> None:
                                                      / max(1, hits + misses), 5),
                   "h2d_bytes_saved": ts1["bytes_saved"] - ts0["bytes_saved"]},
         # the layers' expert tables: host-to-device copies made and skipped (unchanged)
-        "ffn_calls": ("one per width" if args.stack_per_width else "one mixed-width call per layer")
+        "ffn_calls": ("one per width" if args.stack_per_width
+                      else "one mixed-width call per layer from the fp32 hidden state")
         + ("" if args.stack_all_widths else ", widths of the token's experts only"),
         "table_copies": {"tables": "caller" if args.stack_caller_tables else "pool",
                          "made": tb1["copies"] - tb0["copies"], "skipped": tb1["skipped"] - tb0["skipped"]},

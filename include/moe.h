@@ -245,6 +245,19 @@ moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *experts, const
                                 int shared_bits, const uint8_t *expert_bits, int widths_mask, const int8_t *xq,
                                 const float *sx, const int32_t *topk_idx, const float *topk_w, int T, int H, int I,
                                 int E, int k, float *y_slots, float *out);
+/* The same call on fp32 hidden states x (DEVICE fp32 [T][H], 16-byte
+ * aligned) instead of their codes: the activation rule of
+ * moe_quantize_act_i8 ([P-feat]: int8 activations) is applied inside -- for
+ * one token on the single-token kernels, by every gate/up workgroup on its
+ * own copy of the row, so the call launches no quantisation kernel; for more
+ * tokens by the quantisation kernel into the context's io scratch. y_slots
+ * and out are bit-identical to moe_quantize_act_i8 followed by
+ * moe_expert_ffn_mixed. The codes are not returned. Other arguments and
+ * errors as for moe_expert_ffn_mixed. */
+moe_status moe_expert_ffn_mixed_x(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                                  int shared_bits, const uint8_t *expert_bits, int widths_mask, const float *x,
+                                  const int32_t *topk_idx, const float *topk_w, int T, int H, int I, int E, int k,
+                                  float *y_slots, float *out);
 
 /* ---------------------------------------------------------------------- */
 /* Combine ([P-moe], [P-mem])                                             */

@@ -101,6 +101,8 @@ _SIGS = {
     "moe_pool_resident_bits": (_i32, [_vp, _i32, _i32]),
     "moe_expert_ffn_mixed": (_i32, [_vp, _vp, ctypes.POINTER(ExpertW), _i32, _vp, _i32, _vp, _vp, _vp, _vp]
                              + [_i32] * 5 + [_vp, _vp]),
+    "moe_expert_ffn_mixed_x": (_i32, [_vp, _vp, ctypes.POINTER(ExpertW), _i32, _vp, _i32, _vp, _vp, _vp]
+                               + [_i32] * 5 + [_vp, _vp]),
     "moe_pool_call_widths": (_i32, [_vp, ctypes.POINTER(_i32)]),
     "moe_pool_table_stats": (_i32, [_vp] + [ctypes.POINTER(ctypes.c_uint64)] * 2),
     "moe_pool_layer_table": (_i32, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
@@ -312,18 +314,34 @@ def moe_expert_ffn_q2(ctx, table, shared, expert_bits, xq, sx, topk_idx, H, I, E
 FFN_BY_BITS = {4: moe_expert_ffn_q4, 8: moe_expert_ffn_q8, 2: moe_expert_ffn_q2}
 
 
+def _widths_mask(widths):
+    if isinstance(widths, int):
+        return widths
+    mask = 0
+    for b in widths:
+        mask |= 1 << int(b)
+    return mask
+
+
 def moe_expert_ffn_mixed(ctx, table, shared, shared_bits, expert_bits, widths, xq, sx, topk_idx, H, I, E, y_slots,
-                         topk_w=None, out=None):
+                         topk_w=None, out=None, x=None):
     """Every slot at its expert's width (expert_bits, device uint8 [E]);
     widths: the widths the layer has (iterable of 8, 4, 2), or the mask
     itself (an int, as moe_pool_call_widths gives it). With out (and
     topk_w): also the combine of the slots. table and expert_bits may be raw
-    device addresses (a pool's own table, MoePool.layer_table)."""
+    device addresses (a pool's own table, MoePool.layer_table). With x (fp32
+    hidden states [T][H]) in place of xq and sx (both None): the call
+    quantises them itself (moe_expert_ffn_mixed_x)."""
     T, k = topk_idx.shape
     if not isinstance(table, int):
         _dev(table, torch.int64, "experts table", (E, 6))
-    _dev(xq, torch.int8, "xq", (T, H))
-    _dev(sx, torch.float32, "sx", (T,))
+    if x is not None:
+        if xq is not None or sx is not None:
+            raise ValueError("pass either x or (xq, sx)")
+        _dev(x, torch.float32, "x", (T, H))
+    else:
+        _dev(xq, torch.int8, "xq", (T, H))
+        _dev(sx, torch.float32, "sx", (T,))
     _dev(topk_idx, torch.int32, "topk_idx")
     _dev(y_slots, torch.float32, "y_slots", (T, k + 1, H))
     if not isinstance(expert_bits, int):
@@ -331,18 +349,18 @@ def moe_expert_ffn_mixed(ctx, table, shared, shared_bits, expert_bits, widths, x
     if out is not None:
         _dev(out, torch.float32, "out", (T, H))
         _dev(topk_w, torch.float32, "topk_w", (T, k))
-    if isinstance(widths, int):
-        mask = widths
-    else:
-        mask = 0
-        for b in widths:
-            mask |= 1 << int(b)
+    mask = _widths_mask(widths)
     sh = ctypes.byref(shared) if shared is not None else None
     tp = table if isinstance(table, int) else table.data_ptr()
     bp = expert_bits if isinstance(expert_bits, int) else expert_bits.data_ptr()
-    _ck(lib().moe_expert_ffn_mixed(ctx.handle, tp, sh, int(shared_bits), bp, mask,
-                                   xq.data_ptr(), sx.data_ptr(), topk_idx.data_ptr(), _ptr(topk_w), T, H, I, E, k,
-                                   y_slots.data_ptr(), _ptr(out)))
+    if x is not None:
+        _ck(lib().moe_expert_ffn_mixed_x(ctx.handle, tp, sh, int(shared_bits), bp, mask, x.data_ptr(),
+                                         topk_idx.data_ptr(), _ptr(topk_w), T, H, I, E, k, y_slots.data_ptr(),
+                                         _ptr(out)))
+    else:
+        _ck(lib().moe_expert_ffn_mixed(ctx.handle, tp, sh, int(shared_bits), bp, mask,
+                                       xq.data_ptr(), sx.data_ptr(), topk_idx.data_ptr(), _ptr(topk_w), T, H, I, E, k,
+                                       y_slots.data_ptr(), _ptr(out)))
     return y_slots
 
 

@@ -386,13 +386,17 @@ static moe_status ffn_entry(const char *fn, int bits, moe_ctx *ctx, const moe_ex
   return launch_expert_ffn(ctx, bits, experts, shared, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots);
 }
 
-extern "C" moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
-                                           int shared_bits, const uint8_t *expert_bits, int widths_mask,
-                                           const int8_t *xq, const float *sx, const int32_t *topk_idx,
-                                           const float *topk_w, int T, int H, int I, int E, int k, float *y_slots,
-                                           float *out) {
-  const char *fn = "moe_expert_ffn_mixed";
-  moe_status st = ffn_check(fn, ctx, experts, shared, xq, sx, topk_idx, T, H, I, E, k, y_slots);
+// The mixed-width call on codes (xq, sx) or, with xf, on fp32 hidden states:
+// a single token on the single-token kernels quantises inside its gate/up
+// kernel; otherwise the rows are quantised into the context's io scratch first.
+static moe_status ffn_mixed(const char *fn, moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                            int shared_bits, const uint8_t *expert_bits, int widths_mask, const int8_t *xq,
+                            const float *sx, const float *xf, const int32_t *topk_idx, const float *topk_w, int T,
+                            int H, int I, int E, int k, float *y_slots, float *out) {
+  // ffn_check wants codes; with xf it checks xf in their place
+  const void *xin = xf ? (const void *)xf : (const void *)xq;
+  moe_status st = ffn_check(fn, ctx, experts, shared, static_cast<const int8_t *>(xin), xf ? xf : sx, topk_idx, T, H,
+                            I, E, k, y_slots);
   if (st) return st;
   const int all = (1 << 8) | (1 << 4) | (1 << 2);
   REQUIRE(widths_mask != 0 && (widths_mask & ~all) == 0, "%s: widths_mask 0x%x (bits 8, 4 and 2 only)", fn,
@@ -411,14 +415,41 @@ extern "C" moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *exp
     t1 = t1 && decode_t1_supported(b, H, I, k, sh ? 1 : 0, ctx->n_cu);
   }
   if (t1)
-    return launch_ffn_t1_mixed(ctx, widths, n, shared_bits, experts, shared, expert_bits, xq, sx, topk_idx, topk_w, H,
-                               I, E, k, y_slots, out);
+    return launch_ffn_t1_mixed(ctx, widths, n, shared_bits, experts, shared, expert_bits, xq, sx, xf, topk_idx,
+                               topk_w, H, I, E, k, y_slots, out);
+  if (xf) {  // codes of every row first, into the io scratch (the FFN launchers use the other scratch)
+    void *io = nullptr;
+    const size_t xq_bytes = moe_round_up((size_t)T * H, 256);
+    if ((st = moe_io_scratch(ctx, xq_bytes + 4 * (size_t)T, &io))) return st;
+    int8_t *xq_io = static_cast<int8_t *>(io);
+    float *sx_io = reinterpret_cast<float *>(static_cast<char *>(io) + xq_bytes);
+    if ((st = launch_quantize_act(ctx, xf, T, H, xq_io, sx_io))) return st;
+    xq = xq_io;
+    sx = sx_io;
+  }
   for (int w = 0; w < n; ++w) {
     const moe_expert_w *sh = (shared && widths[w] == shared_bits) ? shared : nullptr;
     if ((st = launch_expert_ffn(ctx, widths[w], experts, sh, expert_bits, xq, sx, topk_idx, T, H, I, E, k, y_slots)))
       return st;
   }
   return out ? launch_combine(ctx, y_slots, topk_w, T, k, H, shared ? 1 : 0, out) : MOE_OK;
+}
+
+extern "C" moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                                           int shared_bits, const uint8_t *expert_bits, int widths_mask,
+                                           const int8_t *xq, const float *sx, const int32_t *topk_idx,
+                                           const float *topk_w, int T, int H, int I, int E, int k, float *y_slots,
+                                           float *out) {
+  return ffn_mixed("moe_expert_ffn_mixed", ctx, experts, shared, shared_bits, expert_bits, widths_mask, xq, sx,
+                   nullptr, topk_idx, topk_w, T, H, I, E, k, y_slots, out);
+}
+
+extern "C" moe_status moe_expert_ffn_mixed_x(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
+                                             int shared_bits, const uint8_t *expert_bits, int widths_mask,
+                                             const float *x, const int32_t *topk_idx, const float *topk_w, int T,
+                                             int H, int I, int E, int k, float *y_slots, float *out) {
+  return ffn_mixed("moe_expert_ffn_mixed_x", ctx, experts, shared, shared_bits, expert_bits, widths_mask, nullptr,
+                   nullptr, x, topk_idx, topk_w, T, H, I, E, k, y_slots, out);
 }
 
 extern "C" moe_status moe_expert_ffn_q4(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,

@@ -194,6 +194,7 @@ struct GateUpT1Args {
   // FFN
   const int8_t *xq;  // [H]
   const float *sx;   // [1]
+  const float *xf;   // [H] fp32 hidden state, quantised in the kernel (template flag QX) instead of xq / sx
   int H, I, S;
   float *A;  // [S][I]
   moe_debug_bufs dbg;
@@ -309,9 +310,10 @@ __device__ __forceinline__ void gu_compute(int n, int lane0, int lane, const GuB
 // mixed-width kernel this width's part of it. has_sh: this part computes the
 // shared expert; want_bits: the width whose slots it computes (given
 // routing); write_table: it writes the global slot table and the error flag.
-template <int BITS, int JG, int NB, bool GIVEN>
+template <int BITS, int JG, int NB, bool GIVEN, bool QX = false>
 __device__ __forceinline__ void gateup_t1_body(const GateUpT1Args &a, int vb, int vn, int has_sh, int want_bits,
                                                bool write_table) {
+  static_assert(GIVEN || !QX, "in-kernel quantisation is for given routing");
   static_assert(NB == 1, "routed pairs are taken one at a time");
   constexpr int OFF = QFmt<BITS>::kOff;
   __shared__ float key_s[kMaxE], sig_s[kMaxE];
@@ -365,13 +367,27 @@ __device__ __forceinline__ void gateup_t1_body(const GateUpT1Args &a, int vb, in
       exr[i] = ldg16(a.experts, min(tid + i * kFfnThreads, 3 * a.E - 1));
   constexpr int EPC = QFmt<BITS>::kEpc;
   uint4 xraw[JG][EPC / 16];
+  // QX: the token's fp32 row, this thread's float4s of it (H <= 8192)
+  constexpr int kQx = QX ? kMaxX4 * kThreads / kFfnThreads : 1;
+  __shared__ __align__(16) uint32_t xq_s[QX ? kMaxX4 * kThreads : 4];  // QX: the token's codes
+  __shared__ float qred_s[kFfnWaves];
+  float4 xv[kQx];
+  float sxv = 0.0f;
+  if constexpr (QX) {
 #pragma unroll
-  for (int j = 0; j < JG; ++j) {
-    const int c = min(lane + j * MOE_WAVE, cpr - 1);
+    for (int q = 0; q < kQx; ++q) {
+      const int d = tid + q * kFfnThreads;
+      xv[q] = (d < a.H / 4) ? reinterpret_cast<const float4 *>(a.xf)[d] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
 #pragma unroll
-    for (int u = 0; u < EPC / 16; ++u) xraw[j][u] = ldg16(a.xq + (int64_t)c * EPC, u);
+    for (int j = 0; j < JG; ++j) {
+      const int c = min(lane + j * MOE_WAVE, cpr - 1);
+#pragma unroll
+      for (int u = 0; u < EPC / 16; ++u) xraw[j][u] = ldg16(a.xq + (int64_t)c * EPC, u);
+    }
+    sxv = a.sx[0];
   }
-  const float sxv = a.sx[0];
   asm volatile("" ::: "memory");
 
   // ---- the shared expert's rows: known before routing, so they stream while
@@ -379,18 +395,67 @@ __device__ __forceinline__ void gateup_t1_body(const GateUpT1Args &a, int vb, in
   // expert a dummy in-bounds row of xq is read and dropped) ----
   GuBatch<BITS, JG, NB> b0, b1;
   {
-    const uint8_t *sg_p = has_sh ? a.shared.gate : reinterpret_cast<const uint8_t *>(a.xq);
-    const uint8_t *su_p = has_sh ? a.shared.up : reinterpret_cast<const uint8_t *>(a.xq);
+    // the dummy row: the token's codes (H bytes), or with QX its fp32 row (4 H
+    // bytes; xq and sx are not passed then); a packed row is at most H bytes
+    const uint8_t *dummy = QX ? reinterpret_cast<const uint8_t *>(a.xf) : reinterpret_cast<const uint8_t *>(a.xq);
+    const uint8_t *sg_p = has_sh ? a.shared.gate : dummy;
+    const uint8_t *su_p = has_sh ? a.shared.up : dummy;
     gu_load_shared<BITS, JG, NB>(sg_p, su_p, has_sh ? sh0 : 0, ns, lane, rowbytes, cpr, b0);
   }
   float sg_sh, su_sh;
   {
     const bool use = has_sh != 0;
     const int li = use ? sh0 + min(lane, max(ns - 1, 0)) : 0;
-    sg_sh = gptr(use ? a.shared.s_gate : a.sx)[li];
-    su_sh = gptr(use ? a.shared.s_up : a.sx)[li];
+    const float *dummy_s = QX ? a.xf : a.sx;  // element 0 only
+    sg_sh = gptr(use ? a.shared.s_gate : dummy_s)[li];
+    su_sh = gptr(use ? a.shared.s_up : dummy_s)[li];
   }
   asm volatile("" ::: "memory");
+
+  // QX: the activation rule on the row (the same arithmetic as the
+  // quantisation kernel): sx = max|x| / 127, codes rint(x / sx) clamped to
+  // [-127, 127] (all zero for an all-zero row), into LDS, then this lane's
+  // chunks from there
+  if constexpr (QX) {
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kQx; ++q)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(xv[q].x), fabsf(xv[q].y)), fmaxf(fabsf(xv[q].z), fabsf(xv[q].w))));
+    m = wave_max_all(m);
+    if (lane == 0) qred_s[wave] = m;
+    __syncthreads();
+    m = qred_s[0];
+#pragma unroll
+    for (int w = 1; w < kFfnWaves; ++w) m = fmaxf(m, qred_s[w]);
+    sxv = (m == 0.0f) ? 0.0f : m / 127.0f;
+#pragma unroll
+    for (int q = 0; q < kQx; ++q) {
+      const int d = tid + q * kFfnThreads;
+      const float vv[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int qq = 0;
+        if (m != 0.0f) {
+          float r = __builtin_rintf(vv[j] / sxv);
+          r = fminf(fmaxf(r, -127.0f), 127.0f);
+          qq = (int)r;
+        }
+        word |= (uint32_t)(uint8_t)(int8_t)qq << (8 * j);
+      }
+      if (d < a.H / 4) xq_s[d] = word;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < JG; ++j) {
+      const int c = min(lane + j * MOE_WAVE, cpr - 1);
+#pragma unroll
+      for (int u = 0; u < EPC / 16; ++u) {
+        const uint32_t *src = xq_s + (c * EPC + u * 16) / 4;
+        xraw[j][u] = make_uint4(src[0], src[1], src[2], src[3]);
+      }
+    }
+  }
 
   // ---- now consume: the expert table to LDS, the activations in field
   // order, the routing keys ----
@@ -660,9 +725,9 @@ __device__ __forceinline__ void gateup_t1_body(const GateUpT1Args &a, int vb, in
   }
 }
 
-template <int BITS, int JG, int NB, bool GIVEN>
+template <int BITS, int JG, int NB, bool GIVEN, bool QX = false>
 __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) {
-  gateup_t1_body<BITS, JG, NB, GIVEN>(a, blockIdx.x, gridDim.x, a.has_shared, a.want_bits, blockIdx.x == 0);
+  gateup_t1_body<BITS, JG, NB, GIVEN, QX>(a, blockIdx.x, gridDim.x, a.has_shared, a.want_bits, blockIdx.x == 0);
 }
 
 // One token, every width of a mixed layer in one launch (routing given).
@@ -674,6 +739,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_t1_kernel(GateUpT1Args a) 
 // with its width in pad[1], or expert -1 (no expert, a width outside the
 // call's mask, a repeated id) with valid pointers for the down kernel's
 // unconditional loads; it also raises the error flag for bad ids.
+template <bool QX>
 __global__ __launch_bounds__(kFfnThreads) void gateup_mixed_t1_kernel(GateUpT1Args a, int mask, int shared_bits) {
   const int lane = threadIdx.x & (MOE_WAVE - 1);
   const int wave = threadIdx.x >> 6;
@@ -765,11 +831,11 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_mixed_t1_kernel(GateUpT1Ar
   cnt[big] += rest - given_out;
   const int vb0 = blockIdx.x;
   if (vb0 < cnt[0]) {
-    gateup_t1_body<8, T1Shape<8>::JG, 1, true>(a, vb0, cnt[0], sbits == 8, 8, false);
+    gateup_t1_body<8, T1Shape<8>::JG, 1, true, QX>(a, vb0, cnt[0], sbits == 8, 8, false);
   } else if (vb0 < cnt[0] + cnt[1]) {
-    gateup_t1_body<4, T1Shape<4>::JG, 1, true>(a, vb0 - cnt[0], cnt[1], sbits == 4, 4, false);
+    gateup_t1_body<4, T1Shape<4>::JG, 1, true, QX>(a, vb0 - cnt[0], cnt[1], sbits == 4, 4, false);
   } else if (vb0 < cnt[0] + cnt[1] + cnt[2]) {
-    gateup_t1_body<2, T1Shape<2>::JG, 1, true>(a, vb0 - cnt[0] - cnt[1], cnt[2], sbits == 2, 2, false);
+    gateup_t1_body<2, T1Shape<2>::JG, 1, true, QX>(a, vb0 - cnt[0] - cnt[1], cnt[2], sbits == 2, 2, false);
   }
 }
 
@@ -1336,7 +1402,12 @@ __global__ __launch_bounds__(kFfnThreads) void down_mixed_t1_kernel(DownT1Args a
 // ---------------------------------------------------------------------------
 template <int BITS, int JG, int NB, bool GIVEN = false>
 moe_status launch_gu(moe_ctx *ctx, hipStream_t stream, const GateUpT1Args &g, int nwg) {
-  moe_launch_on(ctx, stream, MOE_STAGE_GATEUP, gateup_t1_kernel<BITS, JG, NB, GIVEN>, dim3(nwg), dim3(kFfnThreads), g);
+  if (GIVEN && g.xf)
+    moe_launch_on(ctx, stream, MOE_STAGE_GATEUP, gateup_t1_kernel<BITS, JG, NB, GIVEN, GIVEN>, dim3(nwg),
+                  dim3(kFfnThreads), g);
+  else
+    moe_launch_on(ctx, stream, MOE_STAGE_GATEUP, gateup_t1_kernel<BITS, JG, NB, GIVEN>, dim3(nwg), dim3(kFfnThreads),
+                  g);
   MOE_CHECK_LAUNCH("gateup_t1_kernel");
   return MOE_OK;
 }
@@ -1525,7 +1596,7 @@ size_t t1_chain_bytes(int I, int S) {
 moe_status t1_chain(moe_ctx *ctx, hipStream_t stream, char *base, int bits, const moe_expert_w *experts,
                     const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
                     const int32_t *topk_idx, int H, int I, int E, int k, float *y_slots, const float *topk_w = nullptr,
-                    float *out = nullptr) {
+                    float *out = nullptr, const float *xf = nullptr) {
   const int S = k + (shared ? 1 : 0);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -1545,6 +1616,7 @@ moe_status t1_chain(moe_ctx *ctx, hipStream_t stream, char *base, int bits, cons
   g.slots = slots;
   g.xq = xq;
   g.sx = sx;
+  g.xf = xf;
   g.H = H; g.I = I; g.S = S;
   g.A = reinterpret_cast<float *>(base + o_A);
   g.dbg = ctx->dbg;
@@ -1627,8 +1699,8 @@ namespace {
 // down projection of every slot at its width with the combine (when out).
 moe_status t1_mixed_chain(moe_ctx *ctx, char *base, int mask, int shared_bits, const moe_expert_w *experts,
                           const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
-                          const int32_t *topk_idx, const float *topk_w, int H, int I, int E, int k, float *y_slots,
-                          float *out) {
+                          const float *xf, const int32_t *topk_idx, const float *topk_w, int H, int I, int E, int k,
+                          float *y_slots, float *out) {
   const int S = k + (shared ? 1 : 0);
   MoeLayout m;
   const size_t o_slots = m.take(sizeof(SlotEntry) * kMaxSlots), o_A = m.take(sizeof(float) * S * I),
@@ -1642,6 +1714,7 @@ moe_status t1_mixed_chain(moe_ctx *ctx, char *base, int mask, int shared_bits, c
   g.slots = slots;
   g.xq = xq;
   g.sx = sx;
+  g.xf = xf;
   g.H = H; g.I = I; g.S = S;
   g.A = reinterpret_cast<float *>(base + o_A);
   g.dbg = ctx->dbg;
@@ -1650,7 +1723,11 @@ moe_status t1_mixed_chain(moe_ctx *ctx, char *base, int mask, int shared_bits, c
   g.expert_bits = expert_bits;
   g.err = ctx->dev_small;
   const int nwg = ctx->n_cu;
-  moe_launch(ctx, MOE_STAGE_GATEUP, gateup_mixed_t1_kernel, dim3(nwg), dim3(kFfnThreads), g, mask, shared_bits);
+  if (xf)
+    moe_launch(ctx, MOE_STAGE_GATEUP, gateup_mixed_t1_kernel<true>, dim3(nwg), dim3(kFfnThreads), g, mask, shared_bits);
+  else
+    moe_launch(ctx, MOE_STAGE_GATEUP, gateup_mixed_t1_kernel<false>, dim3(nwg), dim3(kFfnThreads), g, mask,
+               shared_bits);
   MOE_CHECK_LAUNCH("gateup_mixed_t1_kernel");
   RequantT1Args q{};
   q.A = g.A;
@@ -1701,15 +1778,15 @@ static bool t1_mixed_chain_ok(const moe_ctx *ctx, int mask, int shared_bits, boo
 
 moe_status launch_ffn_t1_mixed(moe_ctx *ctx, const int *widths, int n_widths, int shared_bits,
                                const moe_expert_w *experts, const moe_expert_w *shared, const uint8_t *expert_bits,
-                               const int8_t *xq, const float *sx, const int32_t *topk_idx, const float *topk_w, int H,
-                               int I, int E, int k, float *y_slots, float *out) {
+                               const int8_t *xq, const float *sx, const float *xf, const int32_t *topk_idx,
+                               const float *topk_w, int H, int I, int E, int k, float *y_slots, float *out) {
   void *scr = nullptr;
   moe_status st = moe_scratch(ctx, t1_chain_bytes(I, k + (shared ? 1 : 0)), &scr);
   if (st) return st;
   int mask = 0;
   for (int w = 0; w < n_widths; ++w) mask |= 1 << widths[w];
   if (n_widths > 1 && t1_mixed_chain_ok(ctx, mask, shared_bits, shared != nullptr, I, k))
-    return t1_mixed_chain(ctx, static_cast<char *>(scr), mask, shared_bits, experts, shared, expert_bits, xq, sx,
+    return t1_mixed_chain(ctx, static_cast<char *>(scr), mask, shared_bits, experts, shared, expert_bits, xq, sx, xf,
                           topk_idx, topk_w, H, I, E, k, y_slots, out);
   const int last_bits = shared ? shared_bits : widths[n_widths - 1];
   int order[3], n = 0;
@@ -1719,7 +1796,7 @@ moe_status launch_ffn_t1_mixed(moe_ctx *ctx, const int *widths, int n_widths, in
   for (int w = 0; w < n; ++w) {
     const bool last = w == n - 1;
     st = t1_chain(ctx, ctx->stream, static_cast<char *>(scr), order[w], experts, last ? shared : nullptr,
-                  expert_bits, xq, sx, topk_idx, H, I, E, k, y_slots, last ? topk_w : nullptr, last ? out : nullptr);
+                  expert_bits, xq, sx, topk_idx, H, I, E, k, y_slots, last ? topk_w : nullptr, last ? out : nullptr, xf);
     if (st) return st;
   }
   return MOE_OK;

@@ -167,10 +167,12 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
 moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                          const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
                          int H, int I, int E, int k, float *y_slots);
+// xf (nullable): the token's fp32 row, quantised inside the gate/up kernels
+// (xq and sx are then unused)
 moe_status launch_ffn_t1_mixed(moe_ctx *ctx, const int *widths, int n_widths, int shared_bits,
                                const moe_expert_w *experts, const moe_expert_w *shared, const uint8_t *expert_bits,
-                               const int8_t *xq, const float *sx, const int32_t *topk_idx, const float *topk_w, int H,
-                               int I, int E, int k, float *y_slots, float *out);
+                               const int8_t *xq, const float *sx, const float *xf, const int32_t *topk_idx,
+                               const float *topk_w, int H, int I, int E, int k, float *y_slots, float *out);
 
 // ---------------------------------------------------------------------------
 // Device side

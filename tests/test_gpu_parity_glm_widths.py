@@ -132,3 +132,74 @@ def test_glm_shape_mixed_one_token(moe, orc):
             assert rel_row_err(og, oref).max() < 1e-3
     finally:
         ctx.close()
+
+
+def test_glm_shape_mixed_from_fp32(moe, orc):
+    """moe_expert_ffn_mixed_x (fp32 hidden states in, the activation rule
+    applied inside the call) against moe_quantize_act_i8 followed by
+    moe_expert_ffn_mixed, at the GLM expert shape: every slot and the
+    combined output bit-identical. Cases: one token with int4 and int2
+    experts (the one-chain mixed kernels quantising in gate/up), one token
+    whose experts are all int4 (the single-width chain), one token with int8,
+    int4 and int2 experts (one chain per width, each quantising), and three
+    tokens (the codes made first, then the multi-token path). The int4/int2
+    token's slots are also checked against the oracle."""
+    from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
+    from synth import workloads as wl
+    w = wl.Workload("glm_shape_e16", H=6144, I=2048, E=16, k=8, T=3, seed=13)
+    ctx = moe.MoeCtx(0)
+    try:
+        width = np.array([(4, 2, 8)[e % 3] if e < 12 else 4 for e in range(w.E)], np.uint8)
+        layers = {b: MoeLayer(ctx, w.H, w.I, w.E, w.k, bits=b) for b in (8, 4, 2)}
+        for e, g, u, d in wl.iter_experts(w, range(w.E)):
+            layers[int(width[e])].set_expert_fp32(e, g, u, d)
+        layers[4].set_shared_fp32(*wl.shared_fp32(w))
+        torch.cuda.synchronize()
+        sel = torch.from_numpy(width).cuda()[:, None]
+        table = torch.where(sel == 8, layers[8].experts.table,
+                            torch.where(sel == 4, layers[4].experts.table, layers[2].experts.table)).contiguous()
+        bits_d = torch.from_numpy(width).cuda()
+        shared = layers[4].shared.struct(0)
+        x_all = wl.hidden_fp32(w, 3)
+        cases = [
+            ("int4 + int2, one token", np.array([[0, 1, 3, 4, 6, 7, 9, 10]], np.int32), 1),
+            ("all int4, one token", np.array([[0, 3, 6, 9, 12, 13, 14, 15]], np.int32), 1),
+            ("int8 + int4 + int2, one token", np.array([[0, 1, 2, 3, 4, 5, 6, 7]], np.int32), 1),
+            ("three tokens", np.array([[0, 1, 3, 4, 6, 7, 9, 10], [2, 5, 8, 11, 12, 13, 14, 15],
+                                       [15, 14, 13, 12, 1, 4, 7, 10]], np.int32), 3),
+        ]
+        rng = np.random.default_rng(17)
+        for name, idx, T in cases:
+            log(f"fp32-in mixed call: {name}")
+            x = torch.from_numpy(np.ascontiguousarray(x_all[:T])).cuda()
+            idx_d = torch.from_numpy(idx).cuda()
+            wts = torch.from_numpy(rng.random((T, w.k)).astype(np.float32)).cuda()
+            mask = 0
+            for e in idx.ravel():
+                mask |= 1 << int(width[e])
+            xq = torch.empty((T, w.H), dtype=torch.int8, device="cuda")
+            sx = torch.empty((T,), dtype=torch.float32, device="cuda")
+            moe.moe_quantize_act_i8(ctx, x, xq, sx)
+            y_q = torch.full((T, w.k + 1, w.H), 7.0, dtype=torch.float32, device="cuda")
+            o_q = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+            moe.moe_expert_ffn_mixed(ctx, table, shared, 4, bits_d, mask, xq, sx, idx_d, w.H, w.I, w.E, y_q,
+                                     topk_w=wts, out=o_q)
+            y_x = torch.full((T, w.k + 1, w.H), 7.0, dtype=torch.float32, device="cuda")
+            o_x = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+            moe.moe_expert_ffn_mixed(ctx, table, shared, 4, bits_d, mask, None, None, idx_d, w.H, w.I, w.E, y_x,
+                                     topk_w=wts, out=o_x, x=x)
+            ctx.check()
+            torch.cuda.synchronize()
+            assert np.array_equal(y_x.cpu().numpy().view(np.uint32), y_q.cpu().numpy().view(np.uint32)), name
+            assert np.array_equal(o_x.cpu().numpy().view(np.uint32), o_q.cpu().numpy().view(np.uint32)), name
+            if name.startswith("int4 + int2"):
+                xq_o, sx_o = orc.quantize_act(x_all[:1])
+                assert np.array_equal(xq.cpu().numpy(), xq_o)
+                yg = y_x.cpu().numpy()
+                for j in range(w.k):
+                    e = int(idx[0, j])
+                    ex = orc.pack_expert(int(width[e]), *wl.expert_fp32(w, e))
+                    r = orc.expert_token(ex, xq_o[0], float(sx_o[0]))["y"]
+                    assert np.array_equal(yg[0, j].view(np.uint32), r.view(np.uint32)), (j, e)
+    finally:
+        ctx.close()
