@@ -213,6 +213,23 @@ __device__ __forceinline__ uint4 lds_ld16(const lds_u8 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Weight pieces are loaded four lanes to a 64-byte piece group (lane l: row
+// l / 4 of the 16-row block, piece l % 4 of the step), so a load instruction
+// touches one cache line segment per four lanes, then regrouped across lanes
+// into the matrix-core operand layout (lane m: row m % 16, piece m / 16)
+// with four LDS-crossbar permutes per 16 bytes.
+#ifndef MOE_MFMA_WPERM
+#define MOE_MFMA_WPERM 1
+#endif
+constexpr bool kWPerm = MOE_MFMA_WPERM != 0;
+
+// the 16 bytes lane src holds, for every lane
+__device__ __forceinline__ uint4 lane_gather16(uint4 v, int src) {
+  const int a = src << 2;
+  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.x), (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.y),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.z), (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.w));
+}
+
 // a wave-uniform pointer, held in scalar registers
 template <typename P>
 __device__ __forceinline__ P sgpr_p(P p) {
@@ -275,8 +292,10 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wbase)[NM], 
     }
   };
   uint4 wv[D][NM][NB];
+  const int lpiece = kWPerm ? (tid & 3) : grp;  // the piece of the step this lane loads
+  const int gsrc = 4 * r16 + grp;               // kWPerm: the lane that loaded this lane's operand
   auto bload = [&](int c, int b) {
-    const uint32_t qo = (uint32_t)min(c * 4 + grp, nq - 1) << 4;
+    const uint32_t qo = (uint32_t)min(c * 4 + lpiece, nq - 1) << 4;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -294,6 +313,12 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wbase)[NM], 
 #pragma unroll
     for (int cc = 0; cc < SC; ++cc) {
       const int c = sl * SC + cc, b = cc % D;
+      if constexpr (kWPerm) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) wv[b][m][nb] = lane_gather16(wv[b][m][nb], gsrc);
+      }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         v4i x[MB];
@@ -376,7 +401,8 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int nb = 0; nb < NB; ++nb) {
     row[nb] = ntile * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
     const int rc = min(row[nb], a.I - 1);  // rows past I: re-read, not stored
-    woff[nb] = (uint32_t)rc * (uint32_t)rowbytes;
+    const int rl = min(kWPerm ? row[nb] - r16 + (lane >> 2) : row[nb], a.I - 1);  // the row this lane loads
+    woff[nb] = (uint32_t)rl * (uint32_t)rowbytes;
     // global-space loads: a pending flat load would make every wait in the
     // K loop below a wait for all loads
     sg[nb] = gptr(ex.w.s_gate)[rc];
@@ -578,7 +604,8 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int nb = 0; nb < NB; ++nb) {
     row[nb] = ntile * (64 * NB) + wave * (16 * NB) + nb * 16 + r16;
     const int rc = min(row[nb], a.H - 1);
-    woff[nb] = (uint32_t)rc * (uint32_t)rowbytes;
+    const int rl = min(kWPerm ? row[nb] - r16 + (lane >> 2) : row[nb], a.H - 1);  // the row this lane loads
+    woff[nb] = (uint32_t)rl * (uint32_t)rowbytes;
     sd[nb] = gptr(ex.w.s_down)[rc];
   }
   __syncthreads();
