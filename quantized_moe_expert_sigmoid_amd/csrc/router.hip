@@ -107,6 +107,81 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const float *__restric
   }
 }
 
+// --- logits, general T, on the fp32 matrix cores ----------------------------
+// The same 64x64 tile and K slice as router_gemm_kernel; each wave owns a
+// 32 x 32 quarter as 2 x 2 blocks of v_mfma_f32_16x16x4f32 (lane l holds
+// x[token l % 16][k0 + l / 16] and w[expert l % 16][k0 + l / 16] for a K step
+// of 4, and the results of tokens 4 (l / 16) .. +3 of expert l % 16). K
+// steps of kMfmaK floats go through LDS, stored k-major so a wave's operand
+// read is 16 consecutive words per K row. kl % kMfmaK == 0.
+constexpr int kMfmaK = 32;
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void router_gemm_mfma_kernel(const float *__restrict__ x,
+                                                               const float *__restrict__ wr, int T, int H, int E,
+                                                               int kl, float *__restrict__ partial) {
+  __shared__ float xs[kMfmaK][kTile + 4];
+  __shared__ float ws[kMfmaK][kTile + 4];
+  const int t0 = blockIdx.x * kTile;
+  const int e0 = blockIdx.y * kTile;
+  const int ks = blockIdx.z;
+  const int k0 = ks * kl;
+  const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wave = tid >> 6;
+  const int wt = (wave >> 1) * 32, we = (wave & 1) * 32;  // the wave's quarter of the tile
+  const int l16 = lane & 15, kq = lane >> 4;
+  // staging: thread tid moves 8 consecutive floats of row tid / 4 (x and w)
+  const int r = tid >> 2, c8 = (tid & 3) * 8;
+  const int t = t0 + r, e = e0 + r;
+  const float *xrow = x + (int64_t)min(t, T - 1) * H + k0 + c8;
+  const float *wrow = wr + (int64_t)min(e, E - 1) * H + k0 + c8;
+  v4f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  float4 xa, xb, wa, wb;
+  auto load = [&](int kk) {  // rows past T or E read a valid row; their products are never stored
+    xa = *reinterpret_cast<const float4 *>(xrow + kk);
+    xb = *reinterpret_cast<const float4 *>(xrow + kk + 4);
+    wa = *reinterpret_cast<const float4 *>(wrow + kk);
+    wb = *reinterpret_cast<const float4 *>(wrow + kk + 4);
+  };
+  load(0);
+  for (int kk = 0; kk < kl; kk += kMfmaK) {
+    __syncthreads();  // the previous step's reads are done
+    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      xs[c8 + q][r] = xv[q];
+      ws[c8 + q][r] = wv[q];
+    }
+    __syncthreads();
+    if (kk + kMfmaK < kl) load(kk + kMfmaK);  // the next step's loads fly under this step's products
+#pragma unroll
+    for (int k4 = 0; k4 < kMfmaK; k4 += 4) {
+      const int k = k4 + kq;
+      const float a0 = xs[k][wt + l16], a1 = xs[k][wt + 16 + l16];
+      const float b0 = ws[k][we + l16], b1 = ws[k][we + 16 + l16];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ee = e0 + we + j * 16 + l16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tt = t0 + wt + i * 16 + 4 * kq + q;
+        if (tt < T && ee < E) partial[((int64_t)ks * T + tt) * E + ee] = acc[i][j][q];
+      }
+    }
+}
+
 // --- top-k: one wave per token ---------------------------------------------
 // Each lane sums its experts' logit slices in slice order, forms sigmoid and
 // key (a NaN key ranks last, -0 becomes +0) into the wave's LDS rows; the
@@ -421,8 +496,15 @@ moe_status launch_router(moe_ctx *ctx, const moe_router_cfg *cfg, const float *x
     } else {
       {
         MoeTimer tm_(ctx, MOE_STAGE_ROUTER);
-        hipLaunchKernelGGL(router_gemm_kernel, dim3((T + kTile - 1) / kTile, (E + kTile - 1) / kTile, ks), dim3(256),
-                           0, ctx->stream, x, w_router, T, H, E, kl, part);
+        const dim3 grid((T + kTile - 1) / kTile, (E + kTile - 1) / kTile, ks);
+#ifndef MOE_ROUTER_MFMA
+#define MOE_ROUTER_MFMA 1
+#endif
+        if (MOE_ROUTER_MFMA && kl % kMfmaK == 0)
+          hipLaunchKernelGGL(router_gemm_mfma_kernel, grid, dim3(256), 0, ctx->stream, x, w_router, T, H, E, kl,
+                             part);
+        else
+          hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, ctx->stream, x, w_router, T, H, E, kl, part);
       }
     }
     MOE_CHECK_LAUNCH("router logits kernel");
