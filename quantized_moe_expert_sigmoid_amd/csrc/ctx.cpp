@@ -118,12 +118,12 @@ extern "C" moe_status moe_ctx_create(int device, void *hip_stream, moe_ctx **out
   c->device = device;
   c->stream = (hipStream_t)hip_stream;
   c->n_cu = prop.multiProcessorCount;
-  hipError_t e = hipMalloc(&c->dev_small, 4096);
+  hipError_t e = hipMalloc(&c->dev_small, kDevSmallBytes);
   if (e != hipSuccess) {
     delete c;
     return moe_hip_fail(e, "hipMalloc(ctx counters)");
   }
-  e = hipMemset(c->dev_small, 0, 4096);
+  e = hipMemset(c->dev_small, 0, kDevSmallBytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   // the side stream and its events exist from the start, so no later call
   // (the allocation-free one included) creates them

@@ -40,7 +40,7 @@ struct moe_ctx {
   char *fixed_io = nullptr, *fixed_scr = nullptr;
   size_t fixed_io_bytes = 0, fixed_scr_bytes = 0;
   // small persistent device block: error flags and counters
-  uint32_t *dev_small = nullptr;  // [0] error flags, [1..] counters
+  uint32_t *dev_small = nullptr;  // kDevSmallBytes: [0] error flags; from word kBucketChunkWord, per-chunk counts
   int ffn_kernels = MOE_FFN_AUTO;
   // a second stream for work that may overlap the context stream's, forked
   // from and joined back into it with events (created on first use)
@@ -137,6 +137,13 @@ moe_status launch_bucket_public(moe_ctx *ctx, const int32_t *topk_idx, int T, in
 moe_status launch_expert_ffn(moe_ctx *ctx, int bits, const moe_expert_w *experts, const moe_expert_w *shared,
                              const uint8_t *expert_bits, const int8_t *xq, const float *sx, const int32_t *topk_idx,
                              int T, int H, int I, int E, int k, float *y_slots);
+// The context's small device block (zeroed once, at creation): word 0 holds
+// the error flags; from word kBucketChunkWord, the per-chunk expert counts of
+// the chunked bucketing (at most kBucketChunks chunks of 1024 experts).
+constexpr int kBucketChunks = 64;
+constexpr int kBucketChunkWord = 1024;
+constexpr size_t kDevSmallBytes = 4 * ((size_t)kBucketChunkWord + (size_t)kBucketChunks * 1024);
+
 // Token tiles of the matrix-core expert FFN: up to kUnitM tokens of one
 // expert per tile; a remainder of at most kUnitSmall tokens is a one-block tile
 // (when experts average few tokens; otherwise every tile is full-size).

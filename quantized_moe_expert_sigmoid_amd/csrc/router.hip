@@ -11,6 +11,8 @@
 // sums are added in slice order (deterministic). Top-k runs one wave per
 // token: sigmoid via the library's fp32 exp, key = sigmoid + bias, k rounds
 // of a wave-wide (key desc, id asc) arg-max, weights = sigmoid / sum.
+#include <algorithm>
+
 #include "gemv_common.h"
 
 namespace {
@@ -299,47 +301,13 @@ __device__ __forceinline__ bool token_ids(const BucketArgs &a, int64_t t, int id
   return ok;
 }
 
-constexpr int kIdsCache = 4096;  // (token, slot) ids kept in LDS after the first read
-
-__global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
-  __shared__ int ids_s[kIdsCache];
-  __shared__ int cnt[1024];
-  __shared__ int off[1025];
-  __shared__ int cursor[1024];
-  __shared__ int tmp[kBThreads];
-  __shared__ uint32_t bitmap[kBitmapWords];
-  __shared__ int before[kBitmapWords];  // entries of the expert in earlier words of the chunk
+// Per-expert metadata from the counts, thread tid for expert tid < E (c: its
+// count, eb: its width): counts and offsets (also into off[0 .. E] in LDS),
+// the active list and the tiles of the matrix-core FFN. Every thread of the
+// workgroup takes part (block-wide scans).
+__device__ void bucket_meta(const BucketArgs &a, int c, int eb, int *tmp, int *off) {
   const int tid = threadIdx.x;
-  const int E = a.E, k = a.k, T = a.T;
-  // the width filter is read now, so its latency overlaps the counting
-  const int eb = (a.expert_bits && tid < E) ? a.expert_bits[tid] : 0;
-  // small calls keep the validated ids in LDS for the later passes
-  const bool cached = (int64_t)T * k <= kIdsCache;
-  auto ids_of = [&](int t, int (&ids)[16]) {
-    if (cached) {
-      for (int j = 0; j < k; ++j) ids[j] = ids_s[t * k + j];
-    } else {
-      token_ids(a, t, ids);
-    }
-  };
-
-  for (int e = tid; e < 1024; e += kBThreads) {
-    cnt[e] = 0;
-    cursor[e] = 0;
-  }
-  __syncthreads();
-  bool bad = false;
-  for (int t = tid; t < T; t += kBThreads) {
-    int ids[16];
-    bad |= !token_ids(a, t, ids);
-    for (int j = 0; j < k; ++j) {
-      if (ids[j] >= 0) atomicAdd(&cnt[ids[j]], 1);
-      if (cached) ids_s[t * k + j] = ids[j];
-    }
-  }
-  if (bad) atomicOr(a.err, (uint32_t)ERRF_BAD_INDEX);
-  __syncthreads();
-  const int c = tid < E ? cnt[tid] : 0;
+  const int E = a.E, T = a.T;
   const int ex = block_exclusive_scan(c, tmp);
   if (tid < E) {
     off[tid] = ex;
@@ -384,6 +352,50 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
       a.n_units[1] = nsmall;
     }
   }
+}
+
+constexpr int kIdsCache = 4096;  // (token, slot) ids kept in LDS after the first read
+
+__global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
+  __shared__ int ids_s[kIdsCache];
+  __shared__ int cnt[1024];
+  __shared__ int off[1025];
+  __shared__ int cursor[1024];
+  __shared__ int tmp[kBThreads];
+  __shared__ uint32_t bitmap[kBitmapWords];
+  __shared__ int before[kBitmapWords];  // entries of the expert in earlier words of the chunk
+  const int tid = threadIdx.x;
+  const int E = a.E, k = a.k, T = a.T;
+  // the width filter is read now, so its latency overlaps the counting
+  const int eb = (a.expert_bits && tid < E) ? a.expert_bits[tid] : 0;
+  // small calls keep the validated ids in LDS for the later passes
+  const bool cached = (int64_t)T * k <= kIdsCache;
+  auto ids_of = [&](int t, int (&ids)[16]) {
+    if (cached) {
+      for (int j = 0; j < k; ++j) ids[j] = ids_s[t * k + j];
+    } else {
+      token_ids(a, t, ids);
+    }
+  };
+
+  for (int e = tid; e < 1024; e += kBThreads) {
+    cnt[e] = 0;
+    cursor[e] = 0;
+  }
+  __syncthreads();
+  bool bad = false;
+  for (int t = tid; t < T; t += kBThreads) {
+    int ids[16];
+    bad |= !token_ids(a, t, ids);
+    for (int j = 0; j < k; ++j) {
+      if (ids[j] >= 0) atomicAdd(&cnt[ids[j]], 1);
+      if (cached) ids_s[t * k + j] = ids[j];
+    }
+  }
+  if (bad) atomicOr(a.err, (uint32_t)ERRF_BAD_INDEX);
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  bucket_meta(a, c, eb, tmp, off);
   if (T == 0) return;
 
   // stable placement, tokens in chunks of 32 W (one bit per token and expert
@@ -429,6 +441,100 @@ __global__ __launch_bounds__(kBThreads) void bucket_kernel(BucketArgs a) {
   }
 }
 
+// --- bucketing of many tokens: chunks of tokens, one workgroup each --------
+// Stage 1 counts each chunk's entries per expert (one bit per (expert, token)
+// in LDS) into the context's chunk-count table. Stage 2, on the same chunks,
+// gives every expert its offset from all chunks' counts and each chunk its
+// first rank per expert from the chunks before it, then places the chunk's
+// entries by the same bits: every list ends in token order, exactly as the
+// one-workgroup kernel leaves it. Workgroup 0 of stage 2 also writes the
+// per-expert metadata (bucket_meta).
+struct ChunkGeom {
+  int C, TC, W;  // chunks, tokens per chunk (a multiple of 32), bitmap words per expert
+};
+inline ChunkGeom chunk_geom(int T, int E) {
+  ChunkGeom g;
+  g.C = std::min(kBucketChunks, (T + 31) / 32);
+  g.TC = ((T + g.C - 1) / g.C + 31) / 32 * 32;
+  g.W = g.TC / 32;
+  if (g.W * E > kBitmapWords) g.C = 0;  // too many tokens per chunk for the LDS: the one-workgroup kernel
+  return g;
+}
+
+__global__ __launch_bounds__(256) void bucket_count_kernel(BucketArgs a, int TC, int W, int32_t *cc) {
+  __shared__ uint32_t bitmap[kBitmapWords];
+  const int tid = threadIdx.x, E = a.E, k = a.k;
+  const int c = blockIdx.x, c0 = c * TC, nt = min(TC, a.T - c0);
+  for (int i = tid; i < E * W; i += 256) bitmap[i] = 0u;
+  __syncthreads();
+  bool bad = false;
+  for (int tl = tid; tl < nt; tl += 256) {
+    int ids[16];
+    bad |= !token_ids(a, c0 + tl, ids);
+    for (int j = 0; j < k; ++j)
+      if (ids[j] >= 0) atomicOr(&bitmap[ids[j] * W + (tl >> 5)], 1u << (tl & 31));
+  }
+  if (bad) atomicOr(a.err, (uint32_t)ERRF_BAD_INDEX);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int n = 0;
+    for (int w = 0; w < W; ++w) n += __popc(bitmap[e * W + w]);
+    cc[(int64_t)c * E + e] = n;
+  }
+}
+
+__global__ __launch_bounds__(kBThreads) void bucket_place_kernel(BucketArgs a, int C, int TC, int W,
+                                                                 const int32_t *cc) {
+  __shared__ int off[1025];
+  __shared__ int tmp[kBThreads];
+  __shared__ uint32_t bitmap[kBitmapWords];
+  __shared__ int before[kBitmapWords];  // the rank of the expert's first entry in each word of the chunk
+  const int tid = threadIdx.x, E = a.E, k = a.k;
+  const int c = blockIdx.x, c0 = c * TC, nt = min(TC, a.T - c0);
+  const int eb = (a.expert_bits && tid < E) ? a.expert_bits[tid] : 0;
+  int tot = 0, pre = 0;  // the expert's entries in all chunks, and in the chunks before this one
+  if (tid < E)
+    for (int c2 = 0; c2 < C; ++c2) {
+      const int v = cc[(int64_t)c2 * E + tid];
+      tot += v;
+      pre += c2 < c ? v : 0;
+    }
+  if (c == 0) {
+    bucket_meta(a, tot, eb, tmp, off);  // off[] as well
+  } else {
+    const int ex = block_exclusive_scan(tot, tmp);
+    if (tid < E) off[tid] = ex;
+  }
+  for (int i = tid; i < E * W; i += kBThreads) bitmap[i] = 0u;
+  __syncthreads();
+  for (int tl = tid; tl < nt; tl += kBThreads) {
+    int ids[16];
+    token_ids(a, c0 + tl, ids);
+    for (int j = 0; j < k; ++j)
+      if (ids[j] >= 0) atomicOr(&bitmap[ids[j] * W + (tl >> 5)], 1u << (tl & 31));
+  }
+  __syncthreads();
+  if (tid < E) {
+    int run = off[tid] + pre;
+    for (int w = 0; w < W; ++w) {
+      before[tid * W + w] = run;
+      run += __popc(bitmap[tid * W + w]);
+    }
+  }
+  __syncthreads();
+  for (int tl = tid; tl < nt; tl += kBThreads) {
+    int ids[16];
+    token_ids(a, c0 + tl, ids);
+    const int w = tl >> 5;
+    const uint32_t below = (1u << (tl & 31)) - 1u;
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[j];
+      if (e < 0) continue;
+      a.perm[before[e * W + w] + __popc(bitmap[e * W + w] & below)] = (c0 + tl) * k + j;
+    }
+  }
+}
+
 }  // namespace
 
 moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offsets,
@@ -438,10 +544,22 @@ moe_status launch_bucket(moe_ctx *ctx, const int32_t *idx, int T, int k, int E, 
   BucketArgs a{idx,    T,        k,         E,         counts,     offsets,   perm,
                expert_bits, want_bits, active, n_active, ctx->dev_small, units, n_units,
                ubig_max, has_shared, small_max};
-  {
-    MoeTimer tm_(ctx, MOE_STAGE_BUCKET);
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBThreads), 0, ctx->stream, a);
+  // many entries: the chunked kernels (the one-workgroup kernel keeps small
+  // calls' ids in LDS and needs no second launch)
+#ifndef MOE_BUCKET_CHUNKED
+#define MOE_BUCKET_CHUNKED 1
+#endif
+  const ChunkGeom g = (MOE_BUCKET_CHUNKED && (int64_t)T * k > kIdsCache) ? chunk_geom(T, E) : ChunkGeom{0, 0, 0};
+  MoeTimer tm_(ctx, MOE_STAGE_BUCKET);
+  if (g.C > 0) {
+    int32_t *cc = reinterpret_cast<int32_t *>(ctx->dev_small) + kBucketChunkWord;
+    hipLaunchKernelGGL(bucket_count_kernel, dim3(g.C), dim3(256), 0, ctx->stream, a, g.TC, g.W, cc);
+    MOE_CHECK_LAUNCH("bucket_count_kernel");
+    hipLaunchKernelGGL(bucket_place_kernel, dim3(g.C), dim3(kBThreads), 0, ctx->stream, a, g.C, g.TC, g.W, cc);
+    MOE_CHECK_LAUNCH("bucket_place_kernel");
+    return MOE_OK;
   }
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBThreads), 0, ctx->stream, a);
   MOE_CHECK_LAUNCH("bucket_kernel");
   return MOE_OK;
 }

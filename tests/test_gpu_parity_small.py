@@ -121,7 +121,11 @@ def test_router_logits_zipf_and_ties(moe, ctx, orc, syn):
     assert abs(w_g[0].sum() - 2.5) < 1e-5
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (64, 256, 8), (2048, 256, 8), (37, 8, 2), (1500, 1024, 16)])
+# above 4096 (token, slot) entries the bucketing runs in chunks of tokens
+# (a count pass and a placement pass): 2048, 2049 (a last chunk of one
+# token), 700 x 8, 1500 x 16 over 1024 experts, 10000 (160-token chunks)
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (64, 256, 8), (2048, 256, 8), (37, 8, 2), (1500, 1024, 16),
+                                   (2049, 256, 8), (700, 64, 8), (10000, 256, 8)])
 def test_bucket_exact(moe, ctx, orc, syn, T, E, k):
     log(f"bucket T={T} E={E} k={k}")
     z = syn.normal(5, syn.stream_id(syn.K_MISC, T, E), (T, E))
@@ -132,6 +136,33 @@ def test_bucket_exact(moe, ctx, orc, syn, T, E, k):
     p = torch.empty((T * k,), dtype=torch.int32, device="cuda")
     moe.moe_bucket_tokens(ctx, dev(idx), E, c, o, p)
     assert np.array_equal(host(c), c_o) and np.array_equal(host(o), o_o) and np.array_equal(host(p), p_o)
+
+
+def test_bucket_bad_index_reported_chunked(moe, ctx, orc, syn):
+    """An id out of range in a call large enough for the chunked bucketing:
+    the flag is raised and the other entries are counted and placed as the
+    oracle does without the bad one."""
+    T, E, k = 1024, 64, 8
+    z = syn.normal(6, syn.stream_id(syn.K_MISC, T, E), (T, E))
+    idx, _ = orc.router(z, None, None, k, logits_in=True)
+    idx = idx.copy()
+    idx[700, 3] = E + 5
+    # expected: every other entry, each expert's in ascending (token, slot)
+    # order (a stable sort of the flat entries by expert; the bad one last)
+    flat = idx.ravel()
+    key = np.where(flat < E, flat, E)
+    c_o = np.bincount(flat[flat < E], minlength=E).astype(np.int32)
+    o_o = np.concatenate([[0], np.cumsum(c_o)]).astype(np.int32)
+    p_o = np.argsort(key, kind="stable").astype(np.int32)
+    c = torch.empty((E,), dtype=torch.int32, device="cuda")
+    o = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
+    p = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+    moe.moe_bucket_tokens(ctx, dev(idx), E, c, o, p)
+    with pytest.raises(moe.MoeError):
+        ctx.check()
+    ctx.check()  # cleared
+    n = int(o_o[-1])
+    assert np.array_equal(host(c), c_o) and np.array_equal(host(o), o_o) and np.array_equal(host(p)[:n], p_o[:n])
 
 
 def test_bucket_bad_index_reported(moe, ctx):
