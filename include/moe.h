@@ -185,8 +185,11 @@ moe_status moe_router_topk(moe_ctx *ctx, const moe_router_cfg *cfg, const float 
 
 /* Per-expert bucketing ([P-dedup]): counts int32 [E]; offsets int32 [E+1]
  * (exclusive prefix sums); perm int32 [T*k] = entries t*k+j grouped by
- * expert, ascending (t, j) inside a group. Indices outside [0, E) are not
- * counted and are reported by moe_ctx_check as MOE_EINVAL. */
+ * expert, ascending (t, j) inside a group; only the first offsets[E] entries
+ * are written. An id of -1 (a slot dropped by top-p) gets no entry and is no
+ * error. Any other index outside [0, E), and an id repeated within one
+ * token's k slots (the later slot), gets no entry and is reported by
+ * moe_ctx_check as MOE_EINVAL. */
 moe_status moe_bucket_tokens(moe_ctx *ctx, const int32_t *topk_idx, int T, int k, int E, int32_t *counts,
                              int32_t *offsets, int32_t *perm);
 

@@ -165,6 +165,33 @@ def test_bucket_bad_index_reported_chunked(moe, ctx, orc, syn):
     assert np.array_equal(host(c), c_o) and np.array_equal(host(o), o_o) and np.array_equal(host(p)[:n], p_o[:n])
 
 
+@pytest.mark.parametrize("T", [100, 1024])
+def test_bucket_dropped_slots(moe, ctx, orc, syn, T):
+    """Ids of -1 (slots dropped by top-p) name no expert: they get no entry and
+    raise no error, in the one-workgroup bucketing (T = 100) and in the chunked
+    one (T = 1024, 8192 entries). Expected: a stable sort of the other entries by
+    expert, so each expert's list is in (token, slot) order."""
+    E, k = 64, 8
+    z = syn.normal(7, syn.stream_id(syn.K_MISC, T, E), (T, E))
+    idx, _ = orc.router(z, None, None, k, logits_in=True)
+    idx = idx.copy()
+    rng = np.random.default_rng(T)
+    drop = rng.random(idx.shape) < 0.15
+    drop[:, 0] = False  # top-p keeps at least the first slot
+    idx[drop] = -1
+    flat = idx.ravel()
+    c_o = np.bincount(flat[flat >= 0], minlength=E).astype(np.int32)
+    o_o = np.concatenate([[0], np.cumsum(c_o)]).astype(np.int32)
+    p_o = np.argsort(np.where(flat >= 0, flat, E), kind="stable").astype(np.int32)[: int(o_o[-1])]
+    c = torch.empty((E,), dtype=torch.int32, device="cuda")
+    o = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
+    p = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+    moe.moe_bucket_tokens(ctx, dev(idx), E, c, o, p)
+    ctx.check()
+    assert np.array_equal(host(c), c_o) and np.array_equal(host(o), o_o)
+    assert np.array_equal(host(p)[: int(o_o[-1])], p_o)
+
+
 def test_bucket_bad_index_reported(moe, ctx):
     idx = torch.tensor([[0, 9], [1, 2]], dtype=torch.int32, device="cuda")
     c = torch.empty((8,), dtype=torch.int32, device="cuda")
