@@ -804,6 +804,7 @@ def main():
         traffic_gu = k_["fetch_bytes"] + k_["write_bytes"]
     kernel_names = {"router": "router_gemv_t1_kernel" if T == 1 else "router kernels",
                     "gateup": "gateup_t1_kernel" if T == 1 else "gu_mfma_kernel (64-token and one-block tiles)",
+                    "requant": "requant_t1_kernel" if T == 1 else "requant_mfma_kernel",
                     "down": "down_combine_t1_kernel" if T == 1 else "dn_mfma_kernel (64-token and one-block tiles)"}
     # int8 products of the gate/up launches: every (token, slot) pair and the
     # shared expert's, 2 I rows of H each (multiply and add counted as 2 ops)
@@ -860,7 +861,9 @@ def main():
                      "sum of the 64-token and one-block launches, which overlap on two streams (a lower bound on "
                      "the rate)"},
         "kernels": {k_: {"avg_us": round(v[0] * 1e3, 2), "launches_per_call": v[1]} for k_, v in per_call.items()},
-        "expert_ffn": {"kernels": kernel_names["gateup"] + " + " + kernel_names["down"],
+        # every launch of the expert FFN: (bucketing,) gate/up, requantisation, down
+        "expert_ffn": {"kernels": " + ".join(([] if T == 1 else ["bucketing"])
+                                             + [kernel_names["gateup"], kernel_names["requant"], kernel_names["down"]]),
                        "algorithmic_bytes": round(avg_bytes), "avg_us": round(ffn_ms * 1e3, 2),
                        "achieved_GBps": round(ffn_gbps, 1), "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4)},
         "cold": cold,
