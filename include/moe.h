@@ -239,11 +239,13 @@ moe_status moe_expert_ffn_q2(moe_ctx *ctx, const moe_expert_w *experts, const mo
  * resident) is not computed and not written. out (DEVICE fp32 [T][H],
  * nullable; needs topk_w, DEVICE fp32 [T][k]): also the combine of the
  * y_slots this call leaves, exactly as moe_combine computes it (with the
- * shared slot when shared != NULL). The widths run one after the other on
- * the context stream; with one token each goes through the single-token
- * kernels, the shared expert's width last, whose down kernel then also does
- * the combine. Other arguments, errors and y_slots as for
- * moe_expert_ffn_q4. */
+ * shared slot when shared != NULL). Everything runs on the context stream.
+ * One token whose experts (the shared one included) are int4 and int2 runs
+ * one chain of single-token kernels in which every slot has its own width;
+ * other one-token mixes run each width's single-token kernels in turn, the
+ * shared expert's width last, whose down kernel then also does the combine;
+ * more tokens run each width's call in turn, then the combine. Other
+ * arguments, errors and y_slots as for moe_expert_ffn_q4. */
 moe_status moe_expert_ffn_mixed(moe_ctx *ctx, const moe_expert_w *experts, const moe_expert_w *shared,
                                 int shared_bits, const uint8_t *expert_bits, int widths_mask, const int8_t *xq,
                                 const float *sx, const int32_t *topk_idx, const float *topk_w, int T, int H, int I,
