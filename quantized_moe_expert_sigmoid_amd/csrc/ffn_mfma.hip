@@ -222,6 +222,11 @@ __device__ __forceinline__ uint4 lds_ld16(const lds_u8 *p) {
 #define MOE_MFMA_WPERM 1
 #endif
 constexpr bool kWPerm = MOE_MFMA_WPERM != 0;
+// stage a tile's padding tokens as zeros instead of loading them
+#ifndef MOE_MFMA_SKIP_PAD
+#define MOE_MFMA_SKIP_PAD 1
+#endif
+constexpr bool kSkipPad = MOE_MFMA_SKIP_PAD != 0;
 
 // the 16 bytes lane src holds, for every lane
 __device__ __forceinline__ uint4 lane_gather16(uint4 v, int src) {
@@ -241,8 +246,8 @@ __device__ __forceinline__ P sgpr_p(P p) {
 
 template <int BITS, int MB, int NM, int NB, int D0, int SL>
 __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wbase)[NM], const uint32_t (&woff)[NB],
-                                             const int8_t *abase, int astride, const int *ids, int rowbytes,
-                                             lds_u8 *lds, v4i (&acc)[MB][NM][NB]) {
+                                             const int8_t *abase, int astride, const int *ids, int nt,
+                                             int rowbytes, lds_u8 *lds, v4i (&acc)[MB][NM][NB]) {
   constexpr int EPC = QFmt<BITS>::kEpc, NS = EPC / 16;
   constexpr int SC = SL / (4 * EPC);      // steps per slice
   constexpr int D = D0 < SC ? D0 : SC;    // weight steps in flight (a divisor of SC)
@@ -274,13 +279,18 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wbase)[NM], 
   bool sv = true;      // the unit this thread stages in the slice in flight lies in the row
   bool sfull = true;   // every unit of that slice does (uniform)
   const int fullb = (nq / 4) * 4 * EPC;  // bytes of the row's complete chunks
+  // tokens past the tile's nt (the repeats of its last token) are not
+  // staged: their products are never stored
+  bool sreal[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) sreal[i] = !kSkipPad || tid / UPT + TPI * i < nt;
   auto aload = [&](int sl) {
     const int o = sl * SL + su * 16;
     sv = (o / (4 * EPC)) * 4 + ((o >> 4) & 3) < nq;
     sfull = (sl + 1) * SL <= fullb;
     const int oc = min(o, astride - 16);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) st[i] = ldg16(srow[i] + oc, 0);
+    for (int i = 0; i < NI; ++i) st[i] = sreal[i] ? ldg16(srow[i] + oc, 0) : make_uint4(0u, 0u, 0u, 0u);
   };
   auto astore = [&](int b) {
     if (sfull) {
@@ -414,7 +424,7 @@ __device__ __forceinline__ void gu_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = acc[mb][1][nb] = v4i{0, 0, 0, 0};
-  tile_mma_lds<BITS, MB, 2, NB, D, SL>(wbase, woff, a.xa, a.xstride, tt_s.tok, rowbytes, lds, acc);
+  tile_mma_lds<BITS, MB, 2, NB, D, SL>(wbase, woff, a.xa, a.xstride, tt_s.tok, nt, rowbytes, lds, acc);
   // lane holds tokens 4*grp + r of each block, row row[nb]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -614,7 +624,7 @@ __device__ __forceinline__ void dn_tile(const MArgs &a, TileTokens &tt_s, lds_u8
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][0][nb] = v4i{0, 0, 0, 0};
-  tile_mma_lds<BITS, MB, 1, NB, D, SL>(wbase, woff, a.aq, a.astride, tt_s.pair, rowbytes, lds, acc);
+  tile_mma_lds<BITS, MB, 1, NB, D, SL>(wbase, woff, a.aq, a.astride, tt_s.pair, nt, rowbytes, lds, acc);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
