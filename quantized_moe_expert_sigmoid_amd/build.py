@@ -41,6 +41,20 @@ FLAGS = [
 ]
 
 
+# Per-source device flags. The matrix-core FFN keeps its MFMA accumulators in
+# ordinary VGPRs: with the default accumulation registers the compiler rotates
+# the loop-carried accumulators between them every K slice (about two
+# register moves per MFMA), which left the vector ALU as busy as the matrix
+# cores.
+FILE_FLAGS = {
+    "ffn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
+def file_flags(src: str) -> list[str]:
+    return FILE_FLAGS.get(os.path.basename(src), [])
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
@@ -52,7 +66,7 @@ def headers():
 
 def _compile(src: str, sanitize: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + (".asan.o" if sanitize else ".o"))
-    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *file_flags(src), *(SANITIZE_FLAGS if sanitize else []), "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -222,7 +222,7 @@ __device__ __forceinline__ uint4 lds_ld16(const lds_u8 *p) {
 #define MOE_MFMA_WPERM 1
 #endif
 constexpr bool kWPerm = MOE_MFMA_WPERM != 0;
-// stage a tile's padding tokens as zeros instead of loading them
+// skip the staging of a tile's padding tokens
 #ifndef MOE_MFMA_SKIP_PAD
 #define MOE_MFMA_SKIP_PAD 1
 #endif
@@ -279,8 +279,9 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wbase)[NM], 
   bool sv = true;      // the unit this thread stages in the slice in flight lies in the row
   bool sfull = true;   // every unit of that slice does (uniform)
   const int fullb = (nq / 4) * 4 * EPC;  // bytes of the row's complete chunks
-  // tokens past the tile's nt (the repeats of its last token) are not
-  // staged: their products are never stored
+  // Tokens past the tile's nt (the repeats of its last token) are neither
+  // loaded nor stored: their LDS rows hold whatever they held, and the
+  // products of those rows are never stored.
   bool sreal[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) sreal[i] = !kSkipPad || tid / UPT + TPI * i < nt;
@@ -290,15 +291,18 @@ __device__ __forceinline__ void tile_mma_lds(const uint8_t *const (&wbase)[NM], 
     sfull = (sl + 1) * SL <= fullb;
     const int oc = min(o, astride - 16);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) st[i] = sreal[i] ? ldg16(srow[i] + oc, 0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < NI; ++i)
+      if (sreal[i]) st[i] = ldg16(srow[i] + oc, 0);
   };
   auto astore = [&](int b) {
     if (sfull) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) lds_st16(lds + b * BUF + sdst[i], st[i]);
+      for (int i = 0; i < NI; ++i)
+        if (sreal[i]) lds_st16(lds + b * BUF + sdst[i], st[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) lds_st16(lds + b * BUF + sdst[i], sv ? st[i] : make_uint4(0u, 0u, 0u, 0u));
+      for (int i = 0; i < NI; ++i)
+        if (sreal[i]) lds_st16(lds + b * BUF + sdst[i], sv ? st[i] : make_uint4(0u, 0u, 0u, 0u));
     }
   };
   uint4 wv[D][NM][NB];
