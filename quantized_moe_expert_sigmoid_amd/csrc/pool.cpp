@@ -84,6 +84,7 @@ struct Entry {
   bool prefetched = false;         // refilled by a prefetch, not yet requested
   std::list<int>::iterator lru;    // valid while resident and unpinned
   hipEvent_t ready = nullptr;      // refill completion (copy stream)
+  bool ready_wait = false;         // the context stream has not waited for the latest refill yet
 };
 
 }  // namespace
@@ -119,6 +120,11 @@ struct moe_pool {
   std::vector<uint8_t> build;
   uint64_t table_copies = 0, table_skips = 0;
   int call_widths = 0;  // widths of the latest prepare call's experts (bit b: width b)
+  // [n_layers]: an expert of the layer was refilled or evicted since its
+  // table was last built (the table depends on nothing else)
+  std::vector<uint8_t> dirty;
+  std::vector<uint8_t> want_buf;  // per-call scratch of prepare, kept to avoid reallocation
+  std::vector<uint64_t> wait_buf;
 };
 
 namespace {
@@ -166,7 +172,12 @@ bool fits_free(const moe_pool *p, size_t len) {
 
 // Drops resident entry v from the slab; raises *wait_ep to the epoch whose
 // start event a refill into its bytes must wait for.
+void mark_dirty(moe_pool *p, const Entry &en) {
+  p->dirty[(size_t)(&en - p->entries.data()) / (size_t)p->n_experts] = 1;
+}
+
 void evict(moe_pool *p, Entry &v, uint64_t *wait_ep) {
+  mark_dirty(p, v);
   if (!v.pin) p->lru.erase(v.lru);
   v.resident = false;
   v.prefetched = false;
@@ -188,6 +199,7 @@ moe_status refill(moe_pool *p, Entry &en, uint64_t ep, uint64_t protect, uint64_
     if (p->lru.empty() || p->entries[p->lru.front()].last_use >= protect) return MOE_EPOOL;
     evict(p, p->entries[p->lru.front()], &wait_ep);
   }
+  mark_dirty(p, en);
   en.off = off;
   en.resident = true;
   en.rbits = narrow ? en.alt_bits : en.bits;
@@ -210,6 +222,7 @@ moe_status refill(moe_pool *p, Entry &en, uint64_t ep, uint64_t protect, uint64_
                            p->copy_stream));
     if (!en.ready) MOE_HIP(hipEventCreateWithFlags(&en.ready, hipEventDisableTiming));
     MOE_HIP(hipEventRecord(en.ready, p->copy_stream));
+    en.ready_wait = true;
   }
   return MOE_OK;
 }
@@ -237,6 +250,7 @@ extern "C" moe_status moe_pool_create(moe_ctx *ctx, size_t capacity_bytes, int n
   p->shadow.resize((size_t)n_layers);
   p->gen.assign((size_t)n_layers, 0);
   p->own_gen.assign((size_t)n_layers, 0);
+  p->dirty.assign((size_t)n_layers, 1);
   p->free_list[0] = p->capacity;
   if (ctx) {
     auto fail = [&](hipError_t e, const char *what) {
@@ -338,7 +352,8 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   const int E = p->n_experts;
   Entry *row = &p->entries[(size_t)layer * E];
   // the call's distinct experts, ascending (each expert is read once)
-  std::vector<uint8_t> want(E, 0);
+  std::vector<uint8_t> &want = p->want_buf;
+  want.assign((size_t)E, 0);
   for (int64_t i = 0; i < (int64_t)T * k; ++i) {
     const int e = topk_idx_host[i];
     if (e == -1) continue;  // a slot dropped by top-p needs no expert
@@ -353,7 +368,8 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   const uint64_t ep = ++p->epoch;
   if (p->ctx) MOE_HIP(hipEventRecord(p->epoch_ev[ep % kEpochEvents], p->ctx->stream));
   // hits first: they move to the hot end and cannot be evicted below
-  std::vector<uint64_t> wait(E, 0);
+  std::vector<uint64_t> &wait = p->wait_buf;
+  wait.assign((size_t)E, 0);
   for (int e = 0; e < E; ++e) {
     if (!want[e]) continue;
     ++row[e].uses;
@@ -392,33 +408,42 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
     if (want[e]) p->call_widths |= 1 << row[e].rbits;
   if (!p->ctx) return MOE_OK;
 
-  // the context stream waits for every refill this call's experts depend on
+  // The context stream waits for each refill this call's experts depend on,
+  // once: every later call runs on the same stream, after that wait.
   for (int e = 0; e < E; ++e)
-    if (want[e] && row[e].ready) MOE_HIP(hipStreamWaitEvent(p->ctx->stream, row[e].ready, 0));
-  // the layer's table and widths, built on the host
-  const size_t tab_bytes = (size_t)E * sizeof(moe_expert_w);
-  p->build.assign(tab_bytes + (size_t)E, 0);
-  moe_expert_w *tab = reinterpret_cast<moe_expert_w *>(p->build.data());
-  uint8_t *bits = p->build.data() + tab_bytes;
-  for (int e = 0; e < E; ++e) {
-    const Entry &en = row[e];
-    if (en.resident) {
-      size_t o[6];
-      moe_expert_block_layout(en.rbits, p->H, p->I, o);
-      const char *b = p->slab + en.off;
-      tab[e].gate = reinterpret_cast<const uint8_t *>(b + o[0]);
-      tab[e].up = reinterpret_cast<const uint8_t *>(b + o[1]);
-      tab[e].down = reinterpret_cast<const uint8_t *>(b + o[2]);
-      tab[e].s_gate = reinterpret_cast<const float *>(b + o[3]);
-      tab[e].s_up = reinterpret_cast<const float *>(b + o[4]);
-      tab[e].s_down = reinterpret_cast<const float *>(b + o[5]);
-      bits[e] = (uint8_t)en.rbits;
+    if (want[e] && row[e].ready && row[e].ready_wait) {
+      MOE_HIP(hipStreamWaitEvent(p->ctx->stream, row[e].ready, 0));
+      row[e].ready_wait = false;
     }
+  // the layer's table and widths, built on the host when a refill or an
+  // eviction changed them
+  const size_t tab_bytes = (size_t)E * sizeof(moe_expert_w);
+  if (p->dirty[layer]) {
+    p->build.assign(tab_bytes + (size_t)E, 0);
+    moe_expert_w *tab = reinterpret_cast<moe_expert_w *>(p->build.data());
+    uint8_t *bits = p->build.data() + tab_bytes;
+    for (int e = 0; e < E; ++e) {
+      const Entry &en = row[e];
+      if (en.resident) {
+        size_t o[6];
+        moe_expert_block_layout(en.rbits, p->H, p->I, o);
+        const char *b = p->slab + en.off;
+        tab[e].gate = reinterpret_cast<const uint8_t *>(b + o[0]);
+        tab[e].up = reinterpret_cast<const uint8_t *>(b + o[1]);
+        tab[e].down = reinterpret_cast<const uint8_t *>(b + o[2]);
+        tab[e].s_gate = reinterpret_cast<const float *>(b + o[3]);
+        tab[e].s_up = reinterpret_cast<const float *>(b + o[4]);
+        tab[e].s_down = reinterpret_cast<const float *>(b + o[5]);
+        bits[e] = (uint8_t)en.rbits;
+      }
+    }
+    if (p->build != p->shadow[layer]) {
+      p->shadow[layer].swap(p->build);
+      ++p->gen[layer];
+    }
+    p->dirty[layer] = 0;
   }
-  if (p->build != p->shadow[layer]) {
-    p->shadow[layer] = p->build;
-    ++p->gen[layer];
-  }
+  const std::vector<uint8_t> &cur = p->shadow[layer];
   // the layer's own table already holding these bytes (an earlier call's
   // copy, in stream order) is not written again
   const bool own = table_dev == own_table(p, layer);
@@ -432,7 +457,7 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   const int si = p->staging_next;
   p->staging_next = (si + 1) % kStaging;
   if (p->staging_used[si]) MOE_HIP(hipEventSynchronize(p->staging_ev[si]));
-  std::memcpy(p->staging[si], p->build.data(), p->build.size());
+  std::memcpy(p->staging[si], cur.data(), cur.size());
   if (own || bits_dev == reinterpret_cast<uint8_t *>(table_dev) + tab_bytes) {
     MOE_HIP(hipMemcpyAsync(table_dev, p->staging[si], tab_bytes + (size_t)E, hipMemcpyHostToDevice, p->ctx->stream));
   } else {
