@@ -335,8 +335,12 @@ moe_status moe_layer_forward_noalloc(moe_ctx *ctx, int bits, const moe_router_cf
  * Blocks of different widths share one slab (first fit with coalescing). One
  * least-recently-used order spans every layer's resident experts; a pinned
  * expert, once resident, is never evicted. Refills run on the pool's own copy
- * stream; the context stream waits for them. Not thread-safe; destroy a pool
- * before its context. */
+ * stream; the context stream waits for them. A context re-bound to another
+ * stream (moe_ctx_set_stream) gets those waits and the layer's table again on
+ * the new stream; kernels still pending on the previous stream that read the
+ * slab must be ordered before the next prepare call by the caller (evictions
+ * are ordered against the context's current stream). Not thread-safe;
+ * destroy a pool before its context. */
 typedef struct moe_pool moe_pool;
 
 /* Create a pool of capacity_bytes of HBM (allocated now on ctx's device) for

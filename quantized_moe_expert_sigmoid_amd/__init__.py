@@ -15,6 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 import sys
+_sys = sys  # read by the destructors
 import threading
 import weakref
 
@@ -176,7 +177,9 @@ class MoeCtx:
             self.handle = None
 
     def __del__(self):
-        if sys.is_finalizing():  # the HIP runtime may already be gone
+        # at interpreter teardown the HIP runtime (and this module's globals)
+        # may already be gone
+        if _sys is None or _sys.is_finalizing():
             return
         try:
             self.close()
@@ -501,7 +504,9 @@ class MoePool:
             self._blocks.clear()
 
     def __del__(self):
-        if sys.is_finalizing():  # the HIP runtime may already be gone
+        # at interpreter teardown the HIP runtime (and this module's globals)
+        # may already be gone
+        if _sys is None or _sys.is_finalizing():
             return
         try:
             self.close()

@@ -32,12 +32,15 @@
 //    (the readers of the experts earlier calls made resident) has finished.
 //    A refill into memory freed by evicting an expert last used in epoch n
 //    makes the copy stream wait for the event of epoch n+1 first.
-//  - The context stream waits for this call's refills, then receives the
-//    layer's expert table (and widths) from a pinned staging buffer, unless
-//    the destination already holds them: the pool remembers, per device
-//    buffer range it wrote, which layer's table of which generation went
-//    there (a layer's generation rises whenever its table's bytes change),
-//    so at a high hit rate most calls copy nothing.
+//  - The context stream waits for this call's refills (for each refill once
+//    per stream: later calls on that stream run after the wait), then
+//    receives the layer's expert table (and widths) from a pinned staging
+//    buffer, unless the destination already holds them: the pool remembers,
+//    per device buffer range it wrote, which layer's table of which
+//    generation went there, and on which stream (a layer's generation rises
+//    whenever its table's bytes change), so at a high hit rate most calls
+//    copy nothing. The table is rebuilt on the host only after one of the
+//    layer's experts was refilled or evicted.
 //  - Every requested (layer, expert) is counted; moe_pool_pin_hot pins the
 //    most requested within a byte budget (refilling them now), and the
 //    counts can be saved and given back in a later process.
@@ -84,7 +87,8 @@ struct Entry {
   bool prefetched = false;         // refilled by a prefetch, not yet requested
   std::list<int>::iterator lru;    // valid while resident and unpinned
   hipEvent_t ready = nullptr;      // refill completion (copy stream)
-  bool ready_wait = false;         // the context stream has not waited for the latest refill yet
+  bool waited = false;             // a context stream has waited for the latest refill:
+  hipStream_t waited_on = nullptr;  // that stream (the null stream is a valid one)
 };
 
 }  // namespace
@@ -117,6 +121,7 @@ struct moe_pool {
   std::vector<std::vector<uint8_t>> shadow;  // [n_layers]
   std::vector<uint64_t> gen;                 // [n_layers]
   std::vector<uint64_t> own_gen;             // [n_layers] generation the own table holds (0: none)
+  std::vector<hipStream_t> own_stream;       // [n_layers] the stream that own table's latest copy went on
   std::vector<uint8_t> build;
   uint64_t table_copies = 0, table_skips = 0;
   int call_widths = 0;  // widths of the latest prepare call's experts (bit b: width b)
@@ -222,7 +227,7 @@ moe_status refill(moe_pool *p, Entry &en, uint64_t ep, uint64_t protect, uint64_
                            p->copy_stream));
     if (!en.ready) MOE_HIP(hipEventCreateWithFlags(&en.ready, hipEventDisableTiming));
     MOE_HIP(hipEventRecord(en.ready, p->copy_stream));
-    en.ready_wait = true;
+    en.waited = false;
   }
   return MOE_OK;
 }
@@ -250,6 +255,7 @@ extern "C" moe_status moe_pool_create(moe_ctx *ctx, size_t capacity_bytes, int n
   p->shadow.resize((size_t)n_layers);
   p->gen.assign((size_t)n_layers, 0);
   p->own_gen.assign((size_t)n_layers, 0);
+  p->own_stream.assign((size_t)n_layers, nullptr);
   p->dirty.assign((size_t)n_layers, 1);
   p->free_list[0] = p->capacity;
   if (ctx) {
@@ -409,11 +415,14 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   if (!p->ctx) return MOE_OK;
 
   // The context stream waits for each refill this call's experts depend on,
-  // once: every later call runs on the same stream, after that wait.
+  // once per stream: later calls on the same stream run after that wait (a
+  // context re-bound to another stream waits again).
+  hipStream_t cs = p->ctx->stream;
   for (int e = 0; e < E; ++e)
-    if (want[e] && row[e].ready && row[e].ready_wait) {
-      MOE_HIP(hipStreamWaitEvent(p->ctx->stream, row[e].ready, 0));
-      row[e].ready_wait = false;
+    if (want[e] && row[e].ready && !(row[e].waited && row[e].waited_on == cs)) {
+      MOE_HIP(hipStreamWaitEvent(cs, row[e].ready, 0));
+      row[e].waited = true;
+      row[e].waited_on = cs;
     }
   // the layer's table and widths, built on the host when a refill or an
   // eviction changed them
@@ -445,9 +454,9 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   }
   const std::vector<uint8_t> &cur = p->shadow[layer];
   // the layer's own table already holding these bytes (an earlier call's
-  // copy, in stream order) is not written again
+  // copy on this stream, in stream order) is not written again
   const bool own = table_dev == own_table(p, layer);
-  if (own && p->own_gen[layer] == p->gen[layer]) {
+  if (own && p->own_gen[layer] == p->gen[layer] && p->own_stream[layer] == cs) {
     ++p->table_skips;
     return MOE_OK;
   }
@@ -467,7 +476,10 @@ extern "C" moe_status moe_pool_prepare(moe_pool *p, int layer, const int32_t *to
   }
   MOE_HIP(hipEventRecord(p->staging_ev[si], p->ctx->stream));
   p->staging_used[si] = true;
-  if (own) p->own_gen[layer] = p->gen[layer];
+  if (own) {
+    p->own_gen[layer] = p->gen[layer];
+    p->own_stream[layer] = cs;
+  }
   ++p->table_copies;
   return MOE_OK;
 }

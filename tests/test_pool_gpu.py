@@ -480,3 +480,58 @@ def test_pool_one_token_mixed_loop(moe, ctx, orc, syn, slots):
             assert torch.equal(y, ry) and torch.equal(out, ro) and torch.equal(out, rc), c
     finally:
         pool.close()
+
+
+def test_pool_stream_rebind(moe, orc, syn):
+    """A context re-bound to another stream between calls: the pool makes the
+    new stream wait for the refills of the experts it reads and copies the
+    layer's own table again on it (a wait or a copy on the previous stream
+    does not order the new stream's kernels). Calls come in pairs with the
+    same experts, each pair on the other stream: the first call of a pair
+    copies the table, the second (all hits, same stream) skips the copy.
+    Every slot equals the same call on an all-resident table and the
+    oracle's result, bit for bit."""
+    E, k = 8, 2
+    c2 = moe.MoeCtx(0)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    pool = None
+    try:
+        blocks, host = make_blocks(moe, c2, syn, 4, E, seed=39)
+        pool = moe.MoePool(c2, 4 * blocks.block_bytes, 1, E, H, I)
+        for e in range(E):
+            pool.register(0, e, 4, host[e])
+        tab, wid = pool.layer_table(0)
+        rng = np.random.default_rng(39)
+        calls = []
+        for c in range(24):
+            ids = rng.choice(E, size=k, replace=False).astype(np.int32)[None, :] if c % 2 == 0 else calls[-1][0]
+            xq, sx = token_inputs(moe, c2, syn, 1, seed=300 + c)
+            y = torch.zeros((1, k + 1, H), dtype=torch.float32, device="cuda")
+            calls.append((ids, xq, sx, torch.from_numpy(ids).cuda(), y))
+        torch.cuda.synchronize()
+        for c, (ids, xq, sx, idx, y) in enumerate(calls):
+            c2.set_stream(streams[(c // 2) % 2])
+            t0 = pool.table_stats()
+            pool.prepare(0, ids, tab, wid)
+            t1 = pool.table_stats()
+            made = (t1["copies"] - t0["copies"], t1["skipped"] - t0["skipped"])
+            assert made == ((1, 0) if c % 2 == 0 else (0, 1)), (c, made)
+            moe.moe_expert_ffn_mixed(c2, tab, None, 4, wid, 1 << 4, xq, sx, idx, H, I, E, y)
+        c2.set_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        c2.check()
+        oe = OracleBlocks(orc, syn, 39)
+        all4 = torch.full((E,), 4, dtype=torch.uint8, device="cuda")
+        for c, (ids, xq, sx, idx, y) in enumerate(calls):
+            ref = torch.zeros_like(y)
+            moe.moe_expert_ffn_mixed(c2, blocks.table, None, 4, all4, 1 << 4, xq, sx, idx, H, I, E, ref)
+            torch.cuda.synchronize()
+            assert torch.equal(y, ref), c
+            check_slots_vs_oracle(orc, syn, 300 + c, y, ids, lambda e: oe.get(4, e))
+        st = pool.stats()
+        log(f"pool stream rebind: {st}")
+        assert st["misses"] > 8
+    finally:
+        if pool is not None:
+            pool.close()
+        c2.close()
