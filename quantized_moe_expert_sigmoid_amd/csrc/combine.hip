@@ -9,6 +9,12 @@
 
 namespace {
 
+constexpr int kMaxK = 16;  // the largest top-k the entry points accept
+
+// Every slot's float4 is loaded before the first multiply-add (a loop bounded
+// by the runtime k would issue them one at a time); the multiply-adds then
+// run in slot order. A slot of weight 0 (dropped by top-p) is loaded but not
+// used: its y may never have been written.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w, int T,
                                                       int k, int H, int has_shared, float *__restrict__ out) {
   const int h4 = H / 4;
@@ -19,14 +25,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   const float *ys = y + (int64_t)t * (k + 1) * H;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (has_shared) acc = *reinterpret_cast<const float4 *>(ys + (int64_t)k * H + hh);
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(int64_t)t * k + j];
-    if (wj == 0.0f) continue;  // a slot dropped by top-p: its y is not read (fma(0, y, acc) = acc for finite y)
-    const float4 v = *reinterpret_cast<const float4 *>(ys + (int64_t)j * H + hh);
-    acc.x = __builtin_fmaf(wj, v.x, acc.x);
-    acc.y = __builtin_fmaf(wj, v.y, acc.y);
-    acc.z = __builtin_fmaf(wj, v.z, acc.z);
-    acc.w = __builtin_fmaf(wj, v.w, acc.w);
+  float wv[kMaxK];
+  float4 v[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) {
+      wv[j] = w[(int64_t)t * k + j];
+      v[j] = *reinterpret_cast<const float4 *>(ys + (int64_t)j * H + hh);
+    }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    // fma(0, y, acc) = acc for finite y; a dropped slot's y is not used
+    if (j >= k || wv[j] == 0.0f) continue;
+    acc.x = __builtin_fmaf(wv[j], v[j].x, acc.x);
+    acc.y = __builtin_fmaf(wv[j], v[j].y, acc.y);
+    acc.z = __builtin_fmaf(wv[j], v[j].z, acc.z);
+    acc.w = __builtin_fmaf(wv[j], v[j].w, acc.w);
   }
   *reinterpret_cast<float4 *>(out + (int64_t)t * H + hh) = acc;
 }
