@@ -128,9 +128,9 @@ const char *moe_last_error(void);
 int moe_abi_version(void);
 /* Which kernels compute the expert FFN of moe_expert_ffn_q* and of the
  * multi-token path of moe_layer_forward. MOE_FFN_AUTO (the default), from
- * the measured crossover at the GLM shape: up to 4 tokens the single-token
+ * the measured crossover at the GLM shape: up to 3 tokens the single-token
  * kernels of the whole-layer decode path (without its router and combine)
- * run once per token, where the shape fits them; from 5 tokens on the int8
+ * run once per token, where the shape fits them; from 4 tokens on the int8
  * matrix-core kernels, whose tiles read each expert once for all its
  * tokens; the vector dot-product kernels where neither takes the shape.
  * MOE_FFN_DOT4: always the vector kernels. MOE_FFN_MFMA: always the

@@ -450,11 +450,13 @@ int rows_per_wg_d(int bits) { return kWaves * (bits == 8 ? Shape<8>::kRwD : bits
 // Which kernel family computes a call's expert FFN. MOE_FFN_AUTO follows
 // the measured crossover at the GLM shape (int4, hidden 6144, intermediate
 // 2048, top-8 + shared): up to kT1MaxTokens tokens the single-token kernels
-// run once per token (2 tokens: 77 us against 101 for the vector kernels
-// and 117 for the matrix cores; 4 tokens: 156 against 163 and 167); from 8
-// tokens on the matrix cores win (8: 237 against 279 and 311), their
-// per-expert tiles reading each expert once for all its tokens.
-constexpr int kT1MaxTokens = 4;
+// run once per token (2 tokens: 78 us against 101 for the vector kernels
+// and 110 for the matrix cores; 3 tokens: 116 against 135 and 135); from 4
+// tokens on the matrix cores win (4: 156 against 156 and 163 with
+// hidden-state routing, 148 against 155 and 156 with Zipf routing; 8: 221
+// against 310 and 277), their per-expert tiles reading each expert once for
+// all its tokens.
+constexpr int kT1MaxTokens = 3;
 enum FfnRoute { kRouteMfma, kRouteT1, kRouteDot4, kRouteUnsupported };
 FfnRoute ffn_route(const moe_ctx *ctx, int bits, int has_shared, int T, int H, int I, int k) {
   const bool mfma_ok = expert_ffn_mfma_supported(bits, H, I);

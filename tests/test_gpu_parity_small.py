@@ -291,7 +291,7 @@ def check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, 
                                        (150, 256, 128, 4, 2), (2, 256, 128, 8, 3), (4, 128, 64, 6, 2)])
 def test_ffn_intermediates_bitexact(moe, ctx, orc, syn, kern, bits, T, H, I, E, k):
     """Every intermediate of every (token, slot) pair bit-exact, for each
-    kernel family ("auto": up to 4 tokens the single-token kernels once per
+    kernel family ("auto": up to 3 tokens the single-token kernels once per
     token, more the matrix cores)."""
     idx = random_routing(syn, T, E, k, 42)
     check_ffn_intermediates(moe, ctx, orc, syn, kern, bits, T, H, I, E, k, idx, seed=40 + bits)
