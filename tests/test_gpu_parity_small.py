@@ -622,16 +622,28 @@ def test_ffn_mixed_one_token_graph_replay(moe, ctx, orc, syn):
 # combine and the whole layer
 # --------------------------------------------------------------------------
 
-def test_combine(moe, ctx, orc, syn):
-    T, k, H = 9, 8, 6144
-    y = syn.normal(70, syn.stream_id(syn.K_MISC, 70), (T, k + 1, H))
-    w = np.abs(syn.normal(70, syn.stream_id(syn.K_MISC, 71), (T, k)))
+@pytest.mark.parametrize("k", [1, 2, 8, 16])
+def test_combine(moe, ctx, orc, syn, k):
+    """Against the oracle for k up to the largest the entry points accept,
+    with and without the shared slot. A slot of weight 0 (dropped by top-p)
+    is not read: NaN there leaves the output bit-identical."""
+    T, H = 9, 6144
+    y = syn.normal(70 + k, syn.stream_id(syn.K_MISC, 70), (T, k + 1, H))
+    w = np.abs(syn.normal(70 + k, syn.stream_id(syn.K_MISC, 71), (T, k)))
+    if k >= 2:
+        w[1::2, 1] = 0.0  # odd tokens drop slot 1
     for has_shared in (True, False):
         out = torch.empty((T, H), dtype=torch.float32, device="cuda")
         moe.moe_combine(ctx, dev(y), dev(w), has_shared, out)
         ys = y if has_shared else np.ascontiguousarray(y[:, :k])
         ref = orc.combine(ys, w, has_shared)
         assert rel_row_err(host(out), ref).max() < 1e-5
+        if k >= 2:
+            yn = y.copy()
+            yn[1::2, 1] = np.nan
+            out_n = torch.empty_like(out)
+            moe.moe_combine(ctx, dev(yn), dev(w), has_shared, out_n)
+            assert torch.equal(out_n, out)
 
 
 @pytest.mark.parametrize("bits", [4, 8, 2])
