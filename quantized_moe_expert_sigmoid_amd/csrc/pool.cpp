@@ -66,8 +66,14 @@
 
 namespace {
 
-constexpr int kEpochEvents = 64;  // ring of per-call events on the context stream
-constexpr int kStaging = 8;       // ring of pinned table staging buffers
+// Ring of per-call events on the context stream. It spans more calls than
+// the host runs ahead of the GPU (bounded by the table staging ring), so an
+// eviction victim's own epoch event is still in the ring, usually long
+// complete. A shorter ring (64) made refills that evicted wait for the ring's
+// oldest event, which the GPU reached only shortly before the refilled expert
+// was needed: the context stream then waited for most of each refill.
+constexpr int kEpochEvents = 1024;
+constexpr int kStaging = 8;  // ring of pinned table staging buffers
 
 struct Entry {
   bool registered = false;
