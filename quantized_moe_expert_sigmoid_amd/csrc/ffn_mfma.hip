@@ -674,14 +674,22 @@ moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *x
   // workgroups return at once. The two tile kinds write disjoint rows: the
   // 64-token tiles run on the side stream, overlapping the one-block tiles.
   moe_status st;
-  const bool wide = a.small_max == 0;  // experts average 32 or more tokens
+  if (a.small_max == 0) {
+    // Experts average 32 or more tokens: every remainder is a full-size
+    // tile, the bucketing lists no one-block tile, and the 64-token launches
+    // run alone on the context stream with 256-byte slices.
+    moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4, kSlWide>, dim3(a.ubig_max * g4), dim3(kThreads), a,
+               g4);
+    MOE_CHECK_LAUNCH("gu_mfma_kernel");
+    moe_launch(ctx, MOE_STAGE_REQUANT, requant_mfma_kernel<BITS>, dim3(a.T * (a.k + 1)), dim3(kThreads), a);
+    MOE_CHECK_LAUNCH("requant_mfma_kernel");
+    moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4, kSlWide>, dim3(a.ubig_max * d4), dim3(kThreads), a, d4);
+    MOE_CHECK_LAUNCH("dn_mfma_kernel");
+    return MOE_OK;
+  }
   if ((st = moe_side_fork(ctx))) return st;
-  if (wide)
-    moe_launch_on(ctx, ctx->side, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4, kSlWide>, dim3(a.ubig_max * g4),
-                  dim3(kThreads), a, g4);
-  else
-    moe_launch_on(ctx, ctx->side, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max * g4), dim3(kThreads),
-                  a, g4);
+  moe_launch_on(ctx, ctx->side, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 4>, dim3(a.ubig_max * g4), dim3(kThreads), a,
+                g4);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
   moe_launch(ctx, MOE_STAGE_GATEUP, gu_mfma_kernel<BITS, 1>, dim3(usmall * g1), dim3(kThreads), a, g1);
   MOE_CHECK_LAUNCH("gu_mfma_kernel");
@@ -689,12 +697,8 @@ moe_status launch_bits(moe_ctx *ctx, const MArgs &a, const int8_t *xq, int8_t *x
   moe_launch(ctx, MOE_STAGE_REQUANT, requant_mfma_kernel<BITS>, dim3(a.T * (a.k + 1)), dim3(kThreads), a);
   MOE_CHECK_LAUNCH("requant_mfma_kernel");
   if ((st = moe_side_fork(ctx))) return st;
-  if (wide)
-    moe_launch_on(ctx, ctx->side, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4, kSlWide>, dim3(a.ubig_max * d4),
-                  dim3(kThreads), a, d4);
-  else
-    moe_launch_on(ctx, ctx->side, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max * d4), dim3(kThreads), a,
-                  d4);
+  moe_launch_on(ctx, ctx->side, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 4>, dim3(a.ubig_max * d4), dim3(kThreads), a,
+                d4);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
   moe_launch(ctx, MOE_STAGE_DOWN, dn_mfma_kernel<BITS, 1>, dim3(usmall * d1), dim3(kThreads), a, d1);
   MOE_CHECK_LAUNCH("dn_mfma_kernel");
