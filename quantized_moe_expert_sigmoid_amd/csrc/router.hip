@@ -110,20 +110,26 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const float *__restric
 }
 
 // --- logits, general T, on the fp32 matrix cores ----------------------------
-// The same 64x64 tile and K slice as router_gemm_kernel; each wave owns a
-// 32 x 32 quarter as 2 x 2 blocks of v_mfma_f32_16x16x4f32 (lane l holds
-// x[token l % 16][k0 + l / 16] and w[expert l % 16][k0 + l / 16] for a K step
-// of 4, and the results of tokens 4 (l / 16) .. +3 of expert l % 16). K
-// steps of kMfmaK floats go through LDS, stored k-major so a wave's operand
-// read is 16 consecutive words per K row. kl % kMfmaK == 0.
+// The same 64x64 tile as router_gemm_kernel; each wave owns a 32 x 32
+// quarter as 2 x 2 blocks of v_mfma_f32_16x16x4f32 (lane l holds one x and
+// one w value of token / expert l % 16 per product, at K position l / 16 of
+// its step, and the results of tokens 4 (l / 16) .. +3 of expert l % 16).
+// K steps of kMfmaK floats go through LDS row-major (a token's or expert's
+// floats contiguous, rows padded by one 16-byte unit so the 16 rows a read
+// spans hit distinct banks). Per 16 floats of K a lane reads one 16-byte
+// unit of each of its rows, unit l / 16, and feeds its four floats to four
+// consecutive products: product s of the 16 takes K positions 4q + s
+// (q = 0..3, one per lane group), so the four products cover all 16 and x
+// and w agree on every position. kl % kMfmaK == 0.
 constexpr int kMfmaK = 32;
+constexpr int kMfmaU = kMfmaK / 4 + 1;  // 16-byte units per LDS row (one of padding)
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void router_gemm_mfma_kernel(const float *__restrict__ x,
                                                                const float *__restrict__ wr, int T, int H, int E,
                                                                int kl, float *__restrict__ partial) {
-  __shared__ float xs[kMfmaK][kTile + 4];
-  __shared__ float ws[kMfmaK][kTile + 4];
+  __shared__ float4 xs[kTile][kMfmaU];
+  __shared__ float4 ws[kTile][kMfmaU];
   const int t0 = blockIdx.x * kTile;
   const int e0 = blockIdx.y * kTile;
   const int ks = blockIdx.z;
@@ -131,11 +137,11 @@ __global__ __launch_bounds__(256) void router_gemm_mfma_kernel(const float *__re
   const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wave = tid >> 6;
   const int wt = (wave >> 1) * 32, we = (wave & 1) * 32;  // the wave's quarter of the tile
   const int l16 = lane & 15, kq = lane >> 4;
-  // staging: thread tid moves 8 consecutive floats of row tid / 4 (x and w)
-  const int r = tid >> 2, c8 = (tid & 3) * 8;
+  // staging: thread tid moves 8 consecutive floats (units c2, c2 + 1) of row tid / 4 (x and w)
+  const int r = tid >> 2, c2 = (tid & 3) * 2;
   const int t = t0 + r, e = e0 + r;
-  const float *xrow = x + (int64_t)min(t, T - 1) * H + k0 + c8;
-  const float *wrow = wr + (int64_t)min(e, E - 1) * H + k0 + c8;
+  const float *xrow = x + (int64_t)min(t, T - 1) * H + k0 + 4 * c2;
+  const float *wrow = wr + (int64_t)min(e, E - 1) * H + k0 + 4 * c2;
   v4f acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -151,24 +157,26 @@ __global__ __launch_bounds__(256) void router_gemm_mfma_kernel(const float *__re
   load(0);
   for (int kk = 0; kk < kl; kk += kMfmaK) {
     __syncthreads();  // the previous step's reads are done
-    const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      xs[c8 + q][r] = xv[q];
-      ws[c8 + q][r] = wv[q];
-    }
+    xs[r][c2] = xa;
+    xs[r][c2 + 1] = xb;
+    ws[r][c2] = wa;
+    ws[r][c2 + 1] = wb;
     __syncthreads();
     if (kk + kMfmaK < kl) load(kk + kMfmaK);  // the next step's loads fly under this step's products
 #pragma unroll
-    for (int k4 = 0; k4 < kMfmaK; k4 += 4) {
-      const int k = k4 + kq;
-      const float a0 = xs[k][wt + l16], a1 = xs[k][wt + 16 + l16];
-      const float b0 = ws[k][we + l16], b1 = ws[k][we + 16 + l16];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+    for (int k16 = 0; k16 < kMfmaK / 16; ++k16) {
+      const int u = 4 * k16 + kq;
+      const float4 a0 = xs[wt + l16][u], a1 = xs[wt + 16 + l16][u];
+      const float4 b0 = ws[we + l16][u], b1 = ws[we + 16 + l16][u];
+      const float av[2][4] = {{a0.x, a0.y, a0.z, a0.w}, {a1.x, a1.y, a1.z, a1.w}};
+      const float bv[2][4] = {{b0.x, b0.y, b0.z, b0.w}, {b1.x, b1.y, b1.z, b1.w}};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][q], bv[j][q], acc[i][j], 0, 0, 0);
     }
   }
 #pragma unroll
