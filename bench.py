@@ -100,7 +100,7 @@ def pmc_summary(bench_fetch, bench_write, copy_fetch, copy_write, out_md) -> Non
     bf, bw = _pmc_means(bench_fetch, "FETCH_SIZE"), _pmc_means(bench_write, "WRITE_SIZE")
     rows, traffic = [], {}
     for short, key in (("router", "router_gemv_t1_kernel"), ("gateup", "gateup_t1_kernel"),
-                       ("requant", "requant_t1_kernel"), ("down", "down_combine_t1_kernel")):
+                       ("down", "down_combine_t1_kernel")):
         kf, kw = pick(bf, key), pick(bw, key)
         fb = bf[kf][0] * 1024.0 * f_scale
         wb = bw[kw][0] * 1024.0 * w_scale
@@ -804,8 +804,9 @@ def main():
         traffic_gu = k_["fetch_bytes"] + k_["write_bytes"]
     kernel_names = {"router": "router_gemv_t1_kernel" if T == 1 else "router kernels",
                     "gateup": "gateup_t1_kernel" if T == 1 else "gu_mfma_kernel (64-token and one-block tiles)",
-                    "requant": "requant_t1_kernel" if T == 1 else "requant_mfma_kernel",
-                    "down": "down_combine_t1_kernel" if T == 1 else "dn_mfma_kernel (64-token and one-block tiles)"}
+                    "requant": None if T == 1 else "requant_mfma_kernel",
+                    "down": "down_combine_t1_kernel (with the requantisation)" if T == 1 else
+                            "dn_mfma_kernel (64-token and one-block tiles)"}
     # int8 products of the gate/up launches: every (token, slot) pair and the
     # shared expert's, 2 I rows of H each (multiply and add counted as 2 ops)
     gu_ops = 2.0 * T * (w.k + (1 if w.has_shared else 0)) * 2 * I * H
@@ -863,7 +864,8 @@ def main():
         "kernels": {k_: {"avg_us": round(v[0] * 1e3, 2), "launches_per_call": v[1]} for k_, v in per_call.items()},
         # every launch of the expert FFN: (bucketing,) gate/up, requantisation, down
         "expert_ffn": {"kernels": " + ".join(([] if T == 1 else ["bucketing"])
-                                             + [kernel_names["gateup"], kernel_names["requant"], kernel_names["down"]]),
+                                             + [n_ for n_ in (kernel_names["gateup"], kernel_names["requant"],
+                                                              kernel_names["down"]) if n_]),
                        "algorithmic_bytes": round(avg_bytes), "avg_us": round(ffn_ms * 1e3, 2),
                        "achieved_GBps": round(ffn_gbps, 1), "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4)},
         "cold": cold,

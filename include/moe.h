@@ -285,9 +285,9 @@ moe_status moe_combine(moe_ctx *ctx, const float *y_slots, const float *topk_w, 
  * the shared expert at `bits` (8, 4 or 2; every expert at that width), and
  * the combine. Results equal moe_quantize_act_i8 -> moe_router_topk ->
  * moe_expert_ffn_q* -> moe_combine on the same inputs (the same arithmetic
- * in the same order; a single token runs four fused kernels: router logits
- * with the activation quantisation, top-k with gate/up, requantisation of the
- * intermediate, and down fused with the combine).
+ * in the same order; a single token runs three fused kernels: router logits
+ * with the activation quantisation, top-k with gate/up, and the
+ * requantisation of the intermediate with down and the combine).
  *
  * x fp32 [T][H] hidden states; logits fp32 [T][E] (only with
  * cfg->logits_in, else NULL); w_router fp32 [E][H] (ignored with logits);
@@ -473,8 +473,8 @@ enum {
   MOE_STAGE_ROUTER = 0,   /* activation quantisation + router (+ top-k) */
   MOE_STAGE_BUCKET = 1,   /* per-expert bucketing */
   MOE_STAGE_GATEUP = 2,   /* gate/up GEMV with the SwiGLU epilogue */
-  MOE_STAGE_REQUANT = 3,  /* int8 requantisation of the intermediate */
-  MOE_STAGE_DOWN = 4,     /* down GEMV (fused with the combine for one token) */
+  MOE_STAGE_REQUANT = 3,  /* int8 requantisation of the intermediate (several tokens) */
+  MOE_STAGE_DOWN = 4,     /* down GEMV (one token: with the requantisation and the combine) */
   MOE_STAGE_COMBINE = 5,  /* weighted combine */
   MOE_N_STAGES = 6
 };

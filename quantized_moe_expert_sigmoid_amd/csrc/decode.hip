@@ -1,6 +1,6 @@
-// Single-token (decode) layer path in four kernels: router logits and the
+// Single-token (decode) layer path in three kernels: router logits and the
 // activation quantisation; top-k fused with a streaming gate/up GEMV; the int8
-// requantisation of the SwiGLU intermediate; the down GEMV fused with the
+// requantisation of the SwiGLU intermediate fused with the down GEMV and the
 // combine.
 //
 // Pages: agentlenshq.com, "Colibri: running GLM-5.2 744B MoE on consumer
@@ -28,28 +28,29 @@
 //     waves, stream through 16-byte loads two batches deep against the token's
 //     int8 activations held in registers (field order); DPP reductions; one
 //     store of a = silu(g)*u per row pair.
-//  K3 requant_t1_kernel (one workgroup per slot): max|a| of the slot, the
-//     scale, the int8 codes (written already in the packed weights' field
-//     order) and their sum. Done once per slot rather than by every
-//     workgroup of the down kernel, at full occupancy.
-//  K4 down_combine_t1_kernel (one 512-thread workgroup per CU): the
-//     workgroup loads every slot's codes into LDS (the first down rows of
-//     every slot go out right behind them); each wave multiplies its rows of
-//     every slot's down matrix (one row in flight ahead), writes y per slot
-//     and the combined output out[r] = y_shared + sum_j w_j y_j (the same fma
-//     order as moe_combine). A CU keeps only some tens of KB of loads in
-//     flight and a wave that queues more stalls at issue, so the kernels
-//     queue about that much at a time.
-// The per-step expert FFN of one token (routing given by the caller) runs K2,
-// K3 and K4 without K1 and without the combine: K2 then builds the slot table
+//  K3 down_combine_t1_kernel (one 512-thread workgroup per CU): the
+//     workgroup loads every slot's a (the first down rows of every slot go
+//     out right behind it) and requantises it while those rows are in
+//     flight: max|a| per slot, the scale, the int8 codes (in the packed
+//     weights' field order, into LDS) and their sums. Each wave then
+//     multiplies its rows of every slot's down matrix (one row in flight
+//     ahead), writes y per slot and the combined output
+//     out[r] = y_shared + sum_j w_j y_j (the same fma order as moe_combine).
+//     A CU keeps only some tens of KB of loads in flight and a wave that
+//     queues more stalls at issue, so the kernels queue about that much at a
+//     time.
+// The per-step expert FFN of one token (routing given by the caller) runs K2
+// and K3 without K1 and without the combine: K2 then builds the slot table
 // from the given ids instead of the top-k, keeping only the slots whose expert
 // has the call's width (the others, and ids of -1, are left to their own
-// call), and K4 writes y of those slots and of the shared expert only.
-// Kernel boundaries order the four steps: no atomics across workgroups, no
+// call), and K3 writes y of those slots and of the shared expert only.
+// Kernel boundaries order the three steps: no atomics across workgroups, no
 // cross-workgroup waits (contended device-scope atomics serialise at the
 // memory side). Streaming loads are branch-free: a lane whose chunk index
 // passes the row end reads a clamped in-bounds address and meets zero
 // activation bytes.
+#include <cstdlib>
+
 #include "gemv_common.h"
 
 namespace {
@@ -840,7 +841,7 @@ __global__ __launch_bounds__(kFfnThreads) void gateup_mixed_t1_kernel(GateUpT1Ar
 }
 
 // ---------------------------------------------------------------------------
-// K3: requantisation of every slot's a (one workgroup per slot)
+// The requantisation arithmetic (the activation rule on a)
 // ---------------------------------------------------------------------------
 // int8 code of v under the scale sc = m/127 with inv = 1/sc (both correctly
 // rounded): rint(v * inv) equals rint(v / sc) (the fp32 quotient) unless
@@ -888,139 +889,12 @@ __device__ __forceinline__ uint32_t field_order(uint32_t w, int lane) {
   }
 }
 
-constexpr int kRqThreads = 256;
-
-struct RequantT1Args {
-  const float *A;  // [S][I]
-  const SlotEntry *slots;  // a routed slot with expert -1 was dropped by top-p
-  int I, S, k;
-  uint32_t *aqf;   // [S][I/4] int8 codes, in the packed weights' field order
-  int *sums;       // [S] sum of the codes per slot
-  float *sa;       // [S] per-slot scale
-  moe_debug_bufs dbg;
-  int dbg_on;
-  int given;  // given routing: a routed slot with expert -1 has no work here
-};
-
-// Slot blockIdx.x: sa = max|a|/127 and aq = rint(a/sa) (the activation rule),
-// written as int8 codes in the field order of BITS-bit weights: each thread
-// holds whole field groups (int8: 4 elements, int4: 8, int2: 16), so the
-// reordering stays in registers.
-template <int BITS>
-__device__ __forceinline__ void requant_t1_body(const RequantT1Args &a, int s) {
-  constexpr int G = (BITS == 8) ? 4 : (BITS == 4 ? 8 : 16);
-  constexpr int GD = G / 4;  // dwords (float4 of a) per group
-  __shared__ float red_m[kRqThreads / MOE_WAVE];
-  __shared__ int red_c[kRqThreads / MOE_WAVE];
-  const int tid = threadIdx.x;
-  const int lane = tid & (MOE_WAVE - 1);
-  const int wave = tid >> 6;
-  const float4 *As = reinterpret_cast<const float4 *>(a.A + (int64_t)s * a.I);
-  const int ng = a.I / G;
-  // the thread's groups stay in registers between the two passes
-  constexpr int kIt = (kMaxIDown / G + kRqThreads - 1) / kRqThreads;
-  float4 v4[kIt][GD];
-  float m = 0.0f;
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int g = min(tid + it * kRqThreads, ng - 1);  // past the end: a re-read group, same maximum
-#pragma unroll
-    for (int d = 0; d < GD; ++d) v4[it][d] = As[g * GD + d];
-  }
-#pragma unroll
-  for (int it = 0; it < kIt; ++it)
-#pragma unroll
-    for (int d = 0; d < GD; ++d) {
-      const float4 v = v4[it][d];
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-  m = wave_max_dpp(m);
-  if (lane == 0) red_m[wave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-  // a dropped slot (its a was never written): zero codes and scale, so the
-  // down kernel's y for it is exactly zero
-  const bool zero = m == 0.0f || (s < a.k && a.slots[s].expert == -1);
-  const float sc = zero ? 0.0f : m / 127.0f;
-  const float inv = zero ? 0.0f : 1.0f / sc;
-  const bool fast = sc >= 0x1p-126f && sc <= 0x1.fffffep127f;
-  int csum = 0;
-  uint32_t *dst = a.aqf + (int64_t)s * (a.I / 4);
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int g = tid + it * kRqThreads;
-    if (g >= ng) break;
-    uint32_t nat[GD];
-#pragma unroll
-    for (int d = 0; d < GD; ++d) {
-      const float4 v = v4[it][d];
-      uint32_t word = 0;
-      if (!zero) {
-        bool near = !fast;
-        float q0 = code_fast(v.x, inv, near), q1 = code_fast(v.y, inv, near);
-        float q2 = code_fast(v.z, inv, near), q3 = code_fast(v.w, inv, near);
-        if (near) {
-          q0 = code_exact(v.x, sc);
-          q1 = code_exact(v.y, sc);
-          q2 = code_exact(v.z, sc);
-          q3 = code_exact(v.w, sc);
-        }
-        word = pack_codes(q0, q1, q2, q3);
-      }
-      nat[d] = word;
-      csum = sdot4((int)word, 0x01010101, csum);
-      if (a.dbg_on && a.dbg.aq) reinterpret_cast<uint32_t *>(a.dbg.aq + (int64_t)s * a.I)[g * GD + d] = word;
-    }
-    uint32_t fo[GD];
-    if constexpr (BITS == 4) {
-      act_order_q4(nat[0], nat[1], fo[0], fo[1]);
-    } else if constexpr (BITS == 2) {
-      act_order_q2(nat, fo);
-    } else {
-      fo[0] = nat[0];
-    }
-#pragma unroll
-    for (int d = 0; d < GD; ++d) dst[g * GD + d] = fo[d];
-  }
-  csum = wave_sum_all(csum);
-  if (lane == 0) red_c[wave] = csum;
-  __syncthreads();
-  if (tid == 0) {
-    a.sums[s] = red_c[0] + red_c[1] + red_c[2] + red_c[3];
-    a.sa[s] = sc;
-    if (a.dbg_on && a.dbg.sa) a.dbg.sa[s] = sc;
-  }
-}
-
-template <int BITS>
-__global__ __launch_bounds__(kRqThreads) void requant_t1_kernel(RequantT1Args a) {
-  const int s = blockIdx.x;
-  if (a.given && s < a.k && a.slots[s].expert == -1) return;  // another width's slot: left alone
-  requant_t1_body<BITS>(a, s);
-}
-
-// The mixed-width chain: slot blockIdx.x at its own width (pad[1] of its
-// entry, written by the mixed gate/up kernel); a slot without work is left
-// alone.
-__global__ __launch_bounds__(kRqThreads) void requant_mixed_t1_kernel(RequantT1Args a) {
-  const int s = blockIdx.x;
-  if (s < a.k && a.slots[s].expert == -1) return;
-  switch (a.slots[s].pad[1]) {
-    case 8: requant_t1_body<8>(a, s); break;
-    case 4: requant_t1_body<4>(a, s); break;
-    case 2: requant_t1_body<2>(a, s); break;
-    default: break;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// K4: down projection of every slot + combine
+// K3: requantisation and down projection of every slot + combine
 // ---------------------------------------------------------------------------
 struct DownT1Args {
   const SlotEntry *slots;
-  const uint32_t *aqf;  // [S][I/4] codes in field order
-  const int *sums;      // [S]
-  const float *sa;      // [S]
+  const float *A;  // [S][I] the SwiGLU intermediate (a slot without work here: never written, never used)
   int H, I, S, k, has_shared;
   float *y;    // [S][H] (the token's y_slots; slot stride H)
   float *out;  // [H]; given routing: nullable (no combine)
@@ -1031,13 +905,135 @@ struct DownT1Args {
   const float *w_given;
 };
 
-constexpr int kAq16 = (kMaxSlots * kMaxIDown / 16 + kFfnThreads - 1) / kFfnThreads;  // 16-byte code pieces per thread
+// The requantisation of every slot's a, run by each down workgroup in
+// its prologue: sa = max|a| / 127 and the codes rint(a / sa), clamped to
+// [-127, 127] (the activation rule), in the field order of the slot's
+// weights, with their per-slot sums. A slot dropped by top-p, or without work
+// in a given-routing call, gets zero codes and scale (its a was never
+// written). Every workgroup reads all S slots of a, RQ float4 of each per
+// thread (RQ = ceil(I / 2048)); register group j holds slot (j + blockIdx.x)
+// mod S, so the workgroups of one XCD do not all ask for the same lines at
+// once. The loads go out behind the slot table and before the first down
+// rows, so waiting for a never waits for a weight row (a wave's loads
+// complete in order), and the arithmetic runs while those rows are in flight.
+// This replaced a launch of its own (one workgroup per slot), which cost more
+// than the 74 KB of a every down workgroup now reads from L2.
+template <int RQ>
+struct RqRegs {
+  float4 v[kMaxSlots * RQ];
+  int slot[kMaxSlots];  // the slot of register group j (uniform)
+};
 
-template <int BITS, int JD, int RB, bool GIVEN>
+template <int RQ>
+__device__ __forceinline__ void rq_load(const DownT1Args &a, RqRegs<RQ> &q) {
+  const int S = a.S, n4 = a.I / 4;
+  const int rot = blockIdx.x % S;
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) {
+    const int sj = j + rot >= S ? j + rot - S : j + rot;
+    q.slot[j] = j < S ? sj : q.slot[0];  // groups past S re-read the first group's slot
+    const float *As = a.A + (int64_t)q.slot[j] * a.I;
+#pragma unroll
+    for (int c = 0; c < RQ; ++c) {
+      // past the slot's end: a re-read of its last float4, same maximum
+      const uint4 u = ldg16(As, min((int)threadIdx.x + c * kFfnThreads, n4 - 1));
+      q.v[j * RQ + c] =
+          make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // issued before the wait for the slot table
+}
+
+// The codes of every slot into aq_s (slot s at byte s*I), from the registers
+// rq_load filled. ex_l: lane s < S holds slot s's expert id (-1: no work);
+// width(s): slot s's weight width (s uniform). Returns in lane s < S slot s's
+// code sum and scale. Two barriers; every thread of the workgroup calls it.
+template <int RQ, bool GIVEN, typename Width>
+__device__ __forceinline__ void rq_codes(const DownT1Args &a, const RqRegs<RQ> &q, int ex_l, Width width,
+                                         int8_t *aq_s, float (*red_m)[kFfnWaves], int (*red_c)[kFfnWaves],
+                                         int &aqsum_l, float &sa_l) {
+  const int tid = threadIdx.x, lane = tid & (MOE_WAVE - 1), wave = tid >> 6;
+  const int S = a.S, n4 = a.I / 4;
+  const int ls = lane < S ? lane : S - 1;
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) {
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < RQ; ++c) {
+      const float4 v = q.v[j * RQ + c];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    m = wave_max_dpp(m);
+    if (j < S && lane == 0) red_m[q.slot[j]][wave] = m;
+  }
+  __syncthreads();
+  // lane s < S: slot s's scale, its reciprocal and the fast-path flag
+  float m_l = red_m[ls][0];
+#pragma unroll
+  for (int w = 1; w < kFfnWaves; ++w) m_l = fmaxf(m_l, red_m[ls][w]);
+  const bool zero_l = m_l == 0.0f || (ls < a.k && ex_l == -1);
+  sa_l = zero_l ? 0.0f : m_l / 127.0f;
+  const float inv_l = zero_l ? 0.0f : 1.0f / sa_l;
+  const bool fast_l = sa_l >= 0x1p-126f && sa_l <= 0x1.fffffep127f;
+#pragma unroll
+  for (int j = 0; j < kMaxSlots; ++j) {
+    if (j < S) {
+      const int sj = q.slot[j];
+      const float sc = readlane_f(sa_l, sj), inv = readlane_f(inv_l, sj);
+      const bool zero = __builtin_amdgcn_readlane((int)zero_l, sj) != 0;
+      const bool fast = __builtin_amdgcn_readlane((int)fast_l, sj) != 0;
+      // given routing: a slot without work here (another width's, or -1)
+      // belongs to another call, which writes its captured intermediates
+      const bool mine = !GIVEN || !(sj < a.k && __builtin_amdgcn_readlane(ex_l, sj) == -1);
+      const int wb = width(sj);
+      int csum = 0;
+#pragma unroll
+      for (int c = 0; c < RQ; ++c) {
+        const int f = tid + c * kFfnThreads;
+        const float4 v = q.v[j * RQ + c];
+        uint32_t word = 0;
+        if (!zero) {
+          bool near = !fast;
+          float q0 = code_fast(v.x, inv, near), q1 = code_fast(v.y, inv, near);
+          float q2 = code_fast(v.z, inv, near), q3 = code_fast(v.w, inv, near);
+          if (near) {
+            q0 = code_exact(v.x, sc);
+            q1 = code_exact(v.y, sc);
+            q2 = code_exact(v.z, sc);
+            q3 = code_exact(v.w, sc);
+          }
+          word = pack_codes(q0, q1, q2, q3);
+        }
+        if (f >= n4) word = 0;
+        csum = sdot4((int)word, 0x01010101, csum);
+        // field groups are whole within lane pairs / quads (I is a multiple
+        // of 64), so a lane's neighbours hold dwords of the same group
+        const uint32_t fw = wb == 8 ? word : (wb == 4 ? field_order<4>(word, lane) : field_order<2>(word, lane));
+        if (f < n4) {
+          reinterpret_cast<uint32_t *>(aq_s + sj * a.I)[f] = fw;
+          if (blockIdx.x == 0 && a.dbg_on && a.dbg.aq && mine)
+            reinterpret_cast<uint32_t *>(a.dbg.aq + (int64_t)sj * a.I)[f] = word;
+        }
+      }
+      csum = wave_sum_to63(csum);
+      if (lane == 63) red_c[sj][wave] = csum;
+      if (blockIdx.x == 0 && tid == 0 && a.dbg_on && a.dbg.sa && mine) a.dbg.sa[sj] = sc;
+    }
+  }
+  __syncthreads();
+  int cs = 0;
+#pragma unroll
+  for (int w = 0; w < kFfnWaves; ++w) cs += red_c[ls][w];
+  aqsum_l = cs;
+}
+
+template <int BITS, int JD, int RB, bool GIVEN, int RQ>
 __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args a) {
   constexpr int OFF = QFmt<BITS>::kOff;
   constexpr int EPC = QFmt<BITS>::kEpc;
   __shared__ __align__(16) int8_t aq_s[kMaxSlots * kMaxIDown];
+  __shared__ float rq_m[kMaxSlots][kFfnWaves];
+  __shared__ int rq_c[kMaxSlots][kFfnWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
@@ -1048,14 +1044,19 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
   const int cpr = rowbytes / 16;
   const int S = a.S;
 
-  // ---- slot fields (lane s < S holds slot s's), then the codes ----
+  // ---- slot fields (lane s < S holds slot s's), then every slot's a ----
   const int ls = lane < S ? lane : S - 1;
   const uint8_t *down_l = a.slots[ls].w.down;
   const float *sdown_l = a.slots[ls].w.s_down;
   const float w_l = a.slots[ls].weight;
+  const int ex_l = a.slots[ls].expert;
+  // every slot's a, before anything waits for the slot table (the buffer is
+  // always valid; in a call with no work here it is read and dropped)
+  RqRegs<RQ> rq;
+  rq_load<RQ>(a, rq);
   // given routing: only the slots with work here are written (a slot of
   // another width belongs to that width's call)
-  const bool act_l = GIVEN ? (lane < S && (lane == a.k ? a.has_shared != 0 : a.slots[ls].expert != -1)) : lane < S;
+  const bool act_l = GIVEN ? (lane < S && (lane == a.k ? a.has_shared != 0 : ex_l != -1)) : lane < S;
   const bool comb = GIVEN && a.out != nullptr;
   const float wg_l = (comb && lane < a.k) ? a.w_given[lane] : 0.0f;
   if (GIVEN && __ballot(act_l) == 0) {
@@ -1075,14 +1076,6 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
     }
     return;
   }
-  const int aqsum_l = a.sums[ls];
-  const float sa_l = a.sa[ls];
-  // every slot's codes (S*I bytes), unconditional loads: pieces past the end
-  // re-read the last one
-  const int n16 = S * a.I / 16;
-  uint4 aqv[kAq16];
-#pragma unroll
-  for (int j = 0; j < kAq16; ++j) aqv[j] = ldg16(a.aqf, min(tid + j * kFfnThreads, n16 - 1));
   const uint8_t *dp[kMaxSlots];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s) dp[s] = readlane_p(down_l, s < S ? s : S - 1);
@@ -1110,15 +1103,14 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
     }
   };
   RowBatch b0, b1;
-  load_rows(r0, b0);  // the first down rows of every slot go out right behind the codes
+  load_rows(r0, b0);  // the first down rows of every slot go out right behind a
+  __builtin_amdgcn_sched_barrier(0);  // all of them before a is consumed
+  // (the second batch goes out after the codes: issued here, it made the
+  // kernel slower)
+  int aqsum_l;
+  float sa_l;
+  rq_codes<RQ, GIVEN>(a, rq, ex_l, [](int) { return BITS; }, aq_s, rq_m, rq_c, aqsum_l, sa_l);
 
-  // ---- the codes into LDS ----
-#pragma unroll
-  for (int j = 0; j < kAq16; ++j) {
-    const int i = tid + j * kFfnThreads;
-    if (i < n16) reinterpret_cast<uint4 *>(aq_s)[i] = aqv[j];
-  }
-  __syncthreads();
   if (r0 >= r1) return;
   load_rows(r0 + RB, b1);
 
@@ -1199,12 +1191,13 @@ __global__ __launch_bounds__(kFfnThreads) void down_combine_t1_kernel(DownT1Args
 }
 
 // ---------------------------------------------------------------------------
-// K4 of the mixed-width chain (routing given): the down projection of every
-// slot at its own width (pad[1] of its entry), then the combine. Lane l owns
-// the 32-element units l, l + 64, ... of each slot's rows: a unit is 32 bytes
-// of int8 codes, 16 of int4 and 8 of int2, and meets 32 codes of a in the
-// field order of the slot's width (the requantisation kernel's layout: field
-// groups at their natural positions), so a slot of any width keeps every lane
+// K3 of the mixed-width chain (routing given): the requantisation of every
+// slot at its own width (pad[1] of its entry), the down projection of every
+// slot at that width, then the combine. Lane l owns the 32-element units l,
+// l + 64, ... of each slot's rows: a unit is 32 bytes of int8 codes, 16 of
+// int4 and 8 of int2, and meets 32 codes of a in the field order of the
+// slot's width (field groups at their natural positions, as rq_codes writes
+// them), so a slot of any width keeps every lane
 // busy. The loads are the same for every width -- one 16-byte piece per unit
 // (two when the call has int8 slots) at a per-slot offset, an int2 unit's 8
 // bytes being one half of its piece -- and only the dot product branches on
@@ -1227,6 +1220,8 @@ template <int MAXB, int JU>
 __global__ __launch_bounds__(kFfnThreads) void down_mixed_t1_kernel(DownT1Args a) {
   constexpr int NP = MAXB == 8 ? 2 : 1;  // 16-byte pieces loaded per unit
   __shared__ __align__(16) int8_t aq_s[kMaxSlots * kMaxIDown];
+  __shared__ float rq_m[kMaxSlots][kFfnWaves];
+  __shared__ int rq_c[kMaxSlots][kFfnWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (MOE_WAVE - 1);
   const int wave = tid >> 6;
@@ -1236,12 +1231,17 @@ __global__ __launch_bounds__(kFfnThreads) void down_mixed_t1_kernel(DownT1Args a
   const int S = a.S;
   const int nu = a.I / 32;  // units per row
 
-  // ---- slot fields (lane s < S holds slot s's), then the codes ----
+  // ---- slot fields (lane s < S holds slot s's), then every slot's a ----
   const int ls = lane < S ? lane : S - 1;
   const uint8_t *down_l = a.slots[ls].w.down;
   const float *sdown_l = a.slots[ls].w.s_down;
   const int bits_l = a.slots[ls].pad[1];
-  const bool act_l = lane < S && (lane == a.k ? a.has_shared != 0 : a.slots[ls].expert != -1);
+  const int ex_l = a.slots[ls].expert;
+  // every slot's a, before anything waits for the slot table (the chain runs
+  // for I <= 2048: one float4 of each slot per thread)
+  RqRegs<1> rq;
+  rq_load<1>(a, rq);
+  const bool act_l = lane < S && (lane == a.k ? a.has_shared != 0 : ex_l != -1);
   const bool comb = a.out != nullptr;
   const float wg_l = (comb && lane < a.k) ? a.w_given[lane] : 0.0f;
   if (__ballot(act_l) == 0) {
@@ -1259,12 +1259,6 @@ __global__ __launch_bounds__(kFfnThreads) void down_mixed_t1_kernel(DownT1Args a
     }
     return;
   }
-  const int aqsum_l = a.sums[ls];
-  const float sa_l = a.sa[ls];
-  const int n16 = S * a.I / 16;
-  uint4 aqv[kAq16];
-#pragma unroll
-  for (int j = 0; j < kAq16; ++j) aqv[j] = ldg16(a.aqf, min(tid + j * kFfnThreads, n16 - 1));
   const uint8_t *dp[kMaxSlots];
   int bits[kMaxSlots], rowb[kMaxSlots];
 #pragma unroll
@@ -1303,15 +1297,18 @@ __global__ __launch_bounds__(kFfnThreads) void down_mixed_t1_kernel(DownT1Args a
     bt.sd = gptr(sdown_l)[r];
   };
   RowBatch b0, b1;
-  load_rows(r0, b0);  // the first down rows of every slot go out right behind the codes
-
-  // ---- the codes into LDS ----
-#pragma unroll
-  for (int j = 0; j < kAq16; ++j) {
-    const int i = tid + j * kFfnThreads;
-    if (i < n16) reinterpret_cast<uint4 *>(aq_s)[i] = aqv[j];
-  }
-  __syncthreads();
+  load_rows(r0, b0);  // the first down rows of every slot go out right behind a
+  __builtin_amdgcn_sched_barrier(0);  // all of them before a is consumed
+  // every slot's codes at its own width (a slot without work: zero codes)
+  int aqsum_l;
+  float sa_l;
+  rq_codes<1, true>(
+      a, rq, ex_l,
+      [&](int s) {
+        const int b = __builtin_amdgcn_readlane(bits_l, s);
+        return (b == 8 || b == 2) ? b : 4;
+      },
+      aq_s, rq_m, rq_c, aqsum_l, sa_l);
   if (r0 >= r1) return;
   load_rows(r0 + 1, b1);
 
@@ -1411,10 +1408,16 @@ moe_status launch_gu(moe_ctx *ctx, hipStream_t stream, const GateUpT1Args &g, in
   MOE_CHECK_LAUNCH("gateup_t1_kernel");
   return MOE_OK;
 }
+// the down kernel with the requantisation of its launch: one float4 of each
+// slot's a per thread up to I = 2048, two above (I <= 4096)
 template <int BITS, int JD, int RB, bool GIVEN = false>
 moe_status launch_dn(moe_ctx *ctx, hipStream_t stream, const DownT1Args &d, int nwg) {
-  moe_launch_on(ctx, stream, MOE_STAGE_DOWN, down_combine_t1_kernel<BITS, JD, RB, GIVEN>, dim3(nwg), dim3(kFfnThreads),
-                d);
+  if (d.I / 4 <= kFfnThreads)
+    moe_launch_on(ctx, stream, MOE_STAGE_DOWN, down_combine_t1_kernel<BITS, JD, RB, GIVEN, 1>, dim3(nwg),
+                  dim3(kFfnThreads), d);
+  else
+    moe_launch_on(ctx, stream, MOE_STAGE_DOWN, down_combine_t1_kernel<BITS, JD, RB, GIVEN, 2>, dim3(nwg),
+                  dim3(kFfnThreads), d);
   MOE_CHECK_LAUNCH("down_combine_t1_kernel");
   return MOE_OK;
 }
@@ -1446,7 +1449,7 @@ namespace {
 // caller did not ask for.
 struct T1LayerLayout {
   int ks;
-  size_t o_part, o_slots, o_A, o_aq, o_sum, o_sa, o_idx, o_w, o_xq, o_sx, o_y, size;
+  size_t o_part, o_slots, o_A, o_idx, o_w, o_xq, o_sx, o_y, size;
 };
 T1LayerLayout t1_layer_layout(const moe_ctx *ctx, int E, int k, int S, bool logits_in, int H, int I) {
   T1LayerLayout l;
@@ -1461,9 +1464,6 @@ T1LayerLayout t1_layer_layout(const moe_ctx *ctx, int E, int k, int S, bool logi
   l.o_part = m.take(sizeof(float) * l.ks * E);
   l.o_slots = m.take(sizeof(SlotEntry) * kMaxSlots);
   l.o_A = m.take(sizeof(float) * S * I);
-  l.o_aq = m.take((size_t)S * I);
-  l.o_sum = m.take(4 * S);
-  l.o_sa = m.take(4 * S);
   l.o_idx = m.take(4 * k);
   l.o_w = m.take(4 * k);
   l.o_xq = m.take(H);
@@ -1487,7 +1487,7 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
   const T1LayerLayout l = t1_layer_layout(ctx, E, k, S, logits != nullptr, H, I);
   const int ks = l.ks;
   const int kl = H / ks;
-  const size_t o_part = l.o_part, o_slots = l.o_slots, o_A = l.o_A, o_aq = l.o_aq, o_sum = l.o_sum, o_sa = l.o_sa,
+  const size_t o_part = l.o_part, o_slots = l.o_slots, o_A = l.o_A,
                o_idx = l.o_idx, o_w = l.o_w, o_xq = l.o_xq, o_sx = l.o_sx, o_y = l.o_y;
   void *scr = nullptr;
   moe_status st = moe_scratch(ctx, l.size, &scr);
@@ -1540,29 +1540,9 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
   }
   if (st) return st;
 
-  RequantT1Args q{};
-  q.A = g.A;
-  q.slots = slots;
-  q.k = k;
-  q.I = I;
-  q.S = S;
-  q.aqf = reinterpret_cast<uint32_t *>(base + o_aq);
-  q.sums = reinterpret_cast<int *>(base + o_sum);
-  q.sa = reinterpret_cast<float *>(base + o_sa);
-  q.dbg = ctx->dbg;
-  q.dbg_on = ctx->dbg_on ? 1 : 0;
-  switch (bits) {
-    case 4: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<4>, dim3(S), dim3(kRqThreads), q); break;
-    case 8: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<8>, dim3(S), dim3(kRqThreads), q); break;
-    default: moe_launch(ctx, MOE_STAGE_REQUANT, requant_t1_kernel<2>, dim3(S), dim3(kRqThreads), q); break;
-  }
-  MOE_CHECK_LAUNCH("requant_t1_kernel");
-
   DownT1Args d{};
+  d.A = g.A;
   d.slots = slots;
-  d.aqf = q.aqf;
-  d.sums = q.sums;
-  d.sa = q.sa;
   d.H = H; d.I = I; d.S = S; d.k = k;
   d.has_shared = shared ? 1 : 0;
   d.y = y_slots;
@@ -1579,8 +1559,8 @@ moe_status launch_layer_t1(moe_ctx *ctx, int bits, const moe_router_cfg *cfg, co
 namespace {
 
 // The expert FFN of one token with its routing given (ids, activation codes
-// and scale from the caller): the gate/up, requantisation and down kernels
-// above without the router and the combine, enqueued on `stream` with its
+// and scale from the caller): the gate/up kernel and the requantisation with
+// the down kernel above, without the router and the combine, enqueued on `stream` with its
 // scratch at `base` (t1_chain_bytes). Slot j's output goes to y_slots row j
 // for every valid id whose expert has this width (all of them without a
 // width filter), the shared expert's to row k; the other rows are left as
@@ -1588,7 +1568,7 @@ namespace {
 // the bad-index flag and gives no output (the later copy of a repeated id).
 size_t t1_chain_bytes(int I, int S) {
   size_t off = 0;
-  for (size_t b : {sizeof(SlotEntry) * kMaxSlots, sizeof(float) * S * I, (size_t)S * I, (size_t)4 * S, (size_t)4 * S})
+  for (size_t b : {sizeof(SlotEntry) * kMaxSlots, sizeof(float) * S * I})
     off = moe_round_up(off + b, 256);
   return off;
 }
@@ -1604,8 +1584,7 @@ moe_status t1_chain(moe_ctx *ctx, hipStream_t stream, char *base, int bits, cons
     off = moe_round_up(off + bytes, 256);
     return o;
   };
-  const size_t o_slots = take(sizeof(SlotEntry) * kMaxSlots), o_A = take(sizeof(float) * S * I),
-               o_aq = take((size_t)S * I), o_sum = take(4 * S), o_sa = take(4 * S);
+  const size_t o_slots = take(sizeof(SlotEntry) * kMaxSlots), o_A = take(sizeof(float) * S * I);
   SlotEntry *slots = reinterpret_cast<SlotEntry *>(base + o_slots);
 
   GateUpT1Args g{};
@@ -1634,30 +1613,9 @@ moe_status t1_chain(moe_ctx *ctx, hipStream_t stream, char *base, int bits, cons
   }
   if (st) return st;
 
-  RequantT1Args q{};
-  q.A = g.A;
-  q.slots = slots;
-  q.k = k;
-  q.I = I;
-  q.S = S;
-  q.aqf = reinterpret_cast<uint32_t *>(base + o_aq);
-  q.sums = reinterpret_cast<int *>(base + o_sum);
-  q.sa = reinterpret_cast<float *>(base + o_sa);
-  q.dbg = ctx->dbg;
-  q.dbg_on = ctx->dbg_on ? 1 : 0;
-  q.given = 1;
-  switch (bits) {
-    case 4: moe_launch_on(ctx, stream, MOE_STAGE_REQUANT, requant_t1_kernel<4>, dim3(S), dim3(kRqThreads), q); break;
-    case 8: moe_launch_on(ctx, stream, MOE_STAGE_REQUANT, requant_t1_kernel<8>, dim3(S), dim3(kRqThreads), q); break;
-    default: moe_launch_on(ctx, stream, MOE_STAGE_REQUANT, requant_t1_kernel<2>, dim3(S), dim3(kRqThreads), q); break;
-  }
-  MOE_CHECK_LAUNCH("requant_t1_kernel");
-
   DownT1Args d{};
+  d.A = g.A;
   d.slots = slots;
-  d.aqf = q.aqf;
-  d.sums = q.sums;
-  d.sa = q.sa;
   d.H = H; d.I = I; d.S = S; d.k = k;
   d.has_shared = shared ? 1 : 0;
   d.y = y_slots;
@@ -1694,17 +1652,16 @@ moe_status launch_ffn_t1(moe_ctx *ctx, int bits, const moe_expert_w *experts, co
 // the narrower widths' chains on a second stream beside the first was
 // slower: the fork and join cost more than the overlap gained.
 namespace {
-// Every width of a one-token mixed layer in one chain of three kernels: the
-// width-split gate/up, the requantisation of every slot at its width, the
-// down projection of every slot at its width with the combine (when out).
+// Every width of a one-token mixed layer in one chain of two kernels: the
+// width-split gate/up, then the requantisation and down projection of every
+// slot at its width with the combine (when out).
 moe_status t1_mixed_chain(moe_ctx *ctx, char *base, int mask, int shared_bits, const moe_expert_w *experts,
                           const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
                           const float *xf, const int32_t *topk_idx, const float *topk_w, int H, int I, int E, int k,
                           float *y_slots, float *out) {
   const int S = k + (shared ? 1 : 0);
   MoeLayout m;
-  const size_t o_slots = m.take(sizeof(SlotEntry) * kMaxSlots), o_A = m.take(sizeof(float) * S * I),
-               o_aq = m.take((size_t)S * I), o_sum = m.take(4 * (size_t)S), o_sa = m.take(4 * (size_t)S);
+  const size_t o_slots = m.take(sizeof(SlotEntry) * kMaxSlots), o_A = m.take(sizeof(float) * S * I);
   SlotEntry *slots = reinterpret_cast<SlotEntry *>(base + o_slots);
   GateUpT1Args g{};
   g.E = E; g.k = k; g.ks = 1;
@@ -1729,25 +1686,9 @@ moe_status t1_mixed_chain(moe_ctx *ctx, char *base, int mask, int shared_bits, c
     moe_launch(ctx, MOE_STAGE_GATEUP, gateup_mixed_t1_kernel<false>, dim3(nwg), dim3(kFfnThreads), g, mask,
                shared_bits);
   MOE_CHECK_LAUNCH("gateup_mixed_t1_kernel");
-  RequantT1Args q{};
-  q.A = g.A;
-  q.slots = slots;
-  q.k = k;
-  q.I = I;
-  q.S = S;
-  q.aqf = reinterpret_cast<uint32_t *>(base + o_aq);
-  q.sums = reinterpret_cast<int *>(base + o_sum);
-  q.sa = reinterpret_cast<float *>(base + o_sa);
-  q.dbg = ctx->dbg;
-  q.dbg_on = ctx->dbg_on ? 1 : 0;
-  q.given = 1;
-  moe_launch(ctx, MOE_STAGE_REQUANT, requant_mixed_t1_kernel, dim3(S), dim3(kRqThreads), q);
-  MOE_CHECK_LAUNCH("requant_mixed_t1_kernel");
   DownT1Args d{};
+  d.A = g.A;
   d.slots = slots;
-  d.aqf = q.aqf;
-  d.sums = q.sums;
-  d.sa = q.sa;
   d.H = H; d.I = I; d.S = S; d.k = k;
   d.has_shared = shared ? 1 : 0;
   d.y = y_slots;

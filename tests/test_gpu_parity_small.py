@@ -681,8 +681,8 @@ def test_layer_tiny_end_to_end(moe, ctx, orc, syn, bits):
 @pytest.mark.parametrize("bits", [4, 8, 2])
 @pytest.mark.parametrize("H,I,E,k,shared", [(128, 64, 8, 2, True), (512, 192, 16, 8, True), (256, 128, 8, 3, False)])
 def test_layer_t1_fused_intermediates(moe, ctx, orc, syn, bits, H, I, E, k, shared):
-    """One token through moe_layer_forward (router+top-k+quant, gate/up with
-    last-wave requantisation, down fused with the combine): every captured
+    """One token through moe_layer_forward (router+top-k+quant, gate/up, the
+    requantisation fused with down and the combine): every captured
     intermediate bit-exact against the oracle, and the output bit-identical to
     the per-step entry points."""
     from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
