@@ -738,3 +738,49 @@ def test_layer_t1_fused_intermediates(moe, ctx, orc, syn, bits, H, I, E, k, shar
         torch.cuda.synchronize()
         assert np.array_equal(host(steps["out"]), fused["out"])
         assert np.array_equal(host(steps["idx"]), fused["idx"])
+
+
+def _t1_launches(ctx, fn):
+    """Kernel launches per stage of one call of fn (the library's timing)."""
+    torch.cuda.synchronize()
+    ctx.enable_timing(True)
+    try:
+        fn()
+        torch.cuda.synchronize()
+        tm = ctx.read_timing()
+    finally:
+        ctx.enable_timing(False)
+    return {name: n for name, (_, n) in tm.items()}
+
+
+@pytest.mark.parametrize("I", [2112, 4096])
+def test_layer_t1_long_intermediate_int2(moe, ctx, orc, syn, I):
+    """Past an intermediate of 2048 the single-token path takes int2 layers
+    without a shared expert only; its down launch then requantises two float4
+    of each slot's a per thread (the second partly filled at 2112). Every
+    intermediate bit-exact, and the call is the single-token one (no bucketing,
+    one gate/up and one down launch)."""
+    test_layer_t1_fused_intermediates(moe, ctx, orc, syn, 2, 256, I, 8, 2, False)
+    from quantized_moe_expert_sigmoid_amd.layer import MoeLayer
+    L = MoeLayer(ctx, 256, I, 8, 2, bits=2, has_shared=False)
+    for e in range(8):
+        L.set_expert_fp32(e, *syn.expert_weights(7, 0, e, 256, I))
+    L.set_router(syn.router_weights(7, 0, 8, 256), syn.router_bias(7, 0, 8))
+    x = dev(syn.hidden(7, 1, 256))
+    n = _t1_launches(ctx, lambda: L.forward(x))
+    assert n["bucket"] == 0 and n["gateup"] == 1 and n["down"] == 1 and n["requant"] == 0, n
+
+
+@pytest.mark.parametrize("I", [2112, 4096])
+def test_ffn_one_token_long_intermediate_int2(moe, ctx, orc, syn, I):
+    """The per-step FFN of one token (routing given) on the single-token
+    kernels past an intermediate of 2048 (int2, no shared expert): every
+    intermediate bit-exact, with and without dropped slots."""
+    test_ffn_one_token(moe, ctx, orc, syn, 2, 256, I, 8, 2, False)
+    blocks, _, _, _ = make_experts(moe, orc, syn, 2, 256, I, 8, seed=97)
+    xq_o, sx_o = orc.quantize_act(syn.hidden(98, 1, 256))
+    y = torch.zeros((1, 3, 256), dtype=torch.float32, device="cuda")
+    idx = dev(np.array([[1, 6]], np.int32))
+    n = _t1_launches(ctx, lambda: moe.moe_expert_ffn_q2(ctx, blocks.table, None, None, dev(xq_o), dev(sx_o), idx,
+                                                         256, I, 8, y))
+    assert n["bucket"] == 0 and n["gateup"] == 1 and n["down"] == 1 and n["requant"] == 0, n
