@@ -894,7 +894,7 @@ __device__ __forceinline__ uint32_t field_order(uint32_t w, int lane) {
 // ---------------------------------------------------------------------------
 struct DownT1Args {
   const SlotEntry *slots;
-  const float *A;  // [S][I] the SwiGLU intermediate (a slot without work here: never written, never used)
+  const float *A;  // [S][I] the SwiGLU intermediate (a slot without work here was never written: zero codes)
   int H, I, S, k, has_shared;
   float *y;    // [S][H] (the token's y_slots; slot stride H)
   float *out;  // [H]; given routing: nullable (no combine)
