@@ -1659,6 +1659,9 @@ moe_status t1_mixed_chain(moe_ctx *ctx, char *base, int mask, int shared_bits, c
                           const moe_expert_w *shared, const uint8_t *expert_bits, const int8_t *xq, const float *sx,
                           const float *xf, const int32_t *topk_idx, const float *topk_w, int H, int I, int E, int k,
                           float *y_slots, float *out) {
+  // the down kernel's requantisation holds one float4 of each slot's a per
+  // thread (t1_mixed_chain_ok admits intermediates up to 2048 only)
+  if (I / 4 > kFfnThreads) return moe_fail(MOE_EINVAL, "mixed single-token chain: intermediate %d above 2048", I);
   const int S = k + (shared ? 1 : 0);
   MoeLayout m;
   const size_t o_slots = m.take(sizeof(SlotEntry) * kMaxSlots), o_A = m.take(sizeof(float) * S * I);
